@@ -1,0 +1,256 @@
+// C-ABI entry points: argument checks (all before any launch), workspace
+// carving and path dispatch.  Declarations and contracts: include/adapter_apply.h.
+#include "../../include/adapter_apply.h"
+#include "common.hpp"
+
+using namespace aa;
+
+namespace {
+
+// Auto path: MFMA prefill once slots carry long token runs.
+constexpr int32_t kPrefillMinTokens = 512;
+constexpr int32_t kPrefillMinPerSlot = 64;
+
+inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline lora_status_t launched(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_E_LAUNCH; }
+
+lora_status_t check_sizes(int32_t T, int32_t S, int32_t L, int32_t R, int32_t dtype) {
+    if (dtype != LORA_DT_F32 && dtype != LORA_DT_BF16) return LORA_E_DTYPE;
+    if (T < 0 || L < 1 || L > LORA_MAX_SLOTS) return LORA_E_SHAPE;
+    if (R < 1 || R > LORA_MAX_RANK) return LORA_E_RANK;
+    if (S < 1 || S > LORA_MAX_SLICES) return LORA_E_SLICES;
+    if (R % (dtype == LORA_DT_BF16 ? 8 : 4)) return LORA_E_ALIGN;
+    // decode tiles index grid.y / grid.z
+    if (max_tiles(T, L, kDecTile) > 65535) return LORA_E_SHAPE;
+    return LORA_OK;
+}
+
+lora_status_t check_k(int32_t K, int64_t ldx) {
+    if (K < 1 || ldx < K) return LORA_E_SHAPE;
+    if (K % 8 || ldx % 8) return LORA_E_ALIGN;
+    return LORA_OK;
+}
+
+lora_status_t check_n(const int64_t *N, int32_t S, int64_t ldy, int64_t y_col_offset,
+                      int64_t *total) {
+    if (!N) return LORA_E_NULL;
+    int64_t t = 0;
+    for (int s = 0; s < S; ++s) {
+        if (N[s] < 1) return LORA_E_SHAPE;
+        if (N[s] % 4) return LORA_E_ALIGN;
+        t += N[s];
+    }
+    if (y_col_offset < 0 || ldy < y_col_offset + t) return LORA_E_SHAPE;
+    if (ldy % 4 || y_col_offset % 4) return LORA_E_ALIGN;
+    *total = t;
+    return LORA_OK;
+}
+
+lora_status_t check_ptrs(const void *const *P, int32_t S) {
+    if (!P) return LORA_E_NULL;
+    for (int s = 0; s < S; ++s) {
+        if (!P[s]) return LORA_E_NULL;
+        if (!al(P[s], 16)) return LORA_E_ALIGN;
+    }
+    return LORA_OK;
+}
+
+lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
+                          int *use_prefill) {
+    const bool can_prefill = dtype == LORA_DT_BF16 && R % 16 == 0;
+    if (path == LORA_PATH_DECODE) { *use_prefill = 0; return LORA_OK; }
+    if (path == LORA_PATH_PREFILL) {
+        if (!can_prefill) return LORA_E_PATH;
+        *use_prefill = 1;
+        return LORA_OK;
+    }
+    if (path != LORA_PATH_AUTO) return LORA_E_PATH;
+    const int32_t slots = T < L ? T : L;
+    *use_prefill = can_prefill && T >= kPrefillMinTokens && slots > 0 &&
+                   T / slots >= kPrefillMinPerSlot;
+    return LORA_OK;
+}
+
+lora_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (!ws) return LORA_E_NULL;
+    if (!al(ws, 256)) return LORA_E_ALIGN;
+    if (ws_bytes < need) return LORA_E_WORKSPACE;
+    return LORA_OK;
+}
+
+Slices make_slices(const void *const *A, const void *const *B, const int64_t *N, int32_t S,
+                   int64_t y_col_offset) {
+    Slices sl{};
+    int64_t off = y_col_offset;
+    for (int s = 0; s < S; ++s) {
+        sl.a[s] = A ? A[s] : nullptr;
+        sl.b[s] = B ? B[s] : nullptr;
+        sl.n[s] = N ? N[s] : 0;
+        sl.off[s] = off;
+        off += sl.n[s];
+    }
+    for (int s = S; s <= kMaxSlices; ++s) sl.off[s] = off;
+    return sl;
+}
+
+#define CHECK(expr)                          \
+    do {                                     \
+        lora_status_t _st = (expr);          \
+        if (_st != LORA_OK) return _st;      \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_status_string(lora_status_t s) {
+    switch (s) {
+        case LORA_OK: return "ok";
+        case LORA_E_NULL: return "a required pointer is NULL";
+        case LORA_E_SHAPE: return "a size is out of range or a leading dimension is too small";
+        case LORA_E_DTYPE: return "unknown dtype";
+        case LORA_E_RANK: return "rank outside [1, 512]";
+        case LORA_E_SLICES: return "slice count outside [1, 8]";
+        case LORA_E_WORKSPACE: return "workspace smaller than lora_workspace_size()";
+        case LORA_E_ALIGN: return "pointer or stride alignment not met";
+        case LORA_E_PATH: return "the requested path cannot run these arguments";
+        case LORA_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        default: return "unknown status";
+    }
+}
+
+lora_status_t lora_workspace_size(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L,
+                                  size_t *bytes) {
+    if (!bytes) return LORA_E_NULL;
+    CHECK(check_sizes(T, S, L, R, LORA_DT_F32));
+    if (K < 1) return LORA_E_SHAPE;
+    *bytes = ws_layout(T, K, S, R, L).end;
+    return LORA_OK;
+}
+
+lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return LORA_E_NULL;
+    if (!al(ws, 256)) return LORA_E_ALIGN;
+    return launched(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+lora_status_t lora_segment_layout(int32_t T, int32_t L, lora_segment_layout_t *out) {
+    if (!out) return LORA_E_NULL;
+    if (T < 0 || L < 1 || L > LORA_MAX_SLOTS) return LORA_E_SHAPE;
+    const SegLayout l = seg_layout(T, L);
+    out->header = (int64_t)l.header;
+    out->slot_start = (int64_t)l.slot_start;
+    out->perm = (int64_t)l.perm;
+    out->tiles_decode = (int64_t)l.tiles_dec;
+    out->tiles_prefill = (int64_t)l.tiles_pre;
+    out->tile_decode_tokens = kDecTile;
+    out->tile_prefill_tokens = kPreTile;
+    return LORA_OK;
+}
+
+lora_status_t lora_build_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T,
+                                  int32_t L, int32_t R, void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0 || L < 1 || L > LORA_MAX_SLOTS) return LORA_E_SHAPE;
+    if (R < 1 || R > LORA_MAX_RANK) return LORA_E_RANK;
+    if (max_tiles(T, L, kDecTile) > 65535) return LORA_E_SHAPE;
+    if (T > 0 && !idx) return LORA_E_NULL;
+    const SegLayout l = seg_layout(T, L);
+    CHECK(check_ws(ws, ws_bytes, l.end));
+    return launched(launch_segments(idx, slot_rank, T, L, R, seg_ptrs(ws, l),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int32_t K,
+                          const void *const *A, int32_t S, int32_t L, int32_t R,
+                          const int32_t *idx, const int32_t *slot_rank, int32_t dtype,
+                          int32_t path, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_sizes(T, S, L, R, dtype));
+    CHECK(check_k(K, ldx));
+    int use_prefill = 0;
+    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (T == 0) return LORA_OK;
+    if (!buf || !x || !idx) return LORA_E_NULL;
+    CHECK(check_ptrs(A, S));
+    if (!al(buf, 16) || !al(x, 16)) return LORA_E_ALIGN;
+    const WsLayout wl = ws_layout(T, K, S, R, L);
+    CHECK(check_ws(ws, ws_bytes, wl.end));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const SegPtrs seg = seg_ptrs(ws, wl.seg);
+    const Slices sl = make_slices(A, nullptr, nullptr, S, 0);
+    if (!(flags & LORA_FLAG_SEGMENTS_READY))
+        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
+    if (!(flags & LORA_FLAG_ACTIVE_ONLY))
+        CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
+    if (use_prefill)
+        return launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st));
+    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+    return launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
+                                      wl.n_kchunks, buf, st));
+}
+
+lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const float *buf,
+                          int32_t T, const void *const *B, const int64_t *N, int32_t S,
+                          int32_t L, int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                          const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                          void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_sizes(T, S, L, R, dtype));
+    int64_t ntot = 0;
+    CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
+    int use_prefill = 0;
+    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (T == 0) return LORA_OK;
+    if (!y || !buf || !idx || !scale) return LORA_E_NULL;
+    CHECK(check_ptrs(B, S));
+    if (!al(y, 16) || !al(buf, 16)) return LORA_E_ALIGN;
+    const SegLayout sgl = seg_layout(T, L);
+    CHECK(check_ws(ws, ws_bytes, sgl.end));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const SegPtrs seg = seg_ptrs(ws, sgl);
+    const Slices sl = make_slices(nullptr, B, N, S, y_col_offset);
+    if (!(flags & LORA_FLAG_SEGMENTS_READY))
+        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
+    if (use_prefill)
+        return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+    return launched(launch_dec_expand(dtype, y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+}
+
+lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                                int64_t ldx, int32_t T, int32_t K, const void *const *A,
+                                const void *const *B, const int64_t *N, int32_t S, int32_t L,
+                                int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                                const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_sizes(T, S, L, R, dtype));
+    CHECK(check_k(K, ldx));
+    int64_t ntot = 0;
+    CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
+    int use_prefill = 0;
+    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (T == 0) return LORA_OK;
+    if (!y || !x || !idx || !scale) return LORA_E_NULL;
+    CHECK(check_ptrs(A, S));
+    CHECK(check_ptrs(B, S));
+    if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
+    const WsLayout wl = ws_layout(T, K, S, R, L);
+    CHECK(check_ws(ws, ws_bytes, wl.end));
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const SegPtrs seg = seg_ptrs(ws, wl.seg);
+    const Slices sl = make_slices(A, B, N, S, y_col_offset);
+    float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
+    if (!(flags & LORA_FLAG_SEGMENTS_READY))
+        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
+    if (use_prefill) {
+        CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st)));
+        return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+    }
+    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+    CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
+                                     wl.n_kchunks, buf, st)));
+    return launched(launch_dec_expand(dtype, y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Shared definitions of the HIP library: storage-type helpers, the
+// workspace layout and the kernel argument blocks.  gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace aa {
+
+constexpr int kWave = 64;
+constexpr int kMaxSlices = 8;
+constexpr int kMaxRank = 512;
+constexpr int kMaxSlots = 1024;
+
+// Tile sizes (tokens of one slot handled together).
+constexpr int kDecTile = 32;   // decode (VALU) path: one token per lane half
+constexpr int kPreTile = 64;   // prefill (MFMA) path: two 32-row MFMA blocks
+
+// Decode shrink: K columns per work-group chunk and rank rows per work-group.
+constexpr int kDecKc = 256;    // 4 waves x 64 columns
+constexpr int kDecRows = 16;   // rows of the (slice, rank) space per work-group
+// Arrival counters per decode tile: one per row group, enough for S*R <= 8*512.
+constexpr int kRgStride = kMaxSlices * kMaxRank / kDecRows;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (all offsets 256-byte aligned).
+// ---------------------------------------------------------------------------
+struct SegLayout {
+    size_t header;        // int32[4]: active, invalid, decode tiles, prefill tiles
+    size_t slot_start;    // int32[L+1]
+    size_t perm;          // int32[T]
+    size_t tiles_dec;     // int4[max_tiles_dec]: slot, begin, end, 0
+    size_t tiles_pre;     // int4[max_tiles_pre]
+    size_t counters;      // int32[max_tiles_dec][kRgStride]: split-K arrival counters
+    size_t end;
+    int32_t max_tiles_dec;
+    int32_t max_tiles_pre;
+    int32_t n_counters;
+};
+
+struct WsLayout {
+    SegLayout seg;
+    size_t partial;       // fp32 [n_kchunks][T][S*R]
+    size_t buf;           // fp32 [S][T][R]
+    size_t end;
+    int32_t n_kchunks;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline int32_t max_tiles(int32_t T, int32_t L, int32_t tile) {
+    // sum over slots of ceil(c_s / tile) <= T / tile + (number of non-empty slots)
+    int64_t m = (int64_t)T / tile + (T < L ? T : L) + 1;
+    return (int32_t)m;
+}
+
+inline int32_t row_groups(int32_t S, int32_t R) {
+    return (S * R + kDecRows - 1) / kDecRows;
+}
+
+inline SegLayout seg_layout(int32_t T, int32_t L) {
+    SegLayout l{};
+    size_t o = 0;
+    l.header = o;     o = align256(o + 16 * sizeof(int32_t));
+    l.slot_start = o; o = align256(o + sizeof(int32_t) * (size_t)(L + 1));
+    l.perm = o;       o = align256(o + sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    l.max_tiles_dec = max_tiles(T, L, kDecTile);
+    l.max_tiles_pre = max_tiles(T, L, kPreTile);
+    l.tiles_dec = o;  o = align256(o + 16 * (size_t)l.max_tiles_dec);
+    l.tiles_pre = o;  o = align256(o + 16 * (size_t)l.max_tiles_pre);
+    l.n_counters = l.max_tiles_dec * kRgStride;
+    l.counters = o;   o = align256(o + sizeof(int32_t) * (size_t)l.n_counters);
+    l.end = o;
+    return l;
+}
+
+inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L) {
+    WsLayout w{};
+    w.seg = seg_layout(T, L);
+    size_t o = w.seg.end;
+    w.n_kchunks = (K + kDecKc - 1) / kDecKc;
+    w.partial = o; o = align256(o + sizeof(float) * (size_t)w.n_kchunks * (size_t)T * S * R);
+    w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
+    w.end = o;
+    return w;
+}
+
+// Device view of the segments.
+struct SegPtrs {
+    int32_t *header;
+    int32_t *slot_start;
+    int32_t *perm;
+    int4 *tiles_dec;
+    int4 *tiles_pre;
+    int32_t *counters;
+    int32_t max_tiles_dec;
+    int32_t max_tiles_pre;
+    int32_t n_counters;
+};
+
+inline SegPtrs seg_ptrs(void *ws, const SegLayout &l) {
+    char *b = static_cast<char *>(ws);
+    SegPtrs p;
+    p.header = reinterpret_cast<int32_t *>(b + l.header);
+    p.slot_start = reinterpret_cast<int32_t *>(b + l.slot_start);
+    p.perm = reinterpret_cast<int32_t *>(b + l.perm);
+    p.tiles_dec = reinterpret_cast<int4 *>(b + l.tiles_dec);
+    p.tiles_pre = reinterpret_cast<int4 *>(b + l.tiles_pre);
+    p.counters = reinterpret_cast<int32_t *>(b + l.counters);
+    p.max_tiles_dec = l.max_tiles_dec;
+    p.max_tiles_pre = l.max_tiles_pre;
+    p.n_counters = l.n_counters;
+    return p;
+}
+
+// Per-slice pointers and widths passed by value to kernels.
+struct Slices {
+    const void *a[kMaxSlices];   // lora_a [L][R][K]
+    const void *b[kMaxSlices];   // lora_b [L][N_s][R]
+    int64_t n[kMaxSlices];       // N_s
+    int64_t off[kMaxSlices + 1]; // column offset of each slice in y (incl. y_col_offset)
+};
+
+// Launchers (host side), defined next to their kernels.
+hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
+                           int32_t R, const SegPtrs &seg, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+
+hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, int32_t K,
+                             const Slices &sl, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const SegPtrs &seg, float *partial,
+                             int32_t n_kchunks, float *buf, hipStream_t st);
+hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf, int32_t T,
+                             const Slices &sl, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const float *scale, const SegPtrs &seg,
+                             hipStream_t st);
+
+hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
+                             const SegPtrs &seg, float *buf, hipStream_t st);
+hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
+                             const float *scale, const SegPtrs &seg, hipStream_t st);
+
+}  // namespace aa

@@ -1,0 +1,362 @@
+// Decode path: VALU kernels for short per-slot token runs (BGMV regime).
+//
+// Tokens are grouped by slot into tiles of at most 32 (the segment build), so
+// a slot's lora_a / lora_b rows are streamed from HBM once per tile instead of
+// once per token.  No MFMA: dot products use packed bf16 dot instructions
+// (fp32 accumulate) and one cross-lane add.
+//
+// Shrink (buf = x . A^T): work-group = (tile, 256-column K chunk, 16 rows of
+// the slot's (slice, rank) rows).  Lane = (token, column half); each wave owns
+// 64 columns, so every lane holds 32 x values in registers and streams the
+// rank rows from LDS (broadcast reads).  Partial sums of the K chunks go to
+// the workspace; the last work-group to arrive for a (tile, row group) adds
+// them in ascending chunk order (deterministic) and resets its counter.
+//
+// Expand (y += scale * buf . B^T): work-group = (tile, 128 output columns of
+// one slice).  Lane = 2 adjacent columns, waves split the tile's tokens; the
+// lane's B rows live in registers (rank in chunks of 32), buf rows in LDS.
+#include "common.hpp"
+
+namespace aa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerWg = kThreads / kWave;
+constexpr int kColsPerWave = kDecKc / kWavesPerWg;     // 64
+constexpr int kColsPerLane = kColsPerWave / 2;         // 32
+constexpr int kExpCols = 128;                          // columns per expand work-group
+constexpr int kRankChunk = 32;
+
+struct ShrinkArgs {
+    const void *x;
+    int64_t ldx;
+    int32_t T, K, S, L, R, n_kchunks, n_rg;
+    const int32_t *slot_rank;
+    SegPtrs seg;
+    Slices sl;
+    float *partial;   // [n_kchunks][T][S][R]
+    float *buf;       // [S][T][R]
+};
+
+struct ExpandArgs {
+    void *y;
+    int64_t ldy;
+    const float *buf;
+    int32_t T, S, L, R;
+    const int32_t *slot_rank;
+    const float *scale;
+    SegPtrs seg;
+    Slices sl;
+    int32_t chunk_start[kMaxSlices + 1];
+};
+
+template <bool BF16> struct Elt;
+template <> struct Elt<true> {
+    typedef uint16_t T;
+    static constexpr int kPerVec = 8;   // elements per 16-byte vector
+};
+template <> struct Elt<false> {
+    typedef float T;
+    static constexpr int kPerVec = 4;
+};
+
+__device__ __forceinline__ float dot_vec(const uint4 &x, const uint4 &a, float acc, bool) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.x),
+                                          __builtin_bit_cast(bf16x2_t, a.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.y),
+                                          __builtin_bit_cast(bf16x2_t, a.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.z),
+                                          __builtin_bit_cast(bf16x2_t, a.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.w),
+                                          __builtin_bit_cast(bf16x2_t, a.w), acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ float dot_vec(const float4 &x, const float4 &a, float acc, int) {
+    acc = fmaf(x.x, a.x, acc);
+    acc = fmaf(x.y, a.y, acc);
+    acc = fmaf(x.z, a.z, acc);
+    acc = fmaf(x.w, a.w, acc);
+    return acc;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dec_shrink(ShrinkArgs a) {
+    typedef typename Elt<BF16>::T E;
+    typedef typename std::conditional<BF16, uint4, float4>::type V;
+    constexpr int EPV = Elt<BF16>::kPerVec;
+    constexpr int VPL = kColsPerLane / EPV;     // vectors per lane (4 bf16, 8 fp32)
+    constexpr int VPR = kDecKc / EPV;           // vectors per A row chunk
+
+    const int kc = blockIdx.x;
+    const int g = blockIdx.y;
+    const int tile = blockIdx.z;
+    if (tile >= a.seg.header[2]) return;
+    const int4 tl = a.seg.tiles_dec[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    const int SR = a.S * r;
+    const int q0 = g * kDecRows;
+    if (q0 >= SR) return;
+    const int nrows = min(kDecRows, SR - q0);
+    const int k0 = kc * kDecKc;
+
+    __shared__ __attribute__((aligned(16))) E sA[kDecRows][kDecKc];
+    __shared__ float sRed[kWavesPerWg][kDecRows][32];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+    // Stage the rank rows of this chunk (rows past nrows or columns past K are zero).
+    for (int v = tid; v < kDecRows * VPR; v += kThreads) {
+        const int row = v / VPR, cv = v - row * VPR;
+        const int col = k0 + cv * EPV;
+        V val = {};
+        if (row < nrows && col < a.K) {
+            const int q = q0 + row;
+            const int sg = q / r, j = q - sg * r;
+            const E *src = static_cast<const E *>(a.sl.a[sg]) +
+                           (((int64_t)s * a.R + j) * a.K + col);
+            val = *reinterpret_cast<const V *>(src);
+        }
+        *reinterpret_cast<V *>(&sA[row][cv * EPV]) = val;
+    }
+
+    // This lane's 32 columns of its token's x row.
+    const int tok = lane & 31, h = lane >> 5;
+    const int cbase = w * kColsPerWave + h * kColsPerLane;
+    V xv[VPL];
+    {
+        const bool live = tok < ntok;
+        const int t = live ? a.seg.perm[p0 + tok] : 0;
+        const E *xr = static_cast<const E *>(a.x) + (int64_t)t * a.ldx;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const int col = k0 + cbase + v * EPV;
+            V val = {};
+            if (live && col < a.K) val = *reinterpret_cast<const V *>(xr + col);
+            xv[v] = val;
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int row = 0; row < kDecRows; ++row) {
+        if (row < nrows) {
+            const V *ar = reinterpret_cast<const V *>(&sA[row][cbase]);
+            float acc = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) acc = dot_vec(xv[v], ar[v], acc, 0);
+            acc += __shfl_xor(acc, 32);
+            if (h == 0) sRed[w][row][tok] = acc;
+        }
+    }
+    __syncthreads();
+
+    // Combine the four waves' column ranges and store this chunk's partial sums.
+    const int64_t pstride = (int64_t)a.S * a.R;
+    float *part = a.partial + ((int64_t)kc * a.T + p0) * pstride;
+    for (int i = tid; i < ntok * nrows; i += kThreads) {
+        const int tk = i / nrows, row = i - tk * nrows;
+        const float v = ((sRed[0][row][tk] + sRed[1][row][tk]) + sRed[2][row][tk]) + sRed[3][row][tk];
+        const int q = q0 + row;
+        const int sg = q / r, j = q - sg * r;
+        part[(int64_t)tk * pstride + (int64_t)sg * a.R + j] = v;
+    }
+
+    // Last work-group of this (tile, row group) to finish adds the chunks.
+    __threadfence();
+    __syncthreads();
+    int32_t *cnt = a.seg.counters + (int64_t)tile * kRgStride + g;
+    if (tid == 0) s_last = (atomicAdd(cnt, 1) == a.n_kchunks - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int64_t cstride = (int64_t)a.T * pstride;
+    const float *p_all = a.partial + (int64_t)p0 * pstride;
+    for (int i = tid; i < ntok * nrows; i += kThreads) {
+        const int tk = i / nrows, row = i - tk * nrows;
+        const int q = q0 + row;
+        const int sg = q / r, j = q - sg * r;
+        const float *pp = p_all + (int64_t)tk * pstride + (int64_t)sg * a.R + j;
+        float acc = 0.0f;
+        int c = 0;
+        for (; c + 8 <= a.n_kchunks; c += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = pp[(int64_t)(c + u) * cstride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += v[u];
+        }
+        for (; c < a.n_kchunks; ++c) acc += pp[(int64_t)c * cstride];
+        const int t = a.seg.perm[p0 + tk];
+        a.buf[((int64_t)sg * a.T + t) * a.R + j] = acc;
+    }
+    if (tid == 0) *cnt = 0;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dec_expand(ExpandArgs a) {
+    typedef typename Elt<BF16>::T E;
+    constexpr int EPV = Elt<BF16>::kPerVec;
+    constexpr int VPC = kRankChunk / EPV;       // vectors per rank chunk per column
+    constexpr int TOK_PER_WAVE = kDecTile / kWavesPerWg;   // 8
+
+    const int chunk = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= a.seg.header[2]) return;
+    const int4 tl = a.seg.tiles_dec[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    int sg = 0;
+    while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
+    const int64_t Ns = a.sl.n[sg];
+    const int n0 = (chunk - a.chunk_start[sg]) * kExpCols;
+    const float sc = a.scale[s];
+
+    extern __shared__ float sBuf[];   // [kDecTile][rpad]
+    const int rpad = (r + kRankChunk - 1) / kRankChunk * kRankChunk;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kDecTile * rpad; i += kThreads) {
+        const int tk = i / rpad, j = i - tk * rpad;
+        float v = 0.0f;
+        if (tk < ntok && j < r) {
+            const int t = a.seg.perm[p0 + tk];
+            v = a.buf[((int64_t)sg * a.T + t) * a.R + j];
+        }
+        sBuf[i] = v;
+    }
+    __syncthreads();
+
+    const int n = n0 + 2 * lane;
+    const bool col_ok = n < Ns;
+    const E *brow0 = static_cast<const E *>(a.sl.b[sg]) + ((int64_t)s * Ns + (col_ok ? n : 0)) * a.R;
+    const E *brow1 = brow0 + a.R;
+
+    float acc[TOK_PER_WAVE][2];
+#pragma unroll
+    for (int i = 0; i < TOK_PER_WAVE; ++i) acc[i][0] = acc[i][1] = 0.0f;
+
+    for (int j0 = 0; j0 < r; j0 += kRankChunk) {
+        const int nv = min(VPC, (r - j0 + EPV - 1) / EPV);
+        float b0[kRankChunk], b1[kRankChunk];
+#pragma unroll
+        for (int v = 0; v < VPC; ++v) {
+            if (v < nv && col_ok) {
+                if constexpr (BF16) {
+                    const uint4 u0 = *reinterpret_cast<const uint4 *>(brow0 + j0 + v * 8);
+                    const uint4 u1 = *reinterpret_cast<const uint4 *>(brow1 + j0 + v * 8);
+                    const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
+                    const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b0[v * 8 + 2 * e] = bf16_lo(w0[e]);
+                        b0[v * 8 + 2 * e + 1] = bf16_hi(w0[e]);
+                        b1[v * 8 + 2 * e] = bf16_lo(w1[e]);
+                        b1[v * 8 + 2 * e + 1] = bf16_hi(w1[e]);
+                    }
+                } else {
+                    const float4 f0 = *reinterpret_cast<const float4 *>(brow0 + j0 + v * 4);
+                    const float4 f1 = *reinterpret_cast<const float4 *>(brow1 + j0 + v * 4);
+                    b0[v * 4 + 0] = f0.x; b0[v * 4 + 1] = f0.y; b0[v * 4 + 2] = f0.z; b0[v * 4 + 3] = f0.w;
+                    b1[v * 4 + 0] = f1.x; b1[v * 4 + 1] = f1.y; b1[v * 4 + 2] = f1.z; b1[v * 4 + 3] = f1.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) b0[v * EPV + e] = b1[v * EPV + e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TOK_PER_WAVE; ++i) {
+            const int tk = w * TOK_PER_WAVE + i;
+            const float4 *bb = reinterpret_cast<const float4 *>(sBuf + tk * rpad + j0);
+#pragma unroll
+            for (int v4 = 0; v4 < kRankChunk / 4; ++v4) {
+                if (v4 * 4 < nv * EPV) {
+                    const float4 q = bb[v4];
+                    acc[i][0] = fmaf(q.x, b0[v4 * 4 + 0], acc[i][0]);
+                    acc[i][1] = fmaf(q.x, b1[v4 * 4 + 0], acc[i][1]);
+                    acc[i][0] = fmaf(q.y, b0[v4 * 4 + 1], acc[i][0]);
+                    acc[i][1] = fmaf(q.y, b1[v4 * 4 + 1], acc[i][1]);
+                    acc[i][0] = fmaf(q.z, b0[v4 * 4 + 2], acc[i][0]);
+                    acc[i][1] = fmaf(q.z, b1[v4 * 4 + 2], acc[i][1]);
+                    acc[i][0] = fmaf(q.w, b0[v4 * 4 + 3], acc[i][0]);
+                    acc[i][1] = fmaf(q.w, b1[v4 * 4 + 3], acc[i][1]);
+                }
+            }
+        }
+    }
+
+    if (!col_ok) return;
+    const int64_t col = a.sl.off[sg] + n;
+#pragma unroll
+    for (int i = 0; i < TOK_PER_WAVE; ++i) {
+        const int tk = w * TOK_PER_WAVE + i;
+        if (tk < ntok) {
+            const int t = a.seg.perm[p0 + tk];
+            E *yp = static_cast<E *>(a.y) + (int64_t)t * a.ldy + col;
+            if constexpr (BF16) {
+                const uint32_t yv = *reinterpret_cast<const uint32_t *>(yp);
+                const float lo = bf16_lo(yv) + sc * acc[i][0];
+                const float hi = bf16_hi(yv) + sc * acc[i][1];
+                *reinterpret_cast<uint32_t *>(yp) = pack_bf16x2(lo, hi);
+            } else {
+                float2 yv = *reinterpret_cast<const float2 *>(yp);
+                yv.x = yv.x + sc * acc[i][0];
+                yv.y = yv.y + sc * acc[i][1];
+                *reinterpret_cast<float2 *>(yp) = yv;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, int32_t K,
+                             const Slices &sl, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const SegPtrs &seg, float *partial,
+                             int32_t n_kchunks, float *buf, hipStream_t st) {
+    ShrinkArgs a;
+    a.x = x; a.ldx = ldx; a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
+    a.n_kchunks = n_kchunks;
+    a.n_rg = row_groups(S, R);
+    a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.partial = partial; a.buf = buf;
+    dim3 grid(n_kchunks, a.n_rg, seg.max_tiles_dec);
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_dec_shrink<true>, grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_dec_shrink<false>, grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf, int32_t T,
+                             const Slices &sl, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const float *scale, const SegPtrs &seg,
+                             hipStream_t st) {
+    ExpandArgs a;
+    a.y = y; a.ldy = ldy; a.buf = buf; a.T = T; a.S = S; a.L = L; a.R = R;
+    a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
+    int c = 0;
+    for (int s = 0; s < S; ++s) {
+        a.chunk_start[s] = c;
+        c += (int)((sl.n[s] + kExpCols - 1) / kExpCols);
+    }
+    for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
+    const int rpad = (R + kRankChunk - 1) / kRankChunk * kRankChunk;
+    const size_t lds = sizeof(float) * (size_t)kDecTile * rpad;
+    dim3 grid(c, seg.max_tiles_dec);
+    if (lds > 48 * 1024) {
+        const void *fn = dtype == 1 ? reinterpret_cast<const void *>(k_dec_expand<true>)
+                                    : reinterpret_cast<const void *>(k_dec_expand<false>);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_dec_expand<true>, grid, dim3(kThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL(k_dec_expand<false>, grid, dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace aa

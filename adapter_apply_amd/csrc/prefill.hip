@@ -1,0 +1,261 @@
+// Prefill path: MFMA kernels for long per-slot token runs (SGMV regime).
+//
+// Tokens are grouped by slot into tiles of 64 (two 32-row MFMA blocks).  Both
+// halves use v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate).  Operand
+// fragments are read straight from global memory in the MFMA lane layout:
+// lane l supplies row (l % 32) and 8 consecutive k values starting at
+// 8 * (l / 32), one 16-byte load per fragment, identical for both operands.
+// The accumulator layout of a 32x32 block: lane l holds column (l % 32) and
+// rows 8 * (i / 4) + 4 * (l / 32) + (i % 4) for register i = 0..15.
+//
+// Shrink: work-group = (tile, 64 of the S*R buffer columns); each wave a
+// 32 token x 32 column block over the full K.  Writes fp32 buf[s][t][j] for
+// every column (zeros for j >= rank).
+//
+// Expand: work-group = (tile, group of 512 output columns of one slice);
+// each wave owns 128 columns and both token blocks.  The product is formed
+// transposed, D[n][t] = B[n][:] . buf[t][:], so a lane's accumulators are 4
+// consecutive output columns of one token: y is read and written 8 bytes at a
+// time along rows.  Column groups are dealt to the 8 XCDs round-robin so each
+// XCD keeps its slice of lora_b hot in its own L2 across a slot's tiles.
+#include "common.hpp"
+
+namespace aa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kShrinkCols = 64;        // buffer columns per shrink work-group
+constexpr int kExpGroupCols = 512;     // output columns per expand work-group
+constexpr int kExpWaveCols = kExpGroupCols / 4;
+constexpr int kXcds = 8;
+
+struct PreShrinkArgs {
+    const uint16_t *x;
+    int64_t ldx;
+    int32_t T, K, S, L, R, n_cb;
+    const int32_t *slot_rank;
+    SegPtrs seg;
+    Slices sl;
+    float *buf;
+};
+
+struct PreExpandArgs {
+    uint16_t *y;
+    int64_t ldy;
+    const float *buf;
+    int32_t T, S, L, R, n_cg, per_xcd;
+    const int32_t *slot_rank;
+    const float *scale;
+    SegPtrs seg;
+    Slices sl;
+    int32_t group_start[kMaxSlices + 1];
+};
+
+__device__ __forceinline__ bf16x8_t as_frag(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
+    const int cb = blockIdx.x % a.n_cb;
+    const int tile = blockIdx.x / a.n_cb;
+    if (tile >= a.seg.header[3]) return;
+    const int4 tl = a.seg.tiles_pre[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w & 1, wn = w >> 1;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    // Operand rows of this lane.
+    const int trow = wm * 32 + l32;                    // token within tile
+    const bool tok_ok = trow < ntok;
+    const int t_in = tok_ok ? a.seg.perm[p0 + trow] : 0;
+    const uint16_t *xr = a.x + (int64_t)t_in * a.ldx;
+
+    const int col = cb * kShrinkCols + wn * 32 + l32;  // buffer column (slice, rank)
+    const int SRf = a.S * a.R;
+    const int sg = col / a.R, j = col - (col / a.R) * a.R;
+    const bool col_ok = col < SRf && j < r;
+    const uint16_t *ar = col_ok ? static_cast<const uint16_t *>(a.sl.a[sg]) +
+                                      ((int64_t)s * a.R + j) * (int64_t)a.K
+                                : xr;
+
+    floatx16_t acc = {};
+    const int kofs = 8 * half;
+    // Whole block dead (every column past the rank): skip the contraction.
+    const bool any_col = __ballot(col_ok) != 0;
+    if (any_col) {
+        int k0 = 0;
+        for (; k0 + 64 <= a.K; k0 += 64) {
+            uint4 xa[4], aa_[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xa[u] = tok_ok ? *reinterpret_cast<const uint4 *>(xr + k0 + 16 * u + kofs) : make_uint4(0, 0, 0, 0);
+                aa_[u] = col_ok ? *reinterpret_cast<const uint4 *>(ar + k0 + 16 * u + kofs) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xa[u]), as_frag(aa_[u]), acc, 0, 0, 0);
+        }
+        for (; k0 < a.K; k0 += 16) {
+            const int kk = k0 + kofs;
+            const uint4 xa = (tok_ok && kk < a.K) ? *reinterpret_cast<const uint4 *>(xr + kk) : make_uint4(0, 0, 0, 0);
+            const uint4 av = (col_ok && kk < a.K) ? *reinterpret_cast<const uint4 *>(ar + kk) : make_uint4(0, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xa), as_frag(av), acc, 0, 0, 0);
+        }
+    }
+
+    if (col >= SRf) return;
+    // acc[i] belongs to token row 8*(i/4) + 4*half + (i%4) of this wave's block, column col.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = wm * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (row < ntok) {
+            const int t = a.seg.perm[p0 + row];
+            a.buf[((int64_t)sg * a.T + t) * a.R + j] = col_ok ? acc[i] : 0.0f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
+    const int xcd = blockIdx.x % kXcds;
+    const int local = blockIdx.x / kXcds;
+    const int tile = local / a.per_xcd;
+    const int cg = (local - tile * a.per_xcd) * kXcds + xcd;
+    if (cg >= a.n_cg) return;
+    if (tile >= a.seg.header[3]) return;
+    const int4 tl = a.seg.tiles_pre[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    int sg = 0;
+    while (sg + 1 < a.S && cg >= a.group_start[sg + 1]) ++sg;
+    const int64_t Ns = a.sl.n[sg];
+    const float sc = a.scale[s];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int nks = (r + 15) >> 4;                      // rank steps of 16
+    const int nbase = (cg - a.group_start[sg]) * kExpGroupCols + w * kExpWaveCols;
+    if (nbase >= Ns) return;
+
+    // buf fragments (B operand): token l32 of each token block, rank 16*ks + 8*half .. +7.
+    uint4 bfrag[2][8];
+    int trow_t[2];
+    bool trow_ok[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int row = tb * 32 + l32;
+        trow_ok[tb] = row < ntok;
+        trow_t[tb] = trow_ok[tb] ? a.seg.perm[p0 + row] : 0;
+    }
+    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + (int64_t)s * Ns * a.R;
+    uint16_t *ybase = a.y + a.sl.off[sg];
+
+    // Rank handled in passes of up to 128 (8 MFMA k-steps) so fragments stay in
+    // registers; every pass accumulates before the single rounding of y.
+    auto load_bfrag = [&](int kp, int nk) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const float *bp = a.buf + ((int64_t)sg * a.T + trow_t[tb]) * a.R;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                uint4 f = make_uint4(0, 0, 0, 0);
+                const int jj = (kp + ks) * 16 + 8 * half;
+                if (ks < nk && trow_ok[tb]) {
+                    const float4 v0 = *reinterpret_cast<const float4 *>(bp + jj);
+                    const float4 v1 = *reinterpret_cast<const float4 *>(bp + jj + 4);
+                    // entries at or past the rank are zero in a shrink-written buffer,
+                    // but an expand-only caller may leave them arbitrary.
+                    f.x = pack_bf16x2(jj + 0 < r ? v0.x : 0.f, jj + 1 < r ? v0.y : 0.f);
+                    f.y = pack_bf16x2(jj + 2 < r ? v0.z : 0.f, jj + 3 < r ? v0.w : 0.f);
+                    f.z = pack_bf16x2(jj + 4 < r ? v1.x : 0.f, jj + 5 < r ? v1.y : 0.f);
+                    f.w = pack_bf16x2(jj + 6 < r ? v1.z : 0.f, jj + 7 < r ? v1.w : 0.f);
+                }
+                bfrag[tb][ks] = f;
+            }
+        }
+    };
+    const bool one_pass = nks <= 8;
+    if (one_pass) load_bfrag(0, nks);
+
+    for (int nb = 0; nb < kExpWaveCols / 32; ++nb) {
+        const int n0 = nbase + nb * 32;
+        if (n0 >= Ns) break;
+        const int nrow = n0 + l32;                       // A-operand row (output column)
+        const bool n_ok = nrow < Ns;
+        const uint16_t *brow = bbase + (int64_t)(n_ok ? nrow : 0) * a.R;
+        floatx16_t acc[2] = {{}, {}};
+        for (int kp = 0; kp < nks; kp += 8) {
+            const int nk = min(8, nks - kp);
+            if (!one_pass) load_bfrag(kp, nk);
+            uint4 afrag[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                afrag[ks] = (ks < nk && n_ok)
+                                ? *reinterpret_cast<const uint4 *>(brow + (kp + ks) * 16 + 8 * half)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks < nk) {
+                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(afrag[ks]), as_frag(bfrag[0][ks]), acc[0], 0, 0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(afrag[ks]), as_frag(bfrag[1][ks]), acc[1], 0, 0, 0);
+                }
+            }
+        }
+        // Lane holds columns n0 + 8g + 4*half + {0..3} of token l32 in each token block.
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            if (!trow_ok[tb]) continue;
+            uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 8 * g + 4 * half;
+                if (n < Ns) {
+                    uint2 *yp = reinterpret_cast<uint2 *>(yrow + n);
+                    const uint2 yv = *yp;
+                    uint2 o;
+                    o.x = pack_bf16x2(bf16_lo(yv.x) + sc * acc[tb][4 * g + 0],
+                                      bf16_hi(yv.x) + sc * acc[tb][4 * g + 1]);
+                    o.y = pack_bf16x2(bf16_lo(yv.y) + sc * acc[tb][4 * g + 2],
+                                      bf16_hi(yv.y) + sc * acc[tb][4 * g + 3]);
+                    *yp = o;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
+                             const SegPtrs &seg, float *buf, hipStream_t st) {
+    PreShrinkArgs a;
+    a.x = static_cast<const uint16_t *>(x); a.ldx = ldx; a.T = T; a.K = K; a.S = S; a.L = L;
+    a.R = R; a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.buf = buf;
+    a.n_cb = (S * R + kShrinkCols - 1) / kShrinkCols;
+    dim3 grid((unsigned)(a.n_cb * seg.max_tiles_pre));
+    hipLaunchKernelGGL(k_pre_shrink, grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
+                             const float *scale, const SegPtrs &seg, hipStream_t st) {
+    PreExpandArgs a;
+    a.y = static_cast<uint16_t *>(y); a.ldy = ldy; a.buf = buf; a.T = T; a.S = S; a.L = L;
+    a.R = R; a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
+    int c = 0;
+    for (int s = 0; s < S; ++s) {
+        a.group_start[s] = c;
+        c += (int)((sl.n[s] + kExpGroupCols - 1) / kExpGroupCols);
+    }
+    for (int s = S; s <= kMaxSlices; ++s) a.group_start[s] = c;
+    a.n_cg = c;
+    a.per_xcd = (c + kXcds - 1) / kXcds;
+    dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
+    hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace aa

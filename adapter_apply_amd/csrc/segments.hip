@@ -1,0 +1,196 @@
+// Segment build: stable counting sort of the active tokens by adapter slot,
+// plus the per-slot work tiles of the decode and prefill paths.
+//
+// One work-group of 16 waves.  Wave w owns the contiguous token range
+// [w*chunk, (w+1)*chunk).  Pass 1 counts tokens per (wave, slot); a scan over
+// slots and then over waves turns the counts into write cursors; pass 2 walks
+// the same ranges in order and scatters token ids.  Inside a wave, lanes that
+// share a slot are ranked by lane index through ballots, so the result is the
+// stable order for any schedule.
+#include "common.hpp"
+
+namespace aa {
+
+namespace {
+
+constexpr int kSegThreads = 1024;
+constexpr int kSegWaves = kSegThreads / kWave;
+
+__device__ __forceinline__ int slot_of(const int32_t *idx, const int32_t *slot_rank, int32_t L,
+                                       int32_t R, int t, int *invalid) {
+    int v = idx[t];
+    if (v >= L) { *invalid += 1; return -1; }
+    if (v < 0) return -1;
+    int r = slot_rank ? slot_rank[v] : R;
+    return r > 0 ? v : -1;
+}
+
+// Exclusive scan of one int per thread over the 1024-thread block.
+__device__ int block_exclusive_scan(int v, int *total, int *wsum) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        int s = lane < kSegWaves ? wsum[lane] : 0;
+        int si = s;
+#pragma unroll
+        for (int d = 1; d < kSegWaves; d <<= 1) {
+            int o = __shfl_up(si, d);
+            if (lane >= d) si += o;
+        }
+        if (lane < kSegWaves) wsum[kSegWaves + lane] = si - s;   // exclusive wave offsets
+        if (lane == kSegWaves - 1) wsum[2 * kSegWaves] = si;       // total
+    }
+    __syncthreads();
+    int r = wsum[kSegWaves + w] + incl - v;
+    *total = wsum[2 * kSegWaves];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restrict__ idx,
+                                                          const int32_t *__restrict__ slot_rank,
+                                                          int32_t T, int32_t L, int32_t R,
+                                                          SegPtrs seg) {
+    extern __shared__ int32_t wcnt[];   // [kSegWaves][L]
+    __shared__ int32_t wsum[2 * kSegWaves + 1];
+    __shared__ int32_t s_invalid;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kSegWaves * L; i += kSegThreads) wcnt[i] = 0;
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+
+    const int chunk = (T + kSegWaves - 1) / kSegWaves;
+    const int b0 = w * chunk;
+    const int b1 = min(T, b0 + chunk);
+    int32_t *mycnt = wcnt + w * L;
+
+    // Pass 1: per-wave, per-slot counts.
+    int inv = 0;
+    for (int base = b0; base < b1; base += kWave) {
+        const int t = base + lane;
+        const int s = (t < b1) ? slot_of(idx, slot_rank, L, R, t, &inv) : -1;
+        uint64_t rem = __ballot(s >= 0);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ls = __shfl(s, leader);
+            const uint64_t peers = __ballot(s == ls);
+            if (lane == leader) mycnt[ls] += __popcll(peers);
+            rem &= ~peers;
+        }
+    }
+    if (inv) atomicAdd(&s_invalid, inv);
+    __syncthreads();
+
+    // Slot totals -> slot_start; per-wave counts -> write cursors.
+    int tot = 0;
+    if (tid < L)
+        for (int q = 0; q < kSegWaves; ++q) tot += wcnt[q * L + tid];
+    int n_active = 0;
+    const int start = block_exclusive_scan(tot, &n_active, wsum);
+    if (tid < L) {
+        seg.slot_start[tid] = start;
+        int run = start;
+        for (int q = 0; q < kSegWaves; ++q) {
+            const int c = wcnt[q * L + tid];
+            wcnt[q * L + tid] = run;
+            run += c;
+        }
+    }
+    if (tid == 0) seg.slot_start[L] = n_active;
+    __syncthreads();
+
+    // Pass 2: scatter token ids in stable order.
+    int dummy = 0;
+    for (int base = b0; base < b1; base += kWave) {
+        const int t = base + lane;
+        const int s = (t < b1) ? slot_of(idx, slot_rank, L, R, t, &dummy) : -1;
+        uint64_t rem = __ballot(s >= 0);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ls = __shfl(s, leader);
+            const uint64_t peers = __ballot(s == ls);
+            int pos = 0;
+            if (lane == leader) {
+                pos = mycnt[ls];
+                mycnt[ls] = pos + __popcll(peers);
+            }
+            pos = __shfl(pos, leader);
+            if (s == ls) {
+                const uint64_t below = peers & ((1ull << lane) - 1ull);
+                seg.perm[pos + __popcll(below)] = t;
+            }
+            rem &= ~peers;
+        }
+    }
+    for (int i = n_active + tid; i < T; i += kSegThreads) seg.perm[i] = -1;
+
+    // Work tiles of both paths (slot-major, token ranges of at most the tile size).
+    const int cnt = (tid < L) ? tot : 0;
+    int n_dec = 0, n_pre = 0;
+    const int td = (cnt + kDecTile - 1) / kDecTile;
+    const int tp = (cnt + kPreTile - 1) / kPreTile;
+    const int od = block_exclusive_scan(td, &n_dec, wsum);
+    const int op = block_exclusive_scan(tp, &n_pre, wsum);
+    if (tid < L) {
+        for (int q = 0; q < td; ++q)
+            seg.tiles_dec[od + q] = make_int4(tid, start + q * kDecTile,
+                                              min(start + (q + 1) * kDecTile, start + cnt), 0);
+        for (int q = 0; q < tp; ++q)
+            seg.tiles_pre[op + q] = make_int4(tid, start + q * kPreTile,
+                                              min(start + (q + 1) * kPreTile, start + cnt), 0);
+    }
+    // Split-K arrival counters of the decode shrink start at zero.
+    for (int i = tid; i < n_dec * kRgStride; i += kSegThreads) seg.counters[i] = 0;
+    if (tid == 0) {
+        seg.header[0] = n_active;
+        seg.header[1] = s_invalid;
+        seg.header[2] = n_dec;
+        seg.header[3] = n_pre;
+    }
+}
+
+__global__ void k_fill_zero(uint4 *__restrict__ p, size_t n16, uint8_t *__restrict__ tail,
+                            size_t ntail) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+    if (blockIdx.x == 0)
+        for (size_t k = threadIdx.x; k < ntail; k += blockDim.x) tail[k] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
+                           int32_t R, const SegPtrs &seg, hipStream_t st) {
+    const size_t lds = sizeof(int32_t) * (size_t)kSegWaves * L;
+    if (lds > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_segments),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, T, L, R,
+                       seg);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
+    if (bytes == 0) return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const size_t ntail = bytes - n16 * 16;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<uint4 *>(p), n16, static_cast<uint8_t *>(p) + n16 * 16, ntail);
+    return hipGetLastError();
+}
+
+}  // namespace aa

@@ -1,0 +1,302 @@
+"""Benchmark of the multi-LoRA delta on one MI355X.
+
+One step = one pass of the whole hot path over one batch: segment build,
+shrink and expand of every slice (lora_apply_packed with the segments
+rebuilt), on synthetic seeded inputs already resident in HBM.  Steps rotate
+over distinct copies of the inputs (>= 512 MB in total, twice the 256 MB
+Infinity Cache) so the measured bandwidth is HBM bandwidth.  Launches are
+captured in HIP graphs (torch.cuda.CUDAGraph on ROCm) so host launch cost
+does not hide the GPU time.
+
+Prints one JSON line.  `--workload` picks another configuration for
+development runs; the default is the headline decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROT_BYTES = 512 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--profile", action="store_true",
+                   help="few eager steps, no graphs, for rocprofv3 runs")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one plain 256 MiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+DEFAULTS = {"decode": (4000, 400), "prefill": (200, 20), "many": (1000, 100)}
+
+
+def make_case(name):
+    import synth
+    if name == "decode":
+        return synth.config_decode()
+    if name == "prefill":
+        return synth.config_prefill()
+    return synth.config_many()
+
+
+def algorithmic_bytes(c):
+    """Bytes each kernel must move (per launch) for the realised draw.
+    shrink: x rows of active tokens, the active slots' lora_a rows j < r, and
+    the fp32 buffer of those tokens; expand: the active slots' lora_b
+    columns j < r, the buffer, and the read-modify-write of the active rows of
+    y; segments: idx read, perm written."""
+    import numpy as np
+    el = 2 if c.dtype == "bf16" else 4
+    act = [(t, int(s)) for t, s in enumerate(c.idx) if 0 <= s < c.L and c.slot_rank[s] > 0]
+    slots = sorted({s for _, s in act})
+    ta = len(act)
+    rank_tok = sum(int(c.slot_rank[s]) for _, s in act)
+    rank_slot = sum(int(c.slot_rank[s]) for s in slots)
+    shrink = ta * c.K * el + c.S * rank_slot * c.K * el + c.S * rank_tok * 4
+    expand = rank_slot * c.Ntot * el + c.S * rank_tok * 4 + ta * c.Ntot * el * 2
+    seg = c.T * 4 * 2
+    flops_shrink = 2 * c.S * rank_tok * c.K
+    flops_expand = 2 * rank_tok * c.Ntot
+    return dict(shrink=shrink, expand=expand, segments=seg, total=shrink + expand + seg,
+                flops=flops_shrink + flops_expand, active_tokens=ta, active_slots=len(slots))
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "adapter_apply_amd", "csrc"))):
+        with open(os.path.join(ROOT, "adapter_apply_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, kernel, khash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != khash:
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, seconds):
+    """The CPU oracle, single-threaded, on a bounded sample of the same
+    workload: whole batches (or a token prefix of one) repeated for about
+    `seconds`; tokens/s."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    n = c.T
+    t0 = time.perf_counter()
+    oracle.lora_apply(c.y0[:1], c.x[:1], c.A, c.B, c.idx[:1], c.slot_rank, c.scale)
+    one = max(time.perf_counter() - t0, 1e-6)
+    # choose a token prefix that takes about a second, then repeat it
+    n = int(min(c.T, max(1, 1.0 / one)))
+    done, t0 = 0, time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < seconds:
+        oracle.lora_apply(c.y0[:n], c.x[:n], c.A, c.B, c.idx[:n], c.slot_rank, c.scale)
+        done += n
+        reps += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of the {c.T} tokens of the same batch, {reps} repetitions, "
+                      f"{el:.1f} s, fp32 C loops on 1 host thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    steps, warmup = DEFAULTS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+
+    import numpy as np
+    import torch
+    import adapter_apply_amd as aa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = make_case(args.workload)
+    dt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    to = lambda a, d=None: (torch.from_numpy(np.ascontiguousarray(a)).to(d) if d is not None
+                            else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    base = dict(x=to(c.x, dt), A=[to(a, dt) for a in c.A], B=[to(b, dt) for b in c.B],
+                y=to(c.y0, dt), idx=to(c.idx), rank=to(c.slot_rank), scale=to(c.scale))
+    inst_bytes = (base["x"].numel() + base["y"].numel() + sum(a.numel() for a in base["A"]) +
+                  sum(b.numel() for b in base["B"])) * base["x"].element_size()
+    n_inst = max(2, math.ceil(ROT_BYTES / inst_bytes))
+    if args.profile:
+        n_inst = min(n_inst, 4)
+    insts = []
+    for i in range(n_inst):
+        d = {k: ([t.clone() for t in v] if isinstance(v, list) else v.clone()) for k, v in base.items()}
+        d["ws"] = aa.alloc_workspace(c.T, c.K, c.S, c.R, c.L)
+        d["buf"] = torch.zeros((c.S, c.T, c.R), dtype=torch.float32, device=dev)
+        insts.append(d)
+    del base
+    torch.cuda.synchronize()
+
+    def step(d):
+        aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
+                             d["ws"])
+
+    def shrink_only(d):
+        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"],
+                       flags=aa.LORA_FLAG_SEGMENTS_READY | aa.LORA_FLAG_ACTIVE_ONLY)
+
+    def expand_only(d):
+        aa.lora_expand(d["y"], d["buf"], d["B"], d["idx"], d["rank"], d["scale"], d["ws"],
+                       flags=aa.LORA_FLAG_SEGMENTS_READY)
+
+    def segments_only(d):
+        aa.lora_build_segments(d["idx"], d["rank"], c.L, c.R, d["ws"])
+
+    if args.profile:
+        for i in range(max(steps, 1)):
+            step(insts[i % n_inst])
+        for fn in (segments_only, shrink_only, expand_only):
+            for i in range(n_inst):
+                fn(insts[i])
+        torch.cuda.synchronize()
+        if args.calib_copy:
+            a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps({"profile_run": args.workload, "steps": steps, "instances": n_inst}))
+        return
+
+    # ---- graphs: one replay = one step on each instance, in order ----------
+    def capture(fn, count):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(count):          # warm the path outside capture
+                fn(insts[i % n_inst])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(insts[i % n_inst])
+        torch.cuda.synchronize()
+        return g
+
+    g_full = capture(step, n_inst)
+    tail = steps % n_inst
+    g_tail = capture(step, tail) if tail else None
+
+    def run_steps(k):
+        full, rem = divmod(k, n_inst)
+        assert rem in (0, tail)
+        for _ in range(full):
+            g_full.replay()
+        if rem:
+            g_tail.replay()
+
+    # warmup (untimed): at least `warmup` steps, in whole replays
+    for _ in range(max(1, math.ceil(warmup / n_inst))):
+        g_full.replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_steps(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / steps
+
+    # ---- per-kernel durations, live, with events around graphs of one kernel
+    per_kernel = {}
+    for name, fn in (("segments", segments_only), ("shrink", shrink_only), ("expand", expand_only)):
+        g = capture(fn, n_inst)
+        reps = max(1, 2000 // n_inst)
+        for _ in range(2):
+            g.replay()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            g.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        per_kernel[name] = a0.elapsed_time(a1) * 1e3 / (reps * n_inst)   # us per launch
+        del g
+
+    ab = algorithmic_bytes(c)
+    dom = max(("shrink", "expand"), key=lambda k: per_kernel[k])
+    dom_bytes = ab[dom]
+    achieved = dom_bytes / (per_kernel[dom] * 1e-6) / 1e9
+    khash = kernel_hash()
+    traffic = load_traffic(args.workload, dom, khash)
+    tokens_per_s = c.T / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(c, args.cpu_seconds)
+
+    workload_desc = {
+        "decode": "decode QKV: 256 tokens, hidden 4096, slices 4096/1024/1024, rank 16, 8 slots, 10% no-adapter",
+        "prefill": "prefill gate_up: 8192 tokens in 32 sequences, 16 slots, hidden 4096, slices 2x14336, rank 64",
+        "many": "many-adapter decode: 1024 tokens, 128 slots Zipf(1.1), ranks 8..128 padded to 128, 8192x8192",
+    }[args.workload]
+    out = {
+        "metric": "LoRA-delta tokens/sec (1 GPU)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic (seeded)",
+        "config": {"workload": workload_desc, "tokens": c.T, "hidden": c.K, "slices": c.N,
+                   "rank": c.R, "slots": c.L, "rotating_instances": n_inst,
+                   "active_tokens": ab["active_tokens"]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                     "kernel_us": round(per_kernel[dom], 3)},
+        "kernels_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "step_algorithmic_GBps": round(ab["total"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+        "kernel_hash": khash,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * adapter_apply -- multi-LoRA delta kernels for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument documented "device" is a HIP device pointer;
+ * "host" pointers are read during the call only.  `stream` is a hipStream_t
+ * (NULL = the null stream).  The library allocates nothing and keeps no
+ * pointer after a call returns; every call enqueues work on `stream` and
+ * returns without synchronising.  All argument checks run on the host before
+ * anything is enqueued: a call that returns an error has launched nothing.
+ * No C++ exception crosses this interface.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [vLLM] "vllm.lora.layers" API page.
+ *   [SGL]  SGLang "lora_manager.py" source page.
+ *   [PR]   "PR #48884 report" page (vLLM Inkling LoRA support).
+ *
+ * Common argument conventions
+ * ---------------------------
+ *   T        tokens (rows of x and y), T >= 0 (T == 0 is a no-op).
+ *   K        input features (hidden size), K >= 1, K % 8 == 0.
+ *   S        slices (packed sub-layers: 3 for QKV, 2 for gate_up), 1..8.
+ *   N[S]     host array: output width of each slice, each >= 1 and % 4 == 0.
+ *   L        adapter slots (max_loras), 1..1024.
+ *   R        padded rank of the stacked tensors, 1..512.
+ *   A[S]     host array of S device pointers; A[s] is the stacked lora_a of
+ *            slice s, row-major [L][R][K] ([vLLM] MergedColumnParallelLinear-
+ *            WithLoRA.create_lora_weights; the page's singleton dim dropped).
+ *   B[S]     host array of S device pointers; B[s] is the stacked lora_b of
+ *            slice s, row-major [L][N[s]][R].
+ *   idx      device int32 [T]: adapter slot of each token.  idx < 0 means
+ *            "no adapter" ([vLLM] the -1 entry of adapter_enabled); idx >= L
+ *            is treated the same way and counted as invalid by
+ *            lora_build_segments.
+ *   slot_rank device int32 [L] or NULL: true rank r_s <= R of each slot
+ *            ([SGL] prepare_lora_batch lora_ranks).  0 marks an empty slot,
+ *            whose tokens pass through.  NULL means every slot has rank R.
+ *            Only rank rows/columns j < r_s are read; the stored slot must be
+ *            zero (or at least finite) beyond r_s, as reset_lora/set_lora
+ *            leave it ([vLLM] MergedColumnParallelLinearWithLoRA).
+ *   scale    device float [L]: per-slot scaling applied once to each output
+ *            element of the expand ([SGL] prepare_lora_batch scalings).
+ *   dtype    LORA_DT_BF16 (x, A, B, y all bf16) or LORA_DT_F32 (all fp32;
+ *            decode path only).  The intermediate buffer is always fp32.
+ *   path     LORA_PATH_AUTO chooses per call; DECODE forces the VALU path;
+ *            PREFILL forces the MFMA path (bf16, R % 16 == 0 only).
+ *   ws       device workspace of at least lora_workspace_size() bytes,
+ *            256-byte aligned, owned by the caller.  Calls sharing a
+ *            workspace must be ordered on one stream.  The workspace must be
+ *            zero-filled before its first use (lora_workspace_init); the
+ *            library leaves its counters at zero after every call.
+ *   flags    LORA_FLAG_SEGMENTS_READY: the workspace already holds the
+ *            segments of this (idx, slot_rank, T, L) from lora_build_segments
+ *            (built once per batch and shared by every LoRA layer, as [SGL]
+ *            prepare_lora_batch does); otherwise the call rebuilds them.
+ *            LORA_FLAG_ACTIVE_ONLY (lora_shrink): write only the buffer entries
+ *            of tokens that carry an adapter and ranks j < r; the other
+ *            entries keep their contents (saves a fill when the buffer only
+ *            feeds lora_expand, which never reads them).
+ *
+ * Alignment: x, y, A[s], B[s] 16-byte aligned; ldx % 8 == 0; ldy and
+ * y_col_offset % 4 == 0; buf 16-byte aligned.  Violations -> LORA_E_ALIGN.
+ * Aliasing of y with x, A, B, buf or ws is not allowed.
+ */
+#ifndef ADAPTER_APPLY_H
+#define ADAPTER_APPLY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lora_status_t;
+
+#define LORA_OK           0
+#define LORA_E_NULL       1  /* a required pointer is NULL                        */
+#define LORA_E_SHAPE      2  /* size out of range or ld smaller than the row      */
+#define LORA_E_DTYPE      3  /* unknown dtype                                     */
+#define LORA_E_RANK       4  /* R outside [1, 512]                                */
+#define LORA_E_SLICES     5  /* S outside [1, 8]                                  */
+#define LORA_E_WORKSPACE  6  /* ws_bytes smaller than the required size           */
+#define LORA_E_ALIGN      7  /* pointer or stride alignment not met               */
+#define LORA_E_PATH       8  /* forced path cannot run these arguments            */
+#define LORA_E_LAUNCH     9  /* the HIP runtime rejected a launch                 */
+
+#define LORA_DT_F32   0
+#define LORA_DT_BF16  1
+
+#define LORA_PATH_AUTO     0
+#define LORA_PATH_DECODE   1
+#define LORA_PATH_PREFILL  2
+
+#define LORA_FLAG_SEGMENTS_READY 1u
+#define LORA_FLAG_ACTIVE_ONLY    2u
+
+#define LORA_MAX_SLICES 8
+#define LORA_MAX_RANK   512
+#define LORA_MAX_SLOTS  1024
+
+/* Human-readable text of a status code (static storage). */
+const char *lora_status_string(lora_status_t status);
+
+/* Bytes of workspace needed by the linear calls for these sizes
+ * (covers lora_build_segments, lora_shrink, lora_expand, lora_apply_packed). */
+lora_status_t lora_workspace_size(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L,
+                                  size_t *bytes);
+
+/* Zero-fill a workspace (a fill kernel on `stream`, no memset node). */
+lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Byte offsets, inside the workspace, of the segment arrays written by
+ * lora_build_segments, so callers and tests can read them back:
+ *   header  int32[4] = {active tokens, invalid tokens (idx >= L), decode tiles, prefill tiles}
+ *   slot_start int32[L+1], perm int32[T] (-1 past the active tokens). */
+typedef struct {
+    int64_t header;
+    int64_t slot_start;
+    int64_t perm;
+    int64_t tiles_decode;
+    int64_t tiles_prefill;
+    int32_t tile_decode_tokens;
+    int32_t tile_prefill_tokens;
+} lora_segment_layout_t;
+
+lora_status_t lora_segment_layout(int32_t T, int32_t L, lora_segment_layout_t *out);
+
+/*
+ * Segment build: the active tokens sorted stably by slot, with the start of
+ * each slot's run and the work tiles of both paths.  This is the token
+ * grouping that segmented LoRA GEMMs run on ([SGL] header credit to S-LoRA
+ * and Punica, "triton" backend; prepare_lora_batch builds the batch's slot
+ * list once and shares it across layers).  One launch, bit-exact and
+ * deterministic.
+ */
+lora_status_t lora_build_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T,
+                                  int32_t L, int32_t R, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Shrink ([vLLM] RowParallelLinearWithShardedLoRA.apply, the add_shrink call
+ * into a float32 buffer of shape (n_slices, tokens, rank) with scale 1.0):
+ *   buf[s][t][j] = sum_i x[t][i] * A[s][idx[t]][j][i]   for active t, j < r
+ *   buf[s][t][j] = 0                                      otherwise
+ * buf: device fp32 [S][T][R], overwritten entirely (active entries only with
+ * LORA_FLAG_ACTIVE_ONLY).  x: device [T][ldx].
+ */
+lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int32_t K,
+                          const void *const *A, int32_t S, int32_t L, int32_t R,
+                          const int32_t *idx, const int32_t *slot_rank, int32_t dtype,
+                          int32_t path, uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expand ([vLLM] RowParallelLinearWithShardedLoRA.apply, the add_expand call
+ * with output_slices, offset_start and add_input=True):
+ *   off_s = y_col_offset + N[0] + ... + N[s-1]
+ *   y[t][off_s + n] = round(y[t][off_s + n] + scale[idx[t]] * sum_{j<r} buf[s][t][j] * B[s][idx[t]][n][j])
+ * y: device [T][ldy], updated in place (rows of inactive tokens untouched).
+ * buf: device fp32 [S][T][R] (entries j >= r are not read).  One rounding
+ * to the storage type per output element (round to nearest even).
+ */
+lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const float *buf,
+                          int32_t T, const void *const *B, const int64_t *N, int32_t S,
+                          int32_t L, int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                          const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Packed apply: shrink then expand over all S slices of a merged layer, the
+ * buffer kept in the workspace ([vLLM] MergedColumnParallelLinearWithLoRA,
+ * MergedQKVParallelLinearWithLoRA; the shrink/expand pair of
+ * RowParallelLinearWithShardedLoRA.apply on one device).  Same arguments as
+ * lora_shrink and lora_expand.
+ */
+lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                                int64_t ldx, int32_t T, int32_t K, const void *const *A,
+                                const void *const *B, const int64_t *N, int32_t S, int32_t L,
+                                int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                                const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                                void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAPTER_APPLY_H */

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+launching anything (the pointers passed here are never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import adapter_apply_amd as aa
+
+# The pointers below are fake: never let a validation bug turn one of these
+# calls into a launch on a real device.
+try:
+    import torch
+    _HAS_GPU = torch.cuda.device_count() > 0
+except Exception:  # pragma: no cover
+    _HAS_GPU = False
+pytestmark = pytest.mark.skipif(_HAS_GPU, reason="fake-pointer ABI checks run only without a GPU")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adapter_apply.h")
+
+FAKE = 0x7f0000001000            # 4 KiB aligned, never dereferenced
+FAKE_WS = 0x7f0000100000
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:lora|moe_lora)_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = aa.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+        assert n in aa.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_status_strings():
+    for code in range(0, 10):
+        assert aa.status_string(code)
+    assert aa.status_string(99) == "unknown status"
+
+
+def _ptrs(n, base=FAKE):
+    arr = (C.c_void_p * n)()
+    for i in range(n):
+        arr[i] = base + 0x100000 * i
+    return arr
+
+
+def _apply(**kw):
+    a = dict(y=FAKE, ldy=6144, off=0, x=FAKE, ldx=4096, T=256, K=4096, A=_ptrs(3), B=_ptrs(3),
+             N=(C.c_int64 * 3)(4096, 1024, 1024), S=3, L=8, R=16, idx=FAKE, rank=FAKE,
+             scale=FAKE, dt=aa.LORA_DT_BF16, path=0, flags=0, ws=FAKE_WS, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return aa.lib().lora_apply_packed(a["y"], a["ldy"], a["off"], a["x"], a["ldx"], a["T"], a["K"],
+                                      a["A"], a["B"], a["N"], a["S"], a["L"], a["R"], a["idx"],
+                                      a["rank"], a["scale"], a["dt"], a["path"], a["flags"],
+                                      a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), aa.LORA_E_SHAPE),
+    (dict(L=0), aa.LORA_E_SHAPE),
+    (dict(L=1025), aa.LORA_E_SHAPE),
+    (dict(R=0), aa.LORA_E_RANK),
+    (dict(R=520), aa.LORA_E_RANK),
+    (dict(R=12), aa.LORA_E_ALIGN),             # bf16 needs R % 8 == 0
+    (dict(S=0), aa.LORA_E_SLICES),
+    (dict(S=9), aa.LORA_E_SLICES),
+    (dict(dt=7), aa.LORA_E_DTYPE),
+    (dict(K=0), aa.LORA_E_SHAPE),
+    (dict(K=4100, ldx=4104), aa.LORA_E_ALIGN),
+    (dict(ldx=4000), aa.LORA_E_SHAPE),
+    (dict(ldx=4100), aa.LORA_E_ALIGN),
+    (dict(ldy=6000), aa.LORA_E_SHAPE),
+    (dict(off=4, ldy=6144), aa.LORA_E_SHAPE),
+    (dict(off=2, ldy=6152), aa.LORA_E_ALIGN),
+    (dict(N=(C.c_int64 * 3)(4096, 1022, 1026)), aa.LORA_E_ALIGN),
+    (dict(N=(C.c_int64 * 3)(4096, 0, 1024)), aa.LORA_E_SHAPE),
+    (dict(N=None), aa.LORA_E_NULL),
+    (dict(y=None), aa.LORA_E_NULL),
+    (dict(x=None), aa.LORA_E_NULL),
+    (dict(idx=None), aa.LORA_E_NULL),
+    (dict(scale=None), aa.LORA_E_NULL),
+    (dict(A=None), aa.LORA_E_NULL),
+    (dict(B=None), aa.LORA_E_NULL),
+    (dict(x=FAKE + 8), aa.LORA_E_ALIGN),
+    (dict(y=FAKE + 4), aa.LORA_E_ALIGN),
+    (dict(A=_ptrs(3, FAKE + 2)), aa.LORA_E_ALIGN),
+    (dict(ws=None), aa.LORA_E_NULL),
+    (dict(ws=FAKE_WS + 64), aa.LORA_E_ALIGN),
+    (dict(wsb=1024), aa.LORA_E_WORKSPACE),
+    (dict(path=aa.LORA_PATH_PREFILL, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_PREFILL, R=24), aa.LORA_E_PATH),
+    (dict(path=5), aa.LORA_E_PATH),
+])
+def test_apply_rejects_bad_arguments(kw, code):
+    assert _apply(**kw) == code
+
+
+def test_zero_tokens_is_a_noop_without_launch():
+    # T == 0: validation passes and nothing is launched (no GPU here).
+    assert _apply(T=0, x=None, y=None, idx=None) == aa.LORA_OK
+
+
+def test_shrink_expand_validation():
+    lib = aa.lib()
+    A = _ptrs(2)
+    ok_ws = 1 << 40
+    assert lib.lora_shrink(None, FAKE, 64, 16, 64, A, 2, 3, 8, FAKE, None, 0, 0, 0, FAKE_WS,
+                           ok_ws, None) == aa.LORA_E_NULL
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 8, FAKE, None, 0, 0, 0, FAKE_WS,
+                           16, None) == aa.LORA_E_WORKSPACE
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 8, FAKE, None, 1,
+                           aa.LORA_PATH_PREFILL, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    N = (C.c_int64 * 2)(64, 64)
+    assert lib.lora_expand(FAKE, 128, 0, None, 16, A, N, 2, 3, 8, FAKE, None, FAKE, 0, 0, 0,
+                           FAKE_WS, ok_ws, None) == aa.LORA_E_NULL
+    assert lib.lora_expand(FAKE, 100, 0, FAKE, 16, A, N, 2, 3, 8, FAKE, None, FAKE, 0, 0, 0,
+                           FAKE_WS, ok_ws, None) == aa.LORA_E_SHAPE
+    assert lib.lora_build_segments(FAKE, None, -3, 4, 8, FAKE_WS, ok_ws, None) == aa.LORA_E_SHAPE
+    assert lib.lora_build_segments(None, None, 5, 4, 8, FAKE_WS, ok_ws, None) == aa.LORA_E_NULL
+    assert lib.lora_build_segments(FAKE, None, 5, 4, 8, FAKE_WS, 8, None) == aa.LORA_E_WORKSPACE
+
+
+def test_workspace_size_and_layout():
+    a = aa.lora_workspace_size(256, 4096, 3, 16, 8)
+    b = aa.lora_workspace_size(512, 4096, 3, 16, 8)
+    c = aa.lora_workspace_size(256, 8192, 3, 16, 8)
+    assert 0 < a < b and a < c and a % 256 == 0
+    lay = aa.lora_segment_layout(256, 8)
+    offs = [lay["header"], lay["slot_start"], lay["perm"], lay["tiles_decode"], lay["tiles_prefill"]]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay["perm"] - lay["slot_start"] >= 4 * 9
+    assert lay["tile_decode_tokens"] == 32 and lay["tile_prefill_tokens"] == 64
+    with pytest.raises(aa.LoraError):
+        aa.lora_workspace_size(256, 4096, 9, 16, 8)

@@ -1,0 +1,323 @@
+"""GPU parity of the linear (packed-slice) path against the CPU oracle, through
+the C ABI.  Both paths (decode VALU, prefill MFMA) are forced on the same
+inputs where they apply.  Tolerance for bf16 outputs: max abs error <= 2e-2
+and normwise relative error <= 1e-2 against the fp32 oracle; fp32 outputs
+within the a-priori fp32 rounding bound; integer-exact vectors and every
+passthrough row bit-exact."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import adapter_apply_amd as aa  # noqa: E402
+import synth  # noqa: E402
+from tests import bounds  # noqa: E402
+from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
+
+DEC, PRE = aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aa.lib()
+
+
+def passthrough_rows(c):
+    return [t for t in range(c.T)
+            if c.idx[t] < 0 or c.idx[t] >= c.L or c.slot_rank[c.idx[t]] <= 0]
+
+
+def assert_passthrough(c, y):
+    rows = passthrough_rows(c)
+    if rows:
+        got = y[rows]
+        exp = c.y0[rows]
+        assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), "passthrough row changed"
+
+
+def oracle_y(oracle_mod, c, rows=None):
+    if rows is None:
+        y, _ = oracle_mod.lora_apply(c.y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
+        return y
+    rows = np.asarray(rows)
+    y, _ = oracle_mod.lora_apply(c.y0[rows], c.x[rows], c.A, c.B, c.idx[rows], c.slot_rank, c.scale)
+    return y
+
+
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_decode(oracle_mod):
+    c = synth.config_tiny()
+    log(f"case tiny fp32 T={c.T}")
+    d = LinearOnDevice(c)
+    d.apply(DEC)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    M = bounds.linear_magnitude(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.all(np.abs(y - ref) <= bounds.fp32_bound(M, c.K, c.R))
+    assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("seed,T,K,N,R,L", [
+    (21, 200, 512, [256, 64, 64], 16, 5),
+    (22, 333, 1024, [128, 128], 32, 3),
+    (23, 97, 2056, [520], 64, 7),          # K not a multiple of the K chunk, ragged tail
+    (24, 1, 64, [4], 16, 1),
+])
+def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
+    c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
+    log(f"case integer path={path} T={T} K={K} N={N} R={R} L={L}")
+    d = LinearOnDevice(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    exact = bounds.linear_exact_int(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.array_equal(ref, exact.astype(np.float32))
+    assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+    assert canaries_intact(d.yfull)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_decode_config_qkv(oracle_mod, path):
+    """256 tokens, hidden 4096, QKV 4096/1024/1024, rank 16, 8 slots, 10% idx=-1."""
+    c = synth.config_decode()
+    log(f"case decode_qkv path={path}")
+    d = LinearOnDevice(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    err, rel = bounds.check_bf16_tolerance(y, ref)
+    log(f"  max abs err {err:.3e} rel {rel:.3e}")
+    assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
+def test_prefill_config_gate_up_sampled(oracle_mod):
+    """8192 tokens in 32 sequences, 16 slots, gate_up 2x14336, rank 64: every
+    output of a sample of 96 tokens (first, last and random ones of every
+    sequence) against the oracle."""
+    c = synth.config_prefill()
+    log("case prefill_gate_up full size (auto path)")
+    d = LinearOnDevice(c, guard=False)
+    d.apply(aa.LORA_PATH_AUTO)
+    torch.cuda.synchronize()
+    lens = [int(v) for v in c.note.split("=")[1].split(",")]
+    starts = np.cumsum([0] + lens[:-1])
+    rng = np.random.default_rng(0)
+    rows = sorted(set([int(s) for s in starts] + [int(s + l - 1) for s, l in zip(starts, lens)] +
+                      rng.integers(0, c.T, 32).tolist()))
+    y = host_f32(d.y[torch.tensor(rows, device="cuda")])
+    ref = oracle_y(oracle_mod, c, rows)
+    err, rel = bounds.check_bf16_tolerance(y, ref)
+    log(f"  sampled {len(rows)} rows: max abs err {err:.3e} rel {rel:.3e}")
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_prefill_shape_reduced_both_paths(oracle_mod, path):
+    """Prefill-shaped (long per-slot runs) at a size the oracle checks fully."""
+    rng = np.random.default_rng(7)
+    lens = synth.prefill_lengths(rng, n_seq=6, total=1200, lo=64, hi=400)
+    idx = np.repeat(rng.integers(0, 4, size=6), lens).astype(np.int32)
+    c = synth.make_linear("prefill_small", 1200, 768, [1024, 1024], 64, 4, idx, [64, 48, 16, 64],
+                          [1.0, 0.5, 2.0, 1.0], "bf16", seed=8)
+    log(f"case prefill_small path={path}")
+    d = LinearOnDevice(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    bounds.check_bf16_tolerance(y, ref)
+    assert canaries_intact(d.yfull)
+
+
+def test_many_adapter_config(oracle_mod):
+    """1024 tokens, 128 slots with Zipf(1.1) popularity, ranks {8..128} padded to 128."""
+    c = synth.config_many()
+    log("case many_adapter (auto path)")
+    d = LinearOnDevice(c)
+    d.apply(aa.LORA_PATH_AUTO)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    err, rel = bounds.check_bf16_tolerance(y, ref)
+    log(f"  max abs err {err:.3e} rel {rel:.3e}")
+    assert canaries_intact(d.yfull)
+
+
+def test_many_adapter_alpha_scales(oracle_mod):
+    c = synth.config_many(T=512, scale_mode="alpha")
+    log("case many_adapter alpha scales")
+    d = LinearOnDevice(c)
+    d.apply(DEC)
+    bounds.check_bf16_tolerance(d.y_host(), oracle_y(oracle_mod, c))
+
+
+# ---------------------------------------------------------------------------
+# shrink and expand as separate entry points
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_shrink_buffer(oracle_mod, path):
+    c = synth.make_linear("sh", 300, 1024, [256, 128], 32, 5,
+                          idx=np.random.default_rng(3).integers(-1, 6, 300),
+                          slot_rank=[32, 8, 0, 16, 24], scale=[1, 1, 1, 1, 1], dtype="bf16",
+                          seed=31)
+    log(f"case shrink path={path}")
+    d = LinearOnDevice(c)
+    buf = torch.full((c.S, c.T, c.R), 123.0, dtype=torch.float32, device="cuda")
+    aa.lora_shrink(buf, d.x, d.A, d.idx, d.rank, d.ws, path=path)
+    g = host_f32(buf)
+    ref = oracle_mod.lora_shrink(c.x, c.A, c.idx, c.slot_rank)
+    # both sides sum exact bf16 products in fp32; only the order differs
+    Mb = np.zeros_like(ref, dtype=np.float64)
+    for sg, a in enumerate(c.A):
+        for t in range(c.T):
+            s = c.idx[t]
+            if 0 <= s < c.L and c.slot_rank[s] > 0:
+                Mb[sg, t] = np.abs(a[s].astype(np.float64)) @ np.abs(c.x[t].astype(np.float64))
+    assert np.all(np.abs(g - ref) <= 2 * bounds.gamma(c.K) * Mb + 0.0)
+    zero_mask = ref == 0
+    assert np.all(g[zero_mask & (Mb == 0)] == 0)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE])
+def test_expand_from_given_buffer(oracle_mod, path):
+    rng = np.random.default_rng(41)
+    c = synth.make_linear("ex", 257, 64, [512, 128, 128], 32, 6, idx=rng.integers(-1, 7, 257),
+                          slot_rank=[32, 16, 8, 32, 0, 24], scale=[2, 1, .5, 1, 1, 3],
+                          dtype="bf16", seed=42)
+    buf = rng.standard_normal((c.S, c.T, c.R)).astype(np.float32)
+    if path == PRE:
+        # the MFMA expand consumes the buffer in bf16; give it bf16-exact values
+        buf = synth.round_bf16(buf)
+    log(f"case expand path={path}")
+    d = LinearOnDevice(c)
+    aa.lora_expand(d.y, dev(buf), d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+    y = d.y_host()
+    ref = oracle_mod.lora_expand(c.y0, buf, c.B, c.idx, c.slot_rank, c.scale)
+    bounds.check_bf16_tolerance(y, ref)
+    assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
+# ---------------------------------------------------------------------------
+# segments and edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,T,L", [(0, 1, 1), (1, 256, 8), (2, 8192, 16), (3, 1000, 128),
+                                      (4, 4097, 1024), (5, 70, 3)])
+def test_segments_bit_exact(oracle_mod, seed, T, L):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(-2, L + 2, size=T).astype(np.int32)
+    rank = rng.integers(0, 3, size=L).astype(np.int32) * 8
+    log(f"case segments T={T} L={L}")
+    ws = aa.alloc_workspace(T, 64, 1, 16, L)
+    aa.lora_build_segments(dev(idx), dev(rank), L, 16, ws)
+    torch.cuda.synchronize()
+    lay = aa.lora_segment_layout(T, L)
+    w = ws.cpu().numpy()
+
+    def ints(off, n):
+        return w[off:off + 4 * n].view(np.int32)
+
+    perm, start, ninv = oracle_mod.segments(idx, rank, L, 16)
+    hdr = ints(lay["header"], 4)
+    assert hdr[0] == start[L] and hdr[1] == ninv
+    assert np.array_equal(ints(lay["slot_start"], L + 1), start)
+    assert np.array_equal(ints(lay["perm"], T), perm)
+    for key, G, k in (("tiles_decode", lay["tile_decode_tokens"], 2),
+                      ("tiles_prefill", lay["tile_prefill_tokens"], 3)):
+        tiles = ints(lay[key], 4 * hdr[k]).reshape(-1, 4)
+        exp = [(s, b, min(b + G, start[s + 1]))
+               for s in range(L) for b in range(start[s], start[s + 1], G)]
+        assert [tuple(t[:3]) for t in tiles] == exp
+
+
+def test_all_tokens_without_adapter_unchanged():
+    c = synth.config_decode(T=64)
+    c.idx[:] = -1
+    d = LinearOnDevice(c)
+    for path in (DEC, PRE):
+        d.apply(path)
+        y = d.y_host()
+        assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
+    assert canaries_intact(d.yfull)
+
+
+def test_zero_b_identity_and_invalid_slots(oracle_mod):
+    c = synth.config_decode(T=128)
+    c.idx[::7] = 8        # >= L: passthrough
+    c.idx[::11] = 100
+    c.slot_rank[3] = 0    # empty slot
+    c.B = [np.zeros_like(b) for b in c.B]
+    for path in (DEC, PRE):
+        d = LinearOnDevice(c)
+        d.apply(path)
+        y = d.y_host()
+        assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
+
+
+def test_column_offset_and_wide_rows(oracle_mod):
+    """y_col_offset > 0 inside a wider row: the columns outside the packed
+    slices stay bit-identical."""
+    rng = np.random.default_rng(5)
+    c = synth.make_linear("off", 90, 256, [64, 32], 16, 3, idx=rng.integers(-1, 3, 90),
+                          slot_rank=[16, 8, 16], scale=[1, 2, 1], dtype="bf16", seed=6)
+    wide = rng.standard_normal((c.T, 200)).astype(np.float32)
+    wide = synth.round_bf16(wide)
+    off = 40
+    for path in (DEC, PRE):
+        yw = dev(wide, torch.bfloat16)
+        d = LinearOnDevice(c, guard=False)
+        aa.lora_apply_packed(yw, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, y_col_offset=off,
+                             path=path)
+        got = host_f32(yw)
+        y0 = wide[:, off:off + c.Ntot]
+        ref, _ = oracle_mod.lora_apply(y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
+        bounds.check_bf16_tolerance(got[:, off:off + c.Ntot], ref)
+        assert np.array_equal(got[:, :off], wide[:, :off])
+        assert np.array_equal(got[:, off + c.Ntot:], wide[:, off + c.Ntot:])
+
+
+def test_segments_reused_across_layers(oracle_mod):
+    """Segments built once per batch and reused by several layer shapes."""
+    rng = np.random.default_rng(9)
+    T, L = 200, 6
+    idx = rng.integers(-1, L, T).astype(np.int32)
+    ranks = np.array([16, 8, 16, 0, 16, 8], np.int32)
+    ws = aa.alloc_workspace(T, 2048, 3, 16, L)
+    idx_d, rank_d = dev(idx), dev(ranks)
+    aa.lora_build_segments(idx_d, rank_d, L, 16, ws)
+    for li, (K, N) in enumerate([(512, [256, 64, 64]), (2048, [512]), (256, [128, 128])]):
+        c = synth.make_linear(f"layer{li}", T, K, N, 16, L, idx, ranks, [1.5] * L, "bf16",
+                              seed=100 + li)
+        d = LinearOnDevice(c, guard=False)
+        for path in (DEC, PRE):
+            d.reset_y()
+            aa.lora_apply_packed(d.y, d.x, d.A, d.B, idx_d, rank_d, d.scale, ws, path=path,
+                                 flags=aa.LORA_FLAG_SEGMENTS_READY)
+            bounds.check_bf16_tolerance(d.y_host(), oracle_y(oracle_mod, c))
+
+
+def test_deterministic_run_twice():
+    c = synth.config_many(T=512)
+    outs = []
+    for _ in range(2):
+        d = LinearOnDevice(c, guard=False)
+        d.apply(DEC)
+        outs.append(d.y_host())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_zero_tokens_noop():
+    c = synth.config_decode(T=8)
+    d = LinearOnDevice(c)
+    x0 = d.x[:0]
+    y0 = d.y[:0]
+    aa.lora_apply_packed(y0, x0, d.A, d.B, d.idx[:0], d.rank, d.scale, d.ws)
+    torch.cuda.synchronize()
+    assert canaries_intact(d.yfull)
