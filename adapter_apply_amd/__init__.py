@@ -32,9 +32,11 @@ LORA_DT_BF16 = 1
 LORA_PATH_AUTO = 0
 LORA_PATH_DECODE = 1
 LORA_PATH_PREFILL = 2
+LORA_PATH_FUSED = 3
 
 LORA_FLAG_SEGMENTS_READY = 1
 LORA_FLAG_ACTIVE_ONLY = 2
+LORA_FLAG_PARTIAL = 4
 
 # Every symbol the header declares, with its ctypes signature.
 _vp = C.c_void_p

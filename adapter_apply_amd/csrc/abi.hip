@@ -10,6 +10,9 @@ namespace {
 // Auto path: MFMA prefill once slots carry long token runs.
 constexpr int32_t kPrefillMinTokens = 512;
 constexpr int32_t kPrefillMinPerSlot = 64;
+// Decode: the expand adds the shrink's K-chunk partials itself (one launch
+// fewer) while a tile's partials stay small; beyond that a reduce kernel runs.
+constexpr int32_t kFoldMaxChunkRank = 512;   // n_kchunks * R
 
 inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -56,10 +59,14 @@ lora_status_t check_ptrs(const void *const *P, int32_t S) {
     return LORA_OK;
 }
 
+bool can_fuse(int32_t T, int32_t R, int32_t dtype) {
+    return dtype == LORA_DT_BF16 && R % 16 == 0 && R <= kFusedMaxRank && T <= kFusedMaxTokens;
+}
+
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
                           int *use_prefill) {
     const bool can_prefill = dtype == LORA_DT_BF16 && R % 16 == 0;
-    if (path == LORA_PATH_DECODE) { *use_prefill = 0; return LORA_OK; }
+    if (path == LORA_PATH_DECODE || path == LORA_PATH_FUSED) { *use_prefill = 0; return LORA_OK; }
     if (path == LORA_PATH_PREFILL) {
         if (!can_prefill) return LORA_E_PATH;
         *use_prefill = 1;
@@ -165,6 +172,7 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
                           const void *const *A, int32_t S, int32_t L, int32_t R,
                           const int32_t *idx, const int32_t *slot_rank, int32_t dtype,
                           int32_t path, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+    if (path == LORA_PATH_FUSED) return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     CHECK(check_k(K, ldx));
     int use_prefill = 0;
@@ -181,13 +189,17 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     const Slices sl = make_slices(A, nullptr, nullptr, S, 0);
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
-    if (!(flags & LORA_FLAG_ACTIVE_ONLY))
+    // buf is written unless the decode path keeps partials in the workspace
+    const bool writes_buf = use_prefill || !(flags & LORA_FLAG_PARTIAL);
+    if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
         CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
     if (use_prefill)
         return launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st));
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
-    return launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
-                                      wl.n_kchunks, buf, st));
+    CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
+                                     wl.n_kchunks, st)));
+    if (flags & LORA_FLAG_PARTIAL) return LORA_OK;
+    return launched(launch_dec_reduce(T, S, L, R, slot_rank, seg, partial, wl.n_kchunks, buf, st));
 }
 
 lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const float *buf,
@@ -195,6 +207,7 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
                           int32_t L, int32_t R, const int32_t *idx, const int32_t *slot_rank,
                           const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                           void *ws, size_t ws_bytes, void *stream) {
+    if (path == LORA_PATH_FUSED) return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     int64_t ntot = 0;
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
@@ -214,7 +227,18 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (use_prefill)
         return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
-    return launched(launch_dec_expand(dtype, y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+    if (flags & LORA_FLAG_PARTIAL) {
+        // partial sums sit right after the segments (ws_layout), K-chunk count in the header
+        const float *partial = reinterpret_cast<const float *>(static_cast<char *>(ws) + sgl.end);
+        // the kernel never reads more chunks than this workspace holds
+        const size_t chunk_bytes = sizeof(float) * (size_t)T * S * R;
+        const int32_t fit = (int32_t)((ws_bytes - sgl.end) / chunk_bytes);
+        if (fit < 1) return LORA_E_WORKSPACE;
+        return launched(launch_dec_expand(dtype, y, ldy, nullptr, partial, fit, T, sl, S, L, R,
+                                          slot_rank, scale, seg, st));
+    }
+    return launched(launch_dec_expand(dtype, y, ldy, buf, nullptr, 0, T, sl, S, L, R, slot_rank,
+                                      scale, seg, st));
 }
 
 lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, const void *x,
@@ -229,15 +253,23 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    const bool fuse = !use_prefill && can_fuse(T, R, dtype) &&
+                      (path == LORA_PATH_FUSED || path == LORA_PATH_AUTO);
+    if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!y || !x || !idx || !scale) return LORA_E_NULL;
     CHECK(check_ptrs(A, S));
     CHECK(check_ptrs(B, S));
     if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fuse) {
+        // one launch; no workspace and no segments needed
+        const Slices sl = make_slices(A, B, N, S, y_col_offset);
+        return launched(launch_dec_fused(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale, st));
+    }
     const WsLayout wl = ws_layout(T, K, S, R, L);
     CHECK(check_ws(ws, ws_bytes, wl.end));
 
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const SegPtrs seg = seg_ptrs(ws, wl.seg);
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
@@ -249,8 +281,13 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     }
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
     CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
-                                     wl.n_kchunks, buf, st)));
-    return launched(launch_dec_expand(dtype, y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+                                     wl.n_kchunks, st)));
+    if (wl.n_kchunks * R <= kFoldMaxChunkRank)
+        return launched(launch_dec_expand(dtype, y, ldy, nullptr, partial, wl.n_kchunks, T, sl, S,
+                                          L, R, slot_rank, scale, seg, st));
+    CHECK(launched(launch_dec_reduce(T, S, L, R, slot_rank, seg, partial, wl.n_kchunks, buf, st)));
+    return launched(launch_dec_expand(dtype, y, ldy, buf, nullptr, 0, T, sl, S, L, R, slot_rank,
+                                      scale, seg, st));
 }
 
 }  // extern "C"

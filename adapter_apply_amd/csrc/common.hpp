@@ -20,8 +20,13 @@ constexpr int kPreTile = 64;   // prefill (MFMA) path: two 32-row MFMA blocks
 // Decode shrink: K columns per work-group chunk and rank rows per work-group.
 constexpr int kDecKc = 256;    // 4 waves x 64 columns
 constexpr int kDecRows = 16;   // rows of the (slice, rank) space per work-group
-// Arrival counters per decode tile: one per row group, enough for S*R <= 8*512.
-constexpr int kRgStride = kMaxSlices * kMaxRank / kDecRows;
+
+// Single-launch decode (fused shrink + expand).
+constexpr int kFusedGroup = 16;        // tokens of one slot per work-group
+constexpr int kFusedCols = 512;        // output columns per work-group
+constexpr int kFusedMaxRank = 64;
+constexpr int kFusedMaxTokens = 1024;  // idx staged in LDS
+constexpr int kFusedXcds = 8;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -42,20 +47,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Loads in the pipelined loops are unconditional, from addresses clamped to a
+// valid row; results that belong to padding rows/columns are discarded or
+// zeroed where they are written.  A load under a branch would make the
+// compiler wait for every outstanding load (vmcnt(0)) at the next use and
+// serialise the prefetch.
+template <typename V, typename E>
+__device__ __forceinline__ V ldg(const E *p) { return *reinterpret_cast<const V *>(p); }
+
 // ---------------------------------------------------------------------------
 // Workspace layout (all offsets 256-byte aligned).
 // ---------------------------------------------------------------------------
 struct SegLayout {
-    size_t header;        // int32[4]: active, invalid, decode tiles, prefill tiles
+    size_t header;        // int32[8]: active, invalid, decode tiles, prefill tiles,
+                          //           K chunks of the last decode shrink
     size_t slot_start;    // int32[L+1]
     size_t perm;          // int32[T]
     size_t tiles_dec;     // int4[max_tiles_dec]: slot, begin, end, 0
     size_t tiles_pre;     // int4[max_tiles_pre]
-    size_t counters;      // int32[max_tiles_dec][kRgStride]: split-K arrival counters
     size_t end;
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
-    int32_t n_counters;
 };
 
 struct WsLayout {
@@ -88,8 +100,6 @@ inline SegLayout seg_layout(int32_t T, int32_t L) {
     l.max_tiles_pre = max_tiles(T, L, kPreTile);
     l.tiles_dec = o;  o = align256(o + 16 * (size_t)l.max_tiles_dec);
     l.tiles_pre = o;  o = align256(o + 16 * (size_t)l.max_tiles_pre);
-    l.n_counters = l.max_tiles_dec * kRgStride;
-    l.counters = o;   o = align256(o + sizeof(int32_t) * (size_t)l.n_counters);
     l.end = o;
     return l;
 }
@@ -112,10 +122,8 @@ struct SegPtrs {
     int32_t *perm;
     int4 *tiles_dec;
     int4 *tiles_pre;
-    int32_t *counters;
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
-    int32_t n_counters;
 };
 
 inline SegPtrs seg_ptrs(void *ws, const SegLayout &l) {
@@ -126,10 +134,8 @@ inline SegPtrs seg_ptrs(void *ws, const SegLayout &l) {
     p.perm = reinterpret_cast<int32_t *>(b + l.perm);
     p.tiles_dec = reinterpret_cast<int4 *>(b + l.tiles_dec);
     p.tiles_pre = reinterpret_cast<int4 *>(b + l.tiles_pre);
-    p.counters = reinterpret_cast<int32_t *>(b + l.counters);
     p.max_tiles_dec = l.max_tiles_dec;
     p.max_tiles_pre = l.max_tiles_pre;
-    p.n_counters = l.n_counters;
     return p;
 }
 
@@ -146,14 +152,27 @@ hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t
                            int32_t R, const SegPtrs &seg, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
+// Writes the K-chunk partial sums; launch_dec_reduce (or the expand) adds them.
 hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, int32_t K,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,
                              const int32_t *slot_rank, const SegPtrs &seg, float *partial,
+                             int32_t n_kchunks, hipStream_t st);
+hipError_t launch_dec_reduce(int32_t T, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const SegPtrs &seg, const float *partial,
                              int32_t n_kchunks, float *buf, hipStream_t st);
-hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf, int32_t T,
+// buf == nullptr: the expand sums the K-chunk partials itself (count read from
+// the segment header, at most n_kchunks).
+hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf,
+                             const float *partial, int32_t n_kchunks, int32_t T,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,
                              const int32_t *slot_rank, const float *scale, const SegPtrs &seg,
                              hipStream_t st);
+
+int32_t fused_max_groups(int32_t T, int32_t L);
+hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
+                            int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
+                            const int32_t *idx, const int32_t *slot_rank, const float *scale,
+                            hipStream_t st);
 
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,

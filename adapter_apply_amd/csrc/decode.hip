@@ -9,8 +9,11 @@
 // the slot's (slice, rank) rows).  Lane = (token, column half); each wave owns
 // 64 columns, so every lane holds 32 x values in registers and streams the
 // rank rows from LDS (broadcast reads).  Partial sums of the K chunks go to
-// the workspace; the last work-group to arrive for a (tile, row group) adds
-// them in ascending chunk order (deterministic) and resets its counter.
+// the workspace and are added, in ascending chunk order (deterministic), by a
+// later kernel: the reduce kernel, or the expand itself when the partials of
+// a tile are few.  The kernel boundary is the only synchronisation: an
+// agent-scope release per work-group writes back the whole L2 on this part
+// and costs about a microsecond each.
 //
 // Expand (y += scale * buf . B^T): work-group = (tile, 128 output columns of
 // one slice).  Lane = 2 adjacent columns, waves split the tile's tokens; the
@@ -42,7 +45,9 @@ struct ShrinkArgs {
 struct ExpandArgs {
     void *y;
     int64_t ldy;
-    const float *buf;
+    const float *buf;       // [S][T][R], or
+    const float *partial;   // [n_kchunks][T][S][R] K-chunk partials summed here when non-null
+    int32_t n_kchunks;      // upper bound on the chunk count (the shrink records the real one)
     int32_t T, S, L, R;
     const int32_t *slot_rank;
     const float *scale;
@@ -92,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_shrink(ShrinkArgs a) {
     const int kc = blockIdx.x;
     const int g = blockIdx.y;
     const int tile = blockIdx.z;
+    if ((kc | g | tile) == 0 && threadIdx.x == 0) a.seg.header[4] = a.n_kchunks;
     if (tile >= a.seg.header[2]) return;
     const int4 tl = a.seg.tiles_dec[tile];
     const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
@@ -104,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void k_dec_shrink(ShrinkArgs a) {
 
     __shared__ __attribute__((aligned(16))) E sA[kDecRows][kDecKc];
     __shared__ float sRed[kWavesPerWg][kDecRows][32];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
@@ -165,21 +170,27 @@ __global__ __launch_bounds__(kThreads) void k_dec_shrink(ShrinkArgs a) {
         part[(int64_t)tk * pstride + (int64_t)sg * a.R + j] = v;
     }
 
-    // Last work-group of this (tile, row group) to finish adds the chunks.
-    __threadfence();
-    __syncthreads();
-    int32_t *cnt = a.seg.counters + (int64_t)tile * kRgStride + g;
-    if (tid == 0) s_last = (atomicAdd(cnt, 1) == a.n_kchunks - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
+
+// Sum of the K-chunk partials of one (tile, row group) into buf, chunks in
+// ascending order (deterministic).
+__global__ __launch_bounds__(kThreads) void k_dec_reduce(ShrinkArgs a) {
+    const int g = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= a.seg.header[2]) return;
+    const int4 tl = a.seg.tiles_dec[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    const int q0 = g * kDecRows;
+    if (q0 >= a.S * r) return;
+    const int nrows = min(kDecRows, a.S * r - q0);
+    const int64_t pstride = (int64_t)a.S * a.R;
     const int64_t cstride = (int64_t)a.T * pstride;
-    const float *p_all = a.partial + (int64_t)p0 * pstride;
-    for (int i = tid; i < ntok * nrows; i += kThreads) {
+    for (int i = threadIdx.x; i < ntok * nrows; i += kThreads) {
         const int tk = i / nrows, row = i - tk * nrows;
         const int q = q0 + row;
         const int sg = q / r, j = q - sg * r;
-        const float *pp = p_all + (int64_t)tk * pstride + (int64_t)sg * a.R + j;
+        const float *pp = a.partial + (int64_t)(p0 + tk) * pstride + (int64_t)sg * a.R + j;
         float acc = 0.0f;
         int c = 0;
         for (; c + 8 <= a.n_kchunks; c += 8) {
@@ -193,7 +204,6 @@ __global__ __launch_bounds__(kThreads) void k_dec_shrink(ShrinkArgs a) {
         const int t = a.seg.perm[p0 + tk];
         a.buf[((int64_t)sg * a.T + t) * a.R + j] = acc;
     }
-    if (tid == 0) *cnt = 0;
 }
 
 template <bool BF16>
@@ -209,6 +219,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_expand(ExpandArgs a) {
     const int4 tl = a.seg.tiles_dec[tile];
     const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    // K chunks written by the shrink, bounded by what the workspace holds
+    const int nkc = a.partial ? min(a.seg.header[4], a.n_kchunks) : 0;
     int sg = 0;
     while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
     const int64_t Ns = a.sl.n[sg];
@@ -222,8 +234,15 @@ __global__ __launch_bounds__(kThreads) void k_dec_expand(ExpandArgs a) {
         const int tk = i / rpad, j = i - tk * rpad;
         float v = 0.0f;
         if (tk < ntok && j < r) {
-            const int t = a.seg.perm[p0 + tk];
-            v = a.buf[((int64_t)sg * a.T + t) * a.R + j];
+            if (a.partial) {
+                const int64_t pstride = (int64_t)a.S * a.R;
+                const int64_t cstride = (int64_t)a.T * pstride;
+                const float *pp = a.partial + (int64_t)(p0 + tk) * pstride + (int64_t)sg * a.R + j;
+                for (int c = 0; c < nkc; ++c) v += pp[(int64_t)c * cstride];
+            } else {
+                const int t = a.seg.perm[p0 + tk];
+                v = a.buf[((int64_t)sg * a.T + t) * a.R + j];
+            }
         }
         sBuf[i] = v;
     }
@@ -316,12 +335,12 @@ __global__ __launch_bounds__(kThreads) void k_dec_expand(ExpandArgs a) {
 hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, int32_t K,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,
                              const int32_t *slot_rank, const SegPtrs &seg, float *partial,
-                             int32_t n_kchunks, float *buf, hipStream_t st) {
-    ShrinkArgs a;
+                             int32_t n_kchunks, hipStream_t st) {
+    ShrinkArgs a{};
     a.x = x; a.ldx = ldx; a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
     a.n_kchunks = n_kchunks;
     a.n_rg = row_groups(S, R);
-    a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.partial = partial; a.buf = buf;
+    a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.partial = partial; a.buf = nullptr;
     dim3 grid(n_kchunks, a.n_rg, seg.max_tiles_dec);
     if (dtype == 1)
         hipLaunchKernelGGL(k_dec_shrink<true>, grid, dim3(kThreads), 0, st, a);
@@ -330,12 +349,24 @@ hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, i
     return hipGetLastError();
 }
 
-hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf, int32_t T,
+hipError_t launch_dec_reduce(int32_t T, int32_t S, int32_t L, int32_t R,
+                             const int32_t *slot_rank, const SegPtrs &seg, const float *partial,
+                             int32_t n_kchunks, float *buf, hipStream_t st) {
+    ShrinkArgs a{};
+    a.T = T; a.S = S; a.L = L; a.R = R; a.n_kchunks = n_kchunks; a.n_rg = row_groups(S, R);
+    a.slot_rank = slot_rank; a.seg = seg; a.partial = const_cast<float *>(partial); a.buf = buf;
+    hipLaunchKernelGGL(k_dec_reduce, dim3(a.n_rg, seg.max_tiles_dec), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf,
+                             const float *partial, int32_t n_kchunks, int32_t T,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,
                              const int32_t *slot_rank, const float *scale, const SegPtrs &seg,
                              hipStream_t st) {
     ExpandArgs a;
-    a.y = y; a.ldy = ldy; a.buf = buf; a.T = T; a.S = S; a.L = L; a.R = R;
+    a.y = y; a.ldy = ldy; a.buf = buf; a.partial = partial; a.n_kchunks = n_kchunks;
+    a.T = T; a.S = S; a.L = L; a.R = R;
     a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
     int c = 0;
     for (int s = 0; s < S; ++s) {

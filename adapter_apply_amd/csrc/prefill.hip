@@ -67,41 +67,60 @@ __global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
     const int half = lane >> 5, l32 = lane & 31;
 
     // Operand rows of this lane.
+    // Operand rows are clamped to valid ones (the tile's first token, the
+    // slot's rank row 0 of slice 0); their results are never written.
     const int trow = wm * 32 + l32;                    // token within tile
     const bool tok_ok = trow < ntok;
-    const int t_in = tok_ok ? a.seg.perm[p0 + trow] : 0;
+    const int t_in = a.seg.perm[p0 + (tok_ok ? trow : 0)];
     const uint16_t *xr = a.x + (int64_t)t_in * a.ldx;
 
     const int col = cb * kShrinkCols + wn * 32 + l32;  // buffer column (slice, rank)
     const int SRf = a.S * a.R;
     const int sg = col / a.R, j = col - (col / a.R) * a.R;
     const bool col_ok = col < SRf && j < r;
-    const uint16_t *ar = col_ok ? static_cast<const uint16_t *>(a.sl.a[sg]) +
-                                      ((int64_t)s * a.R + j) * (int64_t)a.K
-                                : xr;
+    const uint16_t *ar = static_cast<const uint16_t *>(a.sl.a[col_ok ? sg : 0]) +
+                         ((int64_t)s * a.R + (col_ok ? j : 0)) * (int64_t)a.K;
 
     floatx16_t acc = {};
     const int kofs = 8 * half;
     // Whole block dead (every column past the rank): skip the contraction.
     const bool any_col = __ballot(col_ok) != 0;
     if (any_col) {
-        int k0 = 0;
-        for (; k0 + 64 <= a.K; k0 += 64) {
-            uint4 xa[4], aa_[4];
+        // Two register stages of 8 k-steps (128 columns of K): the loads of one
+        // stage are in flight while the other is multiplied.
+        constexpr int KS = 8;
+        uint4 xa[KS], av[KS], xb[KS], bv[KS];
+        auto load = [&](uint4 *xs, uint4 *as, int k0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xa[u] = tok_ok ? *reinterpret_cast<const uint4 *>(xr + k0 + 16 * u + kofs) : make_uint4(0, 0, 0, 0);
-                aa_[u] = col_ok ? *reinterpret_cast<const uint4 *>(ar + k0 + 16 * u + kofs) : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < KS; ++u) {
+                xs[u] = ldg<uint4>(xr + k0 + 16 * u + kofs);
+                as[u] = ldg<uint4>(ar + k0 + 16 * u + kofs);
             }
+        };
+        auto mma = [&](const uint4 *xs, const uint4 *as) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xa[u]), as_frag(aa_[u]), acc, 0, 0, 0);
+            for (int u = 0; u < KS; ++u)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xs[u]), as_frag(as[u]), acc, 0, 0, 0);
+        };
+        const int kmain = (a.K / (2 * KS * 16)) * (2 * KS * 16);   // whole 256-column pairs
+        int k0 = 0;
+        if (kmain > 0) {
+            load(xa, av, 0);
+            for (; k0 < kmain; k0 += 2 * KS * 16) {
+                load(xb, bv, k0 + KS * 16);
+                mma(xa, av);
+                if (k0 + 2 * KS * 16 < kmain) load(xa, av, k0 + 2 * KS * 16);
+                mma(xb, bv);
+            }
         }
-        for (; k0 < a.K; k0 += 16) {
+        for (; k0 < a.K; k0 += 16) {          // K tail (K % 8 == 0)
             const int kk = k0 + kofs;
-            const uint4 xa = (tok_ok && kk < a.K) ? *reinterpret_cast<const uint4 *>(xr + kk) : make_uint4(0, 0, 0, 0);
-            const uint4 av = (col_ok && kk < a.K) ? *reinterpret_cast<const uint4 *>(ar + kk) : make_uint4(0, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xa), as_frag(av), acc, 0, 0, 0);
+            uint4 x1 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+            if (kk < a.K) {
+                x1 = ldg<uint4>(xr + kk);
+                a1 = ldg<uint4>(ar + kk);
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(x1), as_frag(a1), acc, 0, 0, 0);
         }
     }
 
@@ -225,6 +244,122 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     }
 }
 
+// Fast expand for ranks <= 16 * NKS (NKS <= 4): every load of the wave (buf
+// fragments, the lora_b fragments and the y values of its 4 column blocks)
+// is issued before the first MFMA, so the wave has ~32 KB in flight.
+template <int NKS>
+__global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
+    constexpr int NB = kExpWaveCols / 32;   // 4 column blocks of 32 per wave
+    const int xcd = blockIdx.x % kXcds;
+    const int local = blockIdx.x / kXcds;
+    const int tile = local / a.per_xcd;
+    const int cg = (local - tile * a.per_xcd) * kXcds + xcd;
+    if (cg >= a.n_cg) return;
+    if (tile >= a.seg.header[3]) return;
+    const int4 tl = a.seg.tiles_pre[tile];
+    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    int sg = 0;
+    while (sg + 1 < a.S && cg >= a.group_start[sg + 1]) ++sg;
+    const int64_t Ns = a.sl.n[sg];
+    const float sc = a.scale[s];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int nk = (r + 15) >> 4;
+    const int nbase = (cg - a.group_start[sg]) * kExpGroupCols + w * kExpWaveCols;
+    if (nbase >= Ns) return;
+
+    // Rows are clamped to valid ones (the tile's first token, the last output
+    // column); what they produce is never stored.  R >= 16 * NKS, so every
+    // rank step's loads are in bounds.
+    int trow_t[2];
+    bool trow_ok[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int row = tb * 32 + l32;
+        trow_ok[tb] = row < ntok;
+        trow_t[tb] = a.seg.perm[p0 + (trow_ok[tb] ? row : 0)];
+    }
+    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + (int64_t)s * Ns * a.R;
+    uint16_t *ybase = a.y + a.sl.off[sg];
+
+    // ---- all loads ----
+    float4 bf[2][NKS][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const float *bp = a.buf + ((int64_t)sg * a.T + trow_t[tb]) * a.R;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int jj = ks * 16 + 8 * half;
+            bf[tb][ks][0] = ldg<float4>(bp + jj);
+            bf[tb][ks][1] = ldg<float4>(bp + jj + 4);
+        }
+    }
+    uint4 af[NB][NKS];
+    uint2 yv[NB][2][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n0 = nbase + nb * 32;
+        const int nrow = min(n0 + l32, (int)Ns - 1);
+        const uint16_t *brow = bbase + (int64_t)nrow * a.R;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) af[nb][ks] = ldg<uint4>(brow + ks * 16 + 8 * half);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = min(n0 + 8 * g + 4 * half, (int)Ns - 4);
+                yv[nb][tb][g] = ldg<uint2>(yrow + n);
+            }
+        }
+    }
+    // ---- buf fragments to bf16 (entries past the rank forced to zero) ----
+    uint4 bfrag[2][NKS];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int jj = ks * 16 + 8 * half;
+            const float4 v0 = bf[tb][ks][0], v1 = bf[tb][ks][1];
+            bfrag[tb][ks] = make_uint4(pack_bf16x2(jj + 0 < r ? v0.x : 0.f, jj + 1 < r ? v0.y : 0.f),
+                                       pack_bf16x2(jj + 2 < r ? v0.z : 0.f, jj + 3 < r ? v0.w : 0.f),
+                                       pack_bf16x2(jj + 4 < r ? v1.x : 0.f, jj + 5 < r ? v1.y : 0.f),
+                                       pack_bf16x2(jj + 6 < r ? v1.z : 0.f, jj + 7 < r ? v1.w : 0.f));
+        }
+    // ---- multiply and update y ----
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n0 = nbase + nb * 32;
+        floatx16_t acc[2] = {{}, {}};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks < nk) {
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[nb][ks]), as_frag(bfrag[0][ks]), acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[nb][ks]), as_frag(bfrag[1][ks]), acc[1], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 8 * g + 4 * half;
+                if (trow_ok[tb] && n < Ns) {
+                    const uint2 y0 = yv[nb][tb][g];
+                    uint2 o;
+                    o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[tb][4 * g + 0],
+                                      bf16_hi(y0.x) + sc * acc[tb][4 * g + 1]);
+                    o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[tb][4 * g + 2],
+                                      bf16_hi(y0.y) + sc * acc[tb][4 * g + 3]);
+                    *reinterpret_cast<uint2 *>(yrow + n) = o;
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
@@ -254,7 +389,13 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.n_cg = c;
     a.per_xcd = (c + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
-    hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
+    switch ((R + 15) / 16) {
+        case 1: hipLaunchKernelGGL(k_pre_expand_fast<1>, grid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_pre_expand_fast<2>, grid, dim3(kThreads), 0, st, a); break;
+        case 3: hipLaunchKernelGGL(k_pre_expand_fast<3>, grid, dim3(kThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(k_pre_expand_fast<4>, grid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a); break;
+    }
     return hipGetLastError();
 }
 

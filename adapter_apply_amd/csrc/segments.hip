@@ -6,7 +6,9 @@
 // slots and then over waves turns the counts into write cursors; pass 2 walks
 // the same ranges in order and scatters token ids.  Inside a wave, lanes that
 // share a slot are ranked by lane index through ballots, so the result is the
-// stable order for any schedule.
+// stable order for any schedule.  The kernel is latency-bound at decode sizes,
+// so every global load (slot indices up to 8192 tokens, slot ranks) is issued
+// before the first barrier and the rest runs out of registers and LDS.
 #include "common.hpp"
 
 namespace aa {
@@ -15,15 +17,6 @@ namespace {
 
 constexpr int kSegThreads = 1024;
 constexpr int kSegWaves = kSegThreads / kWave;
-
-__device__ __forceinline__ int slot_of(const int32_t *idx, const int32_t *slot_rank, int32_t L,
-                                       int32_t R, int t, int *invalid) {
-    int v = idx[t];
-    if (v >= L) { *invalid += 1; return -1; }
-    if (v < 0) return -1;
-    int r = slot_rank ? slot_rank[v] : R;
-    return r > 0 ? v : -1;
-}
 
 // Exclusive scan of one int per thread over the 1024-thread block.
 __device__ int block_exclusive_scan(int v, int *total, int *wsum) {
@@ -54,36 +47,89 @@ __device__ int block_exclusive_scan(int v, int *total, int *wsum) {
     return r;
 }
 
+// Ballot-ranked counting of one 64-token step of a wave: the leader of each
+// group of lanes with the same slot adds the group size to the wave's count.
+__device__ __forceinline__ void count_step(int s, int lane, int32_t *mycnt) {
+    uint64_t rem = __ballot(s >= 0);
+    while (rem) {
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const int ls = __shfl(s, leader);
+        const uint64_t peers = __ballot(s == ls);
+        if (lane == leader) mycnt[ls] += __popcll(peers);
+        rem &= ~peers;
+    }
+}
+
+// Same grouping; each lane writes its token at the group's cursor plus its
+// rank among lower lanes of the group (stable order).
+__device__ __forceinline__ void scatter_step(int s, int t, int lane, int32_t *mycnt,
+                                             int32_t *perm) {
+    uint64_t rem = __ballot(s >= 0);
+    while (rem) {
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const int ls = __shfl(s, leader);
+        const uint64_t peers = __ballot(s == ls);
+        int pos = 0;
+        if (lane == leader) {
+            pos = mycnt[ls];
+            mycnt[ls] = pos + __popcll(peers);
+        }
+        pos = __shfl(pos, leader);
+        if (s == ls) perm[pos + __popcll(peers & ((1ull << lane) - 1ull))] = t;
+        rem &= ~peers;
+    }
+}
+
+constexpr int kRegSteps = 8;   // 64-token steps per wave held in registers (T <= 8192)
+
 __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restrict__ idx,
                                                           const int32_t *__restrict__ slot_rank,
                                                           int32_t T, int32_t L, int32_t R,
                                                           SegPtrs seg) {
-    extern __shared__ int32_t wcnt[];   // [kSegWaves][L]
+    extern __shared__ int32_t lds[];
+    int32_t *wcnt = lds;                       // [kSegWaves][L]
+    int32_t *srank = lds + kSegWaves * L;      // [L]
     __shared__ int32_t wsum[2 * kSegWaves + 1];
     __shared__ int32_t s_invalid;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int chunk = (T + kSegWaves - 1) / kSegWaves;
+    const int b0 = w * chunk;
+    const int b1 = min(T, b0 + chunk);
+    const int nsteps = b1 > b0 ? (b1 - b0 + kWave - 1) / kWave : 0;
+    const bool inreg = chunk <= kWave * kRegSteps;   // uniform over the block
+
+    // Every global load first: the slot indices into registers, the ranks into LDS.
+    int raw[kRegSteps];
+#pragma unroll
+    for (int u = 0; u < kRegSteps; ++u) {
+        const int t = b0 + u * kWave + lane;
+        raw[u] = (inreg && t < b1) ? idx[t] : -1;
+    }
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
     for (int i = tid; i < kSegWaves * L; i += kSegThreads) wcnt[i] = 0;
     if (tid == 0) s_invalid = 0;
     __syncthreads();
 
-    const int chunk = (T + kSegWaves - 1) / kSegWaves;
-    const int b0 = w * chunk;
-    const int b1 = min(T, b0 + chunk);
+    int inv = 0;
+    auto filt = [&](int v) -> int {
+        if (v >= L) { ++inv; return -1; }
+        return (v >= 0 && srank[v] > 0) ? v : -1;
+    };
+    int sl[kRegSteps];
+#pragma unroll
+    for (int u = 0; u < kRegSteps; ++u) sl[u] = filt(raw[u]);
     int32_t *mycnt = wcnt + w * L;
 
     // Pass 1: per-wave, per-slot counts.
-    int inv = 0;
-    for (int base = b0; base < b1; base += kWave) {
-        const int t = base + lane;
-        const int s = (t < b1) ? slot_of(idx, slot_rank, L, R, t, &inv) : -1;
-        uint64_t rem = __ballot(s >= 0);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int ls = __shfl(s, leader);
-            const uint64_t peers = __ballot(s == ls);
-            if (lane == leader) mycnt[ls] += __popcll(peers);
-            rem &= ~peers;
+    if (inreg) {
+#pragma unroll
+        for (int u = 0; u < kRegSteps; ++u)
+            if (u < nsteps) count_step(sl[u], lane, mycnt);
+    } else {
+        for (int base = b0; base < b1; base += kWave) {
+            const int t = base + lane;
+            count_step(t < b1 ? filt(idx[t]) : -1, lane, mycnt);
         }
     }
     if (inv) atomicAdd(&s_invalid, inv);
@@ -108,26 +154,21 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     __syncthreads();
 
     // Pass 2: scatter token ids in stable order.
-    int dummy = 0;
-    for (int base = b0; base < b1; base += kWave) {
-        const int t = base + lane;
-        const int s = (t < b1) ? slot_of(idx, slot_rank, L, R, t, &dummy) : -1;
-        uint64_t rem = __ballot(s >= 0);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int ls = __shfl(s, leader);
-            const uint64_t peers = __ballot(s == ls);
-            int pos = 0;
-            if (lane == leader) {
-                pos = mycnt[ls];
-                mycnt[ls] = pos + __popcll(peers);
+    if (inreg) {
+#pragma unroll
+        for (int u = 0; u < kRegSteps; ++u)
+            if (u < nsteps) scatter_step(sl[u], b0 + u * kWave + lane, lane, mycnt, seg.perm);
+    } else {
+        int dummy = 0;
+        for (int base = b0; base < b1; base += kWave) {
+            const int t = base + lane;
+            int s = -1;
+            if (t < b1) {
+                const int v = idx[t];
+                s = (v >= 0 && v < L && srank[v] > 0) ? v : -1;
             }
-            pos = __shfl(pos, leader);
-            if (s == ls) {
-                const uint64_t below = peers & ((1ull << lane) - 1ull);
-                seg.perm[pos + __popcll(below)] = t;
-            }
-            rem &= ~peers;
+            (void)dummy;
+            scatter_step(s, t, lane, mycnt, seg.perm);
         }
     }
     for (int i = n_active + tid; i < T; i += kSegThreads) seg.perm[i] = -1;
@@ -147,8 +188,6 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
             seg.tiles_pre[op + q] = make_int4(tid, start + q * kPreTile,
                                               min(start + (q + 1) * kPreTile, start + cnt), 0);
     }
-    // Split-K arrival counters of the decode shrink start at zero.
-    for (int i = tid; i < n_dec * kRgStride; i += kSegThreads) seg.counters[i] = 0;
     if (tid == 0) {
         seg.header[0] = n_active;
         seg.header[1] = s_invalid;
@@ -170,7 +209,7 @@ __global__ void k_fill_zero(uint4 *__restrict__ p, size_t n16, uint8_t *__restri
 
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
                            int32_t R, const SegPtrs &seg, hipStream_t st) {
-    const size_t lds = sizeof(int32_t) * (size_t)kSegWaves * L;
+    const size_t lds = sizeof(int32_t) * (size_t)(kSegWaves + 1) * L;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_segments),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -165,13 +165,29 @@ def main():
         aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
                              d["ws"])
 
+    # Kernel-by-kernel calls that launch exactly the kernels of one step: the
+    # decode path folds the K-chunk reduction into the expand while
+    # ceil(K/256) * R <= 512 (the library's rule), else a reduce kernel runs.
+    # the library's auto rule (abi.hip: choose_path, can_fuse)
+    prefill = (c.dtype == "bf16" and c.R % 16 == 0 and c.T >= 512
+               and c.T // min(c.T, c.L) >= 64)
+    fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
+             and c.T <= 1024)
+    fold = not prefill and math.ceil(c.K / 256) * c.R <= 512
+    part = aa.LORA_FLAG_PARTIAL
+    ready = aa.LORA_FLAG_SEGMENTS_READY
+
     def shrink_only(d):
         aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"],
-                       flags=aa.LORA_FLAG_SEGMENTS_READY | aa.LORA_FLAG_ACTIVE_ONLY)
+                       flags=ready | aa.LORA_FLAG_ACTIVE_ONLY | part)
+
+    def shrink_reduce(d):
+        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"],
+                       flags=ready | aa.LORA_FLAG_ACTIVE_ONLY)
 
     def expand_only(d):
         aa.lora_expand(d["y"], d["buf"], d["B"], d["idx"], d["rank"], d["scale"], d["ws"],
-                       flags=aa.LORA_FLAG_SEGMENTS_READY)
+                       flags=ready | (part if fold else 0))
 
     def segments_only(d):
         aa.lora_build_segments(d["idx"], d["rank"], c.L, c.R, d["ws"])
@@ -179,7 +195,7 @@ def main():
     if args.profile:
         for i in range(max(steps, 1)):
             step(insts[i % n_inst])
-        for fn in (segments_only, shrink_only, expand_only):
+        for fn in (segments_only, shrink_reduce, shrink_only, expand_only):
             for i in range(n_inst):
                 fn(insts[i])
         torch.cuda.synchronize()
@@ -237,7 +253,14 @@ def main():
 
     # ---- per-kernel durations, live, with events around graphs of one kernel
     per_kernel = {}
-    for name, fn in (("segments", segments_only), ("shrink", shrink_only), ("expand", expand_only)):
+    if fused:
+        kernel_calls = [("fused", step)]      # the whole step is one kernel
+    else:
+        kernel_calls = [("segments", segments_only), ("shrink", shrink_only)]
+        if not fold and not prefill:
+            kernel_calls.append(("shrink+reduce", shrink_reduce))
+        kernel_calls.append(("expand", expand_only))
+    for name, fn in kernel_calls:
         g = capture(fn, n_inst)
         reps = max(1, 2000 // n_inst)
         for _ in range(2):
@@ -251,10 +274,19 @@ def main():
         torch.cuda.synchronize()
         per_kernel[name] = a0.elapsed_time(a1) * 1e3 / (reps * n_inst)   # us per launch
         del g
+    if "shrink+reduce" in per_kernel:
+        per_kernel["reduce"] = per_kernel.pop("shrink+reduce") - per_kernel["shrink"]
+    # the expand above must leave every instance's buffer state as a step does
+    for i in range(n_inst):
+        step(insts[i])
+    torch.cuda.synchronize()
 
     ab = algorithmic_bytes(c)
-    dom = max(("shrink", "expand"), key=lambda k: per_kernel[k])
-    dom_bytes = ab[dom]
+    if fused:
+        dom, dom_bytes = "fused", ab["shrink"] + ab["expand"]
+    else:
+        dom = max(("shrink", "expand"), key=lambda k: per_kernel[k])
+        dom_bytes = ab[dom]
     achieved = dom_bytes / (per_kernel[dom] * 1e-6) / 1e9
     khash = kernel_hash()
     traffic = load_traffic(args.workload, dom, khash)

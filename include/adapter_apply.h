@@ -41,8 +41,11 @@
  *            element of the expand ([SGL] prepare_lora_batch scalings).
  *   dtype    LORA_DT_BF16 (x, A, B, y all bf16) or LORA_DT_F32 (all fp32;
  *            decode path only).  The intermediate buffer is always fp32.
- *   path     LORA_PATH_AUTO chooses per call; DECODE forces the VALU path;
- *            PREFILL forces the MFMA path (bf16, R % 16 == 0 only).
+ *   path     LORA_PATH_AUTO chooses per call; DECODE forces the split
+ *            (segments, VALU shrink, expand) decode path; PREFILL forces the
+ *            MFMA path (bf16, R % 16 == 0 only); FUSED forces the
+ *            single-launch decode kernel of lora_apply_packed (bf16,
+ *            R % 16 == 0, R <= 64, T <= 1024; it needs no workspace).
  *   ws       device workspace of at least lora_workspace_size() bytes,
  *            256-byte aligned, owned by the caller.  Calls sharing a
  *            workspace must be ordered on one stream.  The workspace must be
@@ -56,6 +59,11 @@
  *            of tokens that carry an adapter and ranks j < r; the other
  *            entries keep their contents (saves a fill when the buffer only
  *            feeds lora_expand, which never reads them).
+ *            LORA_FLAG_PARTIAL (lora_shrink then lora_expand, same ws, buf
+ *            and path): on the decode path the shrink leaves its per-K-chunk
+ *            partial sums in the workspace and the expand adds them (one
+ *            launch fewer); buf is then neither written nor read.  The
+ *            prefill path ignores the flag and goes through buf.
  *
  * Alignment: x, y, A[s], B[s] 16-byte aligned; ldx % 8 == 0; ldy and
  * y_col_offset % 4 == 0; buf 16-byte aligned.  Violations -> LORA_E_ALIGN.
@@ -90,9 +98,11 @@ typedef int32_t lora_status_t;
 #define LORA_PATH_AUTO     0
 #define LORA_PATH_DECODE   1
 #define LORA_PATH_PREFILL  2
+#define LORA_PATH_FUSED    3
 
 #define LORA_FLAG_SEGMENTS_READY 1u
 #define LORA_FLAG_ACTIVE_ONLY    2u
+#define LORA_FLAG_PARTIAL        4u
 
 #define LORA_MAX_SLICES 8
 #define LORA_MAX_RANK   512

@@ -94,9 +94,13 @@ def _apply(**kw):
     (dict(x=FAKE + 8), aa.LORA_E_ALIGN),
     (dict(y=FAKE + 4), aa.LORA_E_ALIGN),
     (dict(A=_ptrs(3, FAKE + 2)), aa.LORA_E_ALIGN),
-    (dict(ws=None), aa.LORA_E_NULL),
-    (dict(ws=FAKE_WS + 64), aa.LORA_E_ALIGN),
-    (dict(wsb=1024), aa.LORA_E_WORKSPACE),
+    # the split decode path needs the workspace (the fused one does not)
+    (dict(ws=None, path=aa.LORA_PATH_DECODE), aa.LORA_E_NULL),
+    (dict(ws=FAKE_WS + 64, path=aa.LORA_PATH_DECODE), aa.LORA_E_ALIGN),
+    (dict(wsb=1024, path=aa.LORA_PATH_DECODE), aa.LORA_E_WORKSPACE),
+    (dict(path=aa.LORA_PATH_FUSED, R=128), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_FUSED, T=2048), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_FUSED, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, R=24), aa.LORA_E_PATH),
     (dict(path=5), aa.LORA_E_PATH),

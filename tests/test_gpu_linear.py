@@ -16,7 +16,7 @@ import synth  # noqa: E402
 from tests import bounds  # noqa: E402
 from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
 
-DEC, PRE = aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL
+DEC, PRE, FUS = aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -63,12 +63,13 @@ def test_tiny_fp32_decode(oracle_mod):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS])
 @pytest.mark.parametrize("seed,T,K,N,R,L", [
     (21, 200, 512, [256, 64, 64], 16, 5),
     (22, 333, 1024, [128, 128], 32, 3),
     (23, 97, 2056, [520], 64, 7),          # K not a multiple of the K chunk, ragged tail
     (24, 1, 64, [4], 16, 1),
+    (25, 1024, 256, [16, 1028], 48, 1024),   # one token per slot, 1024 slots
 ])
 def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
@@ -83,7 +84,7 @@ def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS])
 def test_decode_config_qkv(oracle_mod, path):
     """256 tokens, hidden 4096, QKV 4096/1024/1024, rank 16, 8 slots, 10% idx=-1."""
     c = synth.config_decode()
@@ -204,6 +205,24 @@ def test_expand_from_given_buffer(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
+@pytest.mark.parametrize("cfg", ["decode", "many"])
+def test_partial_flag_split_calls(oracle_mod, cfg):
+    """lora_shrink(PARTIAL) + lora_expand(PARTIAL): partial sums stay in the
+    workspace, the caller's buffer is never touched."""
+    c = synth.config_decode(T=200) if cfg == "decode" else synth.config_many(T=300)
+    log(f"case partial flag {cfg}")
+    d = LinearOnDevice(c)
+    buf = torch.full((c.S, c.T, c.R), 5.0, dtype=torch.float32, device="cuda")
+    aa.lora_shrink(buf, d.x, d.A, d.idx, d.rank, d.ws, path=DEC, flags=aa.LORA_FLAG_PARTIAL)
+    aa.lora_expand(d.y, buf, d.B, d.idx, d.rank, d.scale, d.ws, path=DEC,
+                   flags=aa.LORA_FLAG_PARTIAL | aa.LORA_FLAG_SEGMENTS_READY)
+    y = d.y_host()
+    assert bool(torch.all(buf == 5.0))
+    bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
 # ---------------------------------------------------------------------------
 # segments and edge cases
 # ---------------------------------------------------------------------------
@@ -241,7 +260,7 @@ def test_all_tokens_without_adapter_unchanged():
     c = synth.config_decode(T=64)
     c.idx[:] = -1
     d = LinearOnDevice(c)
-    for path in (DEC, PRE):
+    for path in (DEC, PRE, FUS):
         d.apply(path)
         y = d.y_host()
         assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
@@ -254,7 +273,7 @@ def test_zero_b_identity_and_invalid_slots(oracle_mod):
     c.idx[::11] = 100
     c.slot_rank[3] = 0    # empty slot
     c.B = [np.zeros_like(b) for b in c.B]
-    for path in (DEC, PRE):
+    for path in (DEC, PRE, FUS):
         d = LinearOnDevice(c)
         d.apply(path)
         y = d.y_host()
@@ -270,7 +289,7 @@ def test_column_offset_and_wide_rows(oracle_mod):
     wide = rng.standard_normal((c.T, 200)).astype(np.float32)
     wide = synth.round_bf16(wide)
     off = 40
-    for path in (DEC, PRE):
+    for path in (DEC, PRE, FUS):
         yw = dev(wide, torch.bfloat16)
         d = LinearOnDevice(c, guard=False)
         aa.lora_apply_packed(yw, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, y_col_offset=off,
@@ -303,14 +322,39 @@ def test_segments_reused_across_layers(oracle_mod):
             bounds.check_bf16_tolerance(d.y_host(), oracle_y(oracle_mod, c))
 
 
-def test_deterministic_run_twice():
-    c = synth.config_many(T=512)
+@pytest.mark.parametrize("cfg,path", [("many", DEC), ("decode", FUS), ("decode", PRE)])
+def test_deterministic_run_twice(cfg, path):
+    c = synth.config_many(T=512) if cfg == "many" else synth.config_decode()
     outs = []
     for _ in range(2):
         d = LinearOnDevice(c, guard=False)
-        d.apply(DEC)
+        d.apply(path)
         outs.append(d.y_host())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_fused_skewed_slots(oracle_mod):
+    """All tokens on one slot (many groups of one slot) and ranks below 16."""
+    rng = np.random.default_rng(12)
+    idx = np.zeros(700, np.int32)
+    idx[rng.random(700) < 0.05] = 3
+    idx[::50] = -1
+    c = synth.make_linear("skew", 700, 512, [64, 256], 32, 4, idx, [32, 8, 16, 8],
+                          [1.0, 1.0, 1.0, 0.5], "bf16", seed=13)
+    d = LinearOnDevice(c)
+    d.apply(FUS)
+    y = d.y_host()
+    bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
+def test_fused_rejects_unsupported():
+    c = synth.config_many(T=64)          # rank 128 > 64
+    d = LinearOnDevice(c, guard=False)
+    with pytest.raises(aa.LoraError) as e:
+        d.apply(FUS)
+    assert e.value.code == aa.LORA_E_PATH
 
 
 def test_zero_tokens_noop():
