@@ -59,8 +59,12 @@ lora_status_t check_ptrs(const void *const *P, int32_t S) {
     return LORA_OK;
 }
 
-bool can_fuse(int32_t T, int32_t R, int32_t dtype) {
-    return dtype == LORA_DT_BF16 && R % 16 == 0 && R <= kFusedMaxRank && T <= kFusedMaxTokens;
+bool can_fuse(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int32_t dtype) {
+    if (dtype != LORA_DT_BF16 || R % 16 || R > kFusedMaxRank || T > kFusedMaxTokens) return false;
+    if (K % 1024) return false;                  // 16 waves x whole 64-element lines of K
+    for (int s = 0; s < S; ++s)
+        if (N[s] % 8) return false;              // 8 output columns per lane
+    return true;
 }
 
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
@@ -253,7 +257,7 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
-    const bool fuse = !use_prefill && can_fuse(T, R, dtype) &&
+    const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, dtype) &&
                       (path == LORA_PATH_FUSED || path == LORA_PATH_AUTO);
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
     if (T == 0) return LORA_OK;

@@ -23,8 +23,8 @@ constexpr int kDecRows = 16;   // rows of the (slice, rank) space per work-group
 
 // Single-launch decode (fused shrink + expand).
 constexpr int kFusedGroup = 16;        // tokens of one slot per work-group
-constexpr int kFusedCols = 512;        // output columns per work-group
-constexpr int kFusedMaxRank = 64;
+constexpr int kFusedCols = 1024;       // output columns per work-group
+constexpr int kFusedMaxRank = 32;
 constexpr int kFusedMaxTokens = 1024;  // idx staged in LDS
 constexpr int kFusedXcds = 8;
 

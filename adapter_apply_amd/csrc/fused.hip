@@ -4,7 +4,7 @@
 // extra kernel or dependent global load costs more than the data itself, so
 // this path has no segment build, no workspace and no second launch.
 //
-// Work-group (16 waves) = (token group g, output chunk c).  The groups are the slot-major
+// Work-group (16 waves) = (token group g, output chunk c of 1024 columns).  The groups are the slot-major
 // runs of at most 16 tokens that a stable sort by slot would give; every
 // work-group derives them itself from idx (staged in LDS: histogram, scan over
 // slots, ballot compaction), so its only dependent global loads are
@@ -12,14 +12,17 @@
 // slice.  Each work-group then
 //   1. shrinks its group for that slice with v_mfma_f32_16x16x32_bf16
 //      (16 tokens x 16 ranks blocks; the 16 waves split K and add in LDS),
-//   2. expands its 512 columns with v_mfma_f32_16x16x16_bf16 formed as
-//      D[n][t] = B[n][:] . buf[t][:], so a lane holds 4 consecutive columns of
-//      one token and y moves 8 bytes per lane.
+//   2. expands its columns with v_mfma_f32_16x16x16_bf16 formed as
+//      D[n][t] = B[n][:] . buf[t][:].
 // The shrink of a (group, slice) is recomputed by each chunk of that slice:
 // the price of one launch, paid in L2 reads (x rows and lora_a rows).
-// The kernel is bound by memory latency, so every global load a wave needs
-// (its K slice of x and lora_a, its lora_b rows and y values) is issued
-// before the first of them is consumed.
+// Every global access is row-contiguous (a wave instruction covers whole
+// 128-byte lines): on this part a load that spreads a wave over 16 rows at
+// 64 bytes each runs ~3.5x slower per CU than one covering 8 full lines.
+// Each wave therefore loads its K slice of the x and lora_a rows line by line,
+// all before the first use, and turns them into MFMA fragments through its
+// own swizzled LDS staging area; the output goes through an LDS buffer so y
+// is read and written 16 bytes per lane along rows.
 #include "common.hpp"
 
 namespace aa {
@@ -27,11 +30,11 @@ namespace aa {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;   // 16: each owns 1/16 of K and 2 of the 32 column blocks
-constexpr int kG = kFusedGroup;            // tokens per group
-constexpr int kCols = kFusedCols;          // output columns per work-group
-constexpr int kRmax = kFusedMaxRank;       // ranks held in LDS
-constexpr int kNbPerWave = kCols / 16 / kWaves;
+constexpr int kWaves = kThreads / kWave;   // 16
+constexpr int kG = kFusedGroup;            // tokens per group (16)
+constexpr int kCols = kFusedCols;          // output columns per work-group (1024)
+constexpr int kColsW = kCols / kWaves;     // 64 per wave = 4 blocks of 16
+constexpr int kSub = 64;                   // K elements per sub-chunk: one 128-byte line per row
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
@@ -52,26 +55,43 @@ struct FusedArgs {
 __device__ __forceinline__ bf16x8_t frag8(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ short4_t frag4(const uint2 &u) { return __builtin_bit_cast(short4_t, u); }
 
-// NRB: 16-rank blocks of the padded rank R (1..4); the per-slot rank may be lower.
+// Byte offset of 16-byte unit u of row r in a staging area of 128-byte rows;
+// the unit index is XOR-swizzled with the row so fragment reads of 8
+// consecutive rows hit 8 different bank groups.
+__device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ (r & 7)) << 4); }
+
+// NRB: 16-rank blocks of the padded rank R (1 or 2); the slot's own rank may be lower.
+template <int NRB>
+struct FusedSmem {
+    static constexpr int RR = kG * (1 + NRB);                  // staged rows per sub-chunk: x then lora_a
+    static constexpr int kStage = kWaves * RR * 128;           // per-wave staging areas
+    static constexpr int kDelta = kG * (kCols + 4) * 4;        // fp32 deltas, aliases the staging
+    static constexpr int kUnion = kStage > kDelta ? kStage : kDelta;
+    static constexpr int kPart = kWaves * kG * (NRB * 16 + 4) * 4;
+};
+
 template <int NRB>
 __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
-    constexpr int KB = 8 / NRB;   // k-steps of 32 per load batch (register budget)
+    using SM = FusedSmem<NRB>;
+    constexpr int RR = SM::RR;
+    constexpr int SUBB = 4 / NRB;                  // sub-chunks per load batch (register budget)
+    constexpr int LPS = RR / 8;                    // load instructions per sub-chunk (8 rows x 128 B each)
+    constexpr int BROW = NRB * 32;                 // bytes of one lora_b row (R = 16 * NRB)
+    constexpr int BLD = kColsW * BROW / 1024;      // load instructions for a wave's lora_b rows
+
+    __shared__ __attribute__((aligned(16))) char s_union[SM::kUnion];
+    __shared__ __attribute__((aligned(16))) float s_part[kWaves][kG][NRB * 16 + 4];
     __shared__ int32_t s_slot[kFusedMaxTokens];   // active slot of each token, -1 if none
     __shared__ int32_t s_rank[kMaxSlots];
     __shared__ int32_t s_cnt[kMaxSlots];          // tokens per slot
     __shared__ int32_t s_tok[kG];
     __shared__ int32_t s_info[4];                 // slot, rank within slot of the first token, count
-    __shared__ float s_part[kWaves][kG][NRB * 16 + 4];
     __shared__ __attribute__((aligned(16))) uint16_t s_buf[kG][NRB * 16 + 8];   // bf16 buffer
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // All chunks of a group go to one XCD (work-groups are dealt to the 8 XCDs
-    // round-robin), so the group's x rows and lora_a rows are fetched into one L2.
-    const int xcd = blockIdx.x % kFusedXcds;
-    const int local = blockIdx.x / kFusedXcds;
-    const int chunk = local % a.n_chunks;
-    const int group = xcd + kFusedXcds * (local / a.n_chunks);
-    if (group >= a.max_groups) return;
+    // Live work-groups are the first ones, so they spread evenly over the XCDs.
+    const int chunk = blockIdx.x % a.n_chunks;
+    const int group = blockIdx.x / a.n_chunks;
     const int T = a.T, L = a.L;
 
     // ---- 1. who am I: stage idx and ranks, count per slot -------------------
@@ -81,11 +101,20 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
     }
     for (int i = tid; i < T; i += kThreads) s_slot[i] = a.idx[i];
     __syncthreads();
-    for (int i = tid; i < T; i += kThreads) {
-        const int v = s_slot[i];
-        const bool ok = v >= 0 && v < L && s_rank[v] > 0;
-        s_slot[i] = ok ? v : -1;
-        if (ok) atomicAdd(&s_cnt[v], 1);
+    for (int base = w * kWave; base < T; base += kThreads) {
+        // one LDS atomic per (wave, slot): lanes of a slot are counted by ballot
+        const int i = base + lane;
+        int v = i < T ? s_slot[i] : -1;
+        v = (v >= 0 && v < L && s_rank[v] > 0) ? v : -1;
+        if (i < T) s_slot[i] = v;
+        uint64_t rem = __ballot(v >= 0);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int ls = __shfl(v, leader);
+            const uint64_t peers = __ballot(v == ls);
+            if (lane == leader) atomicAdd(&s_cnt[ls], __popcll(peers));
+            rem &= ~peers;
+        }
     }
     __syncthreads();
     // Wave 0: exclusive scan of groups per slot, find this group's slot.
@@ -132,77 +161,80 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
     }
     int sg = 0;
     while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
-    const int64_t Ns = a.sl.n[sg];
+    const int Ns = (int)a.sl.n[sg];
     const int n_base = (chunk - a.chunk_start[sg]) * kCols;
     __syncthreads();
 
-    const int nrb = (r + 15) >> 4;                       // 16-rank blocks of this slot
     const int row = lane & 15, quad = lane >> 4;
     const float sc = a.scale[s];
+    char *stage = s_union + w * (RR * 128);
 
-    // ---- 2. expand-side loads first: they do not depend on the shrink -------
-    // A operand: lora_b rows (output columns); y: token `row`, 4 columns.
-    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + (int64_t)s * Ns * a.R;
-    // Unconditional loads from clamped rows (the group's first token, the last
-    // output column; R >= 16 * NRB); padding results are never stored.
-    const bool tcol_ok = row < ntok;
-    uint16_t *yrow = a.y + (int64_t)s_tok[tcol_ok ? row : 0] * a.ldy + a.sl.off[sg];
-    uint2 bq[kNbPerWave][NRB], yv[kNbPerWave];
-    bool y_ok[kNbPerWave];
+    // ---- 2. expand-side loads, row-contiguous, issued first ----------------
+    // lora_b rows of this wave's 64 columns: one contiguous block of 64 * BROW bytes.
+    const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) +
+                                                      (int64_t)s * Ns * a.R);
+    uint4 bq[BLD];
 #pragma unroll
-    for (int e = 0; e < kNbPerWave; ++e) {
-        const int n0 = n_base + (w + kWaves * e) * 16;
-        const uint16_t *brow = bbase + (int64_t)min(n0 + row, (int)Ns - 1) * a.R;
-#pragma unroll
-        for (int ks = 0; ks < NRB; ++ks) bq[e][ks] = ldg<uint2>(brow + 16 * ks + 4 * quad);
-        const int n = n0 + 4 * quad;
-        y_ok[e] = tcol_ok && n < Ns;                     // N_s % 4 == 0
-        yv[e] = ldg<uint2>(yrow + min(n, (int)Ns - 4));
+    for (int i = 0; i < BLD; ++i) {
+        const int byte = 1024 * i + 16 * lane;                 // within the wave's block
+        const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
+        bq[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + (int64_t)nr * BROW + byte % BROW));
     }
+    // y: wave w owns token w of the group, 8 columns per lane, 2 x 512 columns.
+    const bool ytok = w < ntok;
+    uint16_t *yrow = a.y + (int64_t)s_tok[ytok ? w : 0] * a.ldy + a.sl.off[sg];
+    uint4 yv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) yv[i] = ldg<uint4>(yrow + min(n_base + 512 * i + 8 * lane, Ns - 8));
 
     // ---- 3. shrink of the group for slice sg (MFMA 16x16x32) ----------------
     {
-        // x rows past the group and lora_a rows past the rank are clamped to valid
-        // rows; the garbage they make is dropped when the buffer is formed.
-        const uint16_t *xr = a.x + (int64_t)s_tok[row < ntok ? row : 0] * a.ldx;
+        // staged row p: x row of token p (p < 16) or lora_a rank row p - 16; rows
+        // past the group or the rank are clamped to valid ones and dropped later.
+        const uint16_t *srcrow[LPS];
         const uint16_t *abase = static_cast<const uint16_t *>(a.sl.a[sg]) + (int64_t)s * a.R * a.K;
-        const uint16_t *arow[NRB];
 #pragma unroll
-        for (int b = 0; b < NRB; ++b) arow[b] = abase + (int64_t)min(16 * b + row, r - 1) * a.K;
-        const int ksteps = (a.K + 31) >> 5;
-        const int kper = (ksteps + kWaves - 1) / kWaves;
-        const int k_lo = w * kper * 32, k_hi = min(a.K, (w + 1) * kper * 32);
+        for (int i = 0; i < LPS; ++i) {
+            const int p = 8 * i + (lane >> 3);
+            srcrow[i] = p < kG ? a.x + (int64_t)s_tok[p < ntok ? p : 0] * a.ldx
+                               : abase + (int64_t)min(p - kG, r - 1) * a.K;
+        }
+        const int ucol = 8 * (lane & 7);                       // element offset of this lane's unit
+        const int kw = a.K / kWaves;                           // K % 1024 == 0
+        const int nsub = kw / kSub;
         floatx4_t acc[NRB];
 #pragma unroll
         for (int b = 0; b < NRB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        int k0 = k_lo;
-        for (; k0 + KB * 32 <= k_hi; k0 += KB * 32) {   // whole batches, no guards
-            uint4 xf[KB], af[KB][NRB];
+        for (int c0 = 0; c0 < nsub; c0 += SUBB) {
+            uint4 v[SUBB][LPS];
 #pragma unroll
-            for (int u = 0; u < KB; ++u) {
-                const int k = k0 + 32 * u + 8 * quad;
-                xf[u] = ldg<uint4>(xr + k);
+            for (int c = 0; c < SUBB; ++c)
 #pragma unroll
-                for (int b = 0; b < NRB; ++b) af[u][b] = ldg<uint4>(arow[b] + k);
+                for (int i = 0; i < LPS; ++i) {
+                    const int k = w * kw + (c0 + min(c, nsub - 1 - c0)) * kSub + ucol;
+                    v[c][i] = ldg<uint4>(srcrow[i] + k);
+                }
+            // all of the batch's loads stay ahead of the first use
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < SUBB; ++c) {
+                // a sub-chunk past the end (batch padding) re-reads the last one and
+                // contributes zero: a select, not a branch, keeps the loads in flight
+                const bool cv = c0 + c < nsub;
+#pragma unroll
+                for (int i = 0; i < LPS; ++i)
+                    *reinterpret_cast<uint4 *>(stage + stage_off(8 * i + (lane >> 3), lane & 7)) = v[c][i];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    uint4 xf = *reinterpret_cast<const uint4 *>(stage + stage_off(row, 4 * ks + quad));
+                    if (!cv) xf = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < NRB; ++b) {
+                        const uint4 af = *reinterpret_cast<const uint4 *>(stage + stage_off(kG + 16 * b + row, 4 * ks + quad));
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag8(xf), frag8(af), acc[b], 0, 0, 0);
+                    }
+                }
             }
-#pragma unroll
-            for (int u = 0; u < KB; ++u)
-#pragma unroll
-                for (int b = 0; b < NRB; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag8(xf[u]), frag8(af[u][b]), acc[b], 0, 0, 0);
-        }
-        for (; k0 < k_hi; k0 += 32) {                     // K tail, guarded (K % 8 == 0)
-            const int k = k0 + 8 * quad;
-            uint4 xf = make_uint4(0, 0, 0, 0), af[NRB];
-            if (k < k_hi) xf = ldg<uint4>(xr + k);
-#pragma unroll
-            for (int b = 0; b < NRB; ++b) {
-                af[b] = make_uint4(0, 0, 0, 0);
-                if (k < k_hi) af[b] = ldg<uint4>(arow[b] + k);
-            }
-#pragma unroll
-            for (int b = 0; b < NRB; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag8(xf), frag8(af[b]), acc[b], 0, 0, 0);
         }
         // acc[b][i]: token 4*quad + i, rank 16*b + row
 #pragma unroll
@@ -223,23 +255,48 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
     __syncthreads();
 
     // ---- 4. expand (MFMA 16x16x16): D[n][t] = B[n][:] . buf[t][:] ----------
+    // The wave's lora_b rows go through its own staging area into fragment order.
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
     uint2 bfr[NRB];
 #pragma unroll
     for (int ks = 0; ks < NRB; ++ks)
         bfr[ks] = *reinterpret_cast<const uint2 *>(&s_buf[row][16 * ks + 4 * quad]);
+    floatx4_t out[kColsW / 16];
 #pragma unroll
-    for (int e = 0; e < kNbPerWave; ++e) {
+    for (int nb = 0; nb < kColsW / 16; ++nb) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NRB; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(bq[e][ks]), frag4(bfr[ks]), acc, 0, 0, 0);
-        // lane: token `row`, columns n0 + 4*quad .. +3
-        if (y_ok[e]) {
-            const int n = n_base + (w + kWaves * e) * 16 + 4 * quad;
-            uint2 o;
-            o.x = pack_bf16x2(bf16_lo(yv[e].x) + sc * acc[0], bf16_hi(yv[e].x) + sc * acc[1]);
-            o.y = pack_bf16x2(bf16_lo(yv[e].y) + sc * acc[2], bf16_hi(yv[e].y) + sc * acc[3]);
-            *reinterpret_cast<uint2 *>(yrow + n) = o;
+        for (int ks = 0; ks < NRB; ++ks) {
+            const uint2 af = *reinterpret_cast<const uint2 *>(stage + (16 * nb + row) * BROW + 32 * ks + 8 * quad);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(af), frag4(bfr[ks]), acc, 0, 0, 0);
+        }
+        out[nb] = acc;
+    }
+    __syncthreads();   // every wave is done with its staging area (the delta buffer aliases it)
+    // lane: token `row`, columns 64w + 16nb + 4*quad .. +3 of the chunk
+    float *s_delta = reinterpret_cast<float *>(s_union);
+#pragma unroll
+    for (int nb = 0; nb < kColsW / 16; ++nb)
+        *reinterpret_cast<float4 *>(s_delta + row * (kCols + 4) + w * kColsW + 16 * nb + 4 * quad) =
+            make_float4(sc * out[nb][0], sc * out[nb][1], sc * out[nb][2], sc * out[nb][3]);
+    __syncthreads();
+    // y: wave w writes token w's row, 16 bytes per lane.
+    if (ytok) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cl = 512 * i + 8 * lane;
+            if (n_base + cl < Ns) {
+                const float4 d0 = *reinterpret_cast<const float4 *>(s_delta + w * (kCols + 4) + cl);
+                const float4 d1 = *reinterpret_cast<const float4 *>(s_delta + w * (kCols + 4) + cl + 4);
+                const uint4 y0 = yv[i];
+                uint4 o;
+                o.x = pack_bf16x2(bf16_lo(y0.x) + d0.x, bf16_hi(y0.x) + d0.y);
+                o.y = pack_bf16x2(bf16_lo(y0.y) + d0.z, bf16_hi(y0.y) + d0.w);
+                o.z = pack_bf16x2(bf16_lo(y0.z) + d1.x, bf16_hi(y0.z) + d1.y);
+                o.w = pack_bf16x2(bf16_lo(y0.w) + d1.z, bf16_hi(y0.w) + d1.w);
+                *reinterpret_cast<uint4 *>(yrow + n_base + cl) = o;
+            }
         }
     }
 }
@@ -267,14 +324,11 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
     for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
     a.n_chunks = c;
     a.max_groups = fused_max_groups(T, L);
-    const int per_xcd = (a.max_groups + kFusedXcds - 1) / kFusedXcds;
-    dim3 grid((unsigned)(kFusedXcds * per_xcd * c));
-    switch ((R + 15) / 16) {
-        case 1: hipLaunchKernelGGL(k_dec_fused<1>, grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(k_dec_fused<2>, grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(k_dec_fused<3>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_dec_fused<4>, grid, dim3(kThreads), 0, st, a); break;
-    }
+    dim3 grid((unsigned)(a.max_groups * c));
+    if (R <= 16)
+        hipLaunchKernelGGL(k_dec_fused<1>, grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_dec_fused<2>, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@
  *            (segments, VALU shrink, expand) decode path; PREFILL forces the
  *            MFMA path (bf16, R % 16 == 0 only); FUSED forces the
  *            single-launch decode kernel of lora_apply_packed (bf16,
- *            R % 16 == 0, R <= 64, T <= 1024; it needs no workspace).
+ *            R % 16 == 0, R <= 32, T <= 1024, K % 1024 == 0, N % 8 == 0;
+ *            it needs no workspace).
  *   ws       device workspace of at least lora_workspace_size() bytes,
  *            256-byte aligned, owned by the caller.  Calls sharing a
  *            workspace must be ordered on one stream.  The workspace must be
