@@ -34,6 +34,9 @@ LORA_PATH_DECODE = 1
 LORA_PATH_PREFILL = 2
 LORA_PATH_FUSED = 3
 
+MOE_LORA_W13 = 0
+MOE_LORA_W2 = 1
+
 LORA_FLAG_SEGMENTS_READY = 1
 LORA_FLAG_ACTIVE_ONLY = 2
 LORA_FLAG_PARTIAL = 4
@@ -64,6 +67,13 @@ SIGNATURES = {
                            _vp, _i32, _i32, _u32, _vp, _sz, _vp]),
     "lora_apply_packed": (_i32, [_vp, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32,
                                  _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "moe_lora_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)]),
+    "moe_lora_align_capacity": (_i32, [_i32, _i32, _i32, _i32, C.POINTER(_i32)]),
+    "moe_lora_align": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                              _vp, _sz, _vp]),
+    "moe_lora_apply": (_i32, [_i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _vp,
+                              _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32,
+                              _u32, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -223,12 +233,66 @@ def lora_apply_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
            "lora_apply_packed")
 
 
-def alloc_workspace(T: int, K: int, S: int, R: int, L: int, device="cuda"):
-    """A zero-filled workspace tensor (uint8) of the required size."""
+def _aligned_ws(n: int, device):
     torch = _torch()
-    n = lora_workspace_size(T, K, S, R, L)
     ws = torch.empty(max(n, 256) + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     ws = ws[off:off + max(n, 256)]
     lora_workspace_init(ws)
     return ws
+
+
+def alloc_workspace(T: int, K: int, S: int, R: int, L: int, device="cuda"):
+    """A zero-filled workspace tensor (uint8) of the required size."""
+    return _aligned_ws(lora_workspace_size(T, K, S, R, L), device)
+
+
+# ---------------------------------------------------------------------------
+# fused MoE
+# ---------------------------------------------------------------------------
+
+def moe_lora_workspace_size(T: int, top_k: int, S: int, R: int, L: int, E: int) -> int:
+    n = _sz(0)
+    _check(lib().moe_lora_workspace_size(T, top_k, S, R, L, E, C.byref(n)),
+           "moe_lora_workspace_size")
+    return int(n.value)
+
+
+def moe_lora_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:
+    c = _i32(0)
+    _check(lib().moe_lora_align_capacity(T, top_k, E, block_m, C.byref(c)),
+           "moe_lora_align_capacity")
+    return int(c.value)
+
+
+def alloc_moe_workspace(T: int, top_k: int, S: int, R: int, L: int, E: int, device="cuda"):
+    return _aligned_ws(moe_lora_workspace_size(T, top_k, S, R, L, E), device)
+
+
+def moe_lora_align(topk_ids, idx, slot_rank, E: int, L: int, R: int, block_m: int, ws,
+                   sorted_ids=None, block_expert=None, num_post_padded=None, stream=None):
+    """topk_ids [T, top_k] int32; outputs (optional) [L, cap], [L, cap/bm], [L] int32."""
+    T, k = topk_ids.shape
+    _check(lib().moe_lora_align(_ptr(topk_ids), _ptr(idx), _ptr(slot_rank), T, k, E, L, R,
+                                block_m, _ptr(sorted_ids), _ptr(block_expert),
+                                _ptr(num_post_padded), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "moe_lora_align")
+
+
+def moe_lora_apply(kind: int, y, x, A: Sequence, B: Sequence, topk_ids, topk_w, idx, slot_rank,
+                   scale, E: int, ws, reduce_k: bool = False, flags: int = 0, stream=None):
+    """A[s] [L, E_a, R, K]; B[s] [L, E_b, N_s, R]; y updated in place."""
+    _rowmajor(x, "x")
+    _rowmajor(y, "y")
+    _stacked(A, "A", 4)
+    _stacked(B, "B", 4)
+    T, k = topk_ids.shape
+    L, E_a, R, K = A[0].shape
+    E_b = B[0].shape[1]
+    S = len(A)
+    N = (_i64 * S)(*[b.shape[2] for b in B])
+    _check(lib().moe_lora_apply(kind, _ptr(y), y.stride(0), int(bool(reduce_k)), _ptr(x),
+                                x.stride(0), T, k, K, _ptr_array(A), E_a, _ptr_array(B), E_b, N, S,
+                                E, L, R, _ptr(topk_ids), _ptr(topk_w), _ptr(idx), _ptr(slot_rank),
+                                _ptr(scale), _dtype_code(x), flags, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "moe_lora_apply")

@@ -90,9 +90,11 @@ inline int32_t row_groups(int32_t S, int32_t R) {
     return (S * R + kDecRows - 1) / kDecRows;
 }
 
-inline SegLayout seg_layout(int32_t T, int32_t L) {
+// T items (tokens, or token-expert pairs), L keys (slots, or slot-expert pairs),
+// placed at byte offset `base` of the workspace.
+inline SegLayout seg_layout(int32_t T, int32_t L, size_t base = 0) {
     SegLayout l{};
-    size_t o = 0;
+    size_t o = base;
     l.header = o;     o = align256(o + 16 * sizeof(int32_t));
     l.slot_start = o; o = align256(o + sizeof(int32_t) * (size_t)(L + 1));
     l.perm = o;       o = align256(o + sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
@@ -113,6 +115,29 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
     w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
     w.end = o;
     return w;
+}
+
+// Fused-MoE workspace: token segments (by slot), pair segments (by slot and
+// expert) and the fp32 buffer [S][T*k][R].
+struct MoeWsLayout {
+    SegLayout tok;
+    SegLayout pair;
+    size_t buf;
+    size_t end;
+};
+
+inline MoeWsLayout moe_ws_layout(int32_t T, int32_t k, int32_t S, int32_t R, int32_t L, int32_t E) {
+    MoeWsLayout m{};
+    m.tok = seg_layout(T, L, 0);
+    m.pair = seg_layout(T * k, L * E, m.tok.end);
+    m.buf = m.pair.end;
+    m.end = align256(m.buf + sizeof(float) * (size_t)S * T * k * R);
+    return m;
+}
+
+inline int32_t moe_align_capacity(int32_t T, int32_t k, int32_t E, int32_t bm) {
+    const int64_t c = (int64_t)T * k + (int64_t)E * (bm - 1);
+    return (int32_t)((c + bm - 1) / bm * bm);
 }
 
 // Device view of the segments.
@@ -150,6 +175,10 @@ struct Slices {
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
                            int32_t R, const SegPtrs &seg, hipStream_t st);
+// Items are tokens (topk == nullptr) or (token, k) pairs keyed by slot * E + expert.
+hipError_t launch_segments_keyed(const int32_t *idx, const int32_t *slot_rank,
+                                 const int32_t *topk, int32_t k, int32_t E, int32_t n_items,
+                                 int32_t L, int32_t R, const SegPtrs &seg, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
 // Writes the K-chunk partial sums; launch_dec_reduce (or the expand) adds them.
@@ -168,17 +197,38 @@ hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf,
                              const int32_t *slot_rank, const float *scale, const SegPtrs &seg,
                              hipStream_t st);
 
+hipError_t launch_moe_align_out(const SegPtrs &pair, int32_t T, int32_t k, int32_t E, int32_t L,
+                                int32_t bm, int32_t *sorted_ids, int32_t *block_expert,
+                                int32_t *num_post_padded, hipStream_t st);
+
 int32_t fused_max_groups(int32_t T, int32_t L);
 hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,
                             hipStream_t st);
 
+// Grouped-problem mapping of the MFMA kernels.  A tile's key is
+// slot * Ekey + expert (Ekey = 1 for token tiles); the lora tensor it reads is
+// group slot * Ew + (Ew == 1 ? 0 : expert).  An item of the row list maps to
+// x row item / x_div, buffer row item / buf_div and y row item / y_div.
+struct GroupMap {
+    int32_t Ekey = 1;
+    int32_t Ew = 1;
+    int32_t x_div = 1;
+    int32_t buf_div = 1;
+    int32_t y_div = 1;
+    int32_t buf_rows = 0;          // rows of the [S][buf_rows][R] buffer
+    const float *coef = nullptr;   // per-item factor (routing weight), or null
+    int32_t ksum = 0;              // expand: buffer row of token t = sum_j coef[t*ksum+j] * buf[t*ksum+j]
+};
+
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
-                             const SegPtrs &seg, float *buf, hipStream_t st);
+                             const SegPtrs &seg, float *buf, hipStream_t st,
+                             const GroupMap &gm = GroupMap());
 hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
-                             const float *scale, const SegPtrs &seg, hipStream_t st);
+                             const float *scale, const SegPtrs &seg, hipStream_t st,
+                             const GroupMap &gm = GroupMap());
 
 }  // namespace aa

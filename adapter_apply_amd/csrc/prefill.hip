@@ -38,6 +38,7 @@ struct PreShrinkArgs {
     SegPtrs seg;
     Slices sl;
     float *buf;
+    GroupMap gm;
 };
 
 struct PreExpandArgs {
@@ -50,6 +51,7 @@ struct PreExpandArgs {
     SegPtrs seg;
     Slices sl;
     int32_t group_start[kMaxSlices + 1];
+    GroupMap gm;
 };
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -59,8 +61,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
     const int tile = blockIdx.x / a.n_cb;
     if (tile >= a.seg.header[3]) return;
     const int4 tl = a.seg.tiles_pre[tile];
-    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w & 1, wn = w >> 1;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
     // slot's rank row 0 of slice 0); their results are never written.
     const int trow = wm * 32 + l32;                    // token within tile
     const bool tok_ok = trow < ntok;
-    const int t_in = a.seg.perm[p0 + (tok_ok ? trow : 0)];
+    const int t_in = a.seg.perm[p0 + (tok_ok ? trow : 0)] / a.gm.x_div;
     const uint16_t *xr = a.x + (int64_t)t_in * a.ldx;
 
     const int col = cb * kShrinkCols + wn * 32 + l32;  // buffer column (slice, rank)
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
     const int sg = col / a.R, j = col - (col / a.R) * a.R;
     const bool col_ok = col < SRf && j < r;
     const uint16_t *ar = static_cast<const uint16_t *>(a.sl.a[col_ok ? sg : 0]) +
-                         ((int64_t)s * a.R + (col_ok ? j : 0)) * (int64_t)a.K;
+                         (grp * a.R + (col_ok ? j : 0)) * (int64_t)a.K;
 
     floatx16_t acc = {};
     const int kofs = 8 * half;
@@ -130,12 +133,63 @@ __global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
     for (int i = 0; i < 16; ++i) {
         const int row = wm * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
         if (row < ntok) {
-            const int t = a.seg.perm[p0 + row];
-            a.buf[((int64_t)sg * a.T + t) * a.R + j] = col_ok ? acc[i] : 0.0f;
+            const int t = a.seg.perm[p0 + row] / a.gm.buf_div;
+            a.buf[((int64_t)sg * a.gm.buf_rows + t) * a.R + j] = col_ok ? acc[i] : 0.0f;
         }
     }
 }
 
+// Per-lane view of one token block of an expand tile: the item, its y row, its
+// scale factor and the 8 buffer values of rank group jj (k-summed if asked).
+struct ExpItem {
+    int item;
+    bool ok;
+    int64_t yrow;
+    float scl;
+};
+
+__device__ __forceinline__ ExpItem exp_item(const PreExpandArgs &a, int p0, int row, int ntok,
+                                            float sc) {
+    ExpItem it;
+    it.ok = row < ntok;
+    it.item = a.seg.perm[p0 + (it.ok ? row : 0)];   // clamped: never stored
+    it.yrow = it.item / a.gm.y_div;
+    const float cf = (a.gm.coef && !a.gm.ksum) ? a.gm.coef[it.item] : 1.0f;
+    it.scl = sc * cf;
+    return it;
+}
+
+// 8 buffer values (ranks jj .. jj+7) of an item for slice sg, as two float4;
+// ranks at or past r are zeroed (an expand-only caller may leave them arbitrary).
+__device__ __forceinline__ void buf_vals(const PreExpandArgs &a, int sg, int item, int jj, int r,
+                                         float4 &v0, float4 &v1) {
+    if (a.gm.ksum) {
+        v0 = make_float4(0, 0, 0, 0);
+        v1 = make_float4(0, 0, 0, 0);
+        for (int j = 0; j < a.gm.ksum; ++j) {
+            const int64_t br = (int64_t)item * a.gm.ksum + j;
+            const float w = a.gm.coef ? a.gm.coef[br] : 1.0f;
+            const float *bp = a.buf + ((int64_t)sg * a.gm.buf_rows + br) * a.R + jj;
+            const float4 u0 = ldg<float4>(bp), u1 = ldg<float4>(bp + 4);
+            v0.x += w * u0.x; v0.y += w * u0.y; v0.z += w * u0.z; v0.w += w * u0.w;
+            v1.x += w * u1.x; v1.y += w * u1.y; v1.z += w * u1.z; v1.w += w * u1.w;
+        }
+    } else {
+        const float *bp = a.buf + ((int64_t)sg * a.gm.buf_rows + item / a.gm.buf_div) * a.R + jj;
+        v0 = ldg<float4>(bp);
+        v1 = ldg<float4>(bp + 4);
+    }
+}
+
+__device__ __forceinline__ uint4 pack_frag(const float4 &v0, const float4 &v1, int jj, int r) {
+    return make_uint4(pack_bf16x2(jj + 0 < r ? v0.x : 0.f, jj + 1 < r ? v0.y : 0.f),
+                      pack_bf16x2(jj + 2 < r ? v0.z : 0.f, jj + 3 < r ? v0.w : 0.f),
+                      pack_bf16x2(jj + 4 < r ? v1.x : 0.f, jj + 5 < r ? v1.y : 0.f),
+                      pack_bf16x2(jj + 6 < r ? v1.z : 0.f, jj + 7 < r ? v1.w : 0.f));
+}
+
+// Generic expand, any rank (passes of up to 128 accumulate before the single
+// rounding of y).
 __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     const int xcd = blockIdx.x % kXcds;
     const int local = blockIdx.x / kXcds;
@@ -144,8 +198,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     if (cg >= a.n_cg) return;
     if (tile >= a.seg.header[3]) return;
     const int4 tl = a.seg.tiles_pre[tile];
-    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
     int sg = 0;
     while (sg + 1 < a.S && cg >= a.group_start[sg + 1]) ++sg;
     const int64_t Ns = a.sl.n[sg];
@@ -157,42 +212,27 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     const int nbase = (cg - a.group_start[sg]) * kExpGroupCols + w * kExpWaveCols;
     if (nbase >= Ns) return;
 
-    // buf fragments (B operand): token l32 of each token block, rank 16*ks + 8*half .. +7.
-    uint4 bfrag[2][8];
-    int trow_t[2];
-    bool trow_ok[2];
+    ExpItem it[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int row = tb * 32 + l32;
-        trow_ok[tb] = row < ntok;
-        trow_t[tb] = trow_ok[tb] ? a.seg.perm[p0 + row] : 0;
-    }
-    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + (int64_t)s * Ns * a.R;
+    for (int tb = 0; tb < 2; ++tb) it[tb] = exp_item(a, p0, tb * 32 + l32, ntok, sc);
+    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * a.R;
     uint16_t *ybase = a.y + a.sl.off[sg];
 
-    // Rank handled in passes of up to 128 (8 MFMA k-steps) so fragments stay in
-    // registers; every pass accumulates before the single rounding of y.
+    uint4 bfrag[2][8];
     auto load_bfrag = [&](int kp, int nk) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const float *bp = a.buf + ((int64_t)sg * a.T + trow_t[tb]) * a.R;
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                uint4 f = make_uint4(0, 0, 0, 0);
                 const int jj = (kp + ks) * 16 + 8 * half;
-                if (ks < nk && trow_ok[tb]) {
-                    const float4 v0 = *reinterpret_cast<const float4 *>(bp + jj);
-                    const float4 v1 = *reinterpret_cast<const float4 *>(bp + jj + 4);
-                    // entries at or past the rank are zero in a shrink-written buffer,
-                    // but an expand-only caller may leave them arbitrary.
-                    f.x = pack_bf16x2(jj + 0 < r ? v0.x : 0.f, jj + 1 < r ? v0.y : 0.f);
-                    f.y = pack_bf16x2(jj + 2 < r ? v0.z : 0.f, jj + 3 < r ? v0.w : 0.f);
-                    f.z = pack_bf16x2(jj + 4 < r ? v1.x : 0.f, jj + 5 < r ? v1.y : 0.f);
-                    f.w = pack_bf16x2(jj + 6 < r ? v1.z : 0.f, jj + 7 < r ? v1.w : 0.f);
+                uint4 f = make_uint4(0, 0, 0, 0);
+                if (ks < nk) {
+                    float4 v0, v1;
+                    buf_vals(a, sg, it[tb].item, jj, r, v0, v1);
+                    f = pack_frag(v0, v1, jj, r);
                 }
                 bfrag[tb][ks] = f;
             }
-        }
     };
     const bool one_pass = nks <= 8;
     if (one_pass) load_bfrag(0, nks);
@@ -200,9 +240,8 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     for (int nb = 0; nb < kExpWaveCols / 32; ++nb) {
         const int n0 = nbase + nb * 32;
         if (n0 >= Ns) break;
-        const int nrow = n0 + l32;                       // A-operand row (output column)
-        const bool n_ok = nrow < Ns;
-        const uint16_t *brow = bbase + (int64_t)(n_ok ? nrow : 0) * a.R;
+        const int nrow = min(n0 + l32, (int)Ns - 1);     // A-operand row (output column)
+        const uint16_t *brow = bbase + (int64_t)nrow * a.R;
         floatx16_t acc[2] = {{}, {}};
         for (int kp = 0; kp < nks; kp += 8) {
             const int nk = min(8, nks - kp);
@@ -210,9 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
             uint4 afrag[8];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
-                afrag[ks] = (ks < nk && n_ok)
-                                ? *reinterpret_cast<const uint4 *>(brow + (kp + ks) * 16 + 8 * half)
-                                : make_uint4(0, 0, 0, 0);
+                afrag[ks] = ks < nk ? ldg<uint4>(brow + (kp + ks) * 16 + 8 * half) : make_uint4(0, 0, 0, 0);
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 if (ks < nk) {
@@ -221,22 +258,23 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
                 }
             }
         }
-        // Lane holds columns n0 + 8g + 4*half + {0..3} of token l32 in each token block.
+        // Lane holds columns n0 + 8g + 4*half + {0..3} of its item in each token block.
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            if (!trow_ok[tb]) continue;
-            uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+            if (!it[tb].ok) continue;
+            uint16_t *yrow = ybase + it[tb].yrow * a.ldy;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + 8 * g + 4 * half;
                 if (n < Ns) {
                     uint2 *yp = reinterpret_cast<uint2 *>(yrow + n);
                     const uint2 yv = *yp;
+                    const float c = it[tb].scl;
                     uint2 o;
-                    o.x = pack_bf16x2(bf16_lo(yv.x) + sc * acc[tb][4 * g + 0],
-                                      bf16_hi(yv.x) + sc * acc[tb][4 * g + 1]);
-                    o.y = pack_bf16x2(bf16_lo(yv.y) + sc * acc[tb][4 * g + 2],
-                                      bf16_hi(yv.y) + sc * acc[tb][4 * g + 3]);
+                    o.x = pack_bf16x2(bf16_lo(yv.x) + c * acc[tb][4 * g + 0],
+                                      bf16_hi(yv.x) + c * acc[tb][4 * g + 1]);
+                    o.y = pack_bf16x2(bf16_lo(yv.y) + c * acc[tb][4 * g + 2],
+                                      bf16_hi(yv.y) + c * acc[tb][4 * g + 3]);
                     *yp = o;
                 }
             }
@@ -244,9 +282,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     }
 }
 
-// Fast expand for ranks <= 16 * NKS (NKS <= 4): every load of the wave (buf
+// Fast expand for ranks <= 16 * NKS (NKS <= 4): every load of the wave (buffer
 // fragments, the lora_b fragments and the y values of its 4 column blocks)
-// is issued before the first MFMA, so the wave has ~32 KB in flight.
+// is issued before the first MFMA.
 template <int NKS>
 __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
     constexpr int NB = kExpWaveCols / 32;   // 4 column blocks of 32 per wave
@@ -257,8 +295,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
     if (cg >= a.n_cg) return;
     if (tile >= a.seg.header[3]) return;
     const int4 tl = a.seg.tiles_pre[tile];
-    const int s = tl.x, p0 = tl.y, ntok = tl.z - tl.y;
+    const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
     int sg = 0;
     while (sg + 1 < a.S && cg >= a.group_start[sg + 1]) ++sg;
     const int64_t Ns = a.sl.n[sg];
@@ -270,32 +309,21 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
     const int nbase = (cg - a.group_start[sg]) * kExpGroupCols + w * kExpWaveCols;
     if (nbase >= Ns) return;
 
-    // Rows are clamped to valid ones (the tile's first token, the last output
-    // column); what they produce is never stored.  R >= 16 * NKS, so every
-    // rank step's loads are in bounds.
-    int trow_t[2];
-    bool trow_ok[2];
+    // Items past the tile are clamped to its first one (valid); their results
+    // are never stored.  R >= 16 * NKS, so every rank step's loads are in bounds.
+    ExpItem it[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const int row = tb * 32 + l32;
-        trow_ok[tb] = row < ntok;
-        trow_t[tb] = a.seg.perm[p0 + (trow_ok[tb] ? row : 0)];
-    }
-    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + (int64_t)s * Ns * a.R;
+    for (int tb = 0; tb < 2; ++tb) it[tb] = exp_item(a, p0, tb * 32 + l32, ntok, sc);
+    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * a.R;
     uint16_t *ybase = a.y + a.sl.off[sg];
 
     // ---- all loads ----
     float4 bf[2][NKS][2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const float *bp = a.buf + ((int64_t)sg * a.T + trow_t[tb]) * a.R;
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int jj = ks * 16 + 8 * half;
-            bf[tb][ks][0] = ldg<float4>(bp + jj);
-            bf[tb][ks][1] = ldg<float4>(bp + jj + 4);
-        }
-    }
+        for (int ks = 0; ks < NKS; ++ks)
+            buf_vals(a, sg, it[tb].item, ks * 16 + 8 * half, r, bf[tb][ks][0], bf[tb][ks][1]);
     uint4 af[NB][NKS];
     uint2 yv[NB][2][4];
 #pragma unroll
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
         for (int ks = 0; ks < NKS; ++ks) af[nb][ks] = ldg<uint4>(brow + ks * 16 + 8 * half);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+            const uint16_t *yrow = ybase + it[tb].yrow * a.ldy;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = min(n0 + 8 * g + 4 * half, (int)Ns - 4);
@@ -315,19 +343,13 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
             }
         }
     }
-    // ---- buf fragments to bf16 (entries past the rank forced to zero) ----
+    // ---- buffer fragments to bf16 (entries past the rank forced to zero) ----
     uint4 bfrag[2][NKS];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int jj = ks * 16 + 8 * half;
-            const float4 v0 = bf[tb][ks][0], v1 = bf[tb][ks][1];
-            bfrag[tb][ks] = make_uint4(pack_bf16x2(jj + 0 < r ? v0.x : 0.f, jj + 1 < r ? v0.y : 0.f),
-                                       pack_bf16x2(jj + 2 < r ? v0.z : 0.f, jj + 3 < r ? v0.w : 0.f),
-                                       pack_bf16x2(jj + 4 < r ? v1.x : 0.f, jj + 5 < r ? v1.y : 0.f),
-                                       pack_bf16x2(jj + 6 < r ? v1.z : 0.f, jj + 7 < r ? v1.w : 0.f));
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+            bfrag[tb][ks] = pack_frag(bf[tb][ks][0], bf[tb][ks][1], ks * 16 + 8 * half, r);
     // ---- multiply and update y ----
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -342,17 +364,18 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
         }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            uint16_t *yrow = ybase + (int64_t)trow_t[tb] * a.ldy;
+            uint16_t *yrow = ybase + it[tb].yrow * a.ldy;
+            const float c = it[tb].scl;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + 8 * g + 4 * half;
-                if (trow_ok[tb] && n < Ns) {
+                if (it[tb].ok && n < Ns) {
                     const uint2 y0 = yv[nb][tb][g];
                     uint2 o;
-                    o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[tb][4 * g + 0],
-                                      bf16_hi(y0.x) + sc * acc[tb][4 * g + 1]);
-                    o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[tb][4 * g + 2],
-                                      bf16_hi(y0.y) + sc * acc[tb][4 * g + 3]);
+                    o.x = pack_bf16x2(bf16_lo(y0.x) + c * acc[tb][4 * g + 0],
+                                      bf16_hi(y0.x) + c * acc[tb][4 * g + 1]);
+                    o.y = pack_bf16x2(bf16_lo(y0.y) + c * acc[tb][4 * g + 2],
+                                      bf16_hi(y0.y) + c * acc[tb][4 * g + 3]);
                     *reinterpret_cast<uint2 *>(yrow + n) = o;
                 }
             }
@@ -364,10 +387,12 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
 
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
-                             const SegPtrs &seg, float *buf, hipStream_t st) {
+                             const SegPtrs &seg, float *buf, hipStream_t st, const GroupMap &gm) {
     PreShrinkArgs a;
     a.x = static_cast<const uint16_t *>(x); a.ldx = ldx; a.T = T; a.K = K; a.S = S; a.L = L;
     a.R = R; a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.buf = buf;
+    a.gm = gm;
+    if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
     a.n_cb = (S * R + kShrinkCols - 1) / kShrinkCols;
     dim3 grid((unsigned)(a.n_cb * seg.max_tiles_pre));
     hipLaunchKernelGGL(k_pre_shrink, grid, dim3(kThreads), 0, st, a);
@@ -376,10 +401,13 @@ hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
 
 hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
-                             const float *scale, const SegPtrs &seg, hipStream_t st) {
+                             const float *scale, const SegPtrs &seg, hipStream_t st,
+                             const GroupMap &gm) {
     PreExpandArgs a;
     a.y = static_cast<uint16_t *>(y); a.ldy = ldy; a.buf = buf; a.T = T; a.S = S; a.L = L;
     a.R = R; a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
+    a.gm = gm;
+    if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
     int c = 0;
     for (int s = 0; s < S; ++s) {
         a.group_start[s] = c;

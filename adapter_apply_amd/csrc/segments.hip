@@ -82,13 +82,17 @@ __device__ __forceinline__ void scatter_step(int s, int t, int lane, int32_t *my
 
 constexpr int kRegSteps = 8;   // 64-token steps per wave held in registers (T <= 8192)
 
+// Items are tokens (topk == nullptr: key = slot of the token) or (token, k)
+// pairs p = t * k + j (key = slot(t) * E + topk[p]); nkeys = L or L * E.
 __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restrict__ idx,
                                                           const int32_t *__restrict__ slot_rank,
-                                                          int32_t T, int32_t L, int32_t R,
-                                                          SegPtrs seg) {
+                                                          const int32_t *__restrict__ topk,
+                                                          int32_t k, int32_t E, int32_t T,
+                                                          int32_t L, int32_t R, SegPtrs seg) {
     extern __shared__ int32_t lds[];
-    int32_t *wcnt = lds;                       // [kSegWaves][L]
-    int32_t *srank = lds + kSegWaves * L;      // [L]
+    const int nkeys = topk ? L * E : L;
+    int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
+    int32_t *srank = lds + kSegWaves * nkeys;  // [L]
     __shared__ int32_t wsum[2 * kSegWaves + 1];
     __shared__ int32_t s_invalid;
 
@@ -99,27 +103,36 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     const int nsteps = b1 > b0 ? (b1 - b0 + kWave - 1) / kWave : 0;
     const bool inreg = chunk <= kWave * kRegSteps;   // uniform over the block
 
-    // Every global load first: the slot indices into registers, the ranks into LDS.
-    int raw[kRegSteps];
+    // Every global load first: the slot indices (and experts) into registers,
+    // the ranks into LDS.
+    int raw[kRegSteps], rex[kRegSteps];
 #pragma unroll
     for (int u = 0; u < kRegSteps; ++u) {
         const int t = b0 + u * kWave + lane;
-        raw[u] = (inreg && t < b1) ? idx[t] : -1;
+        const bool in = inreg && t < b1;
+        raw[u] = in ? idx[topk ? t / k : t] : -1;
+        rex[u] = (in && topk) ? topk[t] : 0;
     }
     for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
-    for (int i = tid; i < kSegWaves * L; i += kSegThreads) wcnt[i] = 0;
+    for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
     if (tid == 0) s_invalid = 0;
     __syncthreads();
 
     int inv = 0;
-    auto filt = [&](int v) -> int {
+    // key of an item from its slot v and expert e; -1 = carries no adapter
+    auto filt = [&](int v, int e) -> int {
         if (v >= L) { ++inv; return -1; }
-        return (v >= 0 && srank[v] > 0) ? v : -1;
+        if (v < 0 || srank[v] <= 0) return -1;
+        if (!topk) return v;
+        return (e >= 0 && e < E) ? v * E + e : -1;
+    };
+    auto key_of = [&](int t) -> int {     // reload path for large item counts
+        return filt(idx[topk ? t / k : t], topk ? topk[t] : 0);
     };
     int sl[kRegSteps];
 #pragma unroll
-    for (int u = 0; u < kRegSteps; ++u) sl[u] = filt(raw[u]);
-    int32_t *mycnt = wcnt + w * L;
+    for (int u = 0; u < kRegSteps; ++u) sl[u] = filt(raw[u], rex[u]);
+    int32_t *mycnt = wcnt + w * nkeys;
 
     // Pass 1: per-wave, per-slot counts.
     if (inreg) {
@@ -129,28 +142,28 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     } else {
         for (int base = b0; base < b1; base += kWave) {
             const int t = base + lane;
-            count_step(t < b1 ? filt(idx[t]) : -1, lane, mycnt);
+            count_step(t < b1 ? key_of(t) : -1, lane, mycnt);
         }
     }
     if (inv) atomicAdd(&s_invalid, inv);
     __syncthreads();
 
-    // Slot totals -> slot_start; per-wave counts -> write cursors.
+    // Key totals -> slot_start (one entry per key); per-wave counts -> write cursors.
     int tot = 0;
-    if (tid < L)
-        for (int q = 0; q < kSegWaves; ++q) tot += wcnt[q * L + tid];
+    if (tid < nkeys)
+        for (int q = 0; q < kSegWaves; ++q) tot += wcnt[q * nkeys + tid];
     int n_active = 0;
     const int start = block_exclusive_scan(tot, &n_active, wsum);
-    if (tid < L) {
+    if (tid < nkeys) {
         seg.slot_start[tid] = start;
         int run = start;
         for (int q = 0; q < kSegWaves; ++q) {
-            const int c = wcnt[q * L + tid];
-            wcnt[q * L + tid] = run;
+            const int c = wcnt[q * nkeys + tid];
+            wcnt[q * nkeys + tid] = run;
             run += c;
         }
     }
-    if (tid == 0) seg.slot_start[L] = n_active;
+    if (tid == 0) seg.slot_start[nkeys] = n_active;
     __syncthreads();
 
     // Pass 2: scatter token ids in stable order.
@@ -159,28 +172,27 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
         for (int u = 0; u < kRegSteps; ++u)
             if (u < nsteps) scatter_step(sl[u], b0 + u * kWave + lane, lane, mycnt, seg.perm);
     } else {
-        int dummy = 0;
         for (int base = b0; base < b1; base += kWave) {
             const int t = base + lane;
-            int s = -1;
+            int kk = -1;
             if (t < b1) {
-                const int v = idx[t];
-                s = (v >= 0 && v < L && srank[v] > 0) ? v : -1;
+                const int v = idx[topk ? t / k : t];
+                const int e = topk ? topk[t] : 0;
+                kk = (v >= 0 && v < L && srank[v] > 0) ? (topk ? ((e >= 0 && e < E) ? v * E + e : -1) : v) : -1;
             }
-            (void)dummy;
-            scatter_step(s, t, lane, mycnt, seg.perm);
+            scatter_step(kk, t, lane, mycnt, seg.perm);
         }
     }
     for (int i = n_active + tid; i < T; i += kSegThreads) seg.perm[i] = -1;
 
-    // Work tiles of both paths (slot-major, token ranges of at most the tile size).
-    const int cnt = (tid < L) ? tot : 0;
+    // Work tiles of both paths (key-major, item ranges of at most the tile size).
+    const int cnt = (tid < nkeys) ? tot : 0;
     int n_dec = 0, n_pre = 0;
     const int td = (cnt + kDecTile - 1) / kDecTile;
     const int tp = (cnt + kPreTile - 1) / kPreTile;
     const int od = block_exclusive_scan(td, &n_dec, wsum);
     const int op = block_exclusive_scan(tp, &n_pre, wsum);
-    if (tid < L) {
+    if (tid < nkeys) {
         for (int q = 0; q < td; ++q)
             seg.tiles_dec[od + q] = make_int4(tid, start + q * kDecTile,
                                               min(start + (q + 1) * kDecTile, start + cnt), 0);
@@ -209,14 +221,21 @@ __global__ void k_fill_zero(uint4 *__restrict__ p, size_t n16, uint8_t *__restri
 
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
                            int32_t R, const SegPtrs &seg, hipStream_t st) {
-    const size_t lds = sizeof(int32_t) * (size_t)(kSegWaves + 1) * L;
+    return launch_segments_keyed(idx, slot_rank, nullptr, 1, 1, T, L, R, seg, st);
+}
+
+hipError_t launch_segments_keyed(const int32_t *idx, const int32_t *slot_rank,
+                                 const int32_t *topk, int32_t k, int32_t E, int32_t n_items,
+                                 int32_t L, int32_t R, const SegPtrs &seg, hipStream_t st) {
+    const int nkeys = topk ? L * E : L;
+    const size_t lds = sizeof(int32_t) * ((size_t)kSegWaves * nkeys + L);
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_segments),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, T, L, R,
-                       seg);
+    hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, topk, k, E,
+                       n_items, L, R, seg);
     return hipGetLastError();
 }
 

@@ -189,6 +189,63 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
                                 const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Fused-MoE LoRA ([vLLM] FusedMoEWithLoRA; shared-outer layout from [PR]
+ * item 4).  Items are the T * top_k (token, k) pairs p = t * top_k + j with
+ * expert topk_ids[p]; pairs whose expert is outside [0, E) carry no delta.
+ * bf16 only; R % 16 == 0; L * E <= 1024.
+ * ------------------------------------------------------------------------ */
+#define MOE_LORA_W13 0   /* delta into the pre-activation gate_up buffer     */
+#define MOE_LORA_W2  1   /* delta into the per-(token, k) w2 output           */
+
+/* Workspace bytes of moe_lora_align / moe_lora_apply for these sizes. */
+lora_status_t moe_lora_workspace_size(int32_t T, int32_t top_k, int32_t S, int32_t R, int32_t L,
+                                      int32_t E, size_t *bytes);
+
+/* Entries per slot of moe_lora_align's padded output:
+ * round_up(T * top_k + E * (block_m - 1), block_m). */
+lora_status_t moe_lora_align_capacity(int32_t T, int32_t top_k, int32_t E, int32_t block_m,
+                                      int32_t *cap);
+
+/*
+ * Alignment ([vLLM] FusedMoEWithLoRA, the moe_lora_align_block_size call
+ * and its per-slot views): groups the pairs of every slot by expert, experts
+ * ascending, pair ids ascending inside an expert, each expert's run padded
+ * with the sentinel T * top_k to a multiple of block_m.  The pages give only
+ * the call; this layout is the plain reading of its outputs.
+ *   sorted_ids      device int32 [L][cap]          pair ids and sentinels
+ *   block_expert    device int32 [L][cap / block_m] expert of each block, -1 unused
+ *   num_post_padded device int32 [L]                used entries per slot
+ * The three outputs may all be NULL: the call then only builds, in `ws`, the
+ * token and pair segments that moe_lora_apply reuses with
+ * LORA_FLAG_SEGMENTS_READY (the w2 hook reuses the w13 hook's alignment).
+ */
+lora_status_t moe_lora_align(const int32_t *topk_ids, const int32_t *idx, const int32_t *slot_rank,
+                             int32_t T, int32_t top_k, int32_t E, int32_t L, int32_t R,
+                             int32_t block_m, int32_t *sorted_ids, int32_t *block_expert,
+                             int32_t *num_post_padded, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Fused-MoE LoRA delta, in place.
+ *   kind MOE_LORA_W13: x [T][ldx] hidden states; y [T*top_k][ldy] gate_up
+ *       (slices side by side); y[p][off_s + n] += scale[s] * (x[t] A_s[s][ea]^T) B_s[s][e]^T
+ *   kind MOE_LORA_W2:  x [T*top_k][ldx] activation output; y [T*top_k][ldy] w2 output,
+ *       weighted by topk_w[p] (NULL = 1); with reduce_k (needs E_b == 1)
+ *       y is [T][ldy] and receives the sum over the token's k pairs.
+ *   A[s]: device [L][E_a][R][K] with E_a in {1, E}; B[s]: device [L][E_b][N[s]][R]
+ *   with E_b in {1, E}; expert dim 1 = shared-outer (expert index pinned to 0).
+ *   topk_ids device int32 [T][top_k]; topk_w device float [T][top_k] or NULL.
+ * ws: moe_lora_workspace_size() bytes; flags: LORA_FLAG_SEGMENTS_READY when
+ * ws holds this batch's alignment (moe_lora_align or a previous apply).
+ */
+lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_k, const void *x,
+                             int64_t ldx, int32_t T, int32_t top_k, int32_t K,
+                             const void *const *A, int32_t E_a, const void *const *B, int32_t E_b,
+                             const int64_t *N, int32_t S, int32_t E, int32_t L, int32_t R,
+                             const int32_t *topk_ids, const float *topk_w, const int32_t *idx,
+                             const int32_t *slot_rank, const float *scale, int32_t dtype,
+                             uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -146,3 +146,56 @@ def test_workspace_size_and_layout():
     assert lay["tile_decode_tokens"] == 32 and lay["tile_prefill_tokens"] == 64
     with pytest.raises(aa.LoraError):
         aa.lora_workspace_size(256, 4096, 9, 16, 8)
+
+
+def _moe(**kw):
+    a = dict(kind=aa.MOE_LORA_W13, y=FAKE, ldy=3072, rk=0, x=FAKE, ldx=4096, T=2048, k=8, K=4096,
+             A=_ptrs(2), Ea=1, B=_ptrs(2), Eb=64, N=(C.c_int64 * 2)(1536, 1536), S=2, E=64, L=8,
+             R=16, ids=FAKE, w=None, idx=FAKE, rank=FAKE, scale=FAKE, dt=aa.LORA_DT_BF16, flags=0,
+             ws=FAKE_WS, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return aa.lib().moe_lora_apply(a["kind"], a["y"], a["ldy"], a["rk"], a["x"], a["ldx"], a["T"],
+                                   a["k"], a["K"], a["A"], a["Ea"], a["B"], a["Eb"], a["N"], a["S"],
+                                   a["E"], a["L"], a["R"], a["ids"], a["w"], a["idx"], a["rank"],
+                                   a["scale"], a["dt"], a["flags"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=2), aa.LORA_E_SHAPE),
+    (dict(dt=aa.LORA_DT_F32), aa.LORA_E_DTYPE),
+    (dict(R=24), aa.LORA_E_ALIGN),
+    (dict(R=0), aa.LORA_E_RANK),
+    (dict(E=200), aa.LORA_E_SHAPE),              # L * E > 1024
+    (dict(Ea=3), aa.LORA_E_SHAPE),
+    (dict(Eb=2), aa.LORA_E_SHAPE),
+    (dict(rk=1), aa.LORA_E_SHAPE),               # k-reduction is a w2 option
+    (dict(kind=aa.MOE_LORA_W2, rk=1, Eb=64, S=1), aa.LORA_E_SHAPE),   # needs shared lora_b
+    (dict(k=0), aa.LORA_E_SHAPE),
+    (dict(T=-1), aa.LORA_E_SHAPE),
+    (dict(S=0), aa.LORA_E_SLICES),
+    (dict(K=4100, ldx=4104), aa.LORA_E_ALIGN),
+    (dict(ldy=3000), aa.LORA_E_SHAPE),
+    (dict(N=(C.c_int64 * 2)(1536, 1534)), aa.LORA_E_ALIGN),
+    (dict(y=None), aa.LORA_E_NULL),
+    (dict(ids=None), aa.LORA_E_NULL),
+    (dict(A=_ptrs(2, FAKE + 4)), aa.LORA_E_ALIGN),
+    (dict(ws=None), aa.LORA_E_NULL),
+    (dict(wsb=4096), aa.LORA_E_WORKSPACE),
+])
+def test_moe_apply_rejects_bad_arguments(kw, code):
+    assert _moe(**kw) == code
+
+
+def test_moe_sizes_and_align_validation():
+    n = aa.moe_lora_workspace_size(2048, 8, 2, 16, 8, 64)
+    assert n > 2048 * 8 * 16 * 2 * 4
+    assert aa.moe_lora_align_capacity(2, 2, 2, 4) == 12
+    assert aa.moe_lora_align_capacity(2, 2, 2, 2) == 6
+    lib = aa.lib()
+    assert lib.moe_lora_align(FAKE, FAKE, FAKE, 16, 2, 4, 3, 16, 0, None, None, None, FAKE_WS,
+                              1 << 30, None) == aa.LORA_E_SHAPE
+    assert lib.moe_lora_align(FAKE, FAKE, FAKE, 16, 2, 4, 3, 16, 4, FAKE, None, None, FAKE_WS,
+                              1 << 30, None) == aa.LORA_E_NULL
+    assert lib.moe_lora_align(FAKE, FAKE, FAKE, 16, 2, 4, 3, 16, 4, None, None, None, FAKE_WS,
+                              16, None) == aa.LORA_E_WORKSPACE
+    assert _moe(T=0, y=None, x=None) == aa.LORA_OK

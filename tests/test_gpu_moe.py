@@ -1,0 +1,224 @@
+"""GPU parity of the fused-MoE LoRA path (alignment, w13 and w2 deltas)
+against the CPU oracle, through the C ABI."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import adapter_apply_amd as aa  # noqa: E402
+import synth  # noqa: E402
+from tests import bounds  # noqa: E402
+from tests.gpu_util import canaries_intact, dev, guarded, host_f32, log  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+W13, W2 = aa.MOE_LORA_W13, aa.MOE_LORA_W2
+BF = torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aa.lib()
+
+
+def pad_to(a, axis, n):
+    pad = [(0, 0)] * a.ndim
+    pad[axis] = (0, n - a.shape[axis])
+    return np.pad(a, pad)
+
+
+def run_moe(kind, y0, x, A, B, topk_ids, topk_w, idx, rank, scale, E, reduce_k=False, ws=None,
+            flags=0, guard=True):
+    T, k = topk_ids.shape
+    L, _, R, _ = A[0].shape
+    if ws is None:
+        ws = aa.alloc_moe_workspace(T, k, len(A), R, L, E)
+    if guard:
+        yfull, y = guarded(y0, BF)
+    else:
+        yfull, y = None, dev(y0, BF)
+    aa.moe_lora_apply(kind, y, dev(x, BF), [dev(a, BF) for a in A], [dev(b, BF) for b in B],
+                      dev(topk_ids), None if topk_w is None else dev(topk_w), dev(idx), dev(rank),
+                      dev(scale), E, ws, reduce_k=reduce_k, flags=flags)
+    torch.cuda.synchronize()
+    if guard:
+        assert canaries_intact(yfull)
+    return host_f32(y)
+
+
+def test_hand_examples_padded():
+    """The hand-worked w13 / w2 examples, zero-padded to K % 8, R % 16 and
+    N % 4 (padding adds exact zeros), reproduce the hand results bit for bit."""
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    for key, kind in (("moe_w13", W13), ("moe_w2", W2)):
+        c = g[key]
+        x = pad_to(np.asarray(c["x"], np.float32), 1, 8)
+        A = [pad_to(pad_to(np.asarray(a, np.float32), 3, 8), 2, 16) for a in c["A"]]
+        Bs = [np.asarray(b, np.float32) for b in c["B"]]
+        n = Bs[0].shape[2]
+        B = [pad_to(pad_to(b, 3, 16), 2, 4) for b in Bs]
+        y0 = pad_to(np.asarray(c["y0"], np.float32), 1, 4)
+        topk_w = np.asarray(c["topk_w"], np.float32) if "topk_w" in c else None
+        args = (x, A, B, np.asarray(c["topk_ids"], np.int32), topk_w,
+                np.asarray(c["idx"], np.int32), np.asarray(c["slot_rank"], np.int32),
+                np.asarray(c["scale"], np.float32), c["E"])
+        y = run_moe(kind, y0, *args)
+        assert np.array_equal(y[:, :n], np.asarray(c["expected_y"], np.float32)), key
+        assert np.all(y[:, n:] == 0)
+        if key == "moe_w2":
+            y = run_moe(kind, np.zeros((c["T"], 4), np.float32), *args, reduce_k=True)
+            assert np.array_equal(y[:, :n], np.asarray(c["expected_y_reduced"], np.float32))
+
+
+def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, L, size=T).astype(np.int32)
+    idx[rng.random(T) < p_none] = -1
+    rank = rng.integers(1, R + 1, size=L).astype(np.int32)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    Ea = 1 if shared else E
+    x = rng.integers(-1, 2, size=(T, K)).astype(np.float32)
+    h = rng.integers(-1, 2, size=(T * k, I)).astype(np.float32)
+    A13 = [synth.ternary_sparse(rng, (L, Ea, R, K), 32) for _ in range(2)]
+    B13 = [synth.ternary_sparse(rng, (L, E, I, R), 2) for _ in range(2)]
+    A2 = synth.ternary_sparse(rng, (L, E, R, I), 32)
+    B2 = synth.ternary_sparse(rng, (L, Ea, K, R), 2)
+    for s in range(L):
+        for a in A13:
+            a[s, :, rank[s]:] = 0
+        for b in B13:
+            b[s, :, :, rank[s]:] = 0
+        A2[s, :, rank[s]:] = 0
+        B2[s, :, :, rank[s]:] = 0
+    w = rng.choice(np.array([0.5, 0.25, 1.0], np.float32), size=(T, k))
+    g0 = rng.integers(-8, 9, size=(T * k, 2 * I)).astype(np.float32)
+    o0 = rng.integers(-8, 9, size=(T * k, K)).astype(np.float32)
+    scale = np.full(L, 2.0, np.float32)
+    return dict(x=x, h=h, A13=A13, B13=B13, A2=A2, B2=B2, ids=ids, w=w, g0=g0, o0=o0, idx=idx,
+                rank=rank, scale=scale, E=E)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+@pytest.mark.parametrize("seed,T,k,E,K,I,R,L", [
+    (1, 37, 2, 4, 64, 40, 16, 3),
+    (2, 130, 8, 16, 256, 96, 32, 4),
+    (3, 1, 1, 1, 8, 8, 16, 1),
+    (4, 300, 4, 64, 128, 64, 16, 16),     # L * E = 1024 keys
+])
+def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L):
+    d = integer_moe(seed, T, k, E, K, I, R, L, shared)
+    log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L}")
+    y = run_moe(W13, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None, d["idx"], d["rank"],
+                d["scale"], E)
+    ref = oracle_mod.moe_lora_apply(0, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None,
+                                    d["idx"], d["rank"], d["scale"], E)
+    assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+    y = run_moe(W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"], d["idx"], d["rank"],
+                d["scale"], E)
+    ref = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
+                                    d["idx"], d["rank"], d["scale"], E)
+    assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+    if shared:
+        z = np.zeros((T, K), np.float32)
+        y = run_moe(W2, z, d["h"], [d["A2"]], [d["B2"]], d["ids"], None, d["idx"], d["rank"],
+                    d["scale"], E, reduce_k=True)
+        ref = oracle_mod.moe_lora_apply(1, z, d["h"], [d["A2"]], [d["B2"]], d["ids"], None,
+                                        d["idx"], d["rank"], d["scale"], E, reduce_k=True)
+        assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+
+
+def sample_tokens(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n)])).astype(np.int64)
+
+
+def oracle_rows(oracle_mod, c, kind, rows, reduce_k=False):
+    """Oracle on a token subset (the delta of a token depends on nothing else)."""
+    ids = c.topk_ids[rows]
+    pr = (rows[:, None] * c.k + np.arange(c.k)[None, :]).reshape(-1)
+    if kind == 0:
+        return oracle_mod.moe_lora_apply(0, c.gate_up0[pr], c.x[rows], c.A13, c.B13, ids, None,
+                                         c.idx[rows], c.slot_rank, c.scale, c.E)
+    y0 = np.zeros((len(rows), c.K), np.float32) if reduce_k else c.out0[pr]
+    return oracle_mod.moe_lora_apply(1, y0, c.h[pr], [c.A2], [c.B2], ids, c.topk_w[rows],
+                                     c.idx[rows], c.slot_rank, c.scale, c.E, reduce_k=reduce_k)
+
+
+def test_moe_config_shared_outer(oracle_mod):
+    """2048 tokens, 64 experts top-8, d_model 4096, d_mlp 1536, rank 16, 8
+    adapters, shared-outer: w13 and w2 (per pair and k-reduced) on the same
+    alignment, every output of a token sample against the oracle."""
+    c = synth.config_moe()
+    log("case moe config (shared-outer)")
+    T, k = c.T, c.k
+    ws = aa.alloc_moe_workspace(T, k, 2, c.R, c.L, c.E)
+    aa.moe_lora_align(dev(c.topk_ids), dev(c.idx), dev(c.slot_rank), c.E, c.L, c.R, 16, ws)
+    rows = sample_tokens(T, 40)
+    pr = (rows[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    ready = aa.LORA_FLAG_SEGMENTS_READY
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
+                c.E, ws=ws, flags=ready, guard=False)
+    err, rel = bounds.check_bf16_tolerance(y[pr], oracle_rows(oracle_mod, c, 0, rows))
+    log(f"  w13 max abs err {err:.3e} rel {rel:.3e}")
+    y = run_moe(W2, c.out0, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
+                c.E, ws=ws, flags=ready, guard=False)
+    err, rel = bounds.check_bf16_tolerance(y[pr], oracle_rows(oracle_mod, c, 1, rows))
+    log(f"  w2 max abs err {err:.3e} rel {rel:.3e}")
+    yr = run_moe(W2, np.zeros((T, c.K), np.float32), c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w,
+                 c.idx, c.slot_rank, c.scale, c.E, ws=ws, flags=ready, reduce_k=True, guard=False)
+    bounds.check_bf16_tolerance(yr[rows], oracle_rows(oracle_mod, c, 1, rows, reduce_k=True))
+
+
+def test_moe_per_expert_layout(oracle_mod):
+    """The non-shared layout (expert dim E on every tensor) at a reduced size."""
+    c = synth.make_moe("per_expert", 256, 4, 16, 512, 384, 16, 4, "bf16", 77, shared_outer=False)
+    rows = np.arange(c.T)
+    log("case moe per-expert")
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
+                c.E)
+    bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 0, rows))
+    y = run_moe(W2, c.out0, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
+                c.E)
+    bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 1, rows))
+
+
+@pytest.mark.parametrize("seed,T,k,E,L,bm", [(0, 7, 2, 4, 3, 4), (1, 2048, 8, 64, 8, 16),
+                                              (2, 1, 1, 1, 1, 1), (3, 333, 3, 5, 6, 8)])
+def test_moe_align_bit_exact(oracle_mod, seed, T, k, E, L, bm):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)     # includes out-of-range experts
+    idx = rng.integers(-1, L + 1, size=T).astype(np.int32)
+    rank = (rng.integers(0, 3, size=L) * 16).astype(np.int32)
+    cap = aa.moe_lora_align_capacity(T, k, E, bm)
+    so = torch.full((L, cap), -7, dtype=torch.int32, device="cuda")
+    be = torch.full((L, cap // bm), -7, dtype=torch.int32, device="cuda")
+    npp = torch.full((L,), -7, dtype=torch.int32, device="cuda")
+    ws = aa.alloc_moe_workspace(T, k, 1, 16, L, E)
+    aa.moe_lora_align(dev(ids), dev(idx), dev(rank), E, L, 16, bm, ws, so, be, npp)
+    torch.cuda.synchronize()
+    eso, ebe, enpp = oracle_mod.moe_align(ids, idx, rank, E, L, bm)
+    assert np.array_equal(npp.cpu().numpy(), enpp)
+    assert np.array_equal(so.cpu().numpy(), eso)
+    assert np.array_equal(be.cpu().numpy(), ebe)
+
+
+def test_moe_passthrough_and_zero_b(oracle_mod):
+    """Tokens without adapter keep their rows bit-exact; zero lora_b leaves
+    every row bit-exact."""
+    c = synth.make_moe("pt", 200, 4, 8, 256, 128, 16, 3, "bf16", 5,
+                       idx=np.where(np.arange(200) % 3 == 0, -1, np.arange(200) % 3).astype(np.int32),
+                       slot_rank=np.array([16, 0, 16], np.int32))
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
+                c.E)
+    dead = [p for p in range(c.T * c.k) if c.idx[p // c.k] < 0 or c.slot_rank[c.idx[p // c.k]] == 0]
+    assert np.array_equal(y[dead].view(np.uint32), c.gate_up0[dead].view(np.uint32))
+    Bz = [np.zeros_like(b) for b in c.B13]
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, Bz, c.topk_ids, None, c.idx, c.slot_rank, c.scale, c.E)
+    assert np.array_equal(y.view(np.uint32), c.gate_up0.view(np.uint32))
