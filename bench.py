@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROT_BYTES = 512 << 20
 
 
@@ -73,7 +74,10 @@ def algorithmic_bytes(c):
     seg = c.T * 4 * 2
     flops_shrink = 2 * c.S * rank_tok * c.K
     flops_expand = 2 * rank_tok * c.Ntot
-    return dict(shrink=shrink, expand=expand, segments=seg, total=shrink + expand + seg,
+    # the single-launch decode kernel keeps the buffer on chip
+    fused = ta * c.K * el + c.S * rank_slot * c.K * el + rank_slot * c.Ntot * el + ta * c.Ntot * el * 2
+    return dict(shrink=shrink, expand=expand, segments=seg, fused=fused,
+                total=shrink + expand + seg,
                 flops=flops_shrink + flops_expand, active_tokens=ta, active_slots=len(slots))
 
 
@@ -283,7 +287,7 @@ def main():
 
     ab = algorithmic_bytes(c)
     if fused:
-        dom, dom_bytes = "fused", ab["shrink"] + ab["expand"]
+        dom, dom_bytes = "fused", ab["fused"]
     else:
         dom = max(("shrink", "expand"), key=lambda k: per_kernel[k])
         dom_bytes = ab[dom]
@@ -302,7 +306,7 @@ def main():
         "many": "many-adapter decode: 1024 tokens, 128 slots Zipf(1.1), ranks 8..128 padded to 128, 8192x8192",
     }[args.workload]
     out = {
-        "metric": "LoRA-delta tokens/sec (1 GPU)",
+        "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -322,7 +326,13 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": round(per_kernel[dom], 3)},
         "kernels_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "step_algorithmic_GBps": round(ab["total"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_algorithmic_GBps": round((ab["fused"] if fused else ab["total"]) /
+                                       (ms_per_step * 1e-3) / 1e9, 1),
+        # dense bf16 MFMA work of the step (2 * rank * (K * slices + N_total)
+        # per active token) against the 2.5 PFLOP/s bf16 peak
+        "mfma": {"achieved": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
+                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
         "kernel_hash": khash,
