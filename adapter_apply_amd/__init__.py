@@ -33,6 +33,7 @@ LORA_PATH_AUTO = 0
 LORA_PATH_DECODE = 1
 LORA_PATH_PREFILL = 2
 LORA_PATH_FUSED = 3
+LORA_PATH_GROUPED = 4
 
 MOE_LORA_W13 = 0
 MOE_LORA_W2 = 1

@@ -59,18 +59,45 @@ lora_status_t check_ptrs(const void *const *P, int32_t S) {
     return LORA_OK;
 }
 
-bool can_fuse(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int32_t dtype) {
+// y rows are read and written 16 bytes (8 columns) at a time
+bool rows_of_8(const int64_t *N, int32_t S, int64_t ldy, int64_t y_col_offset) {
+    if (ldy % 8 || y_col_offset % 8) return false;
+    for (int s = 0; s < S; ++s)
+        if (N[s] % 8) return false;
+    return true;
+}
+
+bool can_fuse(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int64_t ldy,
+              int64_t y_col_offset, int32_t dtype) {
     if (dtype != LORA_DT_BF16 || R % 16 || R > kFusedMaxRank || T > kFusedMaxTokens) return false;
     if (K % 1024) return false;                  // 16 waves x whole 64-element lines of K
-    for (int s = 0; s < S; ++s)
-        if (N[s] % 8) return false;              // 8 output columns per lane
-    return true;
+    return rows_of_8(N, S, ldy, y_col_offset);
+}
+
+// Slot-grouped kernels: the shrink side (K) and the expand side (y rows).
+bool can_group_sizes(int32_t T, int32_t R, int32_t dtype) {
+    return dtype == LORA_DT_BF16 && R % 16 == 0 && R <= kGrpMaxRank && T <= kGrpMaxTokens;
+}
+bool can_group_k(int32_t K) { return K % 64 == 0 && grp_kchunks(K) <= kMaxKcGrp; }
+
+bool can_group(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int64_t ldy,
+               int64_t y_col_offset, int32_t dtype) {
+    return can_group_sizes(T, R, dtype) && can_group_k(K) && rows_of_8(N, S, ldy, y_col_offset);
+}
+
+// Workspace int32 that carries the grouped shrink's K-chunk count to a later
+// expand call (slot 5 of the segment header; the segment kernel uses 0..4).
+int32_t *grp_kc_slot(void *ws, const SegLayout &l) {
+    return reinterpret_cast<int32_t *>(static_cast<char *>(ws) + l.header) + 5;
 }
 
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
                           int *use_prefill) {
     const bool can_prefill = dtype == LORA_DT_BF16 && R % 16 == 0;
-    if (path == LORA_PATH_DECODE || path == LORA_PATH_FUSED) { *use_prefill = 0; return LORA_OK; }
+    if (path == LORA_PATH_DECODE || path == LORA_PATH_FUSED || path == LORA_PATH_GROUPED) {
+        *use_prefill = 0;
+        return LORA_OK;
+    }
     if (path == LORA_PATH_PREFILL) {
         if (!can_prefill) return LORA_E_PATH;
         *use_prefill = 1;
@@ -181,6 +208,8 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     CHECK(check_k(K, ldx));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    const bool group = path == LORA_PATH_GROUPED;
+    if (group && !(can_group_sizes(T, R, dtype) && can_group_k(K))) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!buf || !x || !idx) return LORA_E_NULL;
     CHECK(check_ptrs(A, S));
@@ -191,10 +220,20 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     hipStream_t st = static_cast<hipStream_t>(stream);
     const SegPtrs seg = seg_ptrs(ws, wl.seg);
     const Slices sl = make_slices(A, nullptr, nullptr, S, 0);
-    if (!(flags & LORA_FLAG_SEGMENTS_READY))
-        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     // buf is written unless the decode path keeps partials in the workspace
     const bool writes_buf = use_prefill || !(flags & LORA_FLAG_PARTIAL);
+    if (group) {
+        // groups come from idx inside the kernels: no segments
+        if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
+            CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
+        float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part,
+                                         grp_kc_slot(ws, wl.seg), st)));
+        if (!writes_buf) return LORA_OK;
+        return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf, st));
+    }
+    if (!(flags & LORA_FLAG_SEGMENTS_READY))
+        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
         CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
     if (use_prefill)
@@ -217,6 +256,9 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    const bool group = path == LORA_PATH_GROUPED;
+    if (group && !(can_group_sizes(T, R, dtype) && rows_of_8(N, S, ldy, y_col_offset)))
+        return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!y || !buf || !idx || !scale) return LORA_E_NULL;
     CHECK(check_ptrs(B, S));
@@ -227,6 +269,20 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
     hipStream_t st = static_cast<hipStream_t>(stream);
     const SegPtrs seg = seg_ptrs(ws, sgl);
     const Slices sl = make_slices(nullptr, B, N, S, y_col_offset);
+    if (group) {
+        if (!(flags & LORA_FLAG_PARTIAL))
+            return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
+                                              nullptr, buf, nullptr, st));
+        // partials right after the segments; the chunk count comes from the
+        // shrink, capped by what this workspace holds
+        const float *part = reinterpret_cast<const float *>(static_cast<char *>(ws) + sgl.end);
+        const size_t chunk_bytes = sizeof(float) * (size_t)T * S * R;
+        const int64_t fit = (int64_t)((ws_bytes - sgl.end) / chunk_bytes);
+        if (fit < 1) return LORA_E_WORKSPACE;
+        const int32_t cap = (int32_t)(fit < kMaxKcGrp ? fit : kMaxKcGrp);
+        return launched(launch_grp_expand(y, ldy, T, cap, sl, S, L, R, idx, slot_rank, scale, part,
+                                          nullptr, grp_kc_slot(ws, sgl), st));
+    }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (use_prefill)
@@ -257,9 +313,12 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
-    const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, dtype) &&
+    const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                       (path == LORA_PATH_FUSED || path == LORA_PATH_AUTO);
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
+    const bool group = !use_prefill && !fuse && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+                       (path == LORA_PATH_GROUPED || path == LORA_PATH_AUTO);
+    if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!y || !x || !idx || !scale) return LORA_E_NULL;
     CHECK(check_ptrs(A, S));
@@ -277,6 +336,14 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const SegPtrs seg = seg_ptrs(ws, wl.seg);
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
+    if (group) {
+        // two launches; each derives its token groups from idx (no segments)
+        float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
+                                         st)));
+        return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
+                                          scale, part, nullptr, nullptr, st));
+    }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (use_prefill) {

@@ -22,11 +22,18 @@ constexpr int kDecKc = 256;    // 4 waves x 64 columns
 constexpr int kDecRows = 16;   // rows of the (slice, rank) space per work-group
 
 // Single-launch decode (fused shrink + expand).
-constexpr int kFusedGroup = 16;        // tokens of one slot per work-group
+constexpr int kFusedGroup = 8;         // tokens of one slot per work-group
 constexpr int kFusedCols = 1024;       // output columns per work-group
 constexpr int kFusedMaxRank = 32;
 constexpr int kFusedMaxTokens = 1024;  // idx staged in LDS
 constexpr int kFusedXcds = 8;
+
+// Slot-grouped split decode (split-K MFMA shrink, then expand).
+constexpr int kGrpTokens = 32;         // tokens of one slot per group
+constexpr int kGrpCols = 512;          // output columns per expand work-group
+constexpr int kGrpMaxTokens = 4096;    // idx staged in LDS
+constexpr int kGrpMaxRank = 64;
+constexpr int kMaxKcGrp = 16;          // K chunks of 512: K <= 8192
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -206,6 +213,24 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,
                             hipStream_t st);
+
+int32_t grp_max_groups(int32_t T, int32_t L);
+int32_t grp_kchunks(int32_t K);
+// Partials: fp32 [S][grp_kchunks(K)][T][R], rows by slot-sorted position.
+// n_kc_out (nullable) receives the chunk count for a later expand call.
+hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                             const int32_t *slot_rank, float *part, int32_t *n_kc_out,
+                             hipStream_t st);
+// Adds the partials (n_kc chunks, or the count at n_kc_in capped at n_kc) or,
+// when buf is given, the token-ordered buffer [S][T][R].
+hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                             const int32_t *slot_rank, const float *scale, const float *part,
+                             const float *buf, const int32_t *n_kc_in, hipStream_t st);
+hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                             const int32_t *slot_rank, const float *part, int32_t n_kc,
+                             float *buf, hipStream_t st);
 
 // Grouped-problem mapping of the MFMA kernels.  A tile's key is
 // slot * Ekey + expert (Ekey = 1 for token tiles); the lora tensor it reads is

@@ -4,18 +4,25 @@
 // extra kernel or dependent global load costs more than the data itself, so
 // this path has no segment build, no workspace and no second launch.
 //
-// Work-group (16 waves) = (token group g, output chunk c of 1024 columns).  The groups are the slot-major
-// runs of at most 16 tokens that a stable sort by slot would give; every
-// work-group derives them itself from idx (staged in LDS: histogram, scan over
-// slots, ballot compaction), so its only dependent global loads are
-// idx -> {x, lora_a, lora_b, y}.  The chunk is 512 output columns of one
-// slice.  Each work-group then
+// Work-group (16 waves) = (token group g, output chunk c of 1024 columns of
+// one slice).  The groups are the slot-major runs of at most 8 tokens that a
+// stable sort by slot would give; every work-group derives them itself from
+// idx (discover.hpp), so its only dependent global loads are
+// idx -> {x, lora_a, lora_b, y}.  Work-group i runs on XCD i % 8 (round-robin
+// dispatch); XCD x takes a contiguous range of groups with all their chunks,
+// so the chunks of a group, and mostly the groups of a slot, share one L2.
+// Each work-group then
 //   1. shrinks its group for that slice with v_mfma_f32_16x16x32_bf16
-//      (16 tokens x 16 ranks blocks; the 16 waves split K and add in LDS),
+//      (16-row token tiles, 8 of them real; the 16 waves split K and add in
+//      LDS),
 //   2. expands its columns with v_mfma_f32_16x16x16_bf16 formed as
 //      D[n][t] = B[n][:] . buf[t][:].
+// Group size: a work-group streams its group's x rows and the slot's lora_a
+// slice through one CU (8 tokens: 64 KB + 128 KB at K = 4096); 8 rather than
+// 16 tokens per group cut that volume by a quarter and spread the work over
+// twice as many CUs.
 // The shrink of a (group, slice) is recomputed by each chunk of that slice:
-// the price of one launch, paid in L2 reads (x rows and lora_a rows).
+// the price of one launch, paid in reads of the XCD's L2 (x rows, lora_a rows).
 // Every global access is row-contiguous (a wave instruction covers whole
 // 128-byte lines): on this part a load that spreads a wave over 16 rows at
 // 64 bytes each runs ~3.5x slower per CU than one covering 8 full lines.
@@ -23,7 +30,7 @@
 // all before the first use, and turns them into MFMA fragments through its
 // own swizzled LDS staging area; the output goes through an LDS buffer so y
 // is read and written 16 bytes per lane along rows.
-#include "common.hpp"
+#include "discover.hpp"
 
 namespace aa {
 
@@ -31,7 +38,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;   // 16
-constexpr int kG = kFusedGroup;            // tokens per group (16)
+constexpr int kG = kFusedGroup;            // tokens per group (8)
+constexpr int kM = 16;                     // MFMA tile rows: tokens kG..15 are padding
 constexpr int kCols = kFusedCols;          // output columns per work-group (1024)
 constexpr int kColsW = kCols / kWaves;     // 64 per wave = 4 blocks of 16
 constexpr int kSub = 64;                   // K elements per sub-chunk: one 128-byte line per row
@@ -44,7 +52,7 @@ struct FusedArgs {
     int64_t ldx;
     uint16_t *y;
     int64_t ldy;
-    int32_t T, K, S, L, R, n_chunks, max_groups;
+    int32_t T, K, S, L, R, n_chunks;
     const int32_t *idx;
     const int32_t *slot_rank;
     const float *scale;
@@ -63,11 +71,11 @@ __device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ 
 // NRB: 16-rank blocks of the padded rank R (1 or 2); the slot's own rank may be lower.
 template <int NRB>
 struct FusedSmem {
-    static constexpr int RR = kG * (1 + NRB);                  // staged rows per sub-chunk: x then lora_a
+    static constexpr int RR = kG + 16 * NRB;                   // staged rows per sub-chunk: x then lora_a
     static constexpr int kStage = kWaves * RR * 128;           // per-wave staging areas
-    static constexpr int kDelta = kG * (kCols + 4) * 4;        // fp32 deltas, aliases the staging
+    static constexpr int kDelta = kM * (kCols + 4) * 4;        // fp32 deltas, aliases the staging
     static constexpr int kUnion = kStage > kDelta ? kStage : kDelta;
-    static constexpr int kPart = kWaves * kG * (NRB * 16 + 4) * 4;
+    static constexpr int kPart = kWaves * kM * (NRB * 16 + 4) * 4;
 };
 
 template <int NRB>
@@ -80,117 +88,49 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
     constexpr int BLD = kColsW * BROW / 1024;      // load instructions for a wave's lora_b rows
 
     __shared__ __attribute__((aligned(16))) char s_union[SM::kUnion];
-    __shared__ __attribute__((aligned(16))) float s_part[kWaves][kG][NRB * 16 + 4];
-    __shared__ int32_t s_slot[kFusedMaxTokens];   // active slot of each token, -1 if none
-    __shared__ int32_t s_rank[kMaxSlots];
-    __shared__ int32_t s_cnt[kMaxSlots];          // tokens per slot
-    __shared__ int32_t s_tok[kG];
-    __shared__ int32_t s_info[4];                 // slot, rank within slot of the first token, count
-    __shared__ __attribute__((aligned(16))) uint16_t s_buf[kG][NRB * 16 + 8];   // bf16 buffer
+    __shared__ __attribute__((aligned(16))) float s_part[kWaves][kM][NRB * 16 + 4];
+    __shared__ DiscLds<kG, kFusedMaxTokens, kWaves> g;
+    __shared__ __attribute__((aligned(16))) uint16_t s_buf[kM][NRB * 16 + 8];   // bf16 buffer
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // Live work-groups are the first ones, so they spread evenly over the XCDs.
-    const int chunk = blockIdx.x % a.n_chunks;
-    const int group = blockIdx.x / a.n_chunks;
-    const int T = a.T, L = a.L;
-
-    // ---- 1. who am I: stage idx and ranks, count per slot -------------------
-    for (int i = tid; i < L; i += kThreads) {
-        s_rank[i] = a.slot_rank ? min(a.slot_rank[i], a.R) : a.R;
-        s_cnt[i] = 0;
-    }
-    for (int i = tid; i < T; i += kThreads) s_slot[i] = a.idx[i];
-    __syncthreads();
-    for (int base = w * kWave; base < T; base += kThreads) {
-        // one LDS atomic per (wave, slot): lanes of a slot are counted by ballot
-        const int i = base + lane;
-        int v = i < T ? s_slot[i] : -1;
-        v = (v >= 0 && v < L && s_rank[v] > 0) ? v : -1;
-        if (i < T) s_slot[i] = v;
-        uint64_t rem = __ballot(v >= 0);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int ls = __shfl(v, leader);
-            const uint64_t peers = __ballot(v == ls);
-            if (lane == leader) atomicAdd(&s_cnt[ls], __popcll(peers));
-            rem &= ~peers;
-        }
-    }
-    __syncthreads();
-    // Wave 0: exclusive scan of groups per slot, find this group's slot.
-    if (w == 0) {
-        const int per = (L + kWave - 1) / kWave;
-        const int lo = lane * per, hi = min(L, lo + per);
-        int tot = 0;
-        for (int s = lo; s < hi; ++s) tot += (s_cnt[s] + kG - 1) / kG;
-        int incl = tot;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
-        int run = incl - tot;
-        for (int s = lo; s < hi; ++s) {
-            const int c = s_cnt[s];
-            const int ng = (c + kG - 1) / kG;
-            if (group >= run && group < run + ng) {
-                s_info[0] = s;
-                s_info[1] = (group - run) * kG;
-                s_info[2] = min(kG, c - (group - run) * kG);
-            }
-            run += ng;
-        }
-        if (lane == kWave - 1 && group >= incl) s_info[0] = -1;   // past the last group
-    }
-    __syncthreads();
-    const int s = s_info[0];
+    const int xcd = blockIdx.x % kFusedXcds;
+    const int j = blockIdx.x / kFusedXcds;
+    const int chunk = j % a.n_chunks;
+    const int lg = j / a.n_chunks;
+    const auto pick = [=](int n) {
+        const int per = (n + kFusedXcds - 1) / kFusedXcds;
+        return lg < per ? xcd * per + lg : -1;
+    };
+    const GroupSel gsel = find_group(a.idx, a.slot_rank, a.T, a.L, a.R, g, pick);
+    const int32_t *s_tok = g.tok;
+    const int s = gsel.slot;
     if (s < 0) return;
-    const int first = s_info[1], ntok = s_info[2];
-    const int r = s_rank[s];
-    // Wave 0: the tokens of slot s with rank first .. first+ntok-1, ascending.
-    if (w == 0) {
-        int seen = 0;
-        for (int base = 0; base < T && seen < first + ntok; base += kWave) {
-            const int t = base + lane;
-            const bool m = t < T && s_slot[t] == s;
-            const uint64_t bal = __ballot(m);
-            const int rk = seen + __popcll(bal & ((1ull << lane) - 1ull));
-            if (m && rk >= first && rk < first + ntok) s_tok[rk - first] = t;
-            seen += __popcll(bal);
-        }
-    }
+    const int ntok = gsel.ntok;
+    const int r = gsel.rank;
     int sg = 0;
     while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
     const int Ns = (int)a.sl.n[sg];
     const int n_base = (chunk - a.chunk_start[sg]) * kCols;
-    __syncthreads();
 
     const int row = lane & 15, quad = lane >> 4;
     const float sc = a.scale[s];
     char *stage = s_union + w * (RR * 128);
 
-    // ---- 2. expand-side loads, row-contiguous, issued first ----------------
-    // lora_b rows of this wave's 64 columns: one contiguous block of 64 * BROW bytes.
+    // ---- 2. shrink of the group for slice sg (MFMA 16x16x32) ----------------
+    // The first batch of shrink loads goes out first, then the expand-side
+    // loads (lora_b rows, y rows), which land while the shrink computes.
     const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) +
                                                       (int64_t)s * Ns * a.R);
-    uint4 bq[BLD];
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) {
-        const int byte = 1024 * i + 16 * lane;                 // within the wave's block
-        const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
-        bq[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + (int64_t)nr * BROW + byte % BROW));
-    }
-    // y: wave w owns token w of the group, 8 columns per lane, 2 x 512 columns.
     const bool ytok = w < ntok;
     uint16_t *yrow = a.y + (int64_t)s_tok[ytok ? w : 0] * a.ldy + a.sl.off[sg];
+    uint4 bq[BLD];
     uint4 yv[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) yv[i] = ldg<uint4>(yrow + min(n_base + 512 * i + 8 * lane, Ns - 8));
-
-    // ---- 3. shrink of the group for slice sg (MFMA 16x16x32) ----------------
+    floatx4_t acc[NRB];
     {
-        // staged row p: x row of token p (p < 16) or lora_a rank row p - 16; rows
+        // staged row p: x row of token p (p < kG) or lora_a rank row p - kG; rows
         // past the group or the rank are clamped to valid ones and dropped later.
+        // MFMA rows kG..15 read staged lora_a rows: finite values whose
+        // outputs belong to padding tokens, zeroed with the buffer.
         const uint16_t *srcrow[LPS];
         const uint16_t *abase = static_cast<const uint16_t *>(a.sl.a[sg]) + (int64_t)s * a.R * a.K;
 #pragma unroll
@@ -202,11 +142,12 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
         const int ucol = 8 * (lane & 7);                       // element offset of this lane's unit
         const int kw = a.K / kWaves;                           // K % 1024 == 0
         const int nsub = kw / kSub;
-        floatx4_t acc[NRB];
 #pragma unroll
         for (int b = 0; b < NRB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < nsub; c0 += SUBB) {
-            uint4 v[SUBB][LPS];
+        uint4 v[SUBB][LPS];
+        // batch c0: SUBB sub-chunks of 64 K columns; one past the end re-reads the
+        // last one and contributes zero (a select, not a branch, keeps loads in flight)
+        auto issue = [&](int c0) {
 #pragma unroll
             for (int c = 0; c < SUBB; ++c)
 #pragma unroll
@@ -214,12 +155,10 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
                     const int k = w * kw + (c0 + min(c, nsub - 1 - c0)) * kSub + ucol;
                     v[c][i] = ldg<uint4>(srcrow[i] + k);
                 }
-            // all of the batch's loads stay ahead of the first use
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto consume = [&](int c0) {
 #pragma unroll
             for (int c = 0; c < SUBB; ++c) {
-                // a sub-chunk past the end (batch padding) re-reads the last one and
-                // contributes zero: a select, not a branch, keeps the loads in flight
                 const bool cv = c0 + c < nsub;
 #pragma unroll
                 for (int i = 0; i < LPS; ++i)
@@ -235,6 +174,24 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
                     }
                 }
             }
+        };
+        issue(0);
+        // lora_b rows of this wave's 64 columns: one contiguous block of 64 * BROW bytes
+#pragma unroll
+        for (int i = 0; i < BLD; ++i) {
+            const int byte = 1024 * i + 16 * lane;
+            const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
+            bq[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + (int64_t)nr * BROW + byte % BROW));
+        }
+        // y: wave w owns token w of the group, 8 columns per lane, 2 x 512 columns
+#pragma unroll
+        for (int i = 0; i < 2; ++i) yv[i] = ldg<uint4>(yrow + min(n_base + 512 * i + 8 * lane, Ns - 8));
+        __builtin_amdgcn_sched_barrier(0);
+        consume(0);
+        for (int c0 = SUBB; c0 < nsub; c0 += SUBB) {
+            issue(c0);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(c0);
         }
         // acc[b][i]: token 4*quad + i, rank 16*b + row
 #pragma unroll
@@ -244,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
     }
     __syncthreads();
     // Sum the 16 K slices in order; store bf16 (ranks past r, tokens past ntok: 0).
-    for (int i = tid; i < kG * NRB * 16; i += kThreads) {
+    for (int i = tid; i < kM * NRB * 16; i += kThreads) {
         const int tk = i / (NRB * 16), j = i - tk * (NRB * 16);
         float v = 0.0f;
 #pragma unroll
@@ -323,8 +280,8 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
     }
     for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
     a.n_chunks = c;
-    a.max_groups = fused_max_groups(T, L);
-    dim3 grid((unsigned)(a.max_groups * c));
+    const int per_xcd = (fused_max_groups(T, L) + kFusedXcds - 1) / kFusedXcds;
+    dim3 grid((unsigned)(kFusedXcds * per_xcd * c));
     if (R <= 16)
         hipLaunchKernelGGL(k_dec_fused<1>, grid, dim3(kThreads), 0, st, a);
     else

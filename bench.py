@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many"])
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode"],
+                   help="force a decode path (development runs; the headline uses auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile", action="store_true",
@@ -165,33 +167,44 @@ def main():
     del base
     torch.cuda.synchronize()
 
+    step_path = {"auto": aa.LORA_PATH_AUTO, "fused": aa.LORA_PATH_FUSED,
+                 "grouped": aa.LORA_PATH_GROUPED, "decode": aa.LORA_PATH_DECODE}[args.path]
+
     def step(d):
         aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
-                             d["ws"])
+                             d["ws"], path=step_path)
 
     # Kernel-by-kernel calls that launch exactly the kernels of one step: the
     # decode path folds the K-chunk reduction into the expand while
     # ceil(K/256) * R <= 512 (the library's rule), else a reduce kernel runs.
-    # the library's auto rule (abi.hip: choose_path, can_fuse)
+    # the library's auto rule for lora_apply_packed (abi.hip: choose_path, can_group)
     prefill = (c.dtype == "bf16" and c.R % 16 == 0 and c.T >= 512
                and c.T // min(c.T, c.L) >= 64)
-    fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
-             and c.T <= 1024)
+    rows8 = all(n % 8 == 0 for n in c.N)
+    fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
+             and c.T <= 1024 and c.K % 1024 == 0 and rows8)
+    grouped = (not prefill and not fused and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
+               and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8)
+    if args.path != "auto":
+        prefill = False
+        fused, grouped = args.path == "fused", args.path == "grouped"
     fold = not prefill and math.ceil(c.K / 256) * c.R <= 512
     part = aa.LORA_FLAG_PARTIAL
     ready = aa.LORA_FLAG_SEGMENTS_READY
+    # the kernel-by-kernel calls use the step's path explicitly
+    kpath = aa.LORA_PATH_GROUPED if grouped else aa.LORA_PATH_AUTO
 
     def shrink_only(d):
-        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"],
+        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"], path=kpath,
                        flags=ready | aa.LORA_FLAG_ACTIVE_ONLY | part)
 
     def shrink_reduce(d):
-        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"],
+        aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"], path=kpath,
                        flags=ready | aa.LORA_FLAG_ACTIVE_ONLY)
 
     def expand_only(d):
         aa.lora_expand(d["y"], d["buf"], d["B"], d["idx"], d["rank"], d["scale"], d["ws"],
-                       flags=ready | (part if fold else 0))
+                       path=kpath, flags=ready | (part if (fold or grouped) else 0))
 
     def segments_only(d):
         aa.lora_build_segments(d["idx"], d["rank"], c.L, c.R, d["ws"])
@@ -259,6 +272,8 @@ def main():
     per_kernel = {}
     if fused:
         kernel_calls = [("fused", step)]      # the whole step is one kernel
+    elif grouped:
+        kernel_calls = [("shrink", shrink_only), ("expand", expand_only)]
     else:
         kernel_calls = [("segments", segments_only), ("shrink", shrink_only)]
         if not fold and not prefill:
@@ -326,7 +341,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": round(per_kernel[dom], 3)},
         "kernels_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "step_algorithmic_GBps": round((ab["fused"] if fused else ab["total"]) /
+        "step_algorithmic_GBps": round((ab["fused"] if fused else
+                                        ab["shrink"] + ab["expand"] if grouped else ab["total"]) /
                                        (ms_per_step * 1e-3) / 1e9, 1),
         # dense bf16 MFMA work of the step (2 * rank * (K * slices + N_total)
         # per active token) against the 2.5 PFLOP/s bf16 peak

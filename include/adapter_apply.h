@@ -41,12 +41,23 @@
  *            element of the expand ([SGL] prepare_lora_batch scalings).
  *   dtype    LORA_DT_BF16 (x, A, B, y all bf16) or LORA_DT_F32 (all fp32;
  *            decode path only).  The intermediate buffer is always fp32.
- *   path     LORA_PATH_AUTO chooses per call; DECODE forces the split
- *            (segments, VALU shrink, expand) decode path; PREFILL forces the
- *            MFMA path (bf16, R % 16 == 0 only); FUSED forces the
- *            single-launch decode kernel of lora_apply_packed (bf16,
- *            R % 16 == 0, R <= 32, T <= 1024, K % 1024 == 0, N % 8 == 0;
- *            it needs no workspace).
+ *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
+ *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
+ *            otherwise lora_apply_packed takes FUSED, else GROUPED, where
+ *            the shapes allow, and DECODE elsewhere; lora_shrink / lora_expand
+ *            take DECODE
+ *            (so that a shrink and an expand called apart agree).
+ *            DECODE forces the split (segments, VALU shrink, expand) decode
+ *            path; PREFILL forces the MFMA path (bf16, R % 16 == 0 only);
+ *            GROUPED forces the slot-grouped decode kernels (split-K MFMA
+ *            shrink, MFMA expand; no segment build: bf16, R % 16 == 0,
+ *            R <= 64, T <= 4096, and for the shrink K % 64 == 0, K <= 8192,
+ *            for the expand N % 8 == 0, ldy % 8 == 0, y_col_offset % 8 == 0);
+ *            FUSED forces the single-launch decode kernel of
+ *            lora_apply_packed (bf16, R % 16 == 0, R <= 32, T <= 1024,
+ *            K % 1024 == 0, N, ldy and y_col_offset % 8 == 0; it needs no
+ *            workspace).  A forced path that cannot take the arguments
+ *            returns LORA_E_PATH.
  *   ws       device workspace of at least lora_workspace_size() bytes,
  *            256-byte aligned, owned by the caller.  Calls sharing a
  *            workspace must be ordered on one stream.  The workspace must be
@@ -61,10 +72,10 @@
  *            entries keep their contents (saves a fill when the buffer only
  *            feeds lora_expand, which never reads them).
  *            LORA_FLAG_PARTIAL (lora_shrink then lora_expand, same ws, buf
- *            and path): on the decode path the shrink leaves its per-K-chunk
- *            partial sums in the workspace and the expand adds them (one
- *            launch fewer); buf is then neither written nor read.  The
- *            prefill path ignores the flag and goes through buf.
+ *            and path): on the DECODE and GROUPED paths the shrink leaves its
+ *            per-K-chunk partial sums in the workspace and the expand adds
+ *            them (one launch fewer); buf is then neither written nor read.
+ *            The prefill path ignores the flag and goes through buf.
  *
  * Alignment: x, y, A[s], B[s] 16-byte aligned; ldx % 8 == 0; ldy and
  * y_col_offset % 4 == 0; buf 16-byte aligned.  Violations -> LORA_E_ALIGN.
@@ -100,6 +111,7 @@ typedef int32_t lora_status_t;
 #define LORA_PATH_DECODE   1
 #define LORA_PATH_PREFILL  2
 #define LORA_PATH_FUSED    3
+#define LORA_PATH_GROUPED  4
 
 #define LORA_FLAG_SEGMENTS_READY 1u
 #define LORA_FLAG_ACTIVE_ONLY    2u

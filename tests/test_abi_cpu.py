@@ -103,7 +103,17 @@ def _apply(**kw):
     (dict(path=aa.LORA_PATH_FUSED, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, R=24), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_GROUPED, R=128), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_GROUPED, T=5000), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_GROUPED, K=8256, ldx=8256), aa.LORA_E_PATH),   # 17 K chunks
+    (dict(path=aa.LORA_PATH_GROUPED, K=4104, ldx=4104), aa.LORA_E_PATH),   # K % 64
+    (dict(path=aa.LORA_PATH_GROUPED, ldy=6148), aa.LORA_E_PATH),           # ldy % 8
+    (dict(path=aa.LORA_PATH_GROUPED, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_GROUPED, ws=None), aa.LORA_E_NULL),
+    (dict(path=aa.LORA_PATH_GROUPED, wsb=1024), aa.LORA_E_WORKSPACE),
+    (dict(path=aa.LORA_PATH_FUSED, ldy=6148), aa.LORA_E_PATH),
     (dict(path=5), aa.LORA_E_PATH),
+    (dict(path=6), aa.LORA_E_PATH),
 ])
 def test_apply_rejects_bad_arguments(kw, code):
     assert _apply(**kw) == code
@@ -124,6 +134,16 @@ def test_shrink_expand_validation():
                            16, None) == aa.LORA_E_WORKSPACE
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 8, FAKE, None, 1,
                            aa.LORA_PATH_PREFILL, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    # the fused kernel has no separate shrink; the grouped one takes rank <= 64
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
+                           aa.LORA_PATH_FUSED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 128, FAKE, None, 1,
+                           aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    assert lib.lora_shrink(FAKE, FAKE, 72, 16, 72, A, 2, 3, 16, FAKE, None, 1,
+                           aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    Ng = (C.c_int64 * 2)(64, 68)
+    assert lib.lora_expand(FAKE, 136, 0, FAKE, 16, A, Ng, 2, 3, 16, FAKE, None, FAKE, 1,
+                           aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     N = (C.c_int64 * 2)(64, 64)
     assert lib.lora_expand(FAKE, 128, 0, None, 16, A, N, 2, 3, 8, FAKE, None, FAKE, 0, 0, 0,
                            FAKE_WS, ok_ws, None) == aa.LORA_E_NULL

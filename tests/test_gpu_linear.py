@@ -16,7 +16,8 @@ import synth  # noqa: E402
 from tests import bounds  # noqa: E402
 from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
 
-DEC, PRE, FUS = aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED
+DEC, PRE, FUS, GRP = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
+                      aa.LORA_PATH_GROUPED)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -69,6 +70,19 @@ def fusable(c):
             and c.K % 1024 == 0 and all(n % 8 == 0 for n in c.N))
 
 
+def groupable(c):
+    """Shapes the slot-grouped split decode kernels take."""
+    return (c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64 and c.T <= 4096
+            and c.K % 64 == 0 and c.K <= 8192 and all(n % 8 == 0 for n in c.N))
+
+
+def skip_unless_path_takes(path, c):
+    if path == FUS and not fusable(c):
+        pytest.skip("shape outside the single-launch kernel")
+    if path == GRP and not groupable(c):
+        pytest.skip("shape outside the slot-grouped kernels")
+
+
 INTEGER_CASES = [
     (21, 200, 512, [256, 64, 64], 16, 5),
     (22, 333, 1024, [128, 128], 32, 3),
@@ -79,15 +93,15 @@ INTEGER_CASES = [
     (27, 333, 2048, [1032, 128], 32, 3),     # last 1024-column chunk partial
     (28, 1, 1024, [8], 16, 1),
     (29, 1024, 1024, [16, 1032], 32, 1024),
+    (30, 1024, 1024, [256, 64], 16, 40),     # 40 slots x 16 token chunks: work-group discovery
 ]
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP])
 @pytest.mark.parametrize("seed,T,K,N,R,L", INTEGER_CASES)
 def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
-    if path == FUS and not fusable(c):
-        pytest.skip("shape outside the single-launch kernel")
+    skip_unless_path_takes(path, c)
     log(f"case integer path={path} T={T} K={K} N={N} R={R} L={L}")
     d = LinearOnDevice(c)
     d.apply(path)
@@ -99,7 +113,7 @@ def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP])
 def test_decode_config_qkv(oracle_mod, path):
     """256 tokens, hidden 4096, QKV 4096/1024/1024, rank 16, 8 slots, 10% idx=-1."""
     c = synth.config_decode()
@@ -176,7 +190,7 @@ def test_many_adapter_alpha_scales(oracle_mod):
 # shrink and expand as separate entry points
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GRP])
 def test_shrink_buffer(oracle_mod, path):
     c = synth.make_linear("sh", 300, 1024, [256, 128], 32, 5,
                           idx=np.random.default_rng(3).integers(-1, 6, 300),
@@ -200,15 +214,15 @@ def test_shrink_buffer(oracle_mod, path):
     assert np.all(g[zero_mask & (Mb == 0)] == 0)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE])
+@pytest.mark.parametrize("path", [DEC, PRE, GRP])
 def test_expand_from_given_buffer(oracle_mod, path):
     rng = np.random.default_rng(41)
     c = synth.make_linear("ex", 257, 64, [512, 128, 128], 32, 6, idx=rng.integers(-1, 7, 257),
                           slot_rank=[32, 16, 8, 32, 0, 24], scale=[2, 1, .5, 1, 1, 3],
                           dtype="bf16", seed=42)
     buf = rng.standard_normal((c.S, c.T, c.R)).astype(np.float32)
-    if path == PRE:
-        # the MFMA expand consumes the buffer in bf16; give it bf16-exact values
+    if path in (PRE, GRP):
+        # the MFMA expands consume the buffer in bf16; give them bf16-exact values
         buf = synth.round_bf16(buf)
     log(f"case expand path={path}")
     d = LinearOnDevice(c)
@@ -220,16 +234,16 @@ def test_expand_from_given_buffer(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("cfg", ["decode", "many"])
-def test_partial_flag_split_calls(oracle_mod, cfg):
+@pytest.mark.parametrize("cfg,path", [("decode", DEC), ("many", DEC), ("decode", GRP)])
+def test_partial_flag_split_calls(oracle_mod, cfg, path):
     """lora_shrink(PARTIAL) + lora_expand(PARTIAL): partial sums stay in the
     workspace, the caller's buffer is never touched."""
     c = synth.config_decode(T=200) if cfg == "decode" else synth.config_many(T=300)
-    log(f"case partial flag {cfg}")
+    log(f"case partial flag {cfg} path={path}")
     d = LinearOnDevice(c)
     buf = torch.full((c.S, c.T, c.R), 5.0, dtype=torch.float32, device="cuda")
-    aa.lora_shrink(buf, d.x, d.A, d.idx, d.rank, d.ws, path=DEC, flags=aa.LORA_FLAG_PARTIAL)
-    aa.lora_expand(d.y, buf, d.B, d.idx, d.rank, d.scale, d.ws, path=DEC,
+    aa.lora_shrink(buf, d.x, d.A, d.idx, d.rank, d.ws, path=path, flags=aa.LORA_FLAG_PARTIAL)
+    aa.lora_expand(d.y, buf, d.B, d.idx, d.rank, d.scale, d.ws, path=path,
                    flags=aa.LORA_FLAG_PARTIAL | aa.LORA_FLAG_SEGMENTS_READY)
     y = d.y_host()
     assert bool(torch.all(buf == 5.0))
@@ -275,7 +289,7 @@ def test_all_tokens_without_adapter_unchanged():
     c = synth.config_decode(T=64)
     c.idx[:] = -1
     d = LinearOnDevice(c)
-    for path in (DEC, PRE, FUS):
+    for path in (DEC, PRE, FUS, GRP):
         d.apply(path)
         y = d.y_host()
         assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
@@ -288,7 +302,7 @@ def test_zero_b_identity_and_invalid_slots(oracle_mod):
     c.idx[::11] = 100
     c.slot_rank[3] = 0    # empty slot
     c.B = [np.zeros_like(b) for b in c.B]
-    for path in (DEC, PRE, FUS):
+    for path in (DEC, PRE, FUS, GRP):
         d = LinearOnDevice(c)
         d.apply(path)
         y = d.y_host()
@@ -304,7 +318,7 @@ def test_column_offset_and_wide_rows(oracle_mod):
     wide = rng.standard_normal((c.T, 200)).astype(np.float32)
     wide = synth.round_bf16(wide)
     off = 40
-    for path in (DEC, PRE, FUS):
+    for path in (DEC, PRE, FUS, GRP):
         yw = dev(wide, torch.bfloat16)
         d = LinearOnDevice(c, guard=False)
         aa.lora_apply_packed(yw, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, y_col_offset=off,
@@ -337,7 +351,8 @@ def test_segments_reused_across_layers(oracle_mod):
             bounds.check_bf16_tolerance(d.y_host(), oracle_y(oracle_mod, c))
 
 
-@pytest.mark.parametrize("cfg,path", [("many", DEC), ("decode", FUS), ("decode", PRE)])
+@pytest.mark.parametrize("cfg,path", [("many", DEC), ("decode", FUS), ("decode", PRE),
+                                      ("decode", GRP)])
 def test_deterministic_run_twice(cfg, path):
     c = synth.config_many(T=512) if cfg == "many" else synth.config_decode()
     outs = []
@@ -348,7 +363,8 @@ def test_deterministic_run_twice(cfg, path):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
-def test_fused_skewed_slots(oracle_mod):
+@pytest.mark.parametrize("path", [FUS, GRP])
+def test_fused_skewed_slots(oracle_mod, path):
     """All tokens on one slot (many groups of one slot) and ranks below 16."""
     rng = np.random.default_rng(12)
     idx = np.zeros(700, np.int32)
@@ -357,19 +373,37 @@ def test_fused_skewed_slots(oracle_mod):
     c = synth.make_linear("skew", 700, 1024, [64, 256], 32, 4, idx, [32, 8, 16, 8],
                           [1.0, 1.0, 1.0, 0.5], "bf16", seed=13)
     d = LinearOnDevice(c)
-    d.apply(FUS)
+    d.apply(path)
     y = d.y_host()
     bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
     assert_passthrough(c, y)
     assert canaries_intact(d.yfull)
 
 
-def test_fused_rejects_unsupported():
+@pytest.mark.parametrize("path", [FUS, GRP])
+def test_fused_rejects_unsupported(path):
     c = synth.config_many(T=64)          # rank 128 > 64
     d = LinearOnDevice(c, guard=False)
     with pytest.raises(aa.LoraError) as e:
-        d.apply(FUS)
+        d.apply(path)
     assert e.value.code == aa.LORA_E_PATH
+
+
+@pytest.mark.parametrize("seed,T,K,N,R,L", [
+    (41, 4096, 512, [64] * 8, 64, 7),        # most tokens, 8 slices, rank 64
+    (42, 64, 8192, [520, 1024], 64, 3),      # 16 K chunks, ragged 512-column chunk
+    (43, 300, 576, [8, 16, 24], 48, 2),      # K not a multiple of 512, 3 rank blocks
+])
+def test_grouped_limits_bit_exact(oracle_mod, seed, T, K, N, R, L):
+    c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
+    assert groupable(c)
+    log(f"case grouped limits T={T} K={K} N={N} R={R} L={L}")
+    d = LinearOnDevice(c)
+    d.apply(GRP)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+    assert canaries_intact(d.yfull)
 
 
 def test_zero_tokens_noop():
