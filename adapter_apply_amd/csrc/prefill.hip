@@ -12,12 +12,13 @@
 // 32 token x 32 column block over the full K.  Writes fp32 buf[s][t][j] for
 // every column (zeros for j >= rank).
 //
-// Expand: work-group = (tile, group of 512 output columns of one slice);
-// each wave owns 128 columns and both token blocks.  The product is formed
-// transposed, D[n][t] = B[n][:] . buf[t][:], so a lane's accumulators are 4
-// consecutive output columns of one token: y is read and written 8 bytes at a
-// time along rows.  Column groups are dealt to the 8 XCDs round-robin so each
-// XCD keeps its slice of lora_b hot in its own L2 across a slot's tiles.
+// Expand: work-group = (tile, group of output columns of one slice), the
+// product formed transposed, D[n][t] = B[n][:] . buf[t][:].  For ranks up to
+// 64 (k_pre_expand_rows) the y tile, the lora_b block and the buffer rows go
+// through LDS so that every global access is row-contiguous; larger ranks use
+// k_pre_expand, whose lanes read and write y 8 bytes at a time in the MFMA
+// layout.  Column groups are dealt to the 8 XCDs round-robin so each XCD keeps
+// its slice of lora_b hot in its own L2 across a slot's tiles.
 #include "common.hpp"
 
 namespace aa {
@@ -282,12 +283,39 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     }
 }
 
-// Fast expand for ranks <= 16 * NKS (NKS <= 4): every load of the wave (buffer
-// fragments, the lora_b fragments and the y values of its 4 column blocks)
-// is issued before the first MFMA.
+// Row-oriented expand for ranks <= 64 (R = 16 * NKS): work-group = (64-token
+// tile, 256 output columns of one slice), 4 waves, two work-groups per CU.
+// Every global access is row-contiguous: the y tile is read into LDS with
+// each wave instruction covering two 512-byte row pieces, the lora_b rows of
+// the 256 columns are one contiguous block, the buffer rows are whole rows.
+// The product D[n][t] = B[n][:] . buf[t][:] (v_mfma_f32_32x32x16_bf16) is
+// added to the y tile in LDS, which is then written back row by row.
+constexpr int kRowTok = 64;                  // tokens per tile (kPreTile)
+constexpr int kRowCols = 256;                // output columns per work-group
+constexpr int kRowYStride = kRowCols + 8;    // bf16 elements per LDS y row (528 B)
+
+// 16-byte unit u of row n of an LDS block with U units per row, XOR-swizzled
+// so fragment reads of consecutive rows spread over the banks.
+__device__ __forceinline__ int swz(int n, int u, int U) {
+    const int m = (U & (U - 1)) == 0 ? U - 1 : 1;
+    return (n * U + (u ^ (n & m))) << 4;
+}
+
 template <int NKS>
-__global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
-    constexpr int NB = kExpWaveCols / 32;   // 4 column blocks of 32 per wave
+__global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a) {
+    constexpr int R = 16 * NKS;
+    constexpr int U = R / 8;                       // 16-byte units per lora_b / buffer row
+    constexpr int YU = kRowCols / 8;               // 16-byte units per y row piece (32)
+    constexpr int NY = kRowTok * YU / kThreads;    // y units per thread (8)
+    constexpr int NBU = kRowCols * U / kThreads;   // lora_b units per thread (R / 8)
+    constexpr int NFU = kRowTok * (R / 4) / kThreads;   // fp32 buffer units (float4) per thread
+    static_assert(NFU >= 1, "rank too small for one buffer unit per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * kRowYStride];
+    __shared__ __attribute__((aligned(16))) char s_b[kRowCols * U * 16];
+    __shared__ __attribute__((aligned(16))) char s_buf[kRowTok * U * 16];
+    __shared__ int64_t s_yrow[kRowTok];
+    __shared__ float s_scl[kRowTok];
+
     const int xcd = blockIdx.x % kXcds;
     const int local = blockIdx.x / kXcds;
     const int tile = local / a.per_xcd;
@@ -300,86 +328,132 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand_fast(PreExpandArgs a) {
     const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
     int sg = 0;
     while (sg + 1 < a.S && cg >= a.group_start[sg + 1]) ++sg;
-    const int64_t Ns = a.sl.n[sg];
+    const int Ns = (int)a.sl.n[sg];
+    const int n_base = (cg - a.group_start[sg]) * kRowCols;
     const float sc = a.scale[s];
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int nk = (r + 15) >> 4;
-    const int nbase = (cg - a.group_start[sg]) * kExpGroupCols + w * kExpWaveCols;
-    if (nbase >= Ns) return;
 
-    // Items past the tile are clamped to its first one (valid); their results
-    // are never stored.  R >= 16 * NKS, so every rank step's loads are in bounds.
-    ExpItem it[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) it[tb] = exp_item(a, p0, tb * 32 + l32, ntok, sc);
-    const uint16_t *bbase = static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * a.R;
+    // ---- per-token row, scale and buffer item (tokens past the tile: clamped)
+    if (tid < kRowTok) {
+        const int row = tid < ntok ? tid : 0;
+        const int item = a.seg.perm[p0 + row];
+        s_yrow[tid] = item / a.gm.y_div;
+        s_scl[tid] = sc * ((a.gm.coef && !a.gm.ksum) ? a.gm.coef[item] : 1.0f);
+    }
+    __syncthreads();
+
+    // ---- all loads -------------------------------------------------------
     uint16_t *ybase = a.y + a.sl.off[sg];
-
-    // ---- all loads ----
-    float4 bf[2][NKS][2];
+    uint4 yv[NY];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int i = 0; i < NY; ++i) {
+        const int q = i * kThreads + tid;
+        const int row = q / YU, col = n_base + 8 * (q % YU);
+        yv[i] = ldg<uint4>(ybase + s_yrow[row] * a.ldy + min(col, Ns - 8));
+    }
+    const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * R);
+    uint4 bv[NBU];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            buf_vals(a, sg, it[tb].item, ks * 16 + 8 * half, r, bf[tb][ks][0], bf[tb][ks][1]);
-    uint4 af[NB][NKS];
-    uint2 yv[NB][2][4];
+    for (int i = 0; i < NBU; ++i) {
+        const int q = i * kThreads + tid;
+        const int n = min(n_base + q / U, Ns - 1);
+        bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + q % U) * 16));
+    }
+    float4 fv[NFU];
+    int frow[NFU];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int n0 = nbase + nb * 32;
-        const int nrow = min(n0 + l32, (int)Ns - 1);
-        const uint16_t *brow = bbase + (int64_t)nrow * a.R;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) af[nb][ks] = ldg<uint4>(brow + ks * 16 + 8 * half);
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const uint16_t *yrow = ybase + it[tb].yrow * a.ldy;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = min(n0 + 8 * g + 4 * half, (int)Ns - 4);
-                yv[nb][tb][g] = ldg<uint2>(yrow + n);
+    for (int i = 0; i < NFU; ++i) {
+        const int q = i * kThreads + tid;
+        const int t = q / (R / 4), j = 4 * (q % (R / 4));
+        frow[i] = t;
+        const int row = t < ntok ? t : 0;
+        const int item = a.seg.perm[p0 + row];
+        if (!a.gm.ksum) {
+            fv[i] = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_rows + item / a.gm.buf_div) * R + j);
+        } else {
+            // the k-reduced buffer row of token `item`: sum_j coef * buf over its pairs
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int kk = 0; kk < a.gm.ksum; ++kk) {
+                const int64_t br = (int64_t)item * a.gm.ksum + kk;
+                const float cw = a.gm.coef ? a.gm.coef[br] : 1.0f;
+                const float4 u = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_rows + br) * R + j);
+                acc.x += cw * u.x; acc.y += cw * u.y; acc.z += cw * u.z; acc.w += cw * u.w;
             }
+            fv[i] = acc;
         }
     }
-    // ---- buffer fragments to bf16 (entries past the rank forced to zero) ----
-    uint4 bfrag[2][NKS];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- into LDS --------------------------------------------------------
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int i = 0; i < NY; ++i) {
+        const int q = i * kThreads + tid;
+        *reinterpret_cast<uint4 *>(&s_y[(q / YU) * kRowYStride + 8 * (q % YU)]) = yv[i];
+    }
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            bfrag[tb][ks] = pack_frag(bf[tb][ks][0], bf[tb][ks][1], ks * 16 + 8 * half, r);
-    // ---- multiply and update y ----
+    for (int i = 0; i < NBU; ++i) {
+        const int q = i * kThreads + tid;
+        *reinterpret_cast<uint4 *>(s_b + swz(q / U, q % U, U)) = bv[i];
+    }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int n0 = nbase + nb * 32;
-        floatx16_t acc[2] = {{}, {}};
+    for (int i = 0; i < NFU; ++i) {
+        const int q = i * kThreads + tid;
+        const int t = frow[i], j = 4 * (q % (R / 4));
+        const bool ok = t < ntok;
+        uint2 o;
+        o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
+        o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
+        // 8-byte half of unit j / 8 of row t
+        *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
+    }
+    __syncthreads();
+
+    // ---- D[n][t]: wave w takes columns 64w .. 64w + 63, both token blocks ----
+    floatx16_t acc[2][2] = {{{}, {}}, {{}, {}}};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks < nk) {
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[nb][ks]), as_frag(bfrag[0][ks]), acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[nb][ks]), as_frag(bfrag[1][ks]), acc[1], 0, 0, 0);
-            }
+    for (int ks = 0; ks < NKS; ++ks) {
+        const int u = 2 * ks + half;
+        uint4 bf[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) bf[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(64 * w + 32 * nb + l32, u, U));
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+                acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bf[tb]), acc[nb][tb], 0, 0, 0);
         }
+    }
+    // lane: token 32*tb + l32, columns 64w + 32nb + 8g + 4*half + {0..3}
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            uint16_t *yrow = ybase + it[tb].yrow * a.ldy;
-            const float c = it[tb].scl;
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = 32 * tb + l32;
+        if (t < ntok) {
+            const float c = s_scl[t];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 8 * g + 4 * half;
-                if (it[tb].ok && n < Ns) {
-                    const uint2 y0 = yv[nb][tb][g];
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * kRowYStride + 64 * w + 32 * nb + 8 * g + 4 * half]);
+                    const uint2 y0 = *yp;
                     uint2 o;
-                    o.x = pack_bf16x2(bf16_lo(y0.x) + c * acc[tb][4 * g + 0],
-                                      bf16_hi(y0.x) + c * acc[tb][4 * g + 1]);
-                    o.y = pack_bf16x2(bf16_lo(y0.y) + c * acc[tb][4 * g + 2],
-                                      bf16_hi(y0.y) + c * acc[tb][4 * g + 3]);
-                    *reinterpret_cast<uint2 *>(yrow + n) = o;
+                    o.x = pack_bf16x2(bf16_lo(y0.x) + c * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + c * acc[nb][tb][4 * g + 1]);
+                    o.y = pack_bf16x2(bf16_lo(y0.y) + c * acc[nb][tb][4 * g + 2], bf16_hi(y0.y) + c * acc[nb][tb][4 * g + 3]);
+                    *yp = o;
                 }
-            }
         }
+    }
+    __syncthreads();
+
+    // ---- write the tile back, row by row ----------------------------------
+#pragma unroll
+    for (int i = 0; i < NY; ++i) {
+        const int q = i * kThreads + tid;
+        const int row = q / YU, col = n_base + 8 * (q % YU);
+        if (row < ntok && col < Ns)
+            *reinterpret_cast<uint4 *>(ybase + s_yrow[row] * a.ldy + col) =
+                *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]);
     }
 }
 
@@ -408,21 +482,28 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.R = R; a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
     a.gm = gm;
     if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
+    bool rows = R % 16 == 0 && R <= 64 && ldy % 8 == 0;
+    for (int s = 0; s < S; ++s)
+        rows = rows && sl.n[s] % 8 == 0 && sl.off[s] % 8 == 0;
+    const int cols = rows ? kRowCols : kExpGroupCols;
     int c = 0;
     for (int s = 0; s < S; ++s) {
         a.group_start[s] = c;
-        c += (int)((sl.n[s] + kExpGroupCols - 1) / kExpGroupCols);
+        c += (int)((sl.n[s] + cols - 1) / cols);
     }
     for (int s = S; s <= kMaxSlices; ++s) a.group_start[s] = c;
     a.n_cg = c;
     a.per_xcd = (c + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
-    switch ((R + 15) / 16) {
-        case 1: hipLaunchKernelGGL(k_pre_expand_fast<1>, grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(k_pre_expand_fast<2>, grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(k_pre_expand_fast<3>, grid, dim3(kThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL(k_pre_expand_fast<4>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a); break;
+    if (!rows) {
+        hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    switch (R / 16) {
+        case 1: hipLaunchKernelGGL(k_pre_expand_rows<1>, grid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_pre_expand_rows<2>, grid, dim3(kThreads), 0, st, a); break;
+        case 3: hipLaunchKernelGGL(k_pre_expand_rows<3>, grid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_pre_expand_rows<4>, grid, dim3(kThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }
