@@ -43,16 +43,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16, round to nearest, ties to even (gfx950 converts a pair in one
+// instruction, v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    const bf16x2_t b = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, b);
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // Loads in the pipelined loops are unconditional, from addresses clamped to a
 // valid row; results that belong to padding rows/columns are discarded or

@@ -1,16 +1,13 @@
 // Prefill path: MFMA kernels for long per-slot token runs (SGMV regime).
 //
 // Tokens are grouped by slot into tiles of 64 (two 32-row MFMA blocks).  Both
-// halves use v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate).  Operand
-// fragments are read straight from global memory in the MFMA lane layout:
-// lane l supplies row (l % 32) and 8 consecutive k values starting at
-// 8 * (l / 32), one 16-byte load per fragment, identical for both operands.
-// The accumulator layout of a 32x32 block: lane l holds column (l % 32) and
-// rows 8 * (i / 4) + 4 * (l / 32) + (i % 4) for register i = 0..15.
+// kernels use v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate).  An operand
+// fragment is 16 bytes per lane: row (l % 32), 8 consecutive k values starting
+// at 8 * (l / 32).  The accumulator layout of a 32x32 block: lane l holds
+// column (l % 32) and rows 8 * (i / 4) + 4 * (l / 32) + (i % 4), i = 0..15.
 //
-// Shrink: work-group = (tile, 64 of the S*R buffer columns); each wave a
-// 32 token x 32 column block over the full K.  Writes fp32 buf[s][t][j] for
-// every column (zeros for j >= rank).
+// Shrink (k_pre_shrink_rows): work-group = (tile, up to 128 of the S*R buffer
+// columns), x and lora_a rows staged through LDS in 64-column K stages.
 //
 // Expand: work-group = (tile, group of output columns of one slice), the
 // product formed transposed, D[n][t] = B[n][:] . buf[t][:].  For ranks up to
@@ -26,7 +23,6 @@ namespace aa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kShrinkCols = 64;        // buffer columns per shrink work-group
 constexpr int kExpGroupCols = 512;     // output columns per expand work-group
 constexpr int kExpWaveCols = kExpGroupCols / 4;
 constexpr int kXcds = 8;
@@ -57,86 +53,135 @@ struct PreExpandArgs {
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__global__ __launch_bounds__(kThreads) void k_pre_shrink(PreShrinkArgs a) {
-    const int cb = blockIdx.x % a.n_cb;
-    const int tile = blockIdx.x / a.n_cb;
-    if (tile >= a.seg.header[3]) return;
+// 16-byte unit u of row n of an LDS block with U units per row.  16/U rows
+// share one 256-byte bank window; the unit is XOR-ed with the row's window
+// index so that the 16 rows read together by a quarter-wave fragment load (one
+// unit each) hit 16 different 16-byte bank groups.  Whole-row writes stay
+// conflict-free.  (U = 6 is not swizzled.)
+__device__ __forceinline__ int swz(int n, int u, int U) {
+    const int m = (U & (U - 1)) == 0 ? (n / (16 / U)) & (U - 1) : 0;
+    return (n * U + (u ^ m)) << 4;
+}
+
+// Shrink: work-group = (64-item tile, block of 32 * NCB buffer columns), 8
+// waves.  K advances in stages of 64 columns: a stage is the tile's x rows and
+// the block's lora_a rows, 128 bytes each, loaded row-contiguously (one wave
+// instruction = 8 whole rows), with NPF stages in flight in registers and two
+// LDS buffers (one barrier per stage).  Wave w owns the 32 x 32 output block
+// (token block w & 1, column block w >> 1) and runs v_mfma_f32_32x32x16_bf16
+// over the stage.  Writes fp32 buf[s][t][j] for every column of the block that
+// exists (zeros for j >= rank); K % 8 == 0, any rank.
+constexpr int kShThreads = 512;
+constexpr int kShStageK = 64;          // K columns per stage (128 bytes of a row)
+constexpr int kShNpf = 4;              // stages in flight
+
+template <int NCB>
+__global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a) {
+    constexpr int ROWS = 64 + 32 * NCB;                // x rows, then lora_a rows
+    constexpr int UNITS = ROWS * 8;                    // 16-byte units per stage
+    constexpr int NU = (UNITS + kShThreads - 1) / kShThreads;
+    __shared__ __attribute__((aligned(16))) char s_stage[2][ROWS * 128];
+    __shared__ int64_t s_brow[64];
+
+    // Work-group i runs on XCD i % 8; XCD x takes a contiguous range of the
+    // (slot-ordered) tiles, so each XCD's L2 holds the lora_a rows of only
+    // the few slots its tiles belong to.
+    const int xcd = blockIdx.x % kXcds;
+    const int local = blockIdx.x / kXcds;
+    const int cb = local % a.n_cb;
+    const int n_tiles = a.seg.header[3];
+    const int per = (n_tiles + kXcds - 1) / kXcds;
+    const int lt = local / a.n_cb;
+    if (lt >= per) return;
+    const int tile = xcd * per + lt;
+    if (tile >= n_tiles) return;
     const int4 tl = a.seg.tiles_pre[tile];
     const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
     const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w & 1, wn = w >> 1;
+    const int SRf = a.S * a.R;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
 
-    // Operand rows of this lane.
-    // Operand rows are clamped to valid ones (the tile's first token, the
-    // slot's rank row 0 of slice 0); their results are never written.
-    const int trow = wm * 32 + l32;                    // token within tile
-    const bool tok_ok = trow < ntok;
-    const int t_in = a.seg.perm[p0 + (tok_ok ? trow : 0)] / a.gm.x_div;
-    const uint16_t *xr = a.x + (int64_t)t_in * a.ldx;
+    if (tid < 64) s_brow[tid] = a.seg.perm[p0 + (tid < ntok ? tid : 0)] / a.gm.buf_div;
 
-    const int col = cb * kShrinkCols + wn * 32 + l32;  // buffer column (slice, rank)
-    const int SRf = a.S * a.R;
-    const int sg = col / a.R, j = col - (col / a.R) * a.R;
-    const bool col_ok = col < SRf && j < r;
-    const uint16_t *ar = static_cast<const uint16_t *>(a.sl.a[col_ok ? sg : 0]) +
-                         (grp * a.R + (col_ok ? j : 0)) * (int64_t)a.K;
-
-    floatx16_t acc = {};
-    const int kofs = 8 * half;
-    // Whole block dead (every column past the rank): skip the contraction.
-    const bool any_col = __ballot(col_ok) != 0;
-    if (any_col) {
-        // Two register stages of 8 k-steps (128 columns of K): the loads of one
-        // stage are in flight while the other is multiplied.
-        constexpr int KS = 8;
-        uint4 xa[KS], av[KS], xb[KS], bv[KS];
-        auto load = [&](uint4 *xs, uint4 *as, int k0) {
+    // The rows this thread loads (fixed over K): clamped to valid ones.
+    const uint16_t *rowp[NU];
+    int uoff[NU];
 #pragma unroll
-            for (int u = 0; u < KS; ++u) {
-                xs[u] = ldg<uint4>(xr + k0 + 16 * u + kofs);
-                as[u] = ldg<uint4>(ar + k0 + 16 * u + kofs);
-            }
-        };
-        auto mma = [&](const uint4 *xs, const uint4 *as) {
-#pragma unroll
-            for (int u = 0; u < KS; ++u)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xs[u]), as_frag(as[u]), acc, 0, 0, 0);
-        };
-        const int kmain = (a.K / (2 * KS * 16)) * (2 * KS * 16);   // whole 256-column pairs
-        int k0 = 0;
-        if (kmain > 0) {
-            load(xa, av, 0);
-            for (; k0 < kmain; k0 += 2 * KS * 16) {
-                load(xb, bv, k0 + KS * 16);
-                mma(xa, av);
-                if (k0 + 2 * KS * 16 < kmain) load(xa, av, k0 + 2 * KS * 16);
-                mma(xb, bv);
-            }
-        }
-        for (; k0 < a.K; k0 += 16) {          // K tail (K % 8 == 0)
-            const int kk = k0 + kofs;
-            uint4 x1 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-            if (kk < a.K) {
-                x1 = ldg<uint4>(xr + kk);
-                a1 = ldg<uint4>(ar + kk);
-            }
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(x1), as_frag(a1), acc, 0, 0, 0);
+    for (int v = 0; v < NU; ++v) {
+        const int q = min(v * kShThreads + tid, UNITS - 1);
+        const int row = q >> 3;
+        uoff[v] = 8 * (q & 7);
+        if (row < 64) {
+            const int item = a.seg.perm[p0 + (row < ntok ? row : 0)];
+            rowp[v] = a.x + (int64_t)(item / a.gm.x_div) * a.ldx;
+        } else {
+            const int c = cb * 32 * NCB + row - 64;
+            const int sg = c / a.R, j = c - sg * a.R;
+            const bool ok = c < SRf && j < r;
+            rowp[v] = static_cast<const uint16_t *>(a.sl.a[ok ? sg : 0]) +
+                      (grp * a.R + (ok ? j : 0)) * (int64_t)a.K;
         }
     }
+    const int nst = (a.K + kShStageK - 1) / kShStageK;
+    uint4 ring[kShNpf][NU];
+    auto issue = [&](int slot, int st) {
+#pragma unroll
+        for (int v = 0; v < NU; ++v) {
+            const int k = min(st * kShStageK + uoff[v], a.K - 8);
+            ring[slot][v] = ldg<uint4>(rowp[v] + k);
+        }
+    };
+    auto put = [&](int slot, int st, char *buf) {
+#pragma unroll
+        for (int v = 0; v < NU; ++v) {
+            const int q = v * kShThreads + tid;
+            if (q < UNITS) {
+                const bool kin = st * kShStageK + uoff[v] < a.K;
+                *reinterpret_cast<uint4 *>(buf + swz(q >> 3, q & 7, 8)) = kin ? ring[slot][v] : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    const int tb = w & 1, cbk = w >> 1;
+    floatx16_t acc = {};
+    auto mma = [&](const char *buf) {
+        if (cbk < NCB) {
+#pragma unroll
+            for (int ks = 0; ks < kShStageK / 16; ++ks) {
+                const int u = 2 * ks + half;
+                const uint4 xf = *reinterpret_cast<const uint4 *>(buf + swz(32 * tb + l32, u, 8));
+                const uint4 af = *reinterpret_cast<const uint4 *>(buf + swz(64 + 32 * cbk + l32, u, 8));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xf), as_frag(af), acc, 0, 0, 0);
+            }
+        }
+    };
+    // Stages past the last one (padding to a multiple of kShNpf) stage zeros:
+    // their K columns are all >= K.  No branch around the loads.
+#pragma unroll
+    for (int u = 0; u < kShNpf; ++u) issue(u, min(u, nst - 1));
+    for (int st0 = 0; st0 < nst; st0 += kShNpf) {
+#pragma unroll
+        for (int u = 0; u < kShNpf; ++u) {
+            const int st = st0 + u;
+            char *buf = s_stage[st & 1];
+            put(u, st, buf);
+            __syncthreads();
+            issue(u, min(st + kShNpf, nst - 1));   // refill the slot just consumed
+            mma(buf);
+        }
+    }
+    __syncthreads();   // s_brow visible (and every stage consumed)
 
-    if (col >= SRf) return;
-    // acc[i] belongs to token row 8*(i/4) + 4*half + (i%4) of this wave's block, column col.
+    // acc[i]: token 32*tb + 8*(i/4) + 4*half + (i%4), column 32*(NCB*cb + cbk) + l32
+    if (cbk >= NCB) return;
+    const int c = cb * 32 * NCB + 32 * cbk + l32;
+    if (c >= SRf) return;
+    const int sg = c / a.R, j = c - sg * a.R;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int row = wm * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (row < ntok) {
-            const int t = a.seg.perm[p0 + row] / a.gm.buf_div;
-            a.buf[((int64_t)sg * a.gm.buf_rows + t) * a.R + j] = col_ok ? acc[i] : 0.0f;
-        }
+        const int t = 32 * tb + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (t < ntok) a.buf[((int64_t)sg * a.gm.buf_rows + s_brow[t]) * a.R + j] = j < r ? acc[i] : 0.0f;
     }
 }
 
@@ -293,13 +338,6 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
 constexpr int kRowTok = 64;                  // tokens per tile (kPreTile)
 constexpr int kRowCols = 256;                // output columns per work-group
 constexpr int kRowYStride = kRowCols + 8;    // bf16 elements per LDS y row (528 B)
-
-// 16-byte unit u of row n of an LDS block with U units per row, XOR-swizzled
-// so fragment reads of consecutive rows spread over the banks.
-__device__ __forceinline__ int swz(int n, int u, int U) {
-    const int m = (U & (U - 1)) == 0 ? U - 1 : 1;
-    return (n * U + (u ^ (n & m))) << 4;
-}
 
 template <int NKS>
 __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a) {
@@ -467,9 +505,16 @@ hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
     a.R = R; a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.buf = buf;
     a.gm = gm;
     if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
-    a.n_cb = (S * R + kShrinkCols - 1) / kShrinkCols;
-    dim3 grid((unsigned)(a.n_cb * seg.max_tiles_pre));
-    hipLaunchKernelGGL(k_pre_shrink, grid, dim3(kThreads), 0, st, a);
+    // columns per work-group: all of S * R up to 128, in blocks of 32
+    const int sr = S * R;
+    const int ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
+    a.n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
+    dim3 grid((unsigned)(kXcds * ((seg.max_tiles_pre + kXcds - 1) / kXcds) * a.n_cb));
+    switch (ncb) {
+        case 1: hipLaunchKernelGGL(k_pre_shrink_rows<1>, grid, dim3(kShThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(k_pre_shrink_rows<2>, grid, dim3(kShThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_pre_shrink_rows<4>, grid, dim3(kShThreads), 0, st, a); break;
+    }
     return hipGetLastError();
 }
 
