@@ -495,6 +495,210 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     }
 }
 
+// Persistent, software-pipelined form of k_pre_expand_rows for the common case
+// (no per-item factor, no k-reduction): two work-groups per CU, each walking a
+// strided list of (tile, column group) items of its XCD.  The y / lora_b /
+// buffer loads of item k+1 are in flight while item k is multiplied, added
+// and stored; the per-item token lists (tile descriptor -> perm gather -> y
+// and buffer rows) run two and three items ahead in registers and reach the
+// loads through double-buffered LDS slots, so no dependent load sits on the
+// critical path.  Items are ordered column group first, so an XCD's
+// work-groups share a few column groups of lora_b in its L2 at any time.
+template <int NKS>
+__global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a) {
+    constexpr int R = 16 * NKS;
+    constexpr int U = R / 8;
+    constexpr int YU = kRowCols / 8;
+    constexpr int NY = kRowTok * YU / kThreads;
+    constexpr int NBU = kRowCols * U / kThreads;
+    constexpr int NFU = kRowTok * (R / 4) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * kRowYStride];
+    __shared__ __attribute__((aligned(16))) char s_b[kRowCols * U * 16];
+    __shared__ __attribute__((aligned(16))) char s_buf[kRowTok * U * 16];
+    __shared__ int64_t s_yrow[2][kRowTok];
+    __shared__ int64_t s_brow[2][kRowTok];
+    __shared__ float s_sc[2];
+    __shared__ int s_rk[2];
+
+    const int xcd = blockIdx.x % kXcds;
+    const int lw = blockIdx.x / kXcds;
+    const int nw = gridDim.x / kXcds;
+    const int n_tiles = a.seg.header[3];
+    const int n_x = n_tiles * a.per_xcd;
+    const int cnt = lw < n_x ? (n_x - lw + nw - 1) / nw : 0;
+    if (cnt == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    // item k of this work-group (clamped to its last one): tile and column group
+    auto tile_of = [&](int k) {
+        const int j = lw + min(k, cnt - 1) * nw;
+        return j % n_tiles;
+    };
+    auto cg_of = [&](int k) {
+        const int j = lw + min(k, cnt - 1) * nw;
+        return (j / n_tiles) * kXcds + xcd;
+    };
+    struct Col { int sg, Ns, n_base; bool ok; };
+    auto col_of = [&](int k) {
+        const int cg0 = cg_of(k);
+        Col c;
+        c.ok = cg0 < a.n_cg;
+        const int cg = c.ok ? cg0 : a.n_cg - 1;
+        c.sg = 0;
+        while (c.sg + 1 < a.S && cg >= a.group_start[c.sg + 1]) ++c.sg;
+        c.Ns = (int)a.sl.n[c.sg];
+        c.n_base = (cg - a.group_start[c.sg]) * kRowCols;
+        return c;
+    };
+    // metadata loads of item k: its token (thread < 64), slot rank and scale
+    struct Meta { int item; int rank; float sc; };
+    auto meta_load = [&](const int4 &tl) {
+        Meta m;
+        const int ntok = tl.z - tl.y;
+        m.item = a.seg.perm[tl.y + min(tid & 63, ntok - 1)];
+        const int sl = tl.x / a.gm.Ekey;
+        m.rank = a.slot_rank ? a.slot_rank[sl] : a.R;
+        m.sc = a.scale[sl];
+        return m;
+    };
+    auto meta_put = [&](const Meta &m, int slot) {
+        if (tid < kRowTok) {
+            s_yrow[slot][tid] = m.item / a.gm.y_div;
+            s_brow[slot][tid] = m.item / a.gm.buf_div;
+        }
+        if (tid == 0) {
+            s_rk[slot] = min(m.rank, a.R);
+            s_sc[slot] = m.sc;
+        }
+    };
+    uint4 yv[NY], bv[NBU];
+    float4 fv[NFU];
+    // data loads of item k (its metadata in LDS slot k & 1)
+    auto data_load = [&](const int4 &tl, const Col &c, int slot) {
+        const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
+        const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
+        const uint16_t *ybase = a.y + a.sl.off[c.sg];
+#pragma unroll
+        for (int i = 0; i < NY; ++i) {
+            const int q = i * kThreads + tid;
+            yv[i] = ldg<uint4>(ybase + s_yrow[slot][q / YU] * a.ldy + min(c.n_base + 8 * (q % YU), c.Ns - 8));
+        }
+        const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[c.sg]) + grp * c.Ns * R);
+#pragma unroll
+        for (int i = 0; i < NBU; ++i) {
+            const int q = i * kThreads + tid;
+            const int n = min(c.n_base + q / U, c.Ns - 1);
+            bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + q % U) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < NFU; ++i) {
+            const int q = i * kThreads + tid;
+            const int t = q / (R / 4), j = 4 * (q % (R / 4));
+            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_rows + s_brow[slot][t]) * R + j);
+        }
+    };
+
+    // ---- prologue: items 0, 1, 2 ------------------------------------------
+    int4 tl0 = ldg<int4>(&a.seg.tiles_pre[tile_of(0)]);
+    int4 tl1 = ldg<int4>(&a.seg.tiles_pre[tile_of(1)]);
+    int4 tl2 = ldg<int4>(&a.seg.tiles_pre[tile_of(2)]);
+    meta_put(meta_load(tl0), 0);
+    Meta m1 = meta_load(tl1);
+    Col c0 = col_of(0), c1 = col_of(1);
+    __syncthreads();
+    data_load(tl0, c0, 0);
+
+    for (int k = 0; k < cnt; ++k) {
+        const int slot = k & 1, nslot = slot ^ 1;
+        const int ntok = tl0.z - tl0.y;
+        // 1. item k into LDS; item k+1's metadata into its slot
+        {
+            const int r = s_rk[slot];
+#pragma unroll
+            for (int i = 0; i < NY; ++i) {
+                const int q = i * kThreads + tid;
+                *reinterpret_cast<uint4 *>(&s_y[(q / YU) * kRowYStride + 8 * (q % YU)]) = yv[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NBU; ++i) {
+                const int q = i * kThreads + tid;
+                *reinterpret_cast<uint4 *>(s_b + swz(q / U, q % U, U)) = bv[i];
+            }
+#pragma unroll
+            for (int i = 0; i < NFU; ++i) {
+                const int q = i * kThreads + tid;
+                const int t = q / (R / 4), j = 4 * (q % (R / 4));
+                const bool ok = t < ntok;
+                uint2 o;
+                o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
+                o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
+                *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
+            }
+            meta_put(m1, nslot);
+        }
+        __syncthreads();
+        // 2. loads of item k+1, metadata of item k+2, descriptor of item k+3
+        const float sc = s_sc[slot];
+        const Col ck = c0;
+        data_load(tl1, c1, nslot);
+        const Meta m2 = meta_load(tl2);
+        const int4 tl3 = ldg<int4>(&a.seg.tiles_pre[tile_of(k + 3)]);
+        // 3. D[n][t] for item k, added into the y tile
+        if (ck.ok) {
+            floatx16_t acc[2][2] = {{{}, {}}, {{}, {}}};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int u = 2 * ks + half;
+                uint4 bfr[2];
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(64 * w + 32 * nb + l32, u, U));
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb)
+                        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int t = 32 * tb + l32;
+                if (t < ntok) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * kRowYStride + 64 * w + 32 * nb + 8 * g + 4 * half]);
+                            const uint2 y0 = *yp;
+                            uint2 o;
+                            o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + sc * acc[nb][tb][4 * g + 1]);
+                            o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[nb][tb][4 * g + 2], bf16_hi(y0.y) + sc * acc[nb][tb][4 * g + 3]);
+                            *yp = o;
+                        }
+                }
+            }
+        }
+        __syncthreads();
+        // 4. item k back to y, row by row
+        if (ck.ok) {
+            uint16_t *ybase = a.y + a.sl.off[ck.sg];
+#pragma unroll
+            for (int i = 0; i < NY; ++i) {
+                const int q = i * kThreads + tid;
+                const int row = q / YU, col = ck.n_base + 8 * (q % YU);
+                if (row < ntok && col < ck.Ns)
+                    *reinterpret_cast<uint4 *>(ybase + s_yrow[slot][row] * a.ldy + col) =
+                        *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]);
+            }
+        }
+        __syncthreads();
+        tl0 = tl1; tl1 = tl2; tl2 = tl3;
+        m1 = m2;
+        c0 = c1; c1 = col_of(k + 2);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
@@ -542,6 +746,17 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
     if (!rows) {
         hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    if (!a.gm.coef && !a.gm.ksum) {
+        // two work-groups per CU, 32 CUs per XCD
+        const dim3 pgrid(kXcds * 64);
+        switch (R / 16) {
+            case 1: hipLaunchKernelGGL(k_pre_expand_pipe<1>, pgrid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL(k_pre_expand_pipe<2>, pgrid, dim3(kThreads), 0, st, a); break;
+            case 3: hipLaunchKernelGGL(k_pre_expand_pipe<3>, pgrid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL(k_pre_expand_pipe<4>, pgrid, dim3(kThreads), 0, st, a); break;
+        }
         return hipGetLastError();
     }
     switch (R / 16) {
