@@ -10,48 +10,68 @@ namespace {
 
 constexpr int kAlignThreads = 256;
 
-// Per slot: the pair ids of each expert in ascending order (the pair
-// segments), each run padded with the sentinel T*k to a multiple of bm, the
-// expert of every block, and the padded length.
+// Per slot (blockIdx.y): the pair ids of each expert in ascending order (the
+// pair segments), each run padded with the sentinel T*k to a multiple of bm,
+// the expert of every block, and the padded length.  Work-group blockIdx.x
+// fills positions [256 x, 256 x + 256) of the slot; the padded offsets of the
+// slot's experts come from a block scan (E <= 1024).
 __global__ __launch_bounds__(kAlignThreads) void k_moe_align_out(SegPtrs pair, int32_t T, int32_t k,
                                                                  int32_t E, int32_t bm, int32_t cap,
                                                                  int32_t *sorted_ids,
                                                                  int32_t *block_expert,
                                                                  int32_t *num_post_padded) {
     extern __shared__ int32_t off[];   // [E + 1] padded offsets of the experts in this slot
-    const int s = blockIdx.x;
+    __shared__ int32_t wsum[kAlignThreads / kWave + 1];
+    const int s = blockIdx.y;
     const int P = T * k;
     const int32_t *start = pair.slot_start + (int64_t)s * E;   // key s * E + e
-    if (threadIdx.x == 0) {
-        int o = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = o;
-            const int c = start[e + 1] - start[e];
-            o += (c + bm - 1) / bm * bm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // exclusive scan of the padded run lengths, E in chunks of 256
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kAlignThreads) {
+        const int e = e0 + tid;
+        const int c = e < E ? start[e + 1] - start[e] : 0;
+        const int v = (c + bm - 1) / bm * bm;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
         }
-        off[E] = o;
-        num_post_padded[s] = o;
+        if (lane == kWave - 1) wsum[w] = incl;
+        __syncthreads();
+        int before = 0;
+        for (int q = 0; q < w; ++q) before += wsum[q];
+        int chunk_total = 0;
+        for (int q = 0; q < kAlignThreads / kWave; ++q) chunk_total += wsum[q];
+        if (e < E) off[e] = carry + before + incl - v;
+        carry += chunk_total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        off[E] = carry;
+        if (blockIdx.x == 0) num_post_padded[s] = carry;
     }
     __syncthreads();
     const int total = off[E];
+    const int i = blockIdx.x * kAlignThreads + tid;
+    if (i >= cap) return;
     int32_t *so = sorted_ids + (int64_t)s * cap;
     int32_t *be = block_expert + (int64_t)s * (cap / bm);
-    for (int i = threadIdx.x; i < cap; i += kAlignThreads) {
-        int v = P;
-        if (i < total) {
-            int lo = 0, hi = E - 1;                 // expert e with off[e] <= i < off[e+1]
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= i) lo = mid; else hi = mid - 1;
-            }
-            const int j = i - off[lo];
-            if (j < start[lo + 1] - start[lo]) v = pair.perm[start[lo] + j];
-            if (i % bm == 0) be[i / bm] = lo;
-        } else if (i % bm == 0) {
-            be[i / bm] = -1;
+    int v = P;
+    if (i < total) {
+        int lo = 0, hi = E - 1;                 // expert e with off[e] <= i < off[e+1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= i) lo = mid; else hi = mid - 1;
         }
-        so[i] = v;
+        const int j = i - off[lo];
+        if (j < start[lo + 1] - start[lo]) v = pair.perm[start[lo] + j];
+        if (i % bm == 0) be[i / bm] = lo;
+    } else if (i % bm == 0) {
+        be[i / bm] = -1;
     }
+    so[i] = v;
 }
 
 }  // namespace
@@ -60,7 +80,8 @@ hipError_t launch_moe_align_out(const SegPtrs &pair, int32_t T, int32_t k, int32
                                 int32_t bm, int32_t *sorted_ids, int32_t *block_expert,
                                 int32_t *num_post_padded, hipStream_t st) {
     const int cap = moe_align_capacity(T, k, E, bm);
-    hipLaunchKernelGGL(k_moe_align_out, dim3(L), dim3(kAlignThreads), sizeof(int32_t) * (E + 1), st,
+    const dim3 grid((unsigned)((cap + kAlignThreads - 1) / kAlignThreads), (unsigned)L);
+    hipLaunchKernelGGL(k_moe_align_out, grid, dim3(kAlignThreads), sizeof(int32_t) * (E + 1), st,
                        pair, T, k, E, bm, cap, sorted_ids, block_expert, num_post_padded);
     return hipGetLastError();
 }

@@ -5,10 +5,11 @@
 // [w*chunk, (w+1)*chunk).  Pass 1 counts tokens per (wave, slot); a scan over
 // slots and then over waves turns the counts into write cursors; pass 2 walks
 // the same ranges in order and scatters token ids.  Inside a wave, lanes that
-// share a slot are ranked by lane index through ballots, so the result is the
-// stable order for any schedule.  The kernel is latency-bound at decode sizes,
-// so every global load (slot indices up to 8192 tokens, slot ranks) is issued
-// before the first barrier and the rest runs out of registers and LDS.
+// share a key are found with one ballot per key bit and ranked by lane index,
+// so the result is the stable order for any schedule.  The kernel is
+// latency-bound, so every global load (keys of up to 16384 items, slot ranks)
+// is issued before the first barrier and the rest runs out of registers and
+// LDS.
 #include "common.hpp"
 
 namespace aa {
@@ -47,40 +48,40 @@ __device__ int block_exclusive_scan(int v, int *total, int *wsum) {
     return r;
 }
 
-// Ballot-ranked counting of one 64-token step of a wave: the leader of each
-// group of lanes with the same slot adds the group size to the wave's count.
-__device__ __forceinline__ void count_step(int s, int lane, int32_t *mycnt) {
-    uint64_t rem = __ballot(s >= 0);
-    while (rem) {
-        const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int ls = __shfl(s, leader);
-        const uint64_t peers = __ballot(s == ls);
-        if (lane == leader) mycnt[ls] += __popcll(peers);
-        rem &= ~peers;
+// The lanes of a wave whose key equals this lane's (keys in [0, 2^nbits),
+// -1 = none): one ballot per key bit, so the cost does not grow with the
+// number of distinct keys in the step.
+__device__ __forceinline__ uint64_t same_key(int key, int nbits) {
+    uint64_t m = __ballot(key >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
     }
+    return key >= 0 ? m : 0ull;
 }
 
-// Same grouping; each lane writes its token at the group's cursor plus its
-// rank among lower lanes of the group (stable order).
-__device__ __forceinline__ void scatter_step(int s, int t, int lane, int32_t *mycnt,
+// Counting of one 64-item step of a wave: the lowest lane of each group of
+// lanes with the same key adds the group size to the wave's count.
+__device__ __forceinline__ void count_step(int s, int nbits, int lane, int32_t *mycnt) {
+    const uint64_t peers = same_key(s, nbits);
+    if (s >= 0 && lane == __ffsll((unsigned long long)peers) - 1) mycnt[s] += __popcll(peers);
+}
+
+// Same grouping; each lane writes its item at the group's cursor plus its
+// rank among lower lanes of the group (stable order).  Every lane reads the
+// cursor before the group's lowest lane advances it (one instruction each).
+__device__ __forceinline__ void scatter_step(int s, int t, int nbits, int lane, int32_t *mycnt,
                                              int32_t *perm) {
-    uint64_t rem = __ballot(s >= 0);
-    while (rem) {
-        const int leader = __ffsll((unsigned long long)rem) - 1;
-        const int ls = __shfl(s, leader);
-        const uint64_t peers = __ballot(s == ls);
-        int pos = 0;
-        if (lane == leader) {
-            pos = mycnt[ls];
-            mycnt[ls] = pos + __popcll(peers);
-        }
-        pos = __shfl(pos, leader);
-        if (s == ls) perm[pos + __popcll(peers & ((1ull << lane) - 1ull))] = t;
-        rem &= ~peers;
+    const uint64_t peers = same_key(s, nbits);
+    const int pos = s >= 0 ? mycnt[s] : 0;
+    if (s >= 0) {
+        perm[pos + __popcll(peers & ((1ull << lane) - 1ull))] = t;
+        if (lane == __ffsll((unsigned long long)peers) - 1) mycnt[s] = pos + __popcll(peers);
     }
 }
 
-constexpr int kRegSteps = 8;   // 64-token steps per wave held in registers (T <= 8192)
+constexpr int kRegSteps = 16;  // 64-item steps per wave held in registers (<= 16384 items)
 
 // Items are tokens (topk == nullptr: key = slot of the token) or (token, k)
 // pairs p = t * k + j (key = slot(t) * E + topk[p]); nkeys = L or L * E.
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     __shared__ int32_t s_invalid;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
     const int chunk = (T + kSegWaves - 1) / kSegWaves;
     const int b0 = w * chunk;
     const int b1 = min(T, b0 + chunk);
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     if (inreg) {
 #pragma unroll
         for (int u = 0; u < kRegSteps; ++u)
-            if (u < nsteps) count_step(sl[u], lane, mycnt);
+            if (u < nsteps) count_step(sl[u], nbits, lane, mycnt);
     } else {
         for (int base = b0; base < b1; base += kWave) {
             const int t = base + lane;
-            count_step(t < b1 ? key_of(t) : -1, lane, mycnt);
+            count_step(t < b1 ? key_of(t) : -1, nbits, lane, mycnt);
         }
     }
     if (inv) atomicAdd(&s_invalid, inv);
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     if (inreg) {
 #pragma unroll
         for (int u = 0; u < kRegSteps; ++u)
-            if (u < nsteps) scatter_step(sl[u], b0 + u * kWave + lane, lane, mycnt, seg.perm);
+            if (u < nsteps) scatter_step(sl[u], b0 + u * kWave + lane, nbits, lane, mycnt, seg.perm);
     } else {
         for (int base = b0; base < b1; base += kWave) {
             const int t = base + lane;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
                 const int e = topk ? topk[t] : 0;
                 kk = (v >= 0 && v < L && srank[v] > 0) ? (topk ? ((e >= 0 && e < E) ? v * E + e : -1) : v) : -1;
             }
-            scatter_step(kk, t, lane, mycnt, seg.perm);
+            scatter_step(kk, t, nbits, lane, mycnt, seg.perm);
         }
     }
     for (int i = n_active + tid; i < T; i += kSegThreads) seg.perm[i] = -1;
