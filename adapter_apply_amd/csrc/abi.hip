@@ -210,6 +210,7 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
     const bool group = path == LORA_PATH_GROUPED;
     if (group && !(can_group_sizes(T, R, dtype) && can_group_k(K))) return LORA_E_PATH;
+    if (group && (flags & LORA_FLAG_PARTIAL) && R > kGrpMaxPartialRank) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!buf || !x || !idx) return LORA_E_NULL;
     CHECK(check_ptrs(A, S));
@@ -259,6 +260,7 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
     const bool group = path == LORA_PATH_GROUPED;
     if (group && !(can_group_sizes(T, R, dtype) && rows_of_8(N, S, ldy, y_col_offset)))
         return LORA_E_PATH;
+    if (group && (flags & LORA_FLAG_PARTIAL) && R > kGrpMaxPartialRank) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!y || !buf || !idx || !scale) return LORA_E_NULL;
     CHECK(check_ptrs(B, S));
@@ -316,8 +318,11 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                       (path == LORA_PATH_FUSED || path == LORA_PATH_AUTO);
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
+    // Auto takes the grouped kernels while their in-kernel discovery is the
+    // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
+    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank;
     const bool group = !use_prefill && !fuse && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
-                       (path == LORA_PATH_GROUPED || path == LORA_PATH_AUTO);
+                       (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
     if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
     if (T == 0) return LORA_OK;
     if (!y || !x || !idx || !scale) return LORA_E_NULL;
@@ -341,6 +346,12 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
         CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
                                          st)));
+        if (R > kGrpMaxPartialRank) {
+            // large ranks: the K chunks are summed into the token-ordered buffer first
+            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf, st)));
+            return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
+                                              nullptr, buf, nullptr, st));
+        }
         return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
                                           scale, part, nullptr, nullptr, st));
     }

@@ -32,7 +32,8 @@ constexpr int kFusedXcds = 8;
 constexpr int kGrpTokens = 32;         // tokens of one slot per group
 constexpr int kGrpCols = 512;          // output columns per expand work-group
 constexpr int kGrpMaxTokens = 4096;    // idx staged in LDS
-constexpr int kGrpMaxRank = 64;
+constexpr int kGrpMaxRank = 128;
+constexpr int kGrpMaxPartialRank = 64;   // the expand adds K-chunk partials itself up to this rank
 constexpr int kMaxKcGrp = 16;          // K chunks of 512: K <= 8192
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

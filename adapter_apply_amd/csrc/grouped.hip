@@ -206,14 +206,19 @@ struct GrpExpandArgs {
 };
 
 // RB: R / 16 (1..4).
+// RB: R / 16 (1..8).  lora_b rows are staged per wave in passes of 64 ranks
+// (128 bytes of each row); ranks past 64 need the buffer form (n_kc == 1).
 template <int RB>
 __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     constexpr int R = 16 * RB;
     constexpr int BROW = 2 * R;                       // bytes of one lora_b row
+    constexpr int SROW = BROW < 128 ? BROW : 128;     // staged bytes per row and pass
+    constexpr int NPASS = (BROW + 127) / 128;
     constexpr int BLD = kColsW * BROW / 1024;         // wave load instructions for its lora_b rows
     constexpr int Q = kG * R / 4;                     // float4 units of one K chunk's partials
     constexpr int H = kThreads / Q > 0 ? kThreads / Q : 1;
-    constexpr int kStage = kWaves * kColsW * BROW;
+    constexpr int NQ = (Q + kThreads - 1) / kThreads; // units per thread
+    constexpr int kStage = kWaves * kColsW * SROW;
     constexpr int kDelta = kG * (kCols + 4) * 4;
     constexpr int kUnion = kStage > kDelta ? kStage : kDelta;
     __shared__ __attribute__((aligned(16))) char s_union[kUnion];
@@ -256,31 +261,39 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
         const int t = w + kWaves * i;
         yv[i] = ldg<uint4>(a.y + (int64_t)tokl[t < ntok ? t : 0] * a.ldy + a.sl.off[sg] + ycol);
     }
-    // partials of the group's tokens: thread = (float4 unit q, K-chunk phase h)
-    const int q = tid % Q, h = tid / Q;
-    const int pt = min(q / (R / 4), ntok - 1);
-    const float *pbase = a.buf ? a.buf + ((int64_t)sg * a.T + tokl[pt]) * R + 4 * (q % (R / 4))
-                               : a.part + ((int64_t)sg * n_kc * a.T + pos0 + pt) * R + 4 * (q % (R / 4));
-    constexpr int NPL = (kMaxKcGrp + H - 1) / H;     // K-chunk loads per thread, upper bound
-    float4 pv[NPL];
+    // partials (or buffer rows) of the group's tokens: thread = (float4 units
+    // q = tid % Q + kThreads * v, K-chunk phase h)
+    const int h = tid / Q;
+    constexpr int NPL = RB > 4 ? 1 : (kMaxKcGrp + H - 1) / H;   // K-chunk loads per unit, upper bound
+    float4 pv[NQ][NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int kcl = min(h + H * i, n_kc - 1);
-        pv[i] = ldg<float4>(pbase + (int64_t)kcl * a.T * R);
+    for (int v = 0; v < NQ; ++v) {
+        const int q = min(tid % Q + kThreads * v, Q - 1);
+        const int pt = min(q / (R / 4), ntok - 1);
+        const float *pbase = a.buf ? a.buf + ((int64_t)sg * a.T + tokl[pt]) * R + 4 * (q % (R / 4))
+                                   : a.part + ((int64_t)sg * n_kc * a.T + pos0 + pt) * R + 4 * (q % (R / 4));
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int kcl = min(h + H * i, n_kc - 1);
+            pv[v][i] = ldg<float4>(pbase + (int64_t)kcl * a.T * R);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- buffer: sum the K chunks in order, round to bf16 ------------------
     if (h < H) {
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (h + H * i < n_kc) { sum.x += pv[i].x; sum.y += pv[i].y; sum.z += pv[i].z; sum.w += pv[i].w; }
-        s_red[h][q] = sum;
+        for (int v = 0; v < NQ; ++v) {
+            const int q = tid % Q + kThreads * v;
+            if (q < Q) {
+                float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int i = 0; i < NPL; ++i)
+                    if (h + H * i < n_kc) { sum.x += pv[v][i].x; sum.y += pv[v][i].y; sum.z += pv[v][i].z; sum.w += pv[v][i].w; }
+                s_red[h][q] = sum;
+            }
+        }
     }
-    char *stage = s_union + w * (kColsW * BROW);
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
     __syncthreads();
     for (int u = tid; u < Q; u += kThreads) {
         float4 sum = s_red[0][u];
@@ -299,23 +312,40 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     __syncthreads();
 
     // ---- expand (MFMA 16x16x16): D[n][t] = B[n][:] . buf[t][:] ------------
+    // The wave's lora_b rows pass through its own staging area 64 ranks at a
+    // time; rank steps past the slot's rank are skipped.
     const int row = lane & 15, quad = lane >> 4;
+    const int nks = (r + 15) >> 4;
+    char *stage = s_union + w * (kColsW * SROW);
     floatx4_t out[4][2];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) out[nb][tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < RB; ++ks) {
-        uint2 bfr[2];
+    for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint2 *>(&s_buf[16 * tb + row][16 * ks + 4 * quad]);
+        for (int i = 0; i < BLD; ++i) {
+            const int byte = 1024 * i + 16 * lane;            // within the wave's block of rows
+            const int off = byte % BROW - ps * 128;
+            if (off >= 0 && off < SROW)
+                *reinterpret_cast<uint4 *>(stage + (byte / BROW) * SROW + off) = bq[i];
+        }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const uint2 af = *reinterpret_cast<const uint2 *>(stage + (16 * nb + row) * BROW + 32 * ks + 8 * quad);
+        for (int kq = 0; kq < SROW / 32; ++kq) {
+            const int ks = ps * 4 + kq;
+            if (ks < nks) {
+                uint2 bfr[2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-                out[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(af), frag4(bfr[tb]), out[nb][tb], 0, 0, 0);
+                for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint2 *>(&s_buf[16 * tb + row][16 * ks + 4 * quad]);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const uint2 af = *reinterpret_cast<const uint2 *>(stage + (16 * nb + row) * SROW + 32 * kq + 8 * quad);
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb)
+                        out[nb][tb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(af), frag4(bfr[tb]), out[nb][tb], 0, 0, 0);
+                }
+            }
         }
     }
     __syncthreads();   // every wave is done with its staging area (the deltas alias it)
@@ -437,7 +467,11 @@ hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, cons
         case 1: hipLaunchKernelGGL(k_grp_expand<1>, grid, dim3(kThreads), 0, st, a); break;
         case 2: hipLaunchKernelGGL(k_grp_expand<2>, grid, dim3(kThreads), 0, st, a); break;
         case 3: hipLaunchKernelGGL(k_grp_expand<3>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_grp_expand<4>, grid, dim3(kThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(k_grp_expand<4>, grid, dim3(kThreads), 0, st, a); break;
+        case 5: hipLaunchKernelGGL(k_grp_expand<5>, grid, dim3(kThreads), 0, st, a); break;
+        case 6: hipLaunchKernelGGL(k_grp_expand<6>, grid, dim3(kThreads), 0, st, a); break;
+        case 7: hipLaunchKernelGGL(k_grp_expand<7>, grid, dim3(kThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(k_grp_expand<8>, grid, dim3(kThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }

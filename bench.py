@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe"])
-    p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode"],
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode", "prefill"],
                    help="force a decode path (development runs; the headline uses auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -327,7 +327,7 @@ def main():
     del base
     torch.cuda.synchronize()
 
-    step_path = {"auto": aa.LORA_PATH_AUTO, "fused": aa.LORA_PATH_FUSED,
+    step_path = {"auto": aa.LORA_PATH_AUTO, "fused": aa.LORA_PATH_FUSED, "prefill": aa.LORA_PATH_PREFILL,
                  "grouped": aa.LORA_PATH_GROUPED, "decode": aa.LORA_PATH_DECODE}[args.path]
 
     def step(d):
@@ -344,15 +344,16 @@ def main():
     fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
              and c.T <= 1024 and c.K % 1024 == 0 and rows8)
     grouped = (not prefill and not fused and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
-               and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8)
+               and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8)
     if args.path != "auto":
-        prefill = False
+        prefill = args.path == "prefill"
         fused, grouped = args.path == "fused", args.path == "grouped"
     fold = not prefill and math.ceil(c.K / 256) * c.R <= 512
     part = aa.LORA_FLAG_PARTIAL
     ready = aa.LORA_FLAG_SEGMENTS_READY
     # the kernel-by-kernel calls use the step's path explicitly
-    kpath = aa.LORA_PATH_GROUPED if grouped else aa.LORA_PATH_AUTO
+    kpath = (aa.LORA_PATH_GROUPED if grouped else aa.LORA_PATH_PREFILL if prefill
+             else aa.LORA_PATH_DECODE if args.path == "decode" else aa.LORA_PATH_AUTO)
 
     def shrink_only(d):
         aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"], path=kpath,
@@ -362,9 +363,12 @@ def main():
         aa.lora_shrink(d["buf"], d["x"], d["A"], d["idx"], d["rank"], d["ws"], path=kpath,
                        flags=ready | aa.LORA_FLAG_ACTIVE_ONLY)
 
+    # grouped path above rank 64: shrink, reduce into the buffer, expand from it
+    grouped_buf = grouped and c.R > 64
+
     def expand_only(d):
         aa.lora_expand(d["y"], d["buf"], d["B"], d["idx"], d["rank"], d["scale"], d["ws"],
-                       path=kpath, flags=ready | (part if (fold or grouped) else 0))
+                       path=kpath, flags=ready | (part if (fold or grouped) and not grouped_buf else 0))
 
     def segments_only(d):
         aa.lora_build_segments(d["idx"], d["rank"], c.L, c.R, d["ws"])
@@ -372,7 +376,8 @@ def main():
     if args.profile:
         for i in range(max(steps, 1)):
             step(insts[i % n_inst])
-        for fn in (segments_only, shrink_reduce, shrink_only, expand_only):
+        for fn in ((segments_only, shrink_reduce, expand_only) if grouped_buf else
+                   (segments_only, shrink_reduce, shrink_only, expand_only)):
             for i in range(n_inst):
                 fn(insts[i])
         torch.cuda.synchronize()
@@ -432,6 +437,8 @@ def main():
     per_kernel = {}
     if fused:
         kernel_calls = [("fused", step)]      # the whole step is one kernel
+    elif grouped_buf:
+        kernel_calls = [("shrink+reduce", shrink_reduce), ("expand", expand_only)]
     elif grouped:
         kernel_calls = [("shrink", shrink_only), ("expand", expand_only)]
     else:
@@ -453,7 +460,7 @@ def main():
         torch.cuda.synchronize()
         per_kernel[name] = a0.elapsed_time(a1) * 1e3 / (reps * n_inst)   # us per launch
         del g
-    if "shrink+reduce" in per_kernel:
+    if "shrink+reduce" in per_kernel and "shrink" in per_kernel:
         per_kernel["reduce"] = per_kernel.pop("shrink+reduce") - per_kernel["shrink"]
     # the expand above must leave every instance's buffer state as a step does
     for i in range(n_inst):
@@ -464,8 +471,9 @@ def main():
     if fused:
         dom, dom_bytes = "fused", ab["fused"]
     else:
-        dom = max(("shrink", "expand"), key=lambda k: per_kernel[k])
-        dom_bytes = ab[dom]
+        dom = max((k for k in ("shrink", "shrink+reduce", "expand") if k in per_kernel),
+                  key=lambda k: per_kernel[k])
+        dom_bytes = ab["shrink" if dom == "shrink+reduce" else dom]
     achieved = dom_bytes / (per_kernel[dom] * 1e-6) / 1e9
     khash = kernel_hash()
     traffic = load_traffic(args.workload, dom, khash)

@@ -43,16 +43,17 @@
  *            decode path only).  The intermediate buffer is always fp32.
  *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
  *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
- *            otherwise lora_apply_packed takes FUSED, else GROUPED, where
- *            the shapes allow, and DECODE elsewhere; lora_shrink / lora_expand
- *            take DECODE
+ *            otherwise lora_apply_packed takes FUSED, else GROUPED (when also
+ *            L <= 64 and R <= 64), where the shapes allow, and DECODE
+ *            elsewhere; lora_shrink / lora_expand take DECODE
  *            (so that a shrink and an expand called apart agree).
  *            DECODE forces the split (segments, VALU shrink, expand) decode
  *            path; PREFILL forces the MFMA path (bf16, R % 16 == 0 only);
  *            GROUPED forces the slot-grouped decode kernels (split-K MFMA
  *            shrink, MFMA expand; no segment build: bf16, R % 16 == 0,
- *            R <= 64, T <= 4096, and for the shrink K % 64 == 0, K <= 8192,
- *            for the expand N % 8 == 0, ldy % 8 == 0, y_col_offset % 8 == 0);
+ *            R <= 128, T <= 4096, and for the shrink K % 64 == 0, K <= 8192,
+ *            for the expand N % 8 == 0, ldy % 8 == 0, y_col_offset % 8 == 0;
+ *            LORA_FLAG_PARTIAL only for R <= 64);
  *            FUSED forces the single-launch decode kernel of
  *            lora_apply_packed (bf16, R % 16 == 0, R <= 32, T <= 1024,
  *            K % 1024 == 0, N, ldy and y_col_offset % 8 == 0; it needs no

@@ -103,7 +103,7 @@ def _apply(**kw):
     (dict(path=aa.LORA_PATH_FUSED, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_PREFILL, R=24), aa.LORA_E_PATH),
-    (dict(path=aa.LORA_PATH_GROUPED, R=128), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_GROUPED, R=144), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_GROUPED, T=5000), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_GROUPED, K=8256, ldx=8256), aa.LORA_E_PATH),   # 17 K chunks
     (dict(path=aa.LORA_PATH_GROUPED, K=4104, ldx=4104), aa.LORA_E_PATH),   # K % 64
@@ -137,8 +137,12 @@ def test_shrink_expand_validation():
     # the fused kernel has no separate shrink; the grouped one takes rank <= 64
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
                            aa.LORA_PATH_FUSED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
-    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 128, FAKE, None, 1,
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 144, FAKE, None, 1,
                            aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    # the partial-sum hand-off stops at rank 64 on the grouped path
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 128, FAKE, None, 1,
+                           aa.LORA_PATH_GROUPED, aa.LORA_FLAG_PARTIAL, FAKE_WS, ok_ws,
+                           None) == aa.LORA_E_PATH
     assert lib.lora_shrink(FAKE, FAKE, 72, 16, 72, A, 2, 3, 16, FAKE, None, 1,
                            aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     Ng = (C.c_int64 * 2)(64, 68)

@@ -72,7 +72,7 @@ def fusable(c):
 
 def groupable(c):
     """Shapes the slot-grouped split decode kernels take."""
-    return (c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64 and c.T <= 4096
+    return (c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 128 and c.T <= 4096
             and c.K % 64 == 0 and c.K <= 8192 and all(n % 8 == 0 for n in c.N))
 
 
@@ -94,6 +94,7 @@ INTEGER_CASES = [
     (28, 1, 1024, [8], 16, 1),
     (29, 1024, 1024, [16, 1032], 32, 1024),
     (30, 1024, 1024, [256, 64], 16, 40),     # 40 slots x 16 token chunks: work-group discovery
+    (31, 300, 1024, [512, 64], 128, 9),      # rank 128
 ]
 
 
@@ -382,7 +383,8 @@ def test_fused_skewed_slots(oracle_mod, path):
 
 @pytest.mark.parametrize("path", [FUS, GRP])
 def test_fused_rejects_unsupported(path):
-    c = synth.config_many(T=64)          # rank 128 > 64
+    # rank 128 is past the single-launch kernel, rank 160 past the grouped ones
+    c = synth.config_many(T=64, R=128 if path == FUS else 160)
     d = LinearOnDevice(c, guard=False)
     with pytest.raises(aa.LoraError) as e:
         d.apply(path)
@@ -393,6 +395,8 @@ def test_fused_rejects_unsupported(path):
     (41, 4096, 512, [64] * 8, 64, 7),        # most tokens, 8 slices, rank 64
     (42, 64, 8192, [520, 1024], 64, 3),      # 16 K chunks, ragged 512-column chunk
     (43, 300, 576, [8, 16, 24], 48, 2),      # K not a multiple of 512, 3 rank blocks
+    (44, 200, 2048, [264, 128], 128, 5),     # rank 128 (two rank passes), ragged column chunk
+    (45, 150, 512, [80], 80, 3),             # rank 80: second pass of 16 ranks
 ])
 def test_grouped_limits_bit_exact(oracle_mod, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
