@@ -60,6 +60,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x
 template <typename V, typename E>
 __device__ __forceinline__ V ldg(const E *p) { return *reinterpret_cast<const V *>(p); }
 
+// Streamed-once data (the y tiles of the prefill expand): 16-byte loads and
+// stores with the non-temporal hint, so that they do not push the reused
+// lora_b rows out of the L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <typename E>
+__device__ __forceinline__ uint4 ldg_nt(const E *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <typename E>
+__device__ __forceinline__ void stg_nt(E *p, const uint4 &v) {
+    const u32x4_t u = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout (all offsets 256-byte aligned).
 // ---------------------------------------------------------------------------

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     for (int i = 0; i < NY; ++i) {
         const int q = i * kThreads + tid;
         const int row = q / YU, col = n_base + 8 * (q % YU);
-        yv[i] = ldg<uint4>(ybase + s_yrow[row] * a.ldy + min(col, Ns - 8));
+        yv[i] = ldg_nt(ybase + s_yrow[row] * a.ldy + min(col, Ns - 8));
     }
     const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * R);
     uint4 bv[NBU];
@@ -490,8 +490,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
         const int q = i * kThreads + tid;
         const int row = q / YU, col = n_base + 8 * (q % YU);
         if (row < ntok && col < Ns)
-            *reinterpret_cast<uint4 *>(ybase + s_yrow[row] * a.ldy + col) =
-                *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]);
+            stg_nt(ybase + s_yrow[row] * a.ldy + col,
+                   *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]));
     }
 }
 
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int q = i * kThreads + tid;
-            yv[i] = ldg<uint4>(ybase + s_yrow[slot][q / YU] * a.ldy + min(c.n_base + 8 * (q % YU), c.Ns - 8));
+            yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + min(c.n_base + 8 * (q % YU), c.Ns - 8));
         }
         const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[c.sg]) + grp * c.Ns * R);
 #pragma unroll
@@ -688,8 +688,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
                 const int q = i * kThreads + tid;
                 const int row = q / YU, col = ck.n_base + 8 * (q % YU);
                 if (row < ntok && col < ck.Ns)
-                    *reinterpret_cast<uint4 *>(ybase + s_yrow[slot][row] * a.ldy + col) =
-                        *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]);
+                    stg_nt(ybase + s_yrow[slot][row] * a.ldy + col,
+                           *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]));
             }
         }
         __syncthreads();
