@@ -60,9 +60,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x
 template <typename V, typename E>
 __device__ __forceinline__ V ldg(const E *p) { return *reinterpret_cast<const V *>(p); }
 
-// Streamed-once data (the y tiles of the prefill expand): 16-byte loads and
-// stores with the non-temporal hint, so that they do not push the reused
-// lora_b rows out of the L2.
+// Streamed-once data (y rows): 16-byte loads and stores with the
+// non-temporal hint, so that they do not push reused lora_a / lora_b rows and
+// x rows out of the L2.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <typename E>
 __device__ __forceinline__ uint4 ldg_nt(const E *p) {

@@ -8,11 +8,10 @@
 // round trip are needed.
 //
 // Fast path (L <= 64 and T <= 1024; lane s of a wave stands for slot s): one
-// wave loads idx and the slot ranks, drops tokens whose slot is out of range
-// or has rank 0 (a shuffle of the ranks), counts tokens per slot in its own
-// LDS histogram, scans groups and tokens over the slots with DPP, picks the
-// group's slot by ballot, writes the group's tokens by ballot rank, and
-// publishes the result; one barrier.
+// wave loads idx and the slot ranks, counts tokens per slot in its own LDS
+// histogram (slots of rank 0 then count as empty), scans groups and tokens
+// over the slots with DPP, picks the group's slot by ballot, writes the
+// group's tokens by ballot rank, and publishes the result; one barrier.
 // Generic path (larger L or T): idx staged in LDS, ballot-leader histogram, a
 // one-wave scan over slots and a one-wave ballot compaction.
 #pragma once
@@ -58,6 +57,61 @@ struct DiscLds {
     int32_t gcnt[kMaxSlots];
 };
 
+// One-wave discovery for T <= 64 * MC, L <= 64 (lane s stands for slot s);
+// writes d.tok and d.info (slot or -1, first, ntok, pos0, n_groups, rank).
+// Every token with a slot in [0, L) is counted; slots of rank 0 then get no
+// tokens, which removes their tokens without a per-token rank lookup.
+template <int G, int MC, typename DL, typename Pick>
+__device__ __forceinline__ void one_wave_group(const int32_t *__restrict__ idx,
+                                               const int32_t *__restrict__ slot_rank, int T, int L,
+                                               int R, DL &d, Pick pick) {
+    const int lane = threadIdx.x & 63;
+    int v[MC];
+#pragma unroll
+    for (int c = 0; c < MC; ++c) v[c] = idx[min(kWave * c + lane, T - 1)];
+    const int rk = slot_rank ? min(slot_rank[min(lane, L - 1)], R) : R;
+    d.cnt[lane] = 0;
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+        const int vv = v[c];
+        const bool ok = kWave * c + lane < T && vv >= 0 && vv < L;
+        v[c] = ok ? vv : -1;
+        // this wave's histogram: LDS program order, no barrier
+        if (ok) atomicAdd(&d.cnt[vv], 1);
+    }
+    const int tot = rk > 0 ? d.cnt[lane] : 0;   // lane s: tokens of slot s
+    const int ng = (tot + G - 1) / G;
+    // inclusive scans over the slots, groups in the high half-word
+    const int inc = wave_incl_scan(tot | (ng << 16));
+    const int gi = inc >> 16, ti = inc & 0xffff;
+    const int n_groups = __builtin_amdgcn_readlane(gi, kWave - 1);
+    const int group = pick(n_groups);
+    int info0 = -1, first = 0, ntok = 0, pos0 = 0, rank = 0;
+    if (group >= 0 && group < n_groups) {
+        const uint64_t hit = __ballot(group >= gi - ng && group < gi);
+        const int s = __ffsll((unsigned long long)hit) - 1;
+        first = (group - __builtin_amdgcn_readlane(gi - ng, s)) * G;
+        ntok = min(G, __builtin_amdgcn_readlane(tot, s) - first);
+        pos0 = __builtin_amdgcn_readlane(ti - tot, s) + first;
+        rank = __builtin_amdgcn_readlane(rk, s);
+        info0 = s;
+        uint64_t bal[MC];
+#pragma unroll
+        for (int c = 0; c < MC; ++c) bal[c] = __ballot(v[c] == s);
+        int seen = 0;
+#pragma unroll
+        for (int c = 0; c < MC; ++c) {
+            const int rkk = seen + __popcll(bal[c] & ((1ull << lane) - 1ull));
+            if (v[c] == s && rkk >= first && rkk < first + ntok) d.tok[rkk - first] = kWave * c + lane;
+            seen += __popcll(bal[c]);
+        }
+    }
+    if (lane == 0) {
+        d.info[0] = info0; d.info[1] = first; d.info[2] = ntok;
+        d.info[3] = pos0; d.info[4] = n_groups; d.info[5] = rank;
+    }
+}
+
 // Every thread of the work-group calls this with the same arguments; `pick`
 // maps the batch's group count to this work-group's group id (or -1) and must
 // be uniform.  On return d.tok[0 .. ntok) holds the group's tokens ascending.
@@ -69,57 +123,9 @@ __device__ GroupSel find_group(const int32_t *__restrict__ idx, const int32_t *_
     if (L <= kWave && T <= kWave * kOneWaveChunks) {
         // One wave finds the group; the others wait at the single barrier.
         if (w == 0) {
-            const int C = (T + kWave - 1) / kWave;
-            int v[kOneWaveChunks];
-#pragma unroll
-            for (int c = 0; c < kOneWaveChunks; ++c) v[c] = -1;
-#pragma unroll
-            for (int c = 0; c < kOneWaveChunks; ++c)
-                if (c < C) v[c] = idx[min(kWave * c + lane, T - 1)];
-            const int rk = slot_rank ? min(slot_rank[min(lane, L - 1)], R) : R;
-            d.cnt[lane] = 0;
-#pragma unroll
-            for (int c = 0; c < kOneWaveChunks; ++c) {
-                if (c < C) {
-                    const int vv = v[c];
-                    const bool in = kWave * c + lane < T && vv >= 0 && vv < L;
-                    const int rv = __shfl(rk, in ? vv : 0);
-                    v[c] = in && rv > 0 ? vv : -1;
-                    // this wave's histogram: LDS program order, no barrier
-                    if (v[c] >= 0) atomicAdd(&d.cnt[v[c]], 1);
-                }
-            }
-            const int tot = d.cnt[lane];          // lane s: tokens of slot s
-            const int ng = (tot + G - 1) / G;
-            // inclusive scans over the slots, groups in the high half-word
-            const int inc = wave_incl_scan(tot | (ng << 16));
-            const int gi = inc >> 16, ti = inc & 0xffff;
-            const int n_groups = __builtin_amdgcn_readlane(gi, kWave - 1);
-            const int group = pick(n_groups);
-            int info0 = -1, first = 0, ntok = 0, pos0 = 0, rank = 0;
-            if (group >= 0 && group < n_groups) {
-                const uint64_t hit = __ballot(group >= gi - ng && group < gi);
-                const int s = __ffsll((unsigned long long)hit) - 1;
-                first = (group - __builtin_amdgcn_readlane(gi - ng, s)) * G;
-                ntok = min(G, __builtin_amdgcn_readlane(tot, s) - first);
-                pos0 = __builtin_amdgcn_readlane(ti - tot, s) + first;
-                rank = __builtin_amdgcn_readlane(rk, s);
-                info0 = s;
-                int seen = 0;
-#pragma unroll
-                for (int c = 0; c < kOneWaveChunks; ++c) {
-                    if (c < C && seen < first + ntok) {
-                        const uint64_t bal = __ballot(v[c] == s);
-                        const int rkk = seen + __popcll(bal & ((1ull << lane) - 1ull));
-                        if (v[c] == s && rkk >= first && rkk < first + ntok) d.tok[rkk - first] = kWave * c + lane;
-                        seen += __popcll(bal);
-                    }
-                }
-            }
-            if (lane == 0) {
-                d.info[0] = info0; d.info[1] = first; d.info[2] = ntok;
-                d.info[3] = pos0; d.info[4] = n_groups; d.info[5] = rank;
-            }
+            if (T <= 4 * kWave) one_wave_group<G, 4>(idx, slot_rank, T, L, R, d, pick);
+            else if (T <= 8 * kWave) one_wave_group<G, 8>(idx, slot_rank, T, L, R, d, pick);
+            else one_wave_group<G, kOneWaveChunks>(idx, slot_rank, T, L, R, d, pick);
         }
         __syncthreads();
         sel.slot = d.info[0];

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
         }
         // y: wave w owns token w of the group, 8 columns per lane, 2 x 512 columns
 #pragma unroll
-        for (int i = 0; i < 2; ++i) yv[i] = ldg<uint4>(yrow + min(n_base + 512 * i + 8 * lane, Ns - 8));
+        for (int i = 0; i < 2; ++i) yv[i] = ldg_nt(yrow + min(n_base + 512 * i + 8 * lane, Ns - 8));
         __builtin_amdgcn_sched_barrier(0);
         consume(0);
         for (int c0 = SUBB; c0 < nsub; c0 += SUBB) {
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_fused(FusedArgs a) {
                 o.y = pack_bf16x2(bf16_lo(y0.y) + d0.z, bf16_hi(y0.y) + d0.w);
                 o.z = pack_bf16x2(bf16_lo(y0.z) + d1.x, bf16_hi(y0.z) + d1.y);
                 o.w = pack_bf16x2(bf16_lo(y0.w) + d1.z, bf16_hi(y0.w) + d1.w);
-                *reinterpret_cast<uint4 *>(yrow + n_base + cl) = o;
+                stg_nt(yrow + n_base + cl, o);
             }
         }
     }
