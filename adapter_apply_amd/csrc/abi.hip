@@ -224,14 +224,18 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     // buf is written unless the decode path keeps partials in the workspace
     const bool writes_buf = use_prefill || !(flags & LORA_FLAG_PARTIAL);
     if (group) {
-        // groups come from idx inside the kernels: no segments
+        // groups come from idx inside the kernels, or from the segment table
+        const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
+        if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
+            CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
         if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
             CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
         CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part,
-                                         grp_kc_slot(ws, wl.seg), st)));
+                                         grp_kc_slot(ws, wl.seg), gseg, st)));
         if (!writes_buf) return LORA_OK;
-        return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf, st));
+        return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf,
+                                          gseg, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
@@ -272,9 +276,12 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
     const SegPtrs seg = seg_ptrs(ws, sgl);
     const Slices sl = make_slices(nullptr, B, N, S, y_col_offset);
     if (group) {
+        const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
+        if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
+            CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
         if (!(flags & LORA_FLAG_PARTIAL))
             return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
-                                              nullptr, buf, nullptr, st));
+                                              nullptr, buf, nullptr, gseg, st));
         // partials right after the segments; the chunk count comes from the
         // shrink, capped by what this workspace holds
         const float *part = reinterpret_cast<const float *>(static_cast<char *>(ws) + sgl.end);
@@ -283,7 +290,7 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
         if (fit < 1) return LORA_E_WORKSPACE;
         const int32_t cap = (int32_t)(fit < kMaxKcGrp ? fit : kMaxKcGrp);
         return launched(launch_grp_expand(y, ldy, T, cap, sl, S, L, R, idx, slot_rank, scale, part,
-                                          nullptr, grp_kc_slot(ws, sgl), st));
+                                          nullptr, grp_kc_slot(ws, sgl), gseg, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
@@ -342,18 +349,23 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
     if (group) {
-        // two launches; each derives its token groups from idx (no segments)
+        // two launches that derive their token groups from idx, or the
+        // segment build and launches that read the groups from its table
+        const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
+        if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
+            CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
         CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
-                                         st)));
+                                         gseg, st)));
         if (R > kGrpMaxPartialRank) {
             // large ranks: the K chunks are summed into the token-ordered buffer first
-            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf, st)));
+            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf,
+                                             gseg, st)));
             return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
-                                              nullptr, buf, nullptr, st));
+                                              nullptr, buf, nullptr, gseg, st));
         }
         return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
-                                          scale, part, nullptr, nullptr, st));
+                                          scale, part, nullptr, nullptr, gseg, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));

@@ -229,21 +229,27 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
 
 int32_t grp_max_groups(int32_t T, int32_t L);
 int32_t grp_kchunks(int32_t K);
+// Whether the grouped kernels find their groups from idx in one wave (else
+// they read the segment table's decode tiles).
+inline bool grp_discovers(int32_t T, int32_t L) { return L <= 64 && T <= 1024; }
+// seg (nullable): the segment table the groups are read from, already built
+// on the stream; null: each work-group discovers its group from idx.
 // Partials: fp32 [S][grp_kchunks(K)][T][R], rows by slot-sorted position.
 // n_kc_out (nullable) receives the chunk count for a later expand call.
 hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, float *part, int32_t *n_kc_out,
-                             hipStream_t st);
+                             const SegPtrs *seg, hipStream_t st);
 // Adds the partials (n_kc chunks, or the count at n_kc_in capped at n_kc) or,
 // when buf is given, the token-ordered buffer [S][T][R].
 hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *scale, const float *part,
-                             const float *buf, const int32_t *n_kc_in, hipStream_t st);
+                             const float *buf, const int32_t *n_kc_in, const SegPtrs *seg,
+                             hipStream_t st);
 hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *part, int32_t n_kc,
-                             float *buf, hipStream_t st);
+                             float *buf, const SegPtrs *seg, hipStream_t st);
 
 // Grouped-problem mapping of the MFMA kernels.  A tile's key is
 // slot * Ekey + expert (Ekey = 1 for token tiles); the lora tensor it reads is

@@ -7,10 +7,13 @@
 // spread over K instead, and the expand sums the K-chunk partials.
 //
 // Groups: the slot-major runs of at most 32 tokens that a stable sort of the
-// active tokens by slot gives; both kernels derive their work-group's group
-// from idx themselves (discover.hpp), so there is no separate segment kernel
-// and the only dependent global loads are idx -> {x, lora_a} and
-// idx -> {partials, lora_b, y}.
+// active tokens by slot gives.  While one wave can find them (at most 64
+// slots and 1024 tokens) each work-group derives its group from idx itself
+// (discover.hpp), so there is no separate segment kernel and the only
+// dependent global loads are idx -> {x, lora_a} and idx -> {partials,
+// lora_b, y}.  Beyond that the kernels read the same groups from the segment
+// table (the decode tiles of the segment build): one tile and its token ids
+// per work-group instead of a discovery over the whole batch in each.
 //
 // Shrink work-group = (group, pack of up to 4 blocks of 16 rank rows drawn
 // from the S slices, K chunk of 512).  Each of the 8 waves loads its 64-column
@@ -25,6 +28,8 @@
 // and runs v_mfma_f32_16x16x16_bf16 as D[n][t] = B[n][:] . buf[t][:]; the
 // deltas go through LDS so that y is read and written along rows, 16 bytes
 // per lane: y[t][n] = RNE(y + scale[s] * delta).
+#include <type_traits>
+
 #include "discover.hpp"
 
 namespace aa {
@@ -50,12 +55,46 @@ __device__ __forceinline__ short4_t frag4(const uint2 &u) { return __builtin_bit
 __device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ (r & 7)) << 4); }
 
 using Disc = DiscLds<kG, kGrpMaxTokens, kWaves>;
+struct NoDisc {};
+template <bool TAB>
+using DiscT = typename std::conditional<TAB, NoDisc, Disc>::type;
+
+// Decode tiles of the segment build: (slot, begin, end) runs of at most 32
+// tokens in slot-sorted order, the groups the discovery would find.
+struct GrpTable {
+    const int4 *tiles;
+    const int32_t *perm;
+    const int32_t *header;   // [2]: number of tiles
+    int32_t max_tiles;
+};
 
 // Group `group` of the batch (discover.hpp); *tok receives its token list.
 __device__ __forceinline__ GroupSel discover(const int32_t *idx, const int32_t *slot_rank, int T, int L,
                                              int R, Disc &g, int group, const int32_t **tok) {
     *tok = g.tok;
     return find_group(idx, slot_rank, T, L, R, g, [=](int) { return group; });
+}
+
+// Group `group` from the segment table (TAB) or from idx.
+template <bool TAB, typename D>
+__device__ __forceinline__ GroupSel group_of(const GrpTable &tab, const int32_t *idx,
+                                             const int32_t *slot_rank, int T, int L, int R, D &g,
+                                             int group, const int32_t **tok) {
+    if constexpr (TAB) {
+        GroupSel sel{-1, 0, 0, 0, 0, 0};
+        const int n = tab.header[2];
+        const int4 tl = tab.tiles[min(group, tab.max_tiles - 1)];   // read before the test
+        if (group >= n) return sel;
+        sel.slot = tl.x;
+        sel.pos0 = tl.y;
+        sel.ntok = tl.z - tl.y;
+        sel.n_groups = n;
+        sel.rank = min(slot_rank ? slot_rank[tl.x] : R, R);
+        *tok = tab.perm + tl.y;
+        return sel;
+    } else {
+        return discover(idx, slot_rank, T, L, R, g, group, tok);
+    }
 }
 
 struct GrpShrinkArgs {
@@ -67,10 +106,11 @@ struct GrpShrinkArgs {
     const void *a[kMaxSlices];
     float *part;          // [S][n_kc][T][R]
     int32_t *n_kc_out;    // or null: receives n_kc (read by a separate expand call)
+    GrpTable tab;
 };
 
-// NRB: blocks of 16 rank rows per work-group (1..4).
-template <int NRB>
+// NRB: blocks of 16 rank rows per work-group (1..4); TAB: groups from the segment table.
+template <int NRB, bool TAB>
 __global__ __launch_bounds__(kThreads) void k_grp_shrink(GrpShrinkArgs a) {
     constexpr int RR = kG + 16 * NRB;          // staged rows: 32 x rows, then lora_a rows
     constexpr int LPS = RR / 8;                // wave load instructions (8 rows x 128 B each)
@@ -78,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void k_grp_shrink(GrpShrinkArgs a) {
     constexpr int kPart = kWaves * kG * (16 * NRB + 4) * 4;
     constexpr int kUnion = kStage > kPart ? kStage : kPart;
     __shared__ __attribute__((aligned(16))) char s_union[kUnion];
-    __shared__ Disc g;
+    __shared__ DiscT<TAB> g;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int kc = blockIdx.x % a.n_kc;
@@ -86,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_grp_shrink(GrpShrinkArgs a) {
     const int group = blockIdx.x / (a.n_kc * a.n_packs);
     if (blockIdx.x == 0 && tid == 0 && a.n_kc_out) *a.n_kc_out = a.n_kc;
     const int32_t *tokl;
-    const GroupSel gs = discover(a.idx, a.slot_rank, a.T, a.L, a.R, g, group, &tokl);
+    const GroupSel gs = group_of<TAB>(a.tab, a.idx, a.slot_rank, a.T, a.L, a.R, g, group, &tokl);
     const int s = gs.slot;
     if (s < 0) return;
     const int ntok = gs.ntok, pos0 = gs.pos0;
@@ -203,12 +243,13 @@ struct GrpExpandArgs {
     const int32_t *n_kc_in;  // or null: chunk count written by the shrink, at most n_kc
     Slices sl;
     int32_t chunk_start[kMaxSlices + 1];
+    GrpTable tab;
 };
 
-// RB: R / 16 (1..4).
 // RB: R / 16 (1..8).  lora_b rows are staged per wave in passes of 64 ranks
 // (128 bytes of each row); ranks past 64 need the buffer form (n_kc == 1).
-template <int RB>
+// TAB: groups from the segment table.
+template <int RB, bool TAB>
 __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     constexpr int R = 16 * RB;
     constexpr int BROW = 2 * R;                       // bytes of one lora_b row
@@ -224,14 +265,14 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     __shared__ __attribute__((aligned(16))) char s_union[kUnion];
     __shared__ __attribute__((aligned(16))) float4 s_red[H][Q];
     __shared__ __attribute__((aligned(16))) uint16_t s_buf[kG][R + 8];
-    __shared__ Disc g;
+    __shared__ DiscT<TAB> g;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int chunk = blockIdx.x % a.n_chunks;
     const int group = blockIdx.x / a.n_chunks;
     const int n_kc = a.n_kc_in ? max(1, min(*a.n_kc_in, a.n_kc)) : a.n_kc;
     const int32_t *tokl;
-    const GroupSel gs = discover(a.idx, a.slot_rank, a.T, a.L, R, g, group, &tokl);
+    const GroupSel gs = group_of<TAB>(a.tab, a.idx, a.slot_rank, a.T, a.L, R, g, group, &tokl);
     const int s = gs.slot;
     if (s < 0) return;
     const int ntok = gs.ntok, pos0 = gs.pos0;
@@ -384,15 +425,17 @@ struct GrpReduceArgs {
     const int32_t *slot_rank;
     const float *part;   // [S][n_kc][T][R]
     float *buf;          // [S][T][R]
+    GrpTable tab;
 };
 
 // buf[s][t][j] = sum over K chunks (in order) of the group's partials; ranks
 // j >= r are written as 0.  Rows of tokens without an adapter are not touched.
+template <bool TAB>
 __global__ __launch_bounds__(kThreads) void k_grp_reduce(GrpReduceArgs a) {
-    __shared__ Disc g;
+    __shared__ DiscT<TAB> g;
     const int group = blockIdx.x;
     const int32_t *tokl;
-    const GroupSel gs = discover(a.idx, a.slot_rank, a.T, a.L, a.R, g, group, &tokl);
+    const GroupSel gs = group_of<TAB>(a.tab, a.idx, a.slot_rank, a.T, a.L, a.R, g, group, &tokl);
     const int s = gs.slot;
     if (s < 0) return;
     const int ntok = gs.ntok, pos0 = gs.pos0, r = gs.rank;
@@ -414,6 +457,22 @@ __global__ __launch_bounds__(kThreads) void k_grp_reduce(GrpReduceArgs a) {
     }
 }
 
+GrpTable grp_table(const SegPtrs *seg) {
+    GrpTable t{};
+    if (seg) {
+        t.tiles = seg->tiles_dec;
+        t.perm = seg->perm;
+        t.header = seg->header;
+        t.max_tiles = seg->max_tiles_dec;
+    }
+    return t;
+}
+
+// Work-groups per token group dimension: every possible group.
+int32_t grp_groups(int32_t T, int32_t L, const SegPtrs *seg) {
+    return seg ? seg->max_tiles_dec : grp_max_groups(T, L);
+}
+
 }  // namespace
 
 int32_t grp_max_groups(int32_t T, int32_t L) {
@@ -425,8 +484,9 @@ int32_t grp_kchunks(int32_t K) { return (K + kKC - 1) / kKC; }
 hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, float *part, int32_t *n_kc_out,
-                             hipStream_t st) {
+                             const SegPtrs *seg, hipStream_t st) {
     GrpShrinkArgs a;
+    a.tab = grp_table(seg);
     a.x = static_cast<const uint16_t *>(x); a.ldx = ldx;
     a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
     a.idx = idx; a.slot_rank = slot_rank; a.part = part; a.n_kc_out = n_kc_out;
@@ -435,12 +495,21 @@ hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
     const int nrb = a.n_blocks < 4 ? a.n_blocks : 4;
     a.n_packs = (a.n_blocks + nrb - 1) / nrb;
     a.n_kc = grp_kchunks(K);
-    dim3 grid((unsigned)(grp_max_groups(T, L) * a.n_packs * a.n_kc));
-    switch (nrb) {
-        case 1: hipLaunchKernelGGL(k_grp_shrink<1>, grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(k_grp_shrink<2>, grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(k_grp_shrink<3>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_grp_shrink<4>, grid, dim3(kThreads), 0, st, a); break;
+    dim3 grid((unsigned)(grp_groups(T, L, seg) * a.n_packs * a.n_kc));
+    if (seg) {
+        switch (nrb) {
+            case 1: hipLaunchKernelGGL((k_grp_shrink<1, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_grp_shrink<2, true>), grid, dim3(kThreads), 0, st, a); break;
+            case 3: hipLaunchKernelGGL((k_grp_shrink<3, true>), grid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL((k_grp_shrink<4, true>), grid, dim3(kThreads), 0, st, a); break;
+        }
+    } else {
+        switch (nrb) {
+            case 1: hipLaunchKernelGGL((k_grp_shrink<1, false>), grid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_grp_shrink<2, false>), grid, dim3(kThreads), 0, st, a); break;
+            case 3: hipLaunchKernelGGL((k_grp_shrink<3, false>), grid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL((k_grp_shrink<4, false>), grid, dim3(kThreads), 0, st, a); break;
+        }
     }
     return hipGetLastError();
 }
@@ -448,8 +517,10 @@ hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
 hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *scale, const float *part,
-                             const float *buf, const int32_t *n_kc_in, hipStream_t st) {
+                             const float *buf, const int32_t *n_kc_in, const SegPtrs *seg,
+                             hipStream_t st) {
     GrpExpandArgs a;
+    a.tab = grp_table(seg);
     a.y = static_cast<uint16_t *>(y); a.ldy = ldy;
     a.T = T; a.S = S; a.L = L; a.R = R;
     a.idx = idx; a.slot_rank = slot_rank; a.scale = scale; a.part = part; a.buf = buf;
@@ -462,27 +533,34 @@ hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, cons
     }
     for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
     a.n_chunks = c;
-    dim3 grid((unsigned)(grp_max_groups(T, L) * c));
+    dim3 grid((unsigned)(grp_groups(T, L, seg) * c));
+#define AA_GRP_EXPAND(RB_)                                                             \
+    if (seg) hipLaunchKernelGGL((k_grp_expand<RB_, true>), grid, dim3(kThreads), 0, st, a); \
+    else hipLaunchKernelGGL((k_grp_expand<RB_, false>), grid, dim3(kThreads), 0, st, a)
     switch (R / 16) {
-        case 1: hipLaunchKernelGGL(k_grp_expand<1>, grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(k_grp_expand<2>, grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(k_grp_expand<3>, grid, dim3(kThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL(k_grp_expand<4>, grid, dim3(kThreads), 0, st, a); break;
-        case 5: hipLaunchKernelGGL(k_grp_expand<5>, grid, dim3(kThreads), 0, st, a); break;
-        case 6: hipLaunchKernelGGL(k_grp_expand<6>, grid, dim3(kThreads), 0, st, a); break;
-        case 7: hipLaunchKernelGGL(k_grp_expand<7>, grid, dim3(kThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(k_grp_expand<8>, grid, dim3(kThreads), 0, st, a); break;
+        case 1: AA_GRP_EXPAND(1); break;
+        case 2: AA_GRP_EXPAND(2); break;
+        case 3: AA_GRP_EXPAND(3); break;
+        case 4: AA_GRP_EXPAND(4); break;
+        case 5: AA_GRP_EXPAND(5); break;
+        case 6: AA_GRP_EXPAND(6); break;
+        case 7: AA_GRP_EXPAND(7); break;
+        default: AA_GRP_EXPAND(8); break;
     }
+#undef AA_GRP_EXPAND
     return hipGetLastError();
 }
 
 hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *part, int32_t n_kc,
-                             float *buf, hipStream_t st) {
+                             float *buf, const SegPtrs *seg, hipStream_t st) {
     GrpReduceArgs a;
+    a.tab = grp_table(seg);
     a.T = T; a.S = S; a.L = L; a.R = R; a.n_kc = n_kc;
     a.idx = idx; a.slot_rank = slot_rank; a.part = part; a.buf = buf;
-    hipLaunchKernelGGL(k_grp_reduce, dim3((unsigned)grp_max_groups(T, L)), dim3(kThreads), 0, st, a);
+    const dim3 grid((unsigned)grp_groups(T, L, seg));
+    if (seg) hipLaunchKernelGGL(k_grp_reduce<true>, grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL(k_grp_reduce<false>, grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

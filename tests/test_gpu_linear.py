@@ -166,12 +166,13 @@ def test_prefill_shape_reduced_both_paths(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
-def test_many_adapter_config(oracle_mod):
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, GRP])
+def test_many_adapter_config(oracle_mod, path):
     """1024 tokens, 128 slots with Zipf(1.1) popularity, ranks {8..128} padded to 128."""
     c = synth.config_many()
-    log("case many_adapter (auto path)")
+    log(f"case many_adapter path={path}")
     d = LinearOnDevice(c)
-    d.apply(aa.LORA_PATH_AUTO)
+    d.apply(path)
     y = d.y_host()
     ref = oracle_y(oracle_mod, c)
     err, rel = bounds.check_bf16_tolerance(y, ref)
@@ -235,11 +236,15 @@ def test_expand_from_given_buffer(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("cfg,path", [("decode", DEC), ("many", DEC), ("decode", GRP)])
+@pytest.mark.parametrize("cfg,path", [("decode", DEC), ("many", DEC), ("decode", GRP),
+                                      ("many64", GRP)])
 def test_partial_flag_split_calls(oracle_mod, cfg, path):
     """lora_shrink(PARTIAL) + lora_expand(PARTIAL): partial sums stay in the
-    workspace, the caller's buffer is never touched."""
-    c = synth.config_decode(T=200) if cfg == "decode" else synth.config_many(T=300)
+    workspace, the caller's buffer is never touched.  many64: 128 slots, so the
+    grouped kernels read their groups from the segment table."""
+    c = (synth.config_decode(T=200) if cfg == "decode" else
+         synth.config_many(T=300, R=64, K=2048, N=1024) if cfg == "many64" else
+         synth.config_many(T=300))
     log(f"case partial flag {cfg} path={path}")
     d = LinearOnDevice(c)
     buf = torch.full((c.S, c.T, c.R), 5.0, dtype=torch.float32, device="cuda")
@@ -332,12 +337,13 @@ def test_column_offset_and_wide_rows(oracle_mod):
         assert np.array_equal(got[:, off + c.Ntot:], wide[:, off + c.Ntot:])
 
 
-def test_segments_reused_across_layers(oracle_mod):
-    """Segments built once per batch and reused by several layer shapes."""
+@pytest.mark.parametrize("T,L", [(200, 6), (300, 100)])
+def test_segments_reused_across_layers(oracle_mod, T, L):
+    """Segments built once per batch and reused by several layer shapes (with
+    100 slots the grouped kernels read their groups from these segments)."""
     rng = np.random.default_rng(9)
-    T, L = 200, 6
     idx = rng.integers(-1, L, T).astype(np.int32)
-    ranks = np.array([16, 8, 16, 0, 16, 8], np.int32)
+    ranks = np.resize(np.array([16, 8, 16, 0, 16, 8], np.int32), L)
     ws = aa.alloc_workspace(T, 2048, 3, 16, L)
     idx_d, rank_d = dev(idx), dev(ranks)
     aa.lora_build_segments(idx_d, rank_d, L, 16, ws)
@@ -345,7 +351,7 @@ def test_segments_reused_across_layers(oracle_mod):
         c = synth.make_linear(f"layer{li}", T, K, N, 16, L, idx, ranks, [1.5] * L, "bf16",
                               seed=100 + li)
         d = LinearOnDevice(c, guard=False)
-        for path in (DEC, PRE):
+        for path in (DEC, PRE, GRP):
             d.reset_y()
             aa.lora_apply_packed(d.y, d.x, d.A, d.B, idx_d, rank_d, d.scale, ws, path=path,
                                  flags=aa.LORA_FLAG_SEGMENTS_READY)
@@ -397,6 +403,8 @@ def test_fused_rejects_unsupported(path):
     (43, 300, 576, [8, 16, 24], 48, 2),      # K not a multiple of 512, 3 rank blocks
     (44, 200, 2048, [264, 128], 128, 5),     # rank 128 (two rank passes), ragged column chunk
     (45, 150, 512, [80], 80, 3),             # rank 80: second pass of 16 ranks
+    (46, 1500, 1024, [512, 264], 128, 100),  # 100 slots, 1500 tokens: groups from the segment table
+    (47, 1100, 512, [128], 32, 8),           # past 1024 tokens with few slots: segment table
 ])
 def test_grouped_limits_bit_exact(oracle_mod, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
