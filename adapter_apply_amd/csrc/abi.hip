@@ -59,6 +59,12 @@ lora_status_t check_ptrs(const void *const *P, int32_t S) {
     return LORA_OK;
 }
 
+#define CHECK(expr)                          \
+    do {                                     \
+        lora_status_t _st = (expr);          \
+        if (_st != LORA_OK) return _st;      \
+    } while (0)
+
 // y rows are read and written 16 bytes (8 columns) at a time
 bool rows_of_8(const int64_t *N, int32_t S, int64_t ldy, int64_t y_col_offset) {
     if (ldy % 8 || y_col_offset % 8) return false;
@@ -89,6 +95,62 @@ bool can_group(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int
 // expand call (slot 5 of the segment header; the segment kernel uses 0..4).
 int32_t *grp_kc_slot(void *ws, const SegLayout &l) {
     return reinterpret_cast<int32_t *>(static_cast<char *>(ws) + l.header) + 5;
+}
+
+// K splits of the row-oriented MFMA shrink.  A batch with few 64-token tiles
+// for the CUs (many slots with a few tokens each) would stream each slot's
+// lora_a through one CU; splitting K gives about 1024 work-groups, each with
+// at least 8 stages of 64 columns, while the fp32 partials (written and read
+// once) stay under an eighth of the shrink's input bytes.  1: no split.
+int32_t pre_kspl(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L, int32_t max_tiles,
+                 int32_t cap_chunks) {
+    const int32_t sr = S * R, ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
+    const int32_t n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
+    const int32_t nst = (K + 63) / 64;
+    int32_t k = (1024 + max_tiles * n_cb - 1) / (max_tiles * n_cb);
+    if (k > nst / 8) k = nst / 8;
+    if (k > kMaxKcGrp) k = kMaxKcGrp;
+    if (k > cap_chunks) k = cap_chunks;
+    const double in_bytes = 2.0 * K * ((double)T + (double)(T < L ? T : L) * S * R);
+    while (k > 1 && 8.0 * k * T * S * R > in_bytes / 8) --k;
+    return k < 1 ? 1 : k;
+}
+
+// The row-oriented MFMA shrink into the token-ordered buffer, split over K
+// (partials, then the reduce kernel summing the splits in order) when
+// pre_kspl says so.
+lora_status_t pre_shrink_buf(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
+                             int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                             const int32_t *slot_rank, const SegPtrs &seg, const WsLayout &wl,
+                             void *ws, float *buf, hipStream_t st) {
+    int32_t kspl = pre_kspl(T, K, S, R, L, seg.max_tiles_pre, wl.n_kchunks);
+    if (kspl <= 1)
+        return launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st));
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+    CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, nullptr, st,
+                                     GroupMap(), part, &kspl)));
+    return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, kspl, buf, &seg, st));
+}
+
+// Grouped shrink that writes K-chunk partials for the reduce kernel; the chunk
+// count comes back in *n_kc.  With the segment table and ranks past the
+// partial-sum limit, the row-oriented MFMA shrink runs split over K: it keeps
+// loads in flight across K stages where the grouped shrink loads one
+// 512-column chunk per work-group.
+lora_status_t grp_shrink_part(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
+                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                              const int32_t *slot_rank, float *part, const WsLayout &wl,
+                              const SegPtrs *gseg, hipStream_t st, int32_t *n_kc) {
+    if (gseg && R > kGrpMaxPartialRank) {
+        int32_t kspl = pre_kspl(T, K, S, R, L, gseg->max_tiles_pre, wl.n_kchunks);
+        const lora_status_t e = launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank,
+                                                           *gseg, nullptr, st, GroupMap(), part, &kspl));
+        *n_kc = kspl;
+        return e;
+    }
+    *n_kc = grp_kchunks(K);
+    return launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
+                                      gseg, st));
 }
 
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
@@ -131,12 +193,6 @@ Slices make_slices(const void *const *A, const void *const *B, const int64_t *N,
     for (int s = S; s <= kMaxSlices; ++s) sl.off[s] = off;
     return sl;
 }
-
-#define CHECK(expr)                          \
-    do {                                     \
-        lora_status_t _st = (expr);          \
-        if (_st != LORA_OK) return _st;      \
-    } while (0)
 
 }  // namespace
 
@@ -231,18 +287,19 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
         if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
             CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
-        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part,
-                                         grp_kc_slot(ws, wl.seg), gseg, st)));
-        if (!writes_buf) return LORA_OK;
-        return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf,
-                                          gseg, st));
+        if (!writes_buf)
+            return launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part,
+                                              grp_kc_slot(ws, wl.seg), gseg, st));
+        int32_t n_kc = 0;
+        CHECK(grp_shrink_part(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
+        return launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, n_kc, buf, gseg, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (writes_buf && !(flags & LORA_FLAG_ACTIVE_ONLY))
         CHECK(launched(launch_fill_zero(buf, sizeof(float) * (size_t)S * T * R, st)));
     if (use_prefill)
-        return launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st));
+        return pre_shrink_buf(x, ldx, T, K, sl, S, L, R, idx, slot_rank, seg, wl, ws, buf, st);
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
     CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
                                      wl.n_kchunks, st)));
@@ -331,6 +388,12 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const bool group = !use_prefill && !fuse && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                        (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
     if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
+    // Auto, past the single-launch and discovering grouped kernels (more than
+    // 64 slots, or ranks past 64): the MFMA prefill kernels, the shrink split
+    // over K, while the persistent expand takes the rank.
+    if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && dtype == LORA_DT_BF16 &&
+        (R == 16 || R == 32 || R == 64 || R == 128) && rows_of_8(N, S, ldy, y_col_offset))
+        use_prefill = 1;
     if (T == 0) return LORA_OK;
     if (!y || !x || !idx || !scale) return LORA_E_NULL;
     CHECK(check_ptrs(A, S));
@@ -355,22 +418,23 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
         if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
             CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
-        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
-                                         gseg, st)));
         if (R > kGrpMaxPartialRank) {
             // large ranks: the K chunks are summed into the token-ordered buffer first
-            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, grp_kchunks(K), buf,
-                                             gseg, st)));
+            int32_t n_kc = 0;
+            CHECK(grp_shrink_part(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
+            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, n_kc, buf, gseg, st)));
             return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
                                               nullptr, buf, nullptr, gseg, st));
         }
+        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
+                                         gseg, st)));
         return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
                                           scale, part, nullptr, nullptr, gseg, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (use_prefill) {
-        CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, seg, buf, st)));
+        CHECK(pre_shrink_buf(x, ldx, T, K, sl, S, L, R, idx, slot_rank, seg, wl, ws, buf, st));
         return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
     }
     float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);

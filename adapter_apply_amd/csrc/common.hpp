@@ -266,10 +266,14 @@ struct GroupMap {
     int32_t ksum = 0;              // expand: buffer row of token t = sum_j coef[t*ksum+j] * buf[t*ksum+j]
 };
 
+// part (nullable): split K into *kspl_io chunks (fewer if K has fewer
+// 64-column stages; the count used is written back) and write fp32 partials
+// [S][kspl][T][R] by slot-sorted position instead of buf.
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
                              const SegPtrs &seg, float *buf, hipStream_t st,
-                             const GroupMap &gm = GroupMap());
+                             const GroupMap &gm = GroupMap(), float *part = nullptr,
+                             int32_t *kspl_io = nullptr);
 hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
                              const float *scale, const SegPtrs &seg, hipStream_t st,

@@ -255,7 +255,9 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     constexpr int BROW = 2 * R;                       // bytes of one lora_b row
     constexpr int SROW = BROW < 128 ? BROW : 128;     // staged bytes per row and pass
     constexpr int NPASS = (BROW + 127) / 128;
-    constexpr int BLD = kColsW * BROW / 1024;         // wave load instructions for its lora_b rows
+    constexpr int BLD = kColsW * BROW / 1024;         // wave load instructions for its lora_b rows (2 * RB)
+    constexpr bool kPow2Row = (RB & (RB - 1)) == 0;
+    constexpr int kLgRowUnits = RB == 1 ? 1 : RB == 2 ? 2 : RB == 4 ? 3 : 4;   // log2(2 * RB) when kPow2Row
     constexpr int Q = kG * R / 4;                     // float4 units of one K chunk's partials
     constexpr int H = kThreads / Q > 0 ? kThreads / Q : 1;
     constexpr int NQ = (Q + kThreads - 1) / kThreads; // units per thread
@@ -284,15 +286,24 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     const float sc = a.scale[s];
 
     // ---- loads, all issued before the first use ---------------------------
-    // lora_b rows of this wave's 64 columns: one contiguous block of 64 * BROW bytes.
+    // lora_b rows of this wave's 64 columns: the first U 16-byte units of each
+    // row, U = 2 * ceil(r / 16) rounded up to a power of two when the padded
+    // row is a power-of-two size, else the whole row.  A slot of rank 8 in a
+    // tensor padded to rank 128 reads 32 of its 256 bytes per row.  Load
+    // instruction i holds units 64 i .. 64 i + 63 of the wave's row block
+    // (row-major); instructions past U repeat the last one.
+    const int nks = (r + 15) >> 4;
+    const int lgu = kPow2Row ? min(32 - __clz(2 * nks - 1), kLgRowUnits) : 0;
+    const int U = kPow2Row ? 1 << lgu : 2 * RB;
     const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) +
                                                       (int64_t)s * Ns * R);
     uint4 bq[BLD];
 #pragma unroll
     for (int i = 0; i < BLD; ++i) {
-        const int byte = 1024 * i + 16 * lane;
-        const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
-        bq[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + (int64_t)nr * BROW + byte % BROW));
+        const int f = 64 * min(i, U - 1) + lane;          // BLD == 2 * RB >= U
+        const int rl = kPow2Row ? f >> lgu : f / U, u = kPow2Row ? f & (U - 1) : f % U;
+        const int nr = min(n_base + w * kColsW + rl, Ns - 1);
+        bq[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + (int64_t)nr * BROW + 16 * u));
     }
     // y: wave w owns tokens w, w + 8, w + 16, w + 24 of the group, 8 columns per lane.
     const int ycol = min(n_base + 8 * lane, Ns - 8);
@@ -356,7 +367,6 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     // The wave's lora_b rows pass through its own staging area 64 ranks at a
     // time; rank steps past the slot's rank are skipped.
     const int row = lane & 15, quad = lane >> 4;
-    const int nks = (r + 15) >> 4;
     char *stage = s_union + w * (kColsW * SROW);
     floatx4_t out[4][2];
 #pragma unroll
@@ -367,10 +377,11 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
         for (int i = 0; i < BLD; ++i) {
-            const int byte = 1024 * i + 16 * lane;            // within the wave's block of rows
-            const int off = byte % BROW - ps * 128;
-            if (off >= 0 && off < SROW)
-                *reinterpret_cast<uint4 *>(stage + (byte / BROW) * SROW + off) = bq[i];
+            const int f = 64 * i + lane;
+            const int rl = kPow2Row ? f >> lgu : f / U, u = kPow2Row ? f & (U - 1) : f % U;
+            const int off = 16 * u - ps * 128;
+            if (i < U && off >= 0 && off < SROW)
+                *reinterpret_cast<uint4 *>(stage + rl * SROW + off) = bq[i];
         }
 #pragma unroll
         for (int kq = 0; kq < SROW / 32; ++kq) {
@@ -444,11 +455,14 @@ __global__ __launch_bounds__(kThreads) void k_grp_reduce(GrpReduceArgs a) {
         const int sg = o / (ntok * R4), rem = o - sg * ntok * R4;
         const int t = rem / R4, j = 4 * (rem - t * R4);
         const float *p = a.part + ((int64_t)sg * a.n_kc * a.T + pos0 + t) * a.R + j;
+        // every chunk's load in flight at once (n_kc <= kMaxKcGrp), summed in order
+        float4 v[kMaxKcGrp];
+#pragma unroll
+        for (int kc = 0; kc < kMaxKcGrp; ++kc) v[kc] = ldg<float4>(p + (int64_t)min(kc, a.n_kc - 1) * a.T * a.R);
         float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int kc = 0; kc < a.n_kc; ++kc) {
-            const float4 v = ldg<float4>(p + (int64_t)kc * a.T * a.R);
-            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-        }
+#pragma unroll
+        for (int kc = 0; kc < kMaxKcGrp; ++kc)
+            if (kc < a.n_kc) { sum.x += v[kc].x; sum.y += v[kc].y; sum.z += v[kc].z; sum.w += v[kc].w; }
         sum.x = j < r ? sum.x : 0.f;
         sum.y = j + 1 < r ? sum.y : 0.f;
         sum.z = j + 2 < r ? sum.z : 0.f;

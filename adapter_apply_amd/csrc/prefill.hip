@@ -31,10 +31,12 @@ struct PreShrinkArgs {
     const uint16_t *x;
     int64_t ldx;
     int32_t T, K, S, L, R, n_cb;
+    int32_t kspl, st_per;      // K splits and 64-column stages per split
     const int32_t *slot_rank;
     SegPtrs seg;
     Slices sl;
     float *buf;
+    float *part;               // or null: fp32 [S][kspl][T][R] by slot-sorted position
     GroupMap gm;
 };
 
@@ -89,9 +91,10 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
     const int xcd = blockIdx.x % kXcds;
     const int local = blockIdx.x / kXcds;
     const int cb = local % a.n_cb;
+    const int ks = (local / a.n_cb) % a.kspl;     // K split: stages [sb, sb + nst)
     const int n_tiles = a.seg.header[3];
     const int per = (n_tiles + kXcds - 1) / kXcds;
-    const int lt = local / a.n_cb;
+    const int lt = local / (a.n_cb * a.kspl);
     if (lt >= per) return;
     const int tile = xcd * per + lt;
     if (tile >= n_tiles) return;
@@ -124,12 +127,13 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
                       (grp * a.R + (ok ? j : 0)) * (int64_t)a.K;
         }
     }
-    const int nst = (a.K + kShStageK - 1) / kShStageK;
+    const int sb = ks * a.st_per;
+    const int nst = min((a.K + kShStageK - 1) / kShStageK - sb, a.st_per);   // >= 1 (host)
     uint4 ring[kShNpf][NU];
     auto issue = [&](int slot, int st) {
 #pragma unroll
         for (int v = 0; v < NU; ++v) {
-            const int k = min(st * kShStageK + uoff[v], a.K - 8);
+            const int k = min((sb + st) * kShStageK + uoff[v], a.K - 8);
             ring[slot][v] = ldg<uint4>(rowp[v] + k);
         }
     };
@@ -138,7 +142,9 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
         for (int v = 0; v < NU; ++v) {
             const int q = v * kShThreads + tid;
             if (q < UNITS) {
-                const bool kin = st * kShStageK + uoff[v] < a.K;
+                // stages past this split's last (padding to a multiple of
+                // kShNpf) belong to the next split or lie past K: zeros
+                const bool kin = st < nst && (sb + st) * kShStageK + uoff[v] < a.K;
                 *reinterpret_cast<uint4 *>(buf + swz(q >> 3, q & 7, 8)) = kin ? ring[slot][v] : make_uint4(0, 0, 0, 0);
             }
         }
@@ -156,8 +162,8 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
             }
         }
     };
-    // Stages past the last one (padding to a multiple of kShNpf) stage zeros:
-    // their K columns are all >= K.  No branch around the loads.
+    // Stages past the split's last one (padding to a multiple of kShNpf) stage
+    // zeros.  No branch around the loads.
 #pragma unroll
     for (int u = 0; u < kShNpf; ++u) issue(u, min(u, nst - 1));
     for (int st0 = 0; st0 < nst; st0 += kShNpf) {
@@ -178,6 +184,15 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
     const int c = cb * 32 * NCB + 32 * cbk + l32;
     if (c >= SRf) return;
     const int sg = c / a.R, j = c - sg * a.R;
+    if (a.part) {
+        float *dst = a.part + (((int64_t)sg * a.kspl + ks) * a.T + p0) * a.R + j;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 32 * tb + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (t < ntok) dst[(int64_t)t * a.R] = j < r ? acc[i] : 0.0f;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int t = 32 * tb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -504,16 +519,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
 // loads through double-buffered LDS slots, so no dependent load sits on the
 // critical path.  Items are ordered column group first, so an XCD's
 // work-groups share a few column groups of lora_b in its L2 at any time.
-template <int NKS>
+// Ranks up to 128 (R = 16 * NKS); CW output columns per item (256 up to rank
+// 64, 128 above, so that two work-groups still fit a CU's LDS).  Of each
+// lora_b row only the first 2 * ceil(r / 16) units (rounded up to a power of
+// two) are read, r the item's slot rank: slots of low rank in a tensor padded
+// to a high rank do not pay for the padding.
+template <int NKS, int CW>
 __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a) {
     constexpr int R = 16 * NKS;
-    constexpr int U = R / 8;
-    constexpr int YU = kRowCols / 8;
+    constexpr int U = R / 8;                       // 16-byte units per lora_b row (power of two)
+    constexpr int LGU = U == 2 ? 1 : U == 4 ? 2 : U == 8 ? 3 : 4;
+    constexpr int YS = CW + 8;                     // bf16 elements per LDS y row
+    constexpr int YU = CW / 8;
     constexpr int NY = kRowTok * YU / kThreads;
-    constexpr int NBU = kRowCols * U / kThreads;
+    constexpr int NBU = CW * U / kThreads;
     constexpr int NFU = kRowTok * (R / 4) / kThreads;
-    __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * kRowYStride];
-    __shared__ __attribute__((aligned(16))) char s_b[kRowCols * U * 16];
+    constexpr int WC = CW / 4;                     // columns per wave
+    constexpr int NB = WC / 32;                    // 32-column MFMA blocks per wave
+    static_assert((U & (U - 1)) == 0 && U <= 16, "lora_b rows of 2, 4, 8 or 16 units");
+    __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * YS];
+    __shared__ __attribute__((aligned(16))) char s_b[CW * U * 16];
     __shared__ __attribute__((aligned(16))) char s_buf[kRowTok * U * 16];
     __shared__ int64_t s_yrow[2][kRowTok];
     __shared__ int64_t s_brow[2][kRowTok];
@@ -548,9 +573,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         c.sg = 0;
         while (c.sg + 1 < a.S && cg >= a.group_start[c.sg + 1]) ++c.sg;
         c.Ns = (int)a.sl.n[c.sg];
-        c.n_base = (cg - a.group_start[c.sg]) * kRowCols;
+        c.n_base = (cg - a.group_start[c.sg]) * CW;
         return c;
     };
+    // log2 of the lora_b units per row an item reads: 2 * ceil(r / 16) rounded up
+    auto lg_units = [&](int r) { return min(32 - __clz(2 * ((r + 15) >> 4) - 1), LGU); };
     // metadata loads of item k: its token (thread < 64), slot rank and scale
     struct Meta { int item; int rank; float sc; };
     auto meta_load = [&](const int4 &tl) {
@@ -568,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
             s_brow[slot][tid] = m.item / a.gm.buf_div;
         }
         if (tid == 0) {
-            s_rk[slot] = min(m.rank, a.R);
+            s_rk[slot] = max(1, min(m.rank, a.R));
             s_sc[slot] = m.sc;
         }
     };
@@ -584,12 +611,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
             const int q = i * kThreads + tid;
             yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + min(c.n_base + 8 * (q % YU), c.Ns - 8));
         }
+        // units q < CW * Ue of the block, Ue = 1 << lgu per row; the rest repeat the last
+        const int lgu = lg_units(s_rk[slot]);
+        const int last = (CW << lgu) - 1;
         const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[c.sg]) + grp * c.Ns * R);
 #pragma unroll
         for (int i = 0; i < NBU; ++i) {
-            const int q = i * kThreads + tid;
-            const int n = min(c.n_base + q / U, c.Ns - 1);
-            bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + q % U) * 16));
+            const int q = min(i * kThreads + tid, last);
+            const int n = min(c.n_base + (q >> lgu), c.Ns - 1);
+            bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + (q & ((1 << lgu) - 1))) * 16));
         }
 #pragma unroll
         for (int i = 0; i < NFU; ++i) {
@@ -612,18 +642,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     for (int k = 0; k < cnt; ++k) {
         const int slot = k & 1, nslot = slot ^ 1;
         const int ntok = tl0.z - tl0.y;
+        const int r = s_rk[slot];
+        const int nks = (r + 15) >> 4;
         // 1. item k into LDS; item k+1's metadata into its slot
         {
-            const int r = s_rk[slot];
 #pragma unroll
             for (int i = 0; i < NY; ++i) {
                 const int q = i * kThreads + tid;
-                *reinterpret_cast<uint4 *>(&s_y[(q / YU) * kRowYStride + 8 * (q % YU)]) = yv[i];
+                *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
             }
+            const int lgu = lg_units(r);
 #pragma unroll
             for (int i = 0; i < NBU; ++i) {
                 const int q = i * kThreads + tid;
-                *reinterpret_cast<uint4 *>(s_b + swz(q / U, q % U, U)) = bv[i];
+                if (q < (CW << lgu))
+                    *reinterpret_cast<uint4 *>(s_b + swz(q >> lgu, q & ((1 << lgu) - 1), U)) = bv[i];
             }
 #pragma unroll
             for (int i = 0; i < NFU; ++i) {
@@ -644,21 +677,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         data_load(tl1, c1, nslot);
         const Meta m2 = meta_load(tl2);
         const int4 tl3 = ldg<int4>(&a.seg.tiles_pre[tile_of(k + 3)]);
-        // 3. D[n][t] for item k, added into the y tile
+        // 3. D[n][t] for item k over its slot's rank steps, added into the y tile
         if (ck.ok) {
-            floatx16_t acc[2][2] = {{{}, {}}, {{}, {}}};
+            floatx16_t acc[NB][2];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = floatx16_t{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int u = 2 * ks + half;
-                uint4 bfr[2];
+                if (ks < nks) {
+                    const int u = 2 * ks + half;
+                    uint4 bfr[2];
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
+                    for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(64 * w + 32 * nb + l32, u, U));
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(WC * w + 32 * nb + l32, u, U));
 #pragma unroll
-                    for (int tb = 0; tb < 2; ++tb)
-                        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                        for (int tb = 0; tb < 2; ++tb)
+                            acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
@@ -666,10 +703,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
                 const int t = 32 * tb + l32;
                 if (t < ntok) {
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * kRowYStride + 64 * w + 32 * nb + 8 * g + 4 * half]);
+                            uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * YS + WC * w + 32 * nb + 8 * g + 4 * half]);
                             const uint2 y0 = *yp;
                             uint2 o;
                             o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + sc * acc[nb][tb][4 * g + 1]);
@@ -689,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
                 const int row = q / YU, col = ck.n_base + 8 * (q % YU);
                 if (row < ntok && col < ck.Ns)
                     stg_nt(ybase + s_yrow[slot][row] * a.ldy + col,
-                           *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]));
+                           *reinterpret_cast<const uint4 *>(&s_y[row * YS + 8 * (q % YU)]));
             }
         }
         __syncthreads();
@@ -703,7 +740,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
 
 hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *slot_rank,
-                             const SegPtrs &seg, float *buf, hipStream_t st, const GroupMap &gm) {
+                             const SegPtrs &seg, float *buf, hipStream_t st, const GroupMap &gm,
+                             float *part, int32_t *kspl_io) {
     PreShrinkArgs a;
     a.x = static_cast<const uint16_t *>(x); a.ldx = ldx; a.T = T; a.K = K; a.S = S; a.L = L;
     a.R = R; a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.buf = buf;
@@ -713,7 +751,16 @@ hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
     const int sr = S * R;
     const int ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
     a.n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
-    dim3 grid((unsigned)(kXcds * ((seg.max_tiles_pre + kXcds - 1) / kXcds) * a.n_cb));
+    // K splits: every split gets at least one stage; the count actually used
+    // goes back to the caller (the partials hold that many chunks)
+    const int nst = (K + kShStageK - 1) / kShStageK;
+    int kspl = part && kspl_io ? (*kspl_io < 1 ? 1 : *kspl_io) : 1;
+    if (kspl > nst) kspl = nst;
+    a.st_per = (nst + kspl - 1) / kspl;
+    a.kspl = (nst + a.st_per - 1) / a.st_per;
+    a.part = part;
+    if (kspl_io) *kspl_io = a.kspl;
+    dim3 grid((unsigned)(kXcds * ((seg.max_tiles_pre + kXcds - 1) / kXcds) * a.n_cb * a.kspl));
     switch (ncb) {
         case 1: hipLaunchKernelGGL(k_pre_shrink_rows<1>, grid, dim3(kShThreads), 0, st, a); break;
         case 2: hipLaunchKernelGGL(k_pre_shrink_rows<2>, grid, dim3(kShThreads), 0, st, a); break;
@@ -731,10 +778,14 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.R = R; a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
     a.gm = gm;
     if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
-    bool rows = R % 16 == 0 && R <= 64 && ldy % 8 == 0;
+    bool aligned = R % 16 == 0 && ldy % 8 == 0;
     for (int s = 0; s < S; ++s)
-        rows = rows && sl.n[s] % 8 == 0 && sl.off[s] % 8 == 0;
-    const int cols = rows ? kRowCols : kExpGroupCols;
+        aligned = aligned && sl.n[s] % 8 == 0 && sl.off[s] % 8 == 0;
+    // the persistent kernel: ranks 16, 32, 64, 128 (power-of-two rows), no
+    // per-item factor; the per-launch kernel: ranks up to 64; else the generic one
+    const bool pipe = aligned && (R == 16 || R == 32 || R == 64 || R == 128) && !a.gm.coef && !a.gm.ksum;
+    const bool rows = aligned && R <= 64;
+    const int cols = pipe ? (R <= 64 ? kRowCols : kRowCols / 2) : rows ? kRowCols : kExpGroupCols;
     int c = 0;
     for (int s = 0; s < S; ++s) {
         a.group_start[s] = c;
@@ -744,19 +795,19 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.n_cg = c;
     a.per_xcd = (c + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
-    if (!rows) {
-        hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
-        return hipGetLastError();
-    }
-    if (!a.gm.coef && !a.gm.ksum) {
+    if (pipe) {
         // two work-groups per CU, 32 CUs per XCD
         const dim3 pgrid(kXcds * 64);
         switch (R / 16) {
-            case 1: hipLaunchKernelGGL(k_pre_expand_pipe<1>, pgrid, dim3(kThreads), 0, st, a); break;
-            case 2: hipLaunchKernelGGL(k_pre_expand_pipe<2>, pgrid, dim3(kThreads), 0, st, a); break;
-            case 3: hipLaunchKernelGGL(k_pre_expand_pipe<3>, pgrid, dim3(kThreads), 0, st, a); break;
-            default: hipLaunchKernelGGL(k_pre_expand_pipe<4>, pgrid, dim3(kThreads), 0, st, a); break;
+            case 1: hipLaunchKernelGGL((k_pre_expand_pipe<1, kRowCols>), pgrid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_pre_expand_pipe<2, kRowCols>), pgrid, dim3(kThreads), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_pre_expand_pipe<4, kRowCols>), pgrid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL((k_pre_expand_pipe<8, kRowCols / 2>), pgrid, dim3(kThreads), 0, st, a); break;
         }
+        return hipGetLastError();
+    }
+    if (!rows) {
+        hipLaunchKernelGGL(k_pre_expand, grid, dim3(kThreads), 0, st, a);
         return hipGetLastError();
     }
     switch (R / 16) {

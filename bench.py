@@ -345,6 +345,10 @@ def main():
              and c.T <= 1024 and c.K % 1024 == 0 and rows8)
     grouped = (not prefill and not fused and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
                and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8)
+    # auto past those kernels: the prefill (MFMA) kernels, the shrink split over K
+    if (not prefill and not fused and not grouped and c.dtype == "bf16" and c.R in (16, 32, 64, 128)
+            and rows8):
+        prefill = True
     if args.path != "auto":
         prefill = args.path == "prefill"
         fused, grouped = args.path == "fused", args.path == "grouped"
@@ -365,6 +369,8 @@ def main():
 
     # grouped path above rank 64: shrink, reduce into the buffer, expand from it
     grouped_buf = grouped and c.R > 64
+    # past one-wave discovery the grouped kernels read the segment table
+    grouped_tab = grouped and not (c.L <= 64 and c.T <= 1024)
 
     def expand_only(d):
         aa.lora_expand(d["y"], d["buf"], d["B"], d["idx"], d["rank"], d["scale"], d["ws"],
@@ -437,10 +443,12 @@ def main():
     per_kernel = {}
     if fused:
         kernel_calls = [("fused", step)]      # the whole step is one kernel
-    elif grouped_buf:
-        kernel_calls = [("shrink+reduce", shrink_reduce), ("expand", expand_only)]
     elif grouped:
-        kernel_calls = [("shrink", shrink_only), ("expand", expand_only)]
+        kernel_calls = [("segments", segments_only)] if grouped_tab else []
+        if grouped_buf:
+            kernel_calls += [("shrink+reduce", shrink_reduce), ("expand", expand_only)]
+        else:
+            kernel_calls += [("shrink", shrink_only), ("expand", expand_only)]
     else:
         kernel_calls = [("segments", segments_only), ("shrink", shrink_only)]
         if not fold and not prefill:

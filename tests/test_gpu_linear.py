@@ -95,6 +95,7 @@ INTEGER_CASES = [
     (29, 1024, 1024, [16, 1032], 32, 1024),
     (30, 1024, 1024, [256, 64], 16, 40),     # 40 slots x 16 token chunks: work-group discovery
     (31, 300, 1024, [512, 64], 128, 9),      # rank 128
+    (32, 1500, 2048, [512, 264], 128, 100),  # 100 slots, rank 128: K-split shrink on the MFMA paths
 ]
 
 
@@ -405,6 +406,7 @@ def test_fused_rejects_unsupported(path):
     (45, 150, 512, [80], 80, 3),             # rank 80: second pass of 16 ranks
     (46, 1500, 1024, [512, 264], 128, 100),  # 100 slots, 1500 tokens: groups from the segment table
     (47, 1100, 512, [128], 32, 8),           # past 1024 tokens with few slots: segment table
+    (48, 700, 4096, [264], 96, 80),          # rank 96, 80 slots: K-split row shrink (8 splits)
 ])
 def test_grouped_limits_bit_exact(oracle_mod, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
