@@ -14,6 +14,10 @@ constexpr int kMaxRank = 512;
 constexpr int kMaxSlots = 1024;
 
 // Tile sizes (tokens of one slot handled together).
+// Segment build: threads of its work-groups; item counts past kSegSplitItems
+// use the two-pass build over ceil(items / kSegThreads) work-groups.
+constexpr int kSegThreads = 1024;
+constexpr int kSegSplitItems = 4096;
 constexpr int kDecTile = 32;   // decode (VALU) path: one token per lane half
 constexpr int kPreTile = 64;   // prefill (MFMA) path: two 32-row MFMA blocks
 
@@ -85,6 +89,7 @@ struct SegLayout {
     size_t perm;          // int32[T]
     size_t tiles_dec;     // int4[max_tiles_dec]: slot, begin, end, 0
     size_t tiles_pre;     // int4[max_tiles_pre]
+    size_t counts;        // int32[ceil(T / kSegThreads)][L + 1]: split build, per work-group
     size_t end;
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
@@ -122,6 +127,7 @@ inline SegLayout seg_layout(int32_t T, int32_t L, size_t base = 0) {
     l.max_tiles_pre = max_tiles(T, L, kPreTile);
     l.tiles_dec = o;  o = align256(o + 16 * (size_t)l.max_tiles_dec);
     l.tiles_pre = o;  o = align256(o + 16 * (size_t)l.max_tiles_pre);
+    l.counts = o;     o = align256(o + sizeof(int32_t) * (size_t)((T + kSegThreads - 1) / kSegThreads) * (L + 1));
     l.end = o;
     return l;
 }
@@ -167,6 +173,7 @@ struct SegPtrs {
     int32_t *perm;
     int4 *tiles_dec;
     int4 *tiles_pre;
+    int32_t *counts;
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
 };
@@ -179,6 +186,7 @@ inline SegPtrs seg_ptrs(void *ws, const SegLayout &l) {
     p.perm = reinterpret_cast<int32_t *>(b + l.perm);
     p.tiles_dec = reinterpret_cast<int4 *>(b + l.tiles_dec);
     p.tiles_pre = reinterpret_cast<int4 *>(b + l.tiles_pre);
+    p.counts = reinterpret_cast<int32_t *>(b + l.counts);
     p.max_tiles_dec = l.max_tiles_dec;
     p.max_tiles_pre = l.max_tiles_pre;
     return p;

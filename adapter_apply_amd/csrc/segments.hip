@@ -16,7 +16,6 @@ namespace aa {
 
 namespace {
 
-constexpr int kSegThreads = 1024;
 constexpr int kSegWaves = kSegThreads / kWave;
 
 // Exclusive scan of one int per thread over the 1024-thread block.
@@ -82,6 +81,31 @@ __device__ __forceinline__ void scatter_step(int s, int t, int nbits, int lane, 
 }
 
 constexpr int kRegSteps = 16;  // 64-item steps per wave held in registers (<= 16384 items)
+
+// Work tiles of both paths (key-major, item ranges of at most the tile size)
+// and the header.  Thread tid stands for key tid: cnt items from `start`.
+// Every thread of the block calls it.
+__device__ void emit_tiles(int cnt, int start, int n_active, int n_invalid, const SegPtrs &seg,
+                           int *wsum) {
+    const int tid = threadIdx.x;
+    int n_dec = 0, n_pre = 0;
+    const int td = (cnt + kDecTile - 1) / kDecTile;
+    const int tp = (cnt + kPreTile - 1) / kPreTile;
+    const int od = block_exclusive_scan(td, &n_dec, wsum);
+    const int op = block_exclusive_scan(tp, &n_pre, wsum);
+    for (int q = 0; q < td; ++q)
+        seg.tiles_dec[od + q] = make_int4(tid, start + q * kDecTile,
+                                          min(start + (q + 1) * kDecTile, start + cnt), 0);
+    for (int q = 0; q < tp; ++q)
+        seg.tiles_pre[op + q] = make_int4(tid, start + q * kPreTile,
+                                          min(start + (q + 1) * kPreTile, start + cnt), 0);
+    if (tid == 0) {
+        seg.header[0] = n_active;
+        seg.header[1] = n_invalid;
+        seg.header[2] = n_dec;
+        seg.header[3] = n_pre;
+    }
+}
 
 // Items are tokens (topk == nullptr: key = slot of the token) or (token, k)
 // pairs p = t * k + j (key = slot(t) * E + topk[p]); nkeys = L or L * E.
@@ -187,27 +211,122 @@ __global__ __launch_bounds__(kSegThreads) void k_segments(const int32_t *__restr
     }
     for (int i = n_active + tid; i < T; i += kSegThreads) seg.perm[i] = -1;
 
-    // Work tiles of both paths (key-major, item ranges of at most the tile size).
-    const int cnt = (tid < nkeys) ? tot : 0;
-    int n_dec = 0, n_pre = 0;
-    const int td = (cnt + kDecTile - 1) / kDecTile;
-    const int tp = (cnt + kPreTile - 1) / kPreTile;
-    const int od = block_exclusive_scan(td, &n_dec, wsum);
-    const int op = block_exclusive_scan(tp, &n_pre, wsum);
+    emit_tiles(tid < nkeys ? tot : 0, start, n_active, s_invalid, seg, wsum);
+}
+
+// ---- split build for large item counts: one 64-item step per wave --------
+// Pass 1: work-group b counts its 1024 items per key into counts[b][key] and
+// the slot ids past L into counts[b][nkeys].  Pass 2: every work-group sums
+// the counts of all work-groups per key (totals, and the part before its
+// own), scans the totals into key starts, recounts its own items per wave and
+// scatters them; the order is the single-pass stable order.  Work-group 0
+// also writes slot_start, the tail of perm, the tiles and the header.
+
+// Key of an item from its slot v and expert e (keyed: slot * E + expert),
+// -1 = carries no adapter; *inv += 1 for a slot id past L.
+__device__ __forceinline__ int filt_key(int v, int e, const int32_t *srank, bool keyed, int E, int L,
+                                        int *inv) {
+    if (v >= L) { ++*inv; return -1; }
+    if (v < 0 || srank[v] <= 0) return -1;
+    if (!keyed) return v;
+    return (e >= 0 && e < E) ? v * E + e : -1;
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_seg_count(const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ slot_rank,
+                                                           const int32_t *__restrict__ topk,
+                                                           int32_t k, int32_t E, int32_t n_items,
+                                                           int32_t L, int32_t R,
+                                                           int32_t *__restrict__ counts) {
+    extern __shared__ int32_t lds[];
+    const int nkeys = topk ? L * E : L;
+    int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
+    int32_t *srank = lds + kSegWaves * nkeys;  // [L]
+    __shared__ int32_t s_invalid;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
+    const int t = blockIdx.x * kSegThreads + tid;
+    const bool in = t < n_items;
+    const int v = in ? idx[topk ? t / k : t] : -1;
+    const int e = (in && topk) ? topk[t] : 0;
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
+    for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+    int inv = 0;
+    const int key = filt_key(v, e, srank, topk != nullptr, E, L, &inv);
+    count_step(key, nbits, lane, wcnt + w * nkeys);
+    if (inv) atomicAdd(&s_invalid, inv);
+    __syncthreads();
+    int32_t *mine = counts + (int64_t)blockIdx.x * (nkeys + 1);
+    for (int kk = tid; kk < nkeys; kk += kSegThreads) {
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < kSegWaves; ++q) c += wcnt[q * nkeys + kk];
+        mine[kk] = c;
+    }
+    if (tid == 0) mine[nkeys] = s_invalid;
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_seg_place(const int32_t *__restrict__ idx,
+                                                           const int32_t *__restrict__ slot_rank,
+                                                           const int32_t *__restrict__ topk,
+                                                           int32_t k, int32_t E, int32_t n_items,
+                                                           int32_t L, int32_t R,
+                                                           const int32_t *__restrict__ counts,
+                                                           int32_t n_wg, SegPtrs seg) {
+    extern __shared__ int32_t lds[];
+    const int nkeys = topk ? L * E : L;        // <= kSegThreads
+    int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
+    int32_t *srank = lds + kSegWaves * nkeys;  // [L]
+    __shared__ int32_t wsum[2 * kSegWaves + 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int b = blockIdx.x;
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
+    const int t = b * kSegThreads + tid;
+    const bool in = t < n_items;
+    const int v = in ? idx[topk ? t / k : t] : -1;
+    const int e = (in && topk) ? topk[t] : 0;
+    // Column col of the counts (a key, or nkeys: the invalid ids) summed over
+    // all work-groups, and over those before this one; 16 loads in flight.
+    auto col_sums = [&](int col, int &all, int &pre) {
+        all = 0; pre = 0;
+        for (int q0 = 0; q0 < n_wg; q0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) c[u] = counts[(int64_t)min(q0 + u, n_wg - 1) * (nkeys + 1) + col];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (q0 + u < n_wg) { all += c[u]; pre += q0 + u < b ? c[u] : 0; }
+        }
+    };
+    int tot = 0, before = 0, n_inv = 0, unused = 0;
+    if (tid < nkeys) col_sums(tid, tot, before);
+    if (tid == 0 && b == 0) col_sums(nkeys, n_inv, unused);
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
+    for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
+    __syncthreads();
+    int inv = 0;
+    const int key = filt_key(v, e, srank, topk != nullptr, E, L, &inv);
+    int32_t *mycnt = wcnt + w * nkeys;
+    count_step(key, nbits, lane, mycnt);
+    int n_active = 0;
+    const int start = block_exclusive_scan(tid < nkeys ? tot : 0, &n_active, wsum);   // has barriers
     if (tid < nkeys) {
-        for (int q = 0; q < td; ++q)
-            seg.tiles_dec[od + q] = make_int4(tid, start + q * kDecTile,
-                                              min(start + (q + 1) * kDecTile, start + cnt), 0);
-        for (int q = 0; q < tp; ++q)
-            seg.tiles_pre[op + q] = make_int4(tid, start + q * kPreTile,
-                                              min(start + (q + 1) * kPreTile, start + cnt), 0);
+        int run = start + before;
+        for (int q = 0; q < kSegWaves; ++q) {
+            const int c = wcnt[q * nkeys + tid];
+            wcnt[q * nkeys + tid] = run;
+            run += c;
+        }
+        if (b == 0) seg.slot_start[tid] = start;
     }
-    if (tid == 0) {
-        seg.header[0] = n_active;
-        seg.header[1] = s_invalid;
-        seg.header[2] = n_dec;
-        seg.header[3] = n_pre;
-    }
+    if (b == 0 && tid == 0) seg.slot_start[nkeys] = n_active;
+    __syncthreads();
+    scatter_step(key, t, nbits, lane, mycnt, seg.perm);
+    if (b != 0) return;   // uniform: work-group 0 writes the rest
+    for (int i = n_active + tid; i < n_items; i += kSegThreads) seg.perm[i] = -1;
+    emit_tiles(tid < nkeys ? tot : 0, start, n_active, n_inv, seg, wsum);
 }
 
 __global__ void k_fill_zero(uint4 *__restrict__ p, size_t n16, uint8_t *__restrict__ tail,
@@ -232,9 +351,21 @@ hipError_t launch_segments_keyed(const int32_t *idx, const int32_t *slot_rank,
     const int nkeys = topk ? L * E : L;
     const size_t lds = sizeof(int32_t) * ((size_t)kSegWaves * nkeys + L);
     if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_segments),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+        for (const void *f : {reinterpret_cast<const void *>(k_segments),
+                              reinterpret_cast<const void *>(k_seg_count),
+                              reinterpret_cast<const void *>(k_seg_place)}) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+    }
+    if (n_items > kSegSplitItems && seg.counts) {
+        // split build: one 64-item step per wave in each of n_wg work-groups
+        const int n_wg = (n_items + kSegThreads - 1) / kSegThreads;
+        hipLaunchKernelGGL(k_seg_count, dim3(n_wg), dim3(kSegThreads), lds, st, idx, slot_rank, topk,
+                           k, E, n_items, L, R, seg.counts);
+        hipLaunchKernelGGL(k_seg_place, dim3(n_wg), dim3(kSegThreads), lds, st, idx, slot_rank, topk,
+                           k, E, n_items, L, R, seg.counts, n_wg, seg);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, topk, k, E,
                        n_items, L, R, seg);
