@@ -621,11 +621,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
             const int n = min(c.n_base + (q >> lgu), c.Ns - 1);
             bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + (q & ((1 << lgu) - 1))) * 16));
         }
+        // buffer rows: entries j >= r are dropped, so their loads repeat the
+        // last needed float4 of the row (no extra cache lines)
+        const int jmax = 4 * ((s_rk[slot] + 3) / 4 - 1);
 #pragma unroll
         for (int i = 0; i < NFU; ++i) {
             const int q = i * kThreads + tid;
             const int t = q / (R / 4), j = 4 * (q % (R / 4));
-            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_rows + s_brow[slot][t]) * R + j);
+            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_rows + s_brow[slot][t]) * R + min(j, jmax));
         }
     };
 

@@ -44,13 +44,19 @@
  *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
  *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
  *            otherwise lora_apply_packed takes FUSED, else GROUPED (when also
- *            L <= 64 and R <= 64), where the shapes allow, and DECODE
+ *            L <= 64 and R <= 64), where the shapes allow, else PREFILL for
+ *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0
+ *            (batches of many slots or high ranks: the MFMA kernels, the
+ *            shrink split over K when its tiles are few), and DECODE
  *            elsewhere; lora_shrink / lora_expand take DECODE
  *            (so that a shrink and an expand called apart agree).
  *            DECODE forces the split (segments, VALU shrink, expand) decode
  *            path; PREFILL forces the MFMA path (bf16, R % 16 == 0 only);
  *            GROUPED forces the slot-grouped decode kernels (split-K MFMA
- *            shrink, MFMA expand; no segment build: bf16, R % 16 == 0,
+ *            shrink, MFMA expand; each work-group finds its token group from
+ *            idx while L <= 64 and T <= 1024, past that the call builds the
+ *            segments (or takes them with LORA_FLAG_SEGMENTS_READY) and the
+ *            kernels read the groups from them: bf16, R % 16 == 0,
  *            R <= 128, T <= 4096, and for the shrink K % 64 == 0, K <= 8192,
  *            for the expand N % 8 == 0, ldy % 8 == 0, y_col_offset % 8 == 0;
  *            LORA_FLAG_PARTIAL only for R <= 64);
@@ -154,8 +160,9 @@ lora_status_t lora_segment_layout(int32_t T, int32_t L, lora_segment_layout_t *o
  * each slot's run and the work tiles of both paths.  This is the token
  * grouping that segmented LoRA GEMMs run on ([SGL] header credit to S-LoRA
  * and Punica, "triton" backend; prepare_lora_batch builds the batch's slot
- * list once and shares it across layers).  One launch, bit-exact and
- * deterministic.
+ * list once and shares it across layers).  One launch up to 4096 tokens, two
+ * past that (per-work-group key counts, then the scatter); bit-exact and
+ * deterministic either way.
  */
 lora_status_t lora_build_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T,
                                   int32_t L, int32_t R, void *ws, size_t ws_bytes, void *stream);
