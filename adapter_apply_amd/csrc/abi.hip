@@ -379,18 +379,24 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    // Auto leaves wide outputs (an lm_head's vocabulary) to the tile kernels:
+    // the single-launch kernel recomputes a group's shrink for every
+    // 1024-column chunk, and the persistent expand streams wide rows faster
+    // than the grouped one.
+    const bool narrow = ntot <= kAutoMaxDecodeCols;
     const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
-                      (path == LORA_PATH_FUSED || path == LORA_PATH_AUTO);
+                      (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
     // Auto takes the grouped kernels while their in-kernel discovery is the
     // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
-    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank;
+    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank && narrow;
     const bool group = !use_prefill && !fuse && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                        (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
     if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
     // Auto, past the single-launch and discovering grouped kernels (more than
-    // 64 slots, or ranks past 64): the MFMA prefill kernels, the shrink split
-    // over K, while the persistent expand takes the rank.
+    // 64 slots, ranks past 64, or wide outputs): the MFMA prefill kernels, the
+    // shrink split over K when its tiles are few, while the persistent expand
+    // takes the rank.
     if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && dtype == LORA_DT_BF16 &&
         (R == 16 || R == 32 || R == 64 || R == 128) && rows_of_8(N, S, ldy, y_col_offset))
         use_prefill = 1;

@@ -30,6 +30,9 @@ constexpr int kFusedGroup = 8;         // tokens of one slot per work-group
 constexpr int kFusedCols = 1024;       // output columns per work-group
 constexpr int kFusedMaxRank = 32;
 constexpr int kFusedMaxTokens = 1024;  // idx staged in LDS
+// lora_apply_packed's auto path keeps the fused and grouped decode kernels to
+// outputs of at most this many columns per token (sum over slices)
+constexpr int64_t kAutoMaxDecodeCols = 16384;
 constexpr int kFusedXcds = 8;
 
 // Slot-grouped split decode (split-K MFMA shrink, then expand).

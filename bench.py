@@ -34,7 +34,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe"])
+    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe", "logits"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode", "prefill"],
                    help="force a decode path (development runs; the headline uses auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -46,7 +46,8 @@ def parse():
     return p.parse_args()
 
 
-DEFAULTS = {"decode": (4000, 400), "prefill": (200, 20), "many": (1000, 100), "moe": (200, 20)}
+DEFAULTS = {"decode": (4000, 400), "prefill": (200, 20), "many": (1000, 100), "moe": (200, 20),
+            "logits": (1000, 100)}
 
 
 def make_case(name):
@@ -55,6 +56,8 @@ def make_case(name):
         return synth.config_decode()
     if name == "prefill":
         return synth.config_prefill()
+    if name == "logits":
+        return synth.config_logits()
     return synth.config_many()
 
 
@@ -341,10 +344,12 @@ def main():
     prefill = (c.dtype == "bf16" and c.R % 16 == 0 and c.T >= 512
                and c.T // min(c.T, c.L) >= 64)
     rows8 = all(n % 8 == 0 for n in c.N)
+    narrow = sum(c.N) <= 16384
     fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
-             and c.T <= 1024 and c.K % 1024 == 0 and rows8)
+             and c.T <= 1024 and c.K % 1024 == 0 and rows8 and narrow)
     grouped = (not prefill and not fused and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
-               and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8)
+               and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8
+               and narrow)
     # auto past those kernels: the prefill (MFMA) kernels, the shrink split over K
     if (not prefill and not fused and not grouped and c.dtype == "bf16" and c.R in (16, 32, 64, 128)
             and rows8):
@@ -495,6 +500,7 @@ def main():
         "decode": "decode QKV: 256 tokens, hidden 4096, slices 4096/1024/1024, rank 16, 8 slots, 10% no-adapter",
         "prefill": "prefill gate_up: 8192 tokens in 32 sequences, 16 slots, hidden 4096, slices 2x14336, rank 64",
         "many": "many-adapter decode: 1024 tokens, 128 slots Zipf(1.1), ranks 8..128 padded to 128, 8192x8192",
+        "logits": "lm_head LoRA at decode: 256 tokens, hidden 4096, vocab 128256, rank 16, 8 slots, 10% no-adapter",
     }[args.workload]
     out = {
         "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU",

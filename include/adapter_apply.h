@@ -44,7 +44,8 @@
  *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
  *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
  *            otherwise lora_apply_packed takes FUSED, else GROUPED (when also
- *            L <= 64 and R <= 64), where the shapes allow, else PREFILL for
+ *            L <= 64 and R <= 64), where the shapes allow and the slices sum
+ *            to at most 16384 columns, else PREFILL for
  *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0
  *            (batches of many slots or high ranks: the MFMA kernels, the
  *            shrink split over K when its tiles are few), and DECODE

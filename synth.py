@@ -128,6 +128,18 @@ def config_decode(seed=1002, T=256):
                        [16] * 8, [2.0] * 8, "bf16", seed + 1)
 
 
+def config_logits(seed=1006, T=256, vocab=128256):
+    """lm_head LoRA at decode: 256 tokens, hidden 4096, one vocab-wide slice
+    (128256 columns by default; the pages accept 32000..257024), rank 16,
+    8 slots, 10% idx=-1 else uniform over slots, bf16, A,B~N(0,0.02), scale 1
+    (the logits call passes 1.0)."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, 8, size=T).astype(np.int32)
+    idx[rng.random(T) < 0.1] = -1
+    return make_linear("logits", T, 4096, [vocab], 16, 8, idx, [16] * 8, [1.0] * 8, "bf16",
+                       seed + 1)
+
+
 def prefill_lengths(rng, n_seq=32, total=8192, lo=64, hi=512):
     """Sequence lengths drawn uniform on [lo, hi] and then walked to the
     requested total one seeded step of +-1 at a time, staying in [lo, hi]."""
@@ -176,6 +188,7 @@ LINEAR_CONFIGS = {
     "decode": config_decode,
     "prefill": config_prefill,
     "many": config_many,
+    "logits": config_logits,
 }
 
 

@@ -96,6 +96,7 @@ INTEGER_CASES = [
     (30, 1024, 1024, [256, 64], 16, 40),     # 40 slots x 16 token chunks: work-group discovery
     (31, 300, 1024, [512, 64], 128, 9),      # rank 128
     (32, 1500, 2048, [512, 264], 128, 100),  # 100 slots, rank 128: K-split shrink on the MFMA paths
+    (33, 64, 1024, [32768], 16, 4),          # one vocabulary-wide slice (lm_head LoRA)
 ]
 
 
@@ -164,6 +165,37 @@ def test_prefill_shape_reduced_both_paths(oracle_mod, path):
     y = d.y_host()
     ref = oracle_y(oracle_mod, c)
     bounds.check_bf16_tolerance(y, ref)
+    assert canaries_intact(d.yfull)
+
+
+def test_logits_vocab_32000_every_path(oracle_mod):
+    """lm_head LoRA: 256 decode tokens, hidden 4096, vocabulary 32000 (the
+    smallest the logits layer accepts), rank 16, 8 slots; every path against
+    one oracle result."""
+    c = synth.config_logits(vocab=32000)
+    ref = oracle_y(oracle_mod, c)
+    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP):
+        log(f"case logits vocab=32000 path={path}")
+        d = LinearOnDevice(c)
+        d.apply(path)
+        y = d.y_host()
+        err, rel = bounds.check_bf16_tolerance(y, ref)
+        log(f"  max abs err {err:.3e} rel {rel:.3e}")
+        assert_passthrough(c, y)
+        assert canaries_intact(d.yfull)
+
+
+def test_logits_vocab_128256_auto(oracle_mod):
+    """The lm_head workload at its measured size (vocabulary 128256) on the
+    auto path, which takes the tile kernels for outputs this wide."""
+    c = synth.config_logits()
+    log("case logits vocab=128256 auto")
+    d = LinearOnDevice(c)
+    d.apply(aa.LORA_PATH_AUTO)
+    y = d.y_host()
+    err, rel = bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    log(f"  max abs err {err:.3e} rel {rel:.3e}")
+    assert_passthrough(c, y)
     assert canaries_intact(d.yfull)
 
 
@@ -264,7 +296,7 @@ def test_partial_flag_split_calls(oracle_mod, cfg, path):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("seed,T,L", [(0, 1, 1), (1, 256, 8), (2, 8192, 16), (3, 1000, 128),
-                                      (4, 4097, 1024), (5, 70, 3)])
+                                      (4, 4097, 1024), (5, 70, 3), (6, 20000, 5)])
 def test_segments_bit_exact(oracle_mod, seed, T, L):
     rng = np.random.default_rng(seed)
     idx = rng.integers(-2, L + 2, size=T).astype(np.int32)

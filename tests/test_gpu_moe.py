@@ -190,7 +190,10 @@ def test_moe_per_expert_layout(oracle_mod):
 
 
 @pytest.mark.parametrize("seed,T,k,E,L,bm", [(0, 7, 2, 4, 3, 4), (1, 2048, 8, 64, 8, 16),
-                                              (2, 1, 1, 1, 1, 1), (3, 333, 3, 5, 6, 8)])
+                                              (2, 1, 1, 1, 1, 1), (3, 333, 3, 5, 6, 8),
+                                              # 1024 (slot, expert) keys over 5 work-groups of the
+                                              # two-pass segment build
+                                              (4, 700, 7, 128, 8, 32)])
 def test_moe_align_bit_exact(oracle_mod, seed, T, k, E, L, bm):
     rng = np.random.default_rng(seed)
     ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)     # includes out-of-range experts
