@@ -134,6 +134,32 @@ def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L
         assert np.array_equal(y, ref), np.max(np.abs(y - ref))
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_w13_single_slice_and_interleaved(oracle_mod, shared):
+    """[vLLM] FusedMoE3DWithLoRA: one w13 slice, lora_b [L][E][2I][R] under
+    one lora_a, its gate and up rows either concatenated or interleaved (the
+    order its slicing keeps for GPT-OSS).  Interleaving permutes lora_b's rows
+    and the output columns alike, so the interleaved result is the
+    concatenated one with its columns interleaved, bit for bit."""
+    d = integer_moe(5, 90, 4, 8, 128, 48, 16, 3, shared)
+    E = d["E"]
+    A = [d["A13"][0]]
+    Bcat = [np.concatenate(d["B13"], axis=2)]
+    I = d["B13"][0].shape[2]
+    perm = np.empty(2 * I, np.int64)
+    perm[0::2] = np.arange(I)
+    perm[1::2] = I + np.arange(I)          # interleaved column c = concatenated column perm[c]
+    Bint = [np.ascontiguousarray(Bcat[0][:, :, perm, :])]
+    log(f"case moe w13 single slice shared={shared}")
+    y_cat = run_moe(W13, d["g0"], d["x"], A, Bcat, d["ids"], None, d["idx"], d["rank"], d["scale"], E)
+    ref = oracle_mod.moe_lora_apply(0, d["g0"], d["x"], A, Bcat, d["ids"], None, d["idx"], d["rank"],
+                                    d["scale"], E)
+    assert np.array_equal(y_cat, ref), np.max(np.abs(y_cat - ref))
+    y_int = run_moe(W13, np.ascontiguousarray(d["g0"][:, perm]), d["x"], A, Bint, d["ids"], None,
+                    d["idx"], d["rank"], d["scale"], E)
+    assert np.array_equal(y_int, y_cat[:, perm])
+
+
 def sample_tokens(T, n, seed=0):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n)])).astype(np.int64)
