@@ -210,6 +210,25 @@ hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t
 hipError_t launch_segments_keyed(const int32_t *idx, const int32_t *slot_rank,
                                  const int32_t *topk, int32_t k, int32_t E, int32_t n_items,
                                  int32_t L, int32_t R, const SegPtrs &seg, hipStream_t st);
+// One build of the two-pass (split) segment form: items are tokens (topk
+// null) or (token, k) pairs keyed by slot * E + expert, counted by n_wg
+// work-groups of kSegThreads items into `counts`, placed into `seg`.
+struct SegJob {
+    const int32_t *topk;
+    int32_t k, E, n_items, n_wg;
+    int32_t *counts;
+    SegPtrs seg;
+};
+struct SegJobs {
+    const int32_t *idx;
+    const int32_t *slot_rank;
+    int32_t L, R, n_jobs;
+    SegJob job[2];
+};
+SegJob seg_job_of(const int32_t *topk, int32_t k, int32_t E, int32_t n_items, const SegPtrs &seg);
+// Up to two builds over the same idx in one pair of launches (count, place).
+hipError_t launch_segments_split(const int32_t *idx, const int32_t *slot_rank, int32_t L, int32_t R,
+                                 const SegJob *jobs, int n_jobs, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
 // Writes the K-chunk partial sums; launch_dec_reduce (or the expand) adds them.

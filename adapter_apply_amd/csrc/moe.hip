@@ -113,10 +113,16 @@ lora_status_t moe_check_meta(int32_t T, int32_t k, int32_t E, int32_t L, int32_t
 lora_status_t moe_segments(const int32_t *topk_ids, const int32_t *idx, const int32_t *slot_rank,
                            int32_t T, int32_t k, int32_t E, int32_t L, int32_t R,
                            const MoeWsLayout &ml, void *ws, hipStream_t st) {
-    CHECK(launched(launch_segments_keyed(idx, slot_rank, nullptr, 1, 1, T, L, R,
-                                         seg_ptrs(ws, ml.tok), st)));
-    return launched(launch_segments_keyed(idx, slot_rank, topk_ids, k, E, T * k, L, R,
-                                          seg_ptrs(ws, ml.pair), st));
+    if (T == 0) {
+        CHECK(launched(launch_segments_keyed(idx, slot_rank, nullptr, 1, 1, T, L, R,
+                                             seg_ptrs(ws, ml.tok), st)));
+        return launched(launch_segments_keyed(idx, slot_rank, topk_ids, k, E, T * k, L, R,
+                                              seg_ptrs(ws, ml.pair), st));
+    }
+    // the token and the (token, k) pair segments in one pair of launches
+    const SegJob jobs[2] = {seg_job_of(nullptr, 1, 1, T, seg_ptrs(ws, ml.tok)),
+                            seg_job_of(topk_ids, k, E, T * k, seg_ptrs(ws, ml.pair))};
+    return launched(launch_segments_split(idx, slot_rank, L, R, jobs, 2, st));
 }
 
 }  // namespace

@@ -232,33 +232,38 @@ __device__ __forceinline__ int filt_key(int v, int e, const int32_t *srank, bool
     return (e >= 0 && e < E) ? v * E + e : -1;
 }
 
-__global__ __launch_bounds__(kSegThreads) void k_seg_count(const int32_t *__restrict__ idx,
-                                                           const int32_t *__restrict__ slot_rank,
-                                                           const int32_t *__restrict__ topk,
-                                                           int32_t k, int32_t E, int32_t n_items,
-                                                           int32_t L, int32_t R,
-                                                           int32_t *__restrict__ counts) {
+// Work-group blockIdx.x of a split launch: its job and its index in that job.
+__device__ __forceinline__ SegJob seg_job(const SegJobs &a, int *b) {
+    const bool second = a.n_jobs > 1 && (int)blockIdx.x >= a.job[0].n_wg;
+    *b = (int)blockIdx.x - (second ? a.job[0].n_wg : 0);
+    return second ? a.job[1] : a.job[0];
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_seg_count(SegJobs a) {
     extern __shared__ int32_t lds[];
-    const int nkeys = topk ? L * E : L;
+    int b = 0;
+    const SegJob jb = seg_job(a, &b);
+    const int L = a.L;
+    const int nkeys = jb.topk ? L * jb.E : L;
     int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
     int32_t *srank = lds + kSegWaves * nkeys;  // [L]
     __shared__ int32_t s_invalid;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
-    const int t = blockIdx.x * kSegThreads + tid;
-    const bool in = t < n_items;
-    const int v = in ? idx[topk ? t / k : t] : -1;
-    const int e = (in && topk) ? topk[t] : 0;
-    for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
+    const int t = b * kSegThreads + tid;
+    const bool in = t < jb.n_items;
+    const int v = in ? a.idx[jb.topk ? t / jb.k : t] : -1;
+    const int e = (in && jb.topk) ? jb.topk[t] : 0;
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = a.slot_rank ? a.slot_rank[i] : a.R;
     for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
     if (tid == 0) s_invalid = 0;
     __syncthreads();
     int inv = 0;
-    const int key = filt_key(v, e, srank, topk != nullptr, E, L, &inv);
+    const int key = filt_key(v, e, srank, jb.topk != nullptr, jb.E, L, &inv);
     count_step(key, nbits, lane, wcnt + w * nkeys);
     if (inv) atomicAdd(&s_invalid, inv);
     __syncthreads();
-    int32_t *mine = counts + (int64_t)blockIdx.x * (nkeys + 1);
+    int32_t *mine = jb.counts + (int64_t)b * (nkeys + 1);
     for (int kk = tid; kk < nkeys; kk += kSegThreads) {
         int c = 0;
 #pragma unroll
@@ -268,25 +273,23 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_count(const int32_t *__rest
     if (tid == 0) mine[nkeys] = s_invalid;
 }
 
-__global__ __launch_bounds__(kSegThreads) void k_seg_place(const int32_t *__restrict__ idx,
-                                                           const int32_t *__restrict__ slot_rank,
-                                                           const int32_t *__restrict__ topk,
-                                                           int32_t k, int32_t E, int32_t n_items,
-                                                           int32_t L, int32_t R,
-                                                           const int32_t *__restrict__ counts,
-                                                           int32_t n_wg, SegPtrs seg) {
+__global__ __launch_bounds__(kSegThreads) void k_seg_place(SegJobs a) {
     extern __shared__ int32_t lds[];
-    const int nkeys = topk ? L * E : L;        // <= kSegThreads
+    int b = 0;
+    const SegJob jb = seg_job(a, &b);
+    const int L = a.L;
+    const int nkeys = jb.topk ? L * jb.E : L;  // <= kSegThreads
+    const int n_wg = jb.n_wg;
+    const SegPtrs &seg = jb.seg;
     int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
     int32_t *srank = lds + kSegWaves * nkeys;  // [L]
     __shared__ int32_t wsum[2 * kSegWaves + 1];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int b = blockIdx.x;
     const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
     const int t = b * kSegThreads + tid;
-    const bool in = t < n_items;
-    const int v = in ? idx[topk ? t / k : t] : -1;
-    const int e = (in && topk) ? topk[t] : 0;
+    const bool in = t < jb.n_items;
+    const int v = in ? a.idx[jb.topk ? t / jb.k : t] : -1;
+    const int e = (in && jb.topk) ? jb.topk[t] : 0;
     // Column col of the counts (a key, or nkeys: the invalid ids) summed over
     // all work-groups, and over those before this one; 16 loads in flight.
     auto col_sums = [&](int col, int &all, int &pre) {
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_place(const int32_t *__rest
         for (int q0 = 0; q0 < n_wg; q0 += 16) {
             int c[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) c[u] = counts[(int64_t)min(q0 + u, n_wg - 1) * (nkeys + 1) + col];
+            for (int u = 0; u < 16; ++u) c[u] = jb.counts[(int64_t)min(q0 + u, n_wg - 1) * (nkeys + 1) + col];
 #pragma unroll
             for (int u = 0; u < 16; ++u)
                 if (q0 + u < n_wg) { all += c[u]; pre += q0 + u < b ? c[u] : 0; }
@@ -303,11 +306,11 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_place(const int32_t *__rest
     int tot = 0, before = 0, n_inv = 0, unused = 0;
     if (tid < nkeys) col_sums(tid, tot, before);
     if (tid == 0 && b == 0) col_sums(nkeys, n_inv, unused);
-    for (int i = tid; i < L; i += kSegThreads) srank[i] = slot_rank ? slot_rank[i] : R;
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = a.slot_rank ? a.slot_rank[i] : a.R;
     for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
     __syncthreads();
     int inv = 0;
-    const int key = filt_key(v, e, srank, topk != nullptr, E, L, &inv);
+    const int key = filt_key(v, e, srank, jb.topk != nullptr, jb.E, L, &inv);
     int32_t *mycnt = wcnt + w * nkeys;
     count_step(key, nbits, lane, mycnt);
     int n_active = 0;
@@ -324,8 +327,8 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_place(const int32_t *__rest
     if (b == 0 && tid == 0) seg.slot_start[nkeys] = n_active;
     __syncthreads();
     scatter_step(key, t, nbits, lane, mycnt, seg.perm);
-    if (b != 0) return;   // uniform: work-group 0 writes the rest
-    for (int i = n_active + tid; i < n_items; i += kSegThreads) seg.perm[i] = -1;
+    if (b != 0) return;   // uniform: work-group 0 of each job writes the rest
+    for (int i = n_active + tid; i < jb.n_items; i += kSegThreads) seg.perm[i] = -1;
     emit_tiles(tid < nkeys ? tot : 0, start, n_active, n_inv, seg, wsum);
 }
 
@@ -351,24 +354,53 @@ hipError_t launch_segments_keyed(const int32_t *idx, const int32_t *slot_rank,
     const int nkeys = topk ? L * E : L;
     const size_t lds = sizeof(int32_t) * ((size_t)kSegWaves * nkeys + L);
     if (lds > 48 * 1024) {
-        for (const void *f : {reinterpret_cast<const void *>(k_segments),
-                              reinterpret_cast<const void *>(k_seg_count),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_segments),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (n_items > kSegSplitItems && seg.counts) {
+        const SegJob job = seg_job_of(topk, k, E, n_items, seg);
+        return launch_segments_split(idx, slot_rank, L, R, &job, 1, st);
+    }
+    hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, topk, k, E,
+                       n_items, L, R, seg);
+    return hipGetLastError();
+}
+
+SegJob seg_job_of(const int32_t *topk, int32_t k, int32_t E, int32_t n_items, const SegPtrs &seg) {
+    SegJob j{};
+    j.topk = topk;
+    j.k = k;
+    j.E = E;
+    j.n_items = n_items;
+    j.n_wg = n_items > 0 ? (n_items + kSegThreads - 1) / kSegThreads : 1;
+    j.counts = seg.counts;
+    j.seg = seg;
+    return j;
+}
+
+hipError_t launch_segments_split(const int32_t *idx, const int32_t *slot_rank, int32_t L, int32_t R,
+                                 const SegJob *jobs, int n_jobs, hipStream_t st) {
+    SegJobs a{};
+    a.idx = idx; a.slot_rank = slot_rank; a.L = L; a.R = R; a.n_jobs = n_jobs;
+    size_t lds = 0;
+    int n_wg = 0;
+    for (int j = 0; j < n_jobs; ++j) {
+        a.job[j] = jobs[j];
+        const int nkeys = jobs[j].topk ? L * jobs[j].E : L;
+        const size_t l = sizeof(int32_t) * ((size_t)kSegWaves * nkeys + L);
+        lds = l > lds ? l : lds;
+        n_wg += jobs[j].n_wg;
+    }
+    if (lds > 48 * 1024) {
+        for (const void *f : {reinterpret_cast<const void *>(k_seg_count),
                               reinterpret_cast<const void *>(k_seg_place)}) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
     }
-    if (n_items > kSegSplitItems && seg.counts) {
-        // split build: one 64-item step per wave in each of n_wg work-groups
-        const int n_wg = (n_items + kSegThreads - 1) / kSegThreads;
-        hipLaunchKernelGGL(k_seg_count, dim3(n_wg), dim3(kSegThreads), lds, st, idx, slot_rank, topk,
-                           k, E, n_items, L, R, seg.counts);
-        hipLaunchKernelGGL(k_seg_place, dim3(n_wg), dim3(kSegThreads), lds, st, idx, slot_rank, topk,
-                           k, E, n_items, L, R, seg.counts, n_wg, seg);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(k_segments, dim3(1), dim3(kSegThreads), lds, st, idx, slot_rank, topk, k, E,
-                       n_items, L, R, seg);
+    hipLaunchKernelGGL(k_seg_count, dim3(n_wg), dim3(kSegThreads), lds, st, a);
+    hipLaunchKernelGGL(k_seg_place, dim3(n_wg), dim3(kSegThreads), lds, st, a);
     return hipGetLastError();
 }
 
