@@ -440,6 +440,19 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
     if (use_prefill) {
+        // One lora_a for every slice (the same pointer in each, as a merged
+        // layer holds when its checkpoint has a single lora_a: [vLLM]
+        // MergedQKVParallelLinearWithLoRA duplicates it per slice): the
+        // shrink runs once and every slice's expand reads its buffer.
+        bool shared_a = S > 1;
+        for (int s = 1; s < S && shared_a; ++s) shared_a = A[s] == A[0];
+        if (shared_a) {
+            const Slices sl1 = make_slices(A, B, N, 1, y_col_offset);
+            CHECK(pre_shrink_buf(x, ldx, T, K, sl1, 1, L, R, idx, slot_rank, seg, wl, ws, buf, st));
+            GroupMap gm;
+            gm.buf_sstride = 0;
+            return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st, gm));
+        }
         CHECK(pre_shrink_buf(x, ldx, T, K, sl, S, L, R, idx, slot_rank, seg, wl, ws, buf, st));
         return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
     }

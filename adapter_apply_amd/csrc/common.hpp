@@ -292,6 +292,8 @@ struct GroupMap {
     int32_t buf_div = 1;
     int32_t y_div = 1;
     int32_t buf_rows = 0;          // rows of the [S][buf_rows][R] buffer
+    int32_t buf_sstride = -1;      // expand: rows between the buffer's slices (-1: buf_rows,
+                                   // 0: every slice reads slice 0, the shrink of a shared lora_a)
     const float *coef = nullptr;   // per-item factor (routing weight), or null
     int32_t ksum = 0;              // expand: buffer row of token t = sum_j coef[t*ksum+j] * buf[t*ksum+j]
 };

@@ -230,13 +230,13 @@ __device__ __forceinline__ void buf_vals(const PreExpandArgs &a, int sg, int ite
         for (int j = 0; j < a.gm.ksum; ++j) {
             const int64_t br = (int64_t)item * a.gm.ksum + j;
             const float w = a.gm.coef ? a.gm.coef[br] : 1.0f;
-            const float *bp = a.buf + ((int64_t)sg * a.gm.buf_rows + br) * a.R + jj;
+            const float *bp = a.buf + ((int64_t)sg * a.gm.buf_sstride + br) * a.R + jj;
             const float4 u0 = ldg<float4>(bp), u1 = ldg<float4>(bp + 4);
             v0.x += w * u0.x; v0.y += w * u0.y; v0.z += w * u0.z; v0.w += w * u0.w;
             v1.x += w * u1.x; v1.y += w * u1.y; v1.z += w * u1.z; v1.w += w * u1.w;
         }
     } else {
-        const float *bp = a.buf + ((int64_t)sg * a.gm.buf_rows + item / a.gm.buf_div) * a.R + jj;
+        const float *bp = a.buf + ((int64_t)sg * a.gm.buf_sstride + item / a.gm.buf_div) * a.R + jj;
         v0 = ldg<float4>(bp);
         v1 = ldg<float4>(bp + 4);
     }
@@ -423,14 +423,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
         const int row = t < ntok ? t : 0;
         const int item = a.seg.perm[p0 + row];
         if (!a.gm.ksum) {
-            fv[i] = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_rows + item / a.gm.buf_div) * R + j);
+            fv[i] = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_sstride + item / a.gm.buf_div) * R + j);
         } else {
             // the k-reduced buffer row of token `item`: sum_j coef * buf over its pairs
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int kk = 0; kk < a.gm.ksum; ++kk) {
                 const int64_t br = (int64_t)item * a.gm.ksum + kk;
                 const float cw = a.gm.coef ? a.gm.coef[br] : 1.0f;
-                const float4 u = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_rows + br) * R + j);
+                const float4 u = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_sstride + br) * R + j);
                 acc.x += cw * u.x; acc.y += cw * u.y; acc.z += cw * u.z; acc.w += cw * u.w;
             }
             fv[i] = acc;
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         for (int i = 0; i < NFU; ++i) {
             const int q = i * kThreads + tid;
             const int t = q / (R / 4), j = 4 * (q % (R / 4));
-            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_rows + s_brow[slot][t]) * R + min(j, jmax));
+            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_sstride + s_brow[slot][t]) * R + min(j, jmax));
         }
     };
 
@@ -781,6 +781,7 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.R = R; a.slot_rank = slot_rank; a.scale = scale; a.seg = seg; a.sl = sl;
     a.gm = gm;
     if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
+    if (a.gm.buf_sstride < 0) a.gm.buf_sstride = a.gm.buf_rows;
     bool aligned = R % 16 == 0 && ldy % 8 == 0;
     for (int s = 0; s < S; ++s)
         aligned = aligned && sl.n[s] % 8 == 0 && sl.off[s] % 8 == 0;

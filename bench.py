@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe", "logits"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode", "prefill"],
                    help="force a decode path (development runs; the headline uses auto)")
+    p.add_argument("--shared-a", action="store_true",
+                   help="one lora_a tensor for every slice (the shrink runs once on the tile path)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--profile", action="store_true",
@@ -61,7 +63,7 @@ def make_case(name):
     return synth.config_many()
 
 
-def algorithmic_bytes(c):
+def algorithmic_bytes(c, shared_a=False):
     """Bytes each kernel must move (per launch) for the realised draw.
     shrink: x rows of active tokens, the active slots' lora_a rows j < r, and
     the fp32 buffer of those tokens; expand: the active slots' lora_b
@@ -74,7 +76,8 @@ def algorithmic_bytes(c):
     ta = len(act)
     rank_tok = sum(int(c.slot_rank[s]) for _, s in act)
     rank_slot = sum(int(c.slot_rank[s]) for s in slots)
-    shrink = ta * c.K * el + c.S * rank_slot * c.K * el + c.S * rank_tok * 4
+    sa = 1 if shared_a else c.S          # one lora_a (and one buffer) for every slice
+    shrink = ta * c.K * el + sa * rank_slot * c.K * el + sa * rank_tok * 4
     expand = rank_slot * c.Ntot * el + c.S * rank_tok * 4 + ta * c.Ntot * el * 2
     seg = c.T * 4 * 2
     flops_shrink = 2 * c.S * rank_tok * c.K
@@ -324,6 +327,8 @@ def main():
     insts = []
     for i in range(n_inst):
         d = {k: ([t.clone() for t in v] if isinstance(v, list) else v.clone()) for k, v in base.items()}
+        if args.shared_a:
+            d["A"] = [d["A"][0]] * len(d["A"])   # one tensor, one pointer for every slice
         d["ws"] = aa.alloc_workspace(c.T, c.K, c.S, c.R, c.L)
         d["buf"] = torch.zeros((c.S, c.T, c.R), dtype=torch.float32, device=dev)
         insts.append(d)
@@ -480,7 +485,7 @@ def main():
         step(insts[i])
     torch.cuda.synchronize()
 
-    ab = algorithmic_bytes(c)
+    ab = algorithmic_bytes(c, args.shared_a)
     if fused:
         dom, dom_bytes = "fused", ab["fused"]
     else:
@@ -515,7 +520,8 @@ def main():
         "vs_baseline": None,
         "dtype": c.dtype,
         "data": "synthetic (seeded)",
-        "config": {"workload": workload_desc, "tokens": c.T, "hidden": c.K, "slices": c.N,
+        "config": {"workload": workload_desc + (", one lora_a for every slice" if args.shared_a else ""),
+                   "tokens": c.T, "hidden": c.K, "slices": c.N,
                    "rank": c.R, "slots": c.L, "rotating_instances": n_inst,
                    "active_tokens": ab["active_tokens"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),

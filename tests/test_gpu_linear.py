@@ -4,6 +4,8 @@ inputs where they apply.  Tolerance for bf16 outputs: max abs error <= 2e-2
 and normwise relative error <= 1e-2 against the fp32 oracle; fp32 outputs
 within the a-priori fp32 rounding bound; integer-exact vectors and every
 passthrough row bit-exact."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -449,6 +451,53 @@ def test_grouped_limits_bit_exact(oracle_mod, seed, T, K, N, R, L):
     y = d.y_host()
     ref = oracle_y(oracle_mod, c)
     assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+    assert canaries_intact(d.yfull)
+
+
+def shared_a_case(c):
+    """The same case with slice 0's lora_a used by every slice."""
+    return dataclasses.replace(c, A=[c.A[0]] * len(c.A))
+
+
+def on_device_shared_a(c):
+    d = LinearOnDevice(c)
+    d.A = [d.A[0]] * len(d.A)       # one tensor, so one pointer for every slice
+    return d
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("seed,T,K,N,R,L", [
+    (51, 600, 1024, [256, 64, 64], 16, 3),     # long runs per slot: auto takes the tile kernels
+    (52, 300, 2048, [512, 512], 64, 100),      # 100 slots: auto takes the tile kernels, K split
+    (53, 200, 1024, [256, 128, 128], 32, 5),   # auto takes the single-launch kernel
+])
+def test_shared_lora_a_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
+    """One lora_a pointer for every slice ([vLLM] MergedQKVParallelLinearWithLoRA
+    duplicates a single checkpoint lora_a per slice): the tile path computes
+    its shrink once; every path stays bit-exact on integer vectors."""
+    c = shared_a_case(synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16"))
+    skip_unless_path_takes(path, c)
+    log(f"case shared lora_a path={path} T={T} N={N} R={R} L={L}")
+    d = on_device_shared_a(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+    assert canaries_intact(d.yfull)
+
+
+def test_shared_lora_a_prefill_shape(oracle_mod):
+    """gate_up-like prefill (2048 tokens, 4 slots, two 2048-column slices,
+    rank 64) with one shared lora_a, on the auto (tile) path."""
+    rng = np.random.default_rng(61)
+    idx = np.repeat(rng.integers(0, 4, 8), 256).astype(np.int32)
+    c = shared_a_case(synth.make_linear("shared_a", 2048, 1024, [2048, 2048], 64, 4, idx,
+                                        [64, 32, 64, 16], [1.0] * 4, "bf16", seed=62))
+    d = on_device_shared_a(c)
+    d.apply(aa.LORA_PATH_AUTO)
+    y = d.y_host()
+    err, rel = bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    log(f"  max abs err {err:.3e} rel {rel:.3e}")
     assert canaries_intact(d.yfull)
 
 
