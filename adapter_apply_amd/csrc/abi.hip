@@ -97,25 +97,6 @@ int32_t *grp_kc_slot(void *ws, const SegLayout &l) {
     return reinterpret_cast<int32_t *>(static_cast<char *>(ws) + l.header) + 5;
 }
 
-// K splits of the row-oriented MFMA shrink.  A batch with few 64-token tiles
-// for the CUs (many slots with a few tokens each) would stream each slot's
-// lora_a through one CU; splitting K gives about 1024 work-groups, each with
-// at least 8 stages of 64 columns, while the fp32 partials (written and read
-// once) stay under an eighth of the shrink's input bytes.  1: no split.
-int32_t pre_kspl(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L, int32_t max_tiles,
-                 int32_t cap_chunks) {
-    const int32_t sr = S * R, ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
-    const int32_t n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
-    const int32_t nst = (K + 63) / 64;
-    int32_t k = (1024 + max_tiles * n_cb - 1) / (max_tiles * n_cb);
-    if (k > nst / 8) k = nst / 8;
-    if (k > kMaxKcGrp) k = kMaxKcGrp;
-    if (k > cap_chunks) k = cap_chunks;
-    const double in_bytes = 2.0 * K * ((double)T + (double)(T < L ? T : L) * S * R);
-    while (k > 1 && 8.0 * k * T * S * R > in_bytes / 8) --k;
-    return k < 1 ? 1 : k;
-}
-
 // The row-oriented MFMA shrink into the token-ordered buffer, split over K
 // (partials, then the reduce kernel summing the splits in order) when
 // pre_kspl says so.

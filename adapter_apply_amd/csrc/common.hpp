@@ -148,10 +148,18 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
 
 // Fused-MoE workspace: token segments (by slot), pair segments (by slot and
 // expert) and the fp32 buffer [S][T*k][R].
+// K-split partials of the MoE shrink: kMoeSplitChunks chunks of up to
+// kMoeSplitItems items (the split serves small batches, whose few tiles would
+// otherwise stream K through a few CUs).
+constexpr int kMoeSplitChunks = 16;
+constexpr int kMoeSplitItems = 4096;
+
 struct MoeWsLayout {
     SegLayout tok;
     SegLayout pair;
     size_t buf;
+    size_t part;          // fp32 [S][chunks][items][R], items <= kMoeSplitItems
+    size_t part_bytes;
     size_t end;
 };
 
@@ -160,7 +168,10 @@ inline MoeWsLayout moe_ws_layout(int32_t T, int32_t k, int32_t S, int32_t R, int
     m.tok = seg_layout(T, L, 0);
     m.pair = seg_layout(T * k, L * E, m.tok.end);
     m.buf = m.pair.end;
-    m.end = align256(m.buf + sizeof(float) * (size_t)S * T * k * R);
+    m.part = align256(m.buf + sizeof(float) * (size_t)S * T * k * R);
+    const int64_t items = (int64_t)T * k < kMoeSplitItems ? (int64_t)T * k : kMoeSplitItems;
+    m.part_bytes = sizeof(float) * (size_t)kMoeSplitChunks * items * S * R;
+    m.end = align256(m.part + m.part_bytes);
     return m;
 }
 
@@ -277,9 +288,11 @@ hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, cons
                              const int32_t *slot_rank, const float *scale, const float *part,
                              const float *buf, const int32_t *n_kc_in, const SegPtrs *seg,
                              hipStream_t st);
+// With a segment table of keyed tiles (slot * ekey + expert), pass ekey; T is
+// the number of items (positions of the partials, rows of buf).
 hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *part, int32_t n_kc,
-                             float *buf, const SegPtrs *seg, hipStream_t st);
+                             float *buf, const SegPtrs *seg, hipStream_t st, int32_t ekey = 1);
 
 // Grouped-problem mapping of the MFMA kernels.  A tile's key is
 // slot * Ekey + expert (Ekey = 1 for token tiles); the lora tensor it reads is
@@ -297,6 +310,25 @@ struct GroupMap {
     const float *coef = nullptr;   // per-item factor (routing weight), or null
     int32_t ksum = 0;              // expand: buffer row of token t = sum_j coef[t*ksum+j] * buf[t*ksum+j]
 };
+
+// K splits of the row-oriented MFMA shrink.  A batch with few 64-token tiles
+// for the CUs (many slots with a few tokens each) would stream each slot's
+// lora_a through one CU; splitting K gives about 1024 work-groups, each with
+// at least 8 stages of 64 columns, while the fp32 partials (written and read
+// once) stay under an eighth of the shrink's input bytes.  1: no split.
+inline int32_t pre_kspl(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L, int32_t max_tiles,
+                 int32_t cap_chunks) {
+    const int32_t sr = S * R, ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
+    const int32_t n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
+    const int32_t nst = (K + 63) / 64;
+    int32_t k = (1024 + max_tiles * n_cb - 1) / (max_tiles * n_cb);
+    if (k > nst / 8) k = nst / 8;
+    if (k > kMaxKcGrp) k = kMaxKcGrp;
+    if (k > cap_chunks) k = cap_chunks;
+    const double in_bytes = 2.0 * K * ((double)T + (double)(T < L ? T : L) * S * R);
+    while (k > 1 && 8.0 * k * T * S * R > in_bytes / 8) --k;
+    return k < 1 ? 1 : k;
+}
 
 // part (nullable): split K into *kspl_io chunks (fewer if K has fewer
 // 64-column stages; the count used is written back) and write fp32 partials

@@ -66,6 +66,7 @@ struct GrpTable {
     const int32_t *perm;
     const int32_t *header;   // [2]: number of tiles
     int32_t max_tiles;
+    int32_t ekey;            // tile key = slot * ekey + expert (1: the key is the slot)
 };
 
 // Group `group` of the batch (discover.hpp); *tok receives its token list.
@@ -89,7 +90,7 @@ __device__ __forceinline__ GroupSel group_of(const GrpTable &tab, const int32_t 
         sel.pos0 = tl.y;
         sel.ntok = tl.z - tl.y;
         sel.n_groups = n;
-        sel.rank = min(slot_rank ? slot_rank[tl.x] : R, R);
+        sel.rank = min(slot_rank ? slot_rank[tl.x / tab.ekey] : R, R);
         *tok = tab.perm + tl.y;
         return sel;
     } else {
@@ -471,8 +472,9 @@ __global__ __launch_bounds__(kThreads) void k_grp_reduce(GrpReduceArgs a) {
     }
 }
 
-GrpTable grp_table(const SegPtrs *seg) {
+GrpTable grp_table(const SegPtrs *seg, int32_t ekey = 1) {
     GrpTable t{};
+    t.ekey = ekey;
     if (seg) {
         t.tiles = seg->tiles_dec;
         t.perm = seg->perm;
@@ -567,9 +569,9 @@ hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, cons
 
 hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *part, int32_t n_kc,
-                             float *buf, const SegPtrs *seg, hipStream_t st) {
+                             float *buf, const SegPtrs *seg, hipStream_t st, int32_t ekey) {
     GrpReduceArgs a;
-    a.tab = grp_table(seg);
+    a.tab = grp_table(seg, ekey);
     a.T = T; a.S = S; a.L = L; a.R = R; a.n_kc = n_kc;
     a.idx = idx; a.slot_rank = slot_rank; a.part = part; a.buf = buf;
     const dim3 grid((unsigned)grp_groups(T, L, seg));

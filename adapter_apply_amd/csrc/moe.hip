@@ -236,7 +236,24 @@ lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_
             ex_seg = &pair;
         }
     }
-    CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, *sh_seg, buf, st, sh)));
+    // A small batch has few tiles, each streaming all of K through one CU:
+    // the shrink is then split over K into partials in the workspace, summed
+    // in order into the buffer by the reduce kernel.
+    const int32_t n_items = sh.buf_rows;                   // tokens or (token, k) pairs
+    int32_t kspl = 1;
+    if (n_items <= kMoeSplitItems) {
+        const int32_t cap = (int32_t)(ml.part_bytes / (sizeof(float) * (size_t)n_items * S * R));
+        kspl = pre_kspl(n_items, K, S, R, L * sh.Ekey, sh_seg->max_tiles_pre, cap);
+    }
+    if (kspl > 1) {
+        float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + ml.part);
+        CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, *sh_seg, nullptr, st, sh,
+                                         part, &kspl)));
+        CHECK(launched(launch_grp_reduce(n_items, S, L, R, idx, slot_rank, part, kspl, buf, sh_seg, st,
+                                         sh.Ekey)));
+    } else {
+        CHECK(launched(launch_pre_shrink(x, ldx, T, K, sl, S, L, R, slot_rank, *sh_seg, buf, st, sh)));
+    }
     return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, *ex_seg, st, ex));
 }
 

@@ -36,7 +36,7 @@ struct PreShrinkArgs {
     SegPtrs seg;
     Slices sl;
     float *buf;
-    float *part;               // or null: fp32 [S][kspl][T][R] by slot-sorted position
+    float *part;               // or null: fp32 [S][kspl][buf_rows][R] by slot-sorted position
     GroupMap gm;
 };
 
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
     if (c >= SRf) return;
     const int sg = c / a.R, j = c - sg * a.R;
     if (a.part) {
-        float *dst = a.part + (((int64_t)sg * a.kspl + ks) * a.T + p0) * a.R + j;
+        float *dst = a.part + (((int64_t)sg * a.kspl + ks) * a.gm.buf_rows + p0) * a.R + j;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 32 * tb + 8 * (i >> 2) + 4 * half + (i & 3);

@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe", "logits"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode", "prefill"],
                    help="force a decode path (development runs; the headline uses auto)")
+    p.add_argument("--moe-tokens", type=int, default=2048,
+                   help="tokens of the fused-MoE workload (2048 by default)")
     p.add_argument("--shared-a", action="store_true",
                    help="one lora_a tensor for every slice (the shrink runs once on the tile path)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,7 +172,7 @@ def run_moe(args, steps, warmup):
     import synth
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = synth.config_moe()
+    c = synth.config_moe(T=args.moe_tokens)
     bf = torch.bfloat16
     to = lambda a, d=None: (torch.from_numpy(np.ascontiguousarray(a)).to(d) if d is not None
                             else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
@@ -277,7 +279,7 @@ def run_moe(args, steps, warmup):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded)",
-        "config": {"workload": "fused-MoE LoRA: 2048 tokens, 64 experts top-8, d_model 4096, d_mlp 1536, "
+        "config": {"workload": f"fused-MoE LoRA: {c.T} tokens, 64 experts top-8, d_model 4096, d_mlp 1536, "
                                "rank 16, 8 adapters, shared-outer; align + w13 + w2 per (token, k)",
                    "tokens": c.T, "pairs": ab["pairs"], "used_slot_expert_groups": ab["used_groups"],
                    "rotating_instances": n_inst},

@@ -111,6 +111,7 @@ def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
     (2, 130, 8, 16, 256, 96, 32, 4),
     (3, 1, 1, 1, 8, 8, 16, 1),
     (4, 300, 4, 64, 128, 64, 16, 16),     # L * E = 1024 keys
+    (5, 40, 4, 8, 2048, 1024, 16, 3),     # small batch, long K: the shrinks split over K
 ])
 def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L):
     d = integer_moe(seed, T, k, E, K, I, R, L, shared)
@@ -200,6 +201,21 @@ def test_moe_config_shared_outer(oracle_mod):
     yr = run_moe(W2, np.zeros((T, c.K), np.float32), c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w,
                  c.idx, c.slot_rank, c.scale, c.E, ws=ws, flags=ready, reduce_k=True, guard=False)
     bounds.check_bf16_tolerance(yr[rows], oracle_rows(oracle_mod, c, 1, rows, reduce_k=True))
+
+
+@pytest.mark.parametrize("T", [4, 8])
+def test_moe_config_small_batch(oracle_mod, T):
+    """The fused-MoE workload's shapes at a decode-sized batch (d_model 4096,
+    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): few tiles, so both
+    shrinks run split over K."""
+    c = synth.config_moe(T=T)
+    rows = np.arange(T)
+    log(f"case moe small batch T={T}")
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale, c.E)
+    bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 0, rows))
+    y = run_moe(W2, c.out0, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
+                c.E)
+    bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 1, rows))
 
 
 def test_moe_per_expert_layout(oracle_mod):
