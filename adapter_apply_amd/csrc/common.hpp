@@ -214,6 +214,18 @@ struct Slices {
     int64_t off[kMaxSlices + 1]; // column offset of each slice in y (incl. y_col_offset)
 };
 
+// A fused-MoE call of at most this many (token, k) pairs, rank 16, without
+// the k-reduction and without a prebuilt alignment skips the alignment
+// (moe_small.hip).
+constexpr int kMoeSmallPairs = 128;
+bool moe_small_takes(int32_t pairs, int32_t R, int32_t reduce_k);
+hipError_t launch_moe_small(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T, int32_t top_k,
+                            int32_t K, const Slices &sl, int32_t S, int32_t E, int32_t L, int32_t R,
+                            int32_t Ea, int32_t Eb, int32_t x_div, const int32_t *topk_ids,
+                            const float *coef, const int32_t *idx, const int32_t *slot_rank,
+                            const float *scale, hipStream_t st);
+
+
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
                            int32_t R, const SegPtrs &seg, hipStream_t st);

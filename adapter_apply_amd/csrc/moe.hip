@@ -204,6 +204,20 @@ lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_
     if (ws_bytes < ml.end) return LORA_E_WORKSPACE;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int32_t P = T * top_k;
+    if (!(flags & LORA_FLAG_SEGMENTS_READY) && moe_small_takes(P, R, reduce_k)) {
+        // a few pairs: no alignment, one work-group per (pair, column chunk)
+        Slices s1{};
+        int64_t o = 0;
+        for (int s = 0; s < S; ++s) {
+            s1.a[s] = A[s]; s1.b[s] = B[s]; s1.n[s] = N[s]; s1.off[s] = o; o += N[s];
+        }
+        for (int s = S; s <= kMaxSlices; ++s) s1.off[s] = o;
+        const bool w13 = kind == MOE_LORA_W13;
+        return launched(launch_moe_small(y, ldy, x, ldx, T, top_k, K, s1, S, E, L, R, E_a, E_b,
+                                         w13 ? top_k : 1, topk_ids, w13 ? nullptr : topk_w, idx,
+                                         slot_rank, scale, st));
+    }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(moe_segments(topk_ids, idx, slot_rank, T, top_k, E, L, R, ml, ws, st));
     const SegPtrs tok = seg_ptrs(ws, ml.tok), pair = seg_ptrs(ws, ml.pair);
@@ -214,7 +228,6 @@ lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_
         sl.a[s] = A[s]; sl.b[s] = B[s]; sl.n[s] = N[s]; sl.off[s] = off; off += N[s];
     }
     for (int s = S; s <= kMaxSlices; ++s) sl.off[s] = off;
-    const int32_t P = T * top_k;
 
     GroupMap sh, ex;
     const SegPtrs *sh_seg, *ex_seg;

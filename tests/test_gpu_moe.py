@@ -34,11 +34,17 @@ def pad_to(a, axis, n):
 
 
 def run_moe(kind, y0, x, A, B, topk_ids, topk_w, idx, rank, scale, E, reduce_k=False, ws=None,
-            flags=0, guard=True):
+            flags=0, guard=True, align=False):
+    """One moe_lora_apply call.  align=True runs moe_lora_align first and
+    passes its segments (the aligned path at any size); otherwise a call of a
+    few pairs takes the path without alignment."""
     T, k = topk_ids.shape
     L, _, R, _ = A[0].shape
     if ws is None:
         ws = aa.alloc_moe_workspace(T, k, len(A), R, L, E)
+    if align:
+        aa.moe_lora_align(dev(topk_ids), dev(idx), dev(rank), E, L, R, 16, ws)
+        flags |= aa.LORA_FLAG_SEGMENTS_READY
     if guard:
         yfull, y = guarded(y0, BF)
     else:
@@ -69,9 +75,10 @@ def test_hand_examples_padded():
         args = (x, A, B, np.asarray(c["topk_ids"], np.int32), topk_w,
                 np.asarray(c["idx"], np.int32), np.asarray(c["slot_rank"], np.int32),
                 np.asarray(c["scale"], np.float32), c["E"])
-        y = run_moe(kind, y0, *args)
-        assert np.array_equal(y[:, :n], np.asarray(c["expected_y"], np.float32)), key
-        assert np.all(y[:, n:] == 0)
+        for align in (False, True):       # without, then with the alignment
+            y = run_moe(kind, y0, *args, align=align)
+            assert np.array_equal(y[:, :n], np.asarray(c["expected_y"], np.float32)), (key, align)
+            assert np.all(y[:, n:] == 0)
         if key == "moe_w2":
             y = run_moe(kind, np.zeros((c["T"], 4), np.float32), *args, reduce_k=True)
             assert np.array_equal(y[:, :n], np.asarray(c["expected_y_reduced"], np.float32))
@@ -115,17 +122,19 @@ def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
 ])
 def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L):
     d = integer_moe(seed, T, k, E, K, I, R, L, shared)
-    log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L}")
-    y = run_moe(W13, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None, d["idx"], d["rank"],
-                d["scale"], E)
-    ref = oracle_mod.moe_lora_apply(0, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None,
-                                    d["idx"], d["rank"], d["scale"], E)
-    assert np.array_equal(y, ref), np.max(np.abs(y - ref))
-    y = run_moe(W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"], d["idx"], d["rank"],
-                d["scale"], E)
-    ref = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
-                                    d["idx"], d["rank"], d["scale"], E)
-    assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+    ref13 = oracle_mod.moe_lora_apply(0, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None,
+                                      d["idx"], d["rank"], d["scale"], E)
+    ref2 = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
+                                     d["idx"], d["rank"], d["scale"], E)
+    # both paths where a call is small enough for the one without alignment
+    for align in ((False, True) if T * k <= 128 else (False,)):
+        log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L} align={align}")
+        y = run_moe(W13, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None, d["idx"], d["rank"],
+                    d["scale"], E, align=align)
+        assert np.array_equal(y, ref13), np.max(np.abs(y - ref13))
+        y = run_moe(W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"], d["idx"],
+                    d["rank"], d["scale"], E, align=align)
+        assert np.array_equal(y, ref2), np.max(np.abs(y - ref2))
     if shared:
         z = np.zeros((T, K), np.float32)
         y = run_moe(W2, z, d["h"], [d["A2"]], [d["B2"]], d["ids"], None, d["idx"], d["rank"],
@@ -203,18 +212,20 @@ def test_moe_config_shared_outer(oracle_mod):
     bounds.check_bf16_tolerance(yr[rows], oracle_rows(oracle_mod, c, 1, rows, reduce_k=True))
 
 
-@pytest.mark.parametrize("T", [4, 8])
-def test_moe_config_small_batch(oracle_mod, T):
-    """The fused-MoE workload's shapes at a decode-sized batch (d_model 4096,
-    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): few tiles, so both
-    shrinks run split over K."""
+@pytest.mark.parametrize("T,align", [(4, False), (8, False), (4, True), (8, True), (40, False)])
+def test_moe_config_small_batch(oracle_mod, T, align):
+    """The fused-MoE workload's shapes at decode-sized batches (d_model 4096,
+    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): up to 128 pairs the
+    call skips the alignment; aligned (or at 40 tokens) the few tiles make
+    both shrinks run split over K."""
     c = synth.config_moe(T=T)
     rows = np.arange(T)
-    log(f"case moe small batch T={T}")
-    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale, c.E)
+    log(f"case moe small batch T={T} align={align}")
+    y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
+                c.E, align=align)
     bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 0, rows))
     y = run_moe(W2, c.out0, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
-                c.E)
+                c.E, align=align)
     bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 1, rows))
 
 
