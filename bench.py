@@ -203,8 +203,8 @@ def run_moe(args, steps, warmup):
         aa.moe_lora_apply(aa.MOE_LORA_W2, d["o"], d["h"], d["A2"], d["B2"], d["ids"], d["w"],
                           d["idx"], d["rank"], d["scale"], c.E, d["ws"], flags=ready)
 
-    # a call of at most 128 pairs (rank 16) skips the alignment (the library's rule)
-    small = c.T * c.k <= 128 and c.R == 16
+    # a call of at most 256 pairs (rank 16) skips the alignment (the library's rule)
+    small = c.T * c.k <= 256 and c.R == 16
 
     def w13_small(d):
         aa.moe_lora_apply(aa.MOE_LORA_W13, d["g"], d["x"], d["A13"], d["B13"], d["ids"], None,

@@ -258,6 +258,10 @@ lora_status_t moe_lora_align(const int32_t *topk_ids, const int32_t *idx, const 
  *   topk_ids device int32 [T][top_k]; topk_w device float [T][top_k] or NULL.
  * ws: moe_lora_workspace_size() bytes; flags: LORA_FLAG_SEGMENTS_READY when
  * ws holds this batch's alignment (moe_lora_align or a previous apply).
+ * Without that flag, a call of at most 256 pairs at R == 16 without reduce_k
+ * skips the alignment ([vLLM] FusedMoEWithLoRA's naive regime for small
+ * batches): one work-group per (pair, 1024 output columns).  Small batches
+ * that are aligned run their shrink split over K.
  */
 lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_k, const void *x,
                              int64_t ldx, int32_t T, int32_t top_k, int32_t K,

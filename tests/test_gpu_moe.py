@@ -127,7 +127,7 @@ def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L
     ref2 = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
                                      d["idx"], d["rank"], d["scale"], E)
     # both paths where a call is small enough for the one without alignment
-    for align in ((False, True) if T * k <= 128 else (False,)):
+    for align in ((False, True) if T * k <= 256 else (False,)):
         log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L} align={align}")
         y = run_moe(W13, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None, d["idx"], d["rank"],
                     d["scale"], E, align=align)
@@ -212,12 +212,12 @@ def test_moe_config_shared_outer(oracle_mod):
     bounds.check_bf16_tolerance(yr[rows], oracle_rows(oracle_mod, c, 1, rows, reduce_k=True))
 
 
-@pytest.mark.parametrize("T,align", [(4, False), (8, False), (4, True), (8, True), (40, False)])
+@pytest.mark.parametrize("T,align", [(4, False), (8, False), (4, True), (8, True), (40, False), (40, True)])
 def test_moe_config_small_batch(oracle_mod, T, align):
     """The fused-MoE workload's shapes at decode-sized batches (d_model 4096,
-    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): up to 128 pairs the
-    call skips the alignment; aligned (or at 40 tokens) the few tiles make
-    both shrinks run split over K."""
+    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): up to 256 pairs (32
+    tokens) the call skips the alignment; aligned, the few tiles make both
+    shrinks run split over K."""
     c = synth.config_moe(T=T)
     rows = np.arange(T)
     log(f"case moe small batch T={T} align={align}")
