@@ -170,6 +170,31 @@ def test_w13_single_slice_and_interleaved(oracle_mod, shared):
     assert np.array_equal(y_int, y_cat[:, perm])
 
 
+@pytest.mark.parametrize("align", [False, True])
+def test_small_batch_invalid_experts_and_empty_slots(oracle_mod, align):
+    """Pairs whose expert is outside [0, E), tokens without an adapter and a
+    slot of rank 0 leave their rows bit-exact, on both paths of a small call."""
+    T, k, E, K, I, R, L = 12, 4, 8, 1024, 256, 16, 3
+    d = integer_moe(7, T, k, E, K, I, R, L, shared=True, p_none=0.2)
+    ids = d["ids"].copy()
+    ids[0, 1] = -1
+    ids[3, 2] = E
+    ids[5, 0] = E + 7
+    rank = d["rank"].copy()
+    rank[1] = 0
+    log(f"case moe small invalid experts align={align}")
+    for kind, y0, x, A, B, w in ((W13, d["g0"], d["x"], d["A13"], d["B13"], None),
+                                 (W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["w"])):
+        y = run_moe(kind, y0, x, A, B, ids, w, d["idx"], rank, d["scale"], E, align=align)
+        ref = oracle_mod.moe_lora_apply(kind, y0, x, A, B, ids, w, d["idx"], rank, d["scale"], E)
+        assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+        t_of = np.arange(T * k) // k
+        dead = (ids.reshape(-1) < 0) | (ids.reshape(-1) >= E) | (d["idx"][t_of] < 0) | \
+               (rank[np.maximum(d["idx"][t_of], 0)] == 0)
+        assert dead.any()
+        assert np.array_equal(y[dead], y0[dead])
+
+
 def sample_tokens(T, n, seed=0):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n)])).astype(np.int64)
