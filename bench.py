@@ -139,6 +139,33 @@ def cpu_baseline(c, seconds):
                       f"{el:.1f} s, fp32 C loops on 1 host thread"}
 
 
+def moe_cpu_baseline(c, seconds):
+    """The CPU oracle, single-threaded, on a token prefix of the same MoE batch
+    (w13 then w2 per (token, k) pair), repeated for about `seconds`; tokens/s."""
+    import oracle
+    oracle.build(force=False)
+
+    def run(n):
+        pr = slice(0, n * c.k)
+        oracle.moe_lora_apply(0, c.gate_up0[pr], c.x[:n], c.A13, c.B13, c.topk_ids[:n], None,
+                              c.idx[:n], c.slot_rank, c.scale, c.E)
+        oracle.moe_lora_apply(1, c.out0[pr], c.h[pr], [c.A2], [c.B2], c.topk_ids[:n],
+                              c.topk_w[:n], c.idx[:n], c.slot_rank, c.scale, c.E)
+    t0 = time.perf_counter()
+    run(1)
+    one = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(c.T, max(1, 1.0 / one)))
+    done, reps, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run(n)
+        done += n
+        reps += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of the {c.T} tokens of the same batch (w13 and w2 per pair), "
+                      f"{reps} repetitions, {el:.1f} s, fp32 C loops on 1 host thread"}
+
+
 def moe_algorithmic_bytes(c):
     """Bytes the fused-MoE step must move for the realised routing: w13 reads
     the x rows of tokens with an adapter, the shared lora_a of their slots, the
@@ -308,7 +335,7 @@ def run_moe(args, steps, warmup):
                      "algorithmic_bytes": ab[dom], "kernel_us": round(per_call[dom], 3)},
         "calls_us": {k: round(v, 3) for k, v in per_call.items()},
         "step_algorithmic_GBps": round(ab["total"] / (ms_per_step * 1e-3) / 1e9, 1),
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else moe_cpu_baseline(c, args.cpu_seconds),
         "wall_s": round(wall, 3),
         "kernel_hash": kernel_hash(),
     }
