@@ -153,6 +153,15 @@ lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t
     return LORA_OK;
 }
 
+// Auto for lora_shrink / lora_expand called apart, without LORA_FLAG_PARTIAL:
+// batches of many slots or high ranks take the tile kernels (the buffer
+// between the calls is the same token-ordered fp32 [S][T][R] on every path, so
+// the two calls need not agree on the path).
+bool auto_tiles_apart(int32_t path, uint32_t flags, int32_t L, int32_t R, int32_t dtype) {
+    return path == LORA_PATH_AUTO && !(flags & LORA_FLAG_PARTIAL) && dtype == LORA_DT_BF16 &&
+           (L > 64 || R > 64) && (R == 16 || R == 32 || R == 64 || R == 128);
+}
+
 lora_status_t check_ws(const void *ws, size_t ws_bytes, size_t need) {
     if (!ws) return LORA_E_NULL;
     if (!al(ws, 256)) return LORA_E_ALIGN;
@@ -245,6 +254,7 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
     CHECK(check_k(K, ldx));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (auto_tiles_apart(path, flags, L, R, dtype)) use_prefill = 1;
     const bool group = path == LORA_PATH_GROUPED;
     if (group && !(can_group_sizes(T, R, dtype) && can_group_k(K))) return LORA_E_PATH;
     if (group && (flags & LORA_FLAG_PARTIAL) && R > kGrpMaxPartialRank) return LORA_E_PATH;
@@ -299,6 +309,8 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (auto_tiles_apart(path, flags, L, R, dtype) && rows_of_8(N, S, ldy, y_col_offset))
+        use_prefill = 1;
     const bool group = path == LORA_PATH_GROUPED;
     if (group && !(can_group_sizes(T, R, dtype) && rows_of_8(N, S, ldy, y_col_offset)))
         return LORA_E_PATH;

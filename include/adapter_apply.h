@@ -49,8 +49,12 @@
  *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0
  *            (batches of many slots or high ranks: the MFMA kernels, the
  *            shrink split over K when its tiles are few), and DECODE
- *            elsewhere; lora_shrink / lora_expand take DECODE
- *            (so that a shrink and an expand called apart agree).
+ *            elsewhere; lora_shrink / lora_expand take PREFILL for bf16
+ *            batches with L > 64 or R > 64 (R in {16, 32, 64, 128}; the
+ *            expand also needs N, ldy, y_col_offset % 8 == 0) and DECODE
+ *            otherwise, and DECODE whenever LORA_FLAG_PARTIAL is set (a
+ *            shrink and an expand called apart exchange the token-ordered
+ *            buffer, which every path writes and reads alike).
  *            DECODE forces the split (segments, VALU shrink, expand) decode
  *            path; PREFILL forces the MFMA path (bf16, R % 16 == 0 only);
  *            GROUPED forces the slot-grouped decode kernels (split-K MFMA

@@ -215,6 +215,20 @@ def test_many_adapter_config(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
+def test_many_adapter_separate_calls_auto(oracle_mod):
+    """lora_shrink then lora_expand on auto, apart, for the many-slot batch:
+    both take the tile kernels and exchange the token-ordered buffer."""
+    c = synth.config_many(T=512)
+    log("case many_adapter separate calls (auto)")
+    d = LinearOnDevice(c)
+    buf = torch.full((c.S, c.T, c.R), 3.0, dtype=torch.float32, device="cuda")
+    aa.lora_shrink(buf, d.x, d.A, d.idx, d.rank, d.ws)
+    aa.lora_expand(d.y, buf, d.B, d.idx, d.rank, d.scale, d.ws)
+    y = d.y_host()
+    bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    assert canaries_intact(d.yfull)
+
+
 def test_many_adapter_alpha_scales(oracle_mod):
     c = synth.config_many(T=512, scale_mode="alpha")
     log("case many_adapter alpha scales")
