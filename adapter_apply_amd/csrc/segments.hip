@@ -10,7 +10,7 @@
 // latency-bound, so every global load (keys of up to 16384 items, slot ranks)
 // is issued before the first barrier and the rest runs out of registers and
 // LDS.
-#include "common.hpp"
+#include "discover.hpp"
 
 namespace aa {
 
@@ -18,25 +18,16 @@ namespace {
 
 constexpr int kSegWaves = kSegThreads / kWave;
 
-// Exclusive scan of one int per thread over the 1024-thread block.
+// Exclusive scan of one int per thread over the 1024-thread block (DPP wave
+// scans, then one over the 16 wave totals).
 __device__ int block_exclusive_scan(int v, int *total, int *wsum) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
     if (w == 0) {
-        int s = lane < kSegWaves ? wsum[lane] : 0;
-        int si = s;
-#pragma unroll
-        for (int d = 1; d < kSegWaves; d <<= 1) {
-            int o = __shfl_up(si, d);
-            if (lane >= d) si += o;
-        }
+        const int s = lane < kSegWaves ? wsum[lane] : 0;
+        const int si = wave_incl_scan(s);
         if (lane < kSegWaves) wsum[kSegWaves + lane] = si - s;   // exclusive wave offsets
         if (lane == kSegWaves - 1) wsum[2 * kSegWaves] = si;       // total
     }
