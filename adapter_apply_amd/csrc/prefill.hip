@@ -1,21 +1,27 @@
-// Prefill path: MFMA kernels for long per-slot token runs (SGMV regime).
+// Tile path: MFMA kernels over tiles of at most 64 tokens of one key (slot,
+// or slot and expert for MoE) -- the SGMV regime of long per-slot runs, and
+// batches of many slots or high ranks, whose shrink is then split over K.
 //
-// Tokens are grouped by slot into tiles of 64 (two 32-row MFMA blocks).  Both
+// Tokens are grouped by key into tiles of 64 (two 32-row MFMA blocks).  The
 // kernels use v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate).  An operand
 // fragment is 16 bytes per lane: row (l % 32), 8 consecutive k values starting
 // at 8 * (l / 32).  The accumulator layout of a 32x32 block: lane l holds
 // column (l % 32) and rows 8 * (i / 4) + 4 * (l / 32) + (i % 4), i = 0..15.
 //
 // Shrink (k_pre_shrink_rows): work-group = (tile, up to 128 of the S*R buffer
-// columns), x and lora_a rows staged through LDS in 64-column K stages.
+// columns, K split), x and lora_a rows staged through LDS in 64-column K
+// stages; with a K split it writes fp32 partials that the grouped reduce
+// kernel sums in order.
 //
 // Expand: work-group = (tile, group of output columns of one slice), the
-// product formed transposed, D[n][t] = B[n][:] . buf[t][:].  For ranks up to
-// 64 (k_pre_expand_rows) the y tile, the lora_b block and the buffer rows go
-// through LDS so that every global access is row-contiguous; larger ranks use
-// k_pre_expand, whose lanes read and write y 8 bytes at a time in the MFMA
-// layout.  Column groups are dealt to the 8 XCDs round-robin so each XCD keeps
-// its slice of lora_b hot in its own L2 across a slot's tiles.
+// product formed transposed, D[n][t] = B[n][:] . buf[t][:], with the y tile,
+// the lora_b block and the buffer rows staged through LDS so that every
+// global access is row-contiguous: k_pre_expand_pipe (persistent, ranks 16,
+// 32, 64, 128), k_pre_expand_rows (one item per work-group, ranks up to 64,
+// per-item factors and the k-reduction); other ranks use k_pre_expand, whose
+// lanes read and write y 8 bytes at a time in the MFMA layout.  Column groups
+// are dealt to the 8 XCDs so each XCD keeps its slice of lora_b hot in its
+// own L2 across a slot's tiles.
 #include "common.hpp"
 
 namespace aa {
