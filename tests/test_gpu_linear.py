@@ -515,6 +515,47 @@ def test_shared_lora_a_prefill_shape(oracle_mod):
     assert canaries_intact(d.yfull)
 
 
+# [SGL] the DeepSeek MLA fused_qkv_a_proj_with_mqa module: one lora_a, and the
+# output split at q_lora_rank into two lora_b partitions (q_a: 1536 columns;
+# kv_a with the rope part: 512 + 64), hidden 7168.
+MLA_K, MLA_N = 7168, [1536, 576]
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("seed,T,R,L", [
+    (55, 48, 16, 4),       # decode batch: auto takes the single-launch kernel
+    (56, 900, 64, 6),      # long runs per slot: auto takes the tile kernels, one shrink
+])
+def test_mla_two_partition_lora_b_bit_exact(oracle_mod, path, seed, T, R, L):
+    """Two output partitions behind one lora_a are two slices with equal
+    lora_a pointers: bit-exact on integer vectors on every path."""
+    c = shared_a_case(synth.make_integer_linear(T, MLA_K, MLA_N, R, L, seed=seed, dtype="bf16"))
+    skip_unless_path_takes(path, c)
+    log(f"case mla two partitions path={path} T={T} R={R} L={L}")
+    d = on_device_shared_a(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+    assert canaries_intact(d.yfull)
+
+
+def test_mla_two_partition_lora_b_tolerance(oracle_mod):
+    """The MLA shape at a decode batch on gaussian inputs (rank 16, 8 slots,
+    10 % of tokens without an adapter), auto path."""
+    rng = np.random.default_rng(57)
+    idx = rng.integers(0, 8, size=256).astype(np.int32)
+    idx[rng.random(256) < 0.1] = -1
+    c = shared_a_case(synth.make_linear("mla_qkv_a", 256, MLA_K, MLA_N, 16, 8, idx, [16] * 8,
+                                        [2.0] * 8, "bf16", seed=58))
+    d = on_device_shared_a(c)
+    d.apply(aa.LORA_PATH_AUTO)
+    y = d.y_host()
+    err, rel = bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+    log(f"  max abs err {err:.3e} rel {rel:.3e}")
+    assert canaries_intact(d.yfull)
+
+
 def test_zero_tokens_noop():
     c = synth.config_decode(T=8)
     d = LinearOnDevice(c)
