@@ -99,6 +99,8 @@ INTEGER_CASES = [
     (31, 300, 1024, [512, 64], 128, 9),      # rank 128
     (32, 1500, 2048, [512, 264], 128, 100),  # 100 slots, rank 128: K-split shrink on the MFMA paths
     (33, 64, 1024, [32768], 16, 4),          # one vocabulary-wide slice (lm_head LoRA)
+    (34, 150, 1024, [256, 64], 512, 3),      # the largest rank the library takes
+    (35, 400, 512, [128, 200], 256, 5),      # rank 256: several 128-rank passes
 ]
 
 

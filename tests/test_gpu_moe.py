@@ -119,6 +119,7 @@ def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
     (3, 1, 1, 1, 8, 8, 16, 1),
     (4, 300, 4, 64, 128, 64, 16, 16),     # L * E = 1024 keys
     (5, 40, 4, 8, 2048, 1024, 16, 3),     # small batch, long K: the shrinks split over K
+    (6, 30, 2, 4, 256, 128, 512, 2),      # the largest rank the library takes
 ])
 def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L):
     d = integer_moe(seed, T, k, E, K, I, R, L, shared)
