@@ -114,6 +114,21 @@ def load_traffic(workload, kernel, khash):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def load_mfma_counters(workload, khash):
+    """MFMA flops executed per step (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, summed
+    over the step's kernels) from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"pmc_mfma_{workload}.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != khash:
+        return None
+    return d.get("step_mfma_bf16_flops")
+
+
 def cpu_baseline(c, seconds):
     """The CPU oracle, single-threaded, on a bounded sample of the same
     workload: whole batches (or a token prefix of one) repeated for about
@@ -543,6 +558,8 @@ def main():
     achieved = dom_bytes / (per_kernel[dom] * 1e-6) / 1e9
     khash = kernel_hash()
     traffic = load_traffic(args.workload, dom, khash)
+    mfma_exec = (load_mfma_counters(args.workload, khash)
+                 if args.path == "auto" and not args.shared_a else None)
     tokens_per_s = c.T / (ms_per_step * 1e-3)
 
     cpu = None
@@ -584,7 +601,12 @@ def main():
         # per active token) against the 2.5 PFLOP/s bf16 peak
         "mfma": {"achieved": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+                 "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                 # what the MFMA units executed (padding rows included), from
+                 # the counters, over this run's step time; null without them
+                 "executed_frac": (None if mfma_exec is None else
+                                   round(mfma_exec / (ms_per_step * 1e-3) / 1e12 /
+                                         MFMA_BF16_PEAK_TFLOPS, 5))},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
         "kernel_hash": khash,
