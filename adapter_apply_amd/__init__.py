@@ -34,6 +34,7 @@ LORA_PATH_DECODE = 1
 LORA_PATH_PREFILL = 2
 LORA_PATH_FUSED = 3
 LORA_PATH_GROUPED = 4
+LORA_PATH_RELAY = 5
 
 MOE_LORA_W13 = 0
 MOE_LORA_W2 = 1

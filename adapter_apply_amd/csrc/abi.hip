@@ -80,6 +80,15 @@ bool can_fuse(int32_t T, int32_t K, int32_t R, const int64_t *N, int32_t S, int6
     return rows_of_8(N, S, ldy, y_col_offset);
 }
 
+// Single-launch decode with the shrink split over K (relay.hip): one-wave
+// group discovery (L <= 64, T <= 1024), whole 256-column K chunks.
+bool can_relay(int32_t T, int32_t K, int32_t R, int32_t L, const int64_t *N, int32_t S,
+               int64_t ldy, int64_t y_col_offset, int32_t dtype) {
+    if (dtype != LORA_DT_BF16 || (R != 16 && R != 32) || T > 1024 || L > 64) return false;
+    if (K % kRelayKc || K / kRelayKc > kRelayMaxKc) return false;
+    return rows_of_8(N, S, ldy, y_col_offset);
+}
+
 // Slot-grouped kernels: the shrink side (K) and the expand side (y rows).
 bool can_group_sizes(int32_t T, int32_t R, int32_t dtype) {
     return dtype == LORA_DT_BF16 && R % 16 == 0 && R <= kGrpMaxRank && T <= kGrpMaxTokens;
@@ -137,7 +146,8 @@ lora_status_t grp_shrink_part(const void *x, int64_t ldx, int32_t T, int32_t K, 
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
                           int *use_prefill) {
     const bool can_prefill = dtype == LORA_DT_BF16 && R % 16 == 0;
-    if (path == LORA_PATH_DECODE || path == LORA_PATH_FUSED || path == LORA_PATH_GROUPED) {
+    if (path == LORA_PATH_DECODE || path == LORA_PATH_FUSED || path == LORA_PATH_GROUPED ||
+        path == LORA_PATH_RELAY) {
         *use_prefill = 0;
         return LORA_OK;
     }
@@ -249,7 +259,7 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
                           const void *const *A, int32_t S, int32_t L, int32_t R,
                           const int32_t *idx, const int32_t *slot_rank, int32_t dtype,
                           int32_t path, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
-    if (path == LORA_PATH_FUSED) return LORA_E_PATH;
+    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY) return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     CHECK(check_k(K, ldx));
     int use_prefill = 0;
@@ -303,7 +313,7 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
                           int32_t L, int32_t R, const int32_t *idx, const int32_t *slot_rank,
                           const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                           void *ws, size_t ws_bytes, void *stream) {
-    if (path == LORA_PATH_FUSED) return LORA_E_PATH;
+    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY) return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     int64_t ntot = 0;
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
@@ -372,25 +382,33 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
-    // Auto leaves wide outputs (an lm_head's vocabulary) to the tile kernels:
-    // the single-launch kernel recomputes a group's shrink for every
-    // 1024-column chunk, and the persistent expand streams wide rows faster
-    // than the grouped one.
+    // Auto takes the single-launch kernel with the K-split shrink for decode
+    // batches of narrow outputs when the workspace is there, else the
+    // single-launch kernel without a workspace.  Auto leaves wide outputs (an
+    // lm_head's vocabulary) to the tile kernels: the persistent expand streams
+    // wide rows faster than either single-launch kernel's expand work-groups
+    // (and the one without a workspace recomputes a group's shrink for every
+    // 1024-column chunk).
     const bool narrow = ntot <= kAutoMaxDecodeCols;
-    const bool fuse = !use_prefill && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+    const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
+    if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
+    const bool relay = path == LORA_PATH_RELAY ||
+                       (path == LORA_PATH_AUTO && !use_prefill && narrow && relay_ok && ws &&
+                        ws_bytes >= ws_layout(T, K, S, R, L).end);
+    const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                       (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
     // Auto takes the grouped kernels while their in-kernel discovery is the
     // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
     const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank && narrow;
-    const bool group = !use_prefill && !fuse && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+    const bool group = !use_prefill && !fuse && !relay && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                        (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
     if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
     // Auto, past the single-launch and discovering grouped kernels (more than
     // 64 slots, ranks past 64, or wide outputs): the MFMA prefill kernels, the
     // shrink split over K when its tiles are few, while the persistent expand
     // takes the rank.
-    if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && dtype == LORA_DT_BF16 &&
+    if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && !relay && dtype == LORA_DT_BF16 &&
         (R == 16 || R == 32 || R == 64 || R == 128) && rows_of_8(N, S, ldy, y_col_offset))
         use_prefill = 1;
     if (T == 0) return LORA_OK;
@@ -410,6 +428,13 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const SegPtrs seg = seg_ptrs(ws, wl.seg);
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
+    if (relay) {
+        // one launch; partials and counters in the workspace
+        char *w = static_cast<char *>(ws);
+        return launched(launch_dec_relay(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale,
+                                         reinterpret_cast<float *>(w + wl.partial),
+                                         reinterpret_cast<int32_t *>(w + wl.sync), st));
+    }
     if (group) {
         // two launches that derive their token groups from idx, or the
         // segment build and launches that read the groups from its table

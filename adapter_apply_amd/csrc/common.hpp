@@ -35,6 +35,13 @@ constexpr int kFusedMaxTokens = 1024;  // idx staged in LDS
 constexpr int64_t kAutoMaxDecodeCols = 16384;
 constexpr int kFusedXcds = 8;
 
+// Single-launch decode with the shrink split over K (relay.hip).
+constexpr int kRelayGroup = 32;        // tokens of one slot per shrink item
+constexpr int kRelaySubTokens = 8;     // tokens per expand item
+constexpr int kRelayKc = 256;          // K columns per shrink item
+constexpr int kRelayCols = 512;        // output columns per expand item
+constexpr int kRelayMaxKc = 32;        // K <= 8192
+
 // Slot-grouped split decode (split-K MFMA shrink, then expand).
 constexpr int kGrpTokens = 32;         // tokens of one slot per group
 constexpr int kGrpCols = 512;          // output columns per expand work-group
@@ -102,9 +109,12 @@ struct WsLayout {
     SegLayout seg;
     size_t partial;       // fp32 [n_kchunks][T][S*R]
     size_t buf;           // fp32 [S][T][R]
+    size_t sync;          // int32 counters of the single-launch split decode (left at zero)
     size_t end;
     int32_t n_kchunks;
 };
+
+int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S);
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -142,6 +152,7 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
     w.n_kchunks = (K + kDecKc - 1) / kDecKc;
     w.partial = o; o = align256(o + sizeof(float) * (size_t)w.n_kchunks * (size_t)T * S * R);
     w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
+    w.sync = o;    o = align256(o + sizeof(int32_t) * (size_t)relay_sync_ints(T, L, S));
     w.end = o;
     return w;
 }
@@ -279,6 +290,15 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,
                             hipStream_t st);
+
+int32_t relay_max_groups(int32_t T, int32_t L);
+// part: fp32 [S][K / kRelayKc][T][R]; sync: relay_sync_ints() int32, zero on
+// entry and left at zero (the last int is an error word: set when a wait ran
+// past its bound).
+hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
+                            int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
+                            const int32_t *idx, const int32_t *slot_rank, const float *scale,
+                            float *part, int32_t *sync, hipStream_t st);
 
 int32_t grp_max_groups(int32_t T, int32_t L);
 int32_t grp_kchunks(int32_t K);

@@ -1,0 +1,477 @@
+// Single-launch decode with the shrink split over K: shrink work-groups hand
+// their fp32 partial sums to expand work-groups inside the same kernel.
+//
+// The single-launch kernel of fused.hip recomputes a group's shrink in every
+// 1024-column chunk, so each of its work-groups streams the group's x rows and
+// the slot's lora_a slice (192 KB at K = 4096) through one CU.  Here the shrink
+// of a (group, slice) is done once, split over K chunks of 256 columns; every
+// expand work-group of that (group, slice) adds the chunks' partials.
+//
+// Roles.  Blocks [0, 8 * per_p) shrink, the rest expand.  Work-groups are
+// dispatched in block order, so when an expand work-group starts waiting, every
+// shrink work-group has already been dispatched; shrink work-groups wait for
+// nothing, so every wait ends.  The waits are bounded all the same: past kSpin
+// polls the work-group sets the error word of the workspace and goes on
+// (results are then not valid; nothing hangs).
+//
+// Hand-over.  A partial is stored as its fp32 bit pattern XOR kReady, a quiet
+// NaN whose payload has non-zero low bits: no sum of bf16 products yields it
+// (bf16 NaNs and the default NaN have zero low bits), so a stored word is never
+// zero and zero means "not written yet".  Words cross work-groups only through
+// agent-scope relaxed atomic stores and loads (on gfx950: global stores and
+// loads with the sc1 bit), so no L2 write-back or invalidate is needed and no
+// counter stands between the data and its reader: an expand work-group loads
+// all its words and repeats while any is still zero.  The last expand work-group to
+// read a block of 8 tokens (a counter per block, each on its own 256-byte line:
+// counters sharing a line serialise every poll and add of the batch on one
+// memory channel) writes the block back to zero, so the workspace is left as
+// it was found.
+//
+// Work items.
+//   shrink (g, kc, s): group g of at most 32 tokens of one slot (slot-major
+//     runs of a stable sort by slot), K columns [256 kc, 256 kc + 256), slice
+//     s.  4 waves, 64 K columns each: the wave loads its x rows and the slot's
+//     lora_a rows line by line (8 rows x 128 B per instruction), stages them
+//     in swizzled LDS and runs v_mfma_f32_16x16x32_bf16 (two 16-token tiles);
+//     the 4 waves are summed in order.  Output: fp32 [S][n_kc][T][R] by
+//     slot-sorted token position.
+//   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g, 512 output columns
+//     of one slice.  lora_b rows and y rows are loaded before the wait; after
+//     it the K-chunk partials are summed in a fixed order into a bf16 buffer,
+//     and v_mfma_f32_16x16x16_bf16 forms D[n][t] = B[n][:] . buf[t][:]; y is
+//     read and written 16 bytes per lane along rows (non-temporal).
+// XCD placement (block i runs on XCD i % 8): the three slices of a (g, kc)
+// share one XCD (its x rows are read once from HBM), and the four token
+// blocks of a (g, chunk) share one XCD (its lora_b rows are read once).
+#include "discover.hpp"
+
+namespace aa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;     // 4
+constexpr int kG = kRelayGroup;              // tokens per group (32)
+constexpr int kSubTok = kRelaySubTokens;     // tokens per expand work-group
+constexpr int kSubs = kG / kSubTok;          // expand work-groups per (group, chunk)
+constexpr int kKc = kRelayKc;                // K columns per shrink item (256)
+constexpr int kCols = kRelayCols;            // output columns per expand item (512)
+constexpr int kColsW = kCols / kWaves;       // 128 per wave
+constexpr int kSpin = 1 << 20;
+constexpr uint32_t kReady = 0x7fc0deadu;   // stored word = fp32 bits ^ kReady (never 0)
+constexpr int kLine = 64;                  // int32 per counter: one 256-byte line each
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+struct RelayArgs {
+    const uint16_t *x;
+    int64_t ldx;
+    uint16_t *y;
+    int64_t ldy;
+    int32_t T, K, S, L, R;
+    int32_t n_kc;        // K / kKc
+    int32_t n_chunks;    // 512-column chunks over all slices
+    int32_t max_groups;
+    int32_t per_p;       // shrink blocks per XCD
+    const int32_t *idx;
+    const int32_t *slot_rank;
+    const float *scale;
+    Slices sl;
+    int32_t chunk_start[kMaxSlices + 1];
+    float *part;         // fp32 [S][n_kc][T][R]
+    int32_t *sync;       // per (group, slice, token block) reader count, then the error word;
+                         // kLine int32 apart
+};
+
+struct RelayDisc {
+    int32_t cnt[kWave];
+    int32_t tok[kG];
+    int32_t info[6];
+};
+
+// The work item's slice parameters (kernel arguments indexed at run time),
+// resolved by an otherwise idle wave during the group discovery.
+struct RelaySlice {
+    const uint16_t *a;
+    const uint16_t *b;
+    int64_t n, off;
+    int32_t sg, c0, c1;
+};
+
+__device__ __forceinline__ bf16x8_t frag8(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ short4_t frag4(const uint2 &u) { return __builtin_bit_cast(short4_t, u); }
+
+// Byte offset of 16-byte unit u of row r in a staging area of 128-byte rows,
+// the unit XOR-swizzled with the row (fragment reads of 8 rows hit 8 bank groups).
+__device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ (r & 7)) << 4); }
+
+// Barrier for LDS traffic only: global loads and atomics stay in flight across
+// it (__syncthreads() also waits for every outstanding global access).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A load through a pointer read from LDS: the compiler cannot see that it is
+// a global address and would emit a flat load, which also counts against
+// lgkmcnt (every later LDS or scalar wait would then wait for it).
+// A pointer that every lane of the wave holds, moved into scalar registers.
+template <typename P>
+__device__ __forceinline__ P *uniform_ptr(P *p) {
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<P *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint4 ldg_as1(const void *p) {
+    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t *>(
+        reinterpret_cast<uintptr_t>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_coherent(float *p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t encode2(float a, float b) {
+    return (uint64_t)(__float_as_uint(a) ^ kReady) | ((uint64_t)(__float_as_uint(b) ^ kReady) << 32);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const float *p) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NRB>
+struct RelaySmem {
+    static constexpr int RP = 16 * NRB;                        // padded rank
+    static constexpr int RR = kG + RP;                         // staged rows per wave: x then lora_a
+    static constexpr int kStage = kWaves * RR * 128;
+    static constexpr int kPart = kWaves * kG * (RP + 4) * 4;   // aliases the staging
+    static constexpr int kProd = kStage > kPart ? kStage : kPart;
+    static constexpr int kBStage = kWaves * kColsW * RP * 2;   // expand: lora_b rows
+    static constexpr int kDelta = kSubTok * (kCols + 4) * 4;   // expand: fp32 deltas (aliases)
+    static constexpr int kCons = kBStage > kDelta ? kBStage : kDelta;
+    static constexpr int kUnion = kProd > kCons ? kProd : kCons;
+    static constexpr int PP = kSubTok * RP / 2;                // partial pairs per K chunk
+    static constexpr int Q = kThreads / PP;                    // K-chunk groups of the sum
+};
+
+// NRB: 16-rank blocks of R (1 or 2); MKC: bound on the K chunks (16 or 32).
+template <int NRB, int MKC>
+__global__ __launch_bounds__(kThreads) void k_dec_relay(RelayArgs a) {
+    using SM = RelaySmem<NRB>;
+    constexpr int RP = SM::RP, RR = SM::RR;
+    constexpr int LPS = RR / 8;                    // load instructions per wave (8 rows x 128 B)
+    constexpr int BROW = RP * 2;                   // bytes of one lora_b row
+    constexpr int BLD = kColsW * BROW / 1024;      // load instructions for a wave's lora_b rows
+    constexpr int PP = SM::PP, Q = SM::Q;
+    constexpr int KCQ = MKC / Q;                     // K chunks per summing thread, at most
+    constexpr int TW = kSubTok / kWaves;             // y rows per wave
+
+    __shared__ __attribute__((aligned(16))) char s_union[SM::kUnion];
+    __shared__ __attribute__((aligned(16))) float s_red[Q][kSubTok][RP];
+    __shared__ __attribute__((aligned(16))) uint16_t s_buf[16][RP + 8];   // MFMA tile: 16 tokens
+    __shared__ RelayDisc d;
+    __shared__ int s_flag;
+    __shared__ float s_scale[kWave];
+    __shared__ RelaySlice s_sl;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int row = lane & 15, quad = lane >> 4;
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const bool shrink = j < a.per_p;
+    int g, kc = 0, chunk = 0, sub = 0;
+    if (shrink) {
+        const int u = (j / a.S) * 8 + xcd;
+        g = u / a.n_kc;
+        kc = u % a.n_kc;
+    } else {
+        const int jc = j - a.per_p;
+        const int v = (jc / kSubs) * 8 + xcd;
+        sub = jc % kSubs;
+        g = v / a.n_chunks;
+        chunk = v % a.n_chunks;
+    }
+    if (g >= a.max_groups) g = -1;
+    {
+        const auto pick = [=](int n) { return g < n ? g : -1; };
+        // wave 1 fetches the slot scales (L <= 64) and the item's slice
+        // parameters while wave 0 finds the group
+        if (w == 1) {
+            s_scale[lane] = a.scale[min(lane, a.L - 1)];
+            if (lane == 0) {
+                int sg = 0;
+                if (shrink) sg = j % a.S;
+                else
+                    while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
+                s_sl.sg = sg;
+                s_sl.a = static_cast<const uint16_t *>(a.sl.a[sg]);
+                s_sl.b = static_cast<const uint16_t *>(a.sl.b[sg]);
+                s_sl.n = a.sl.n[sg];
+                s_sl.off = a.sl.off[sg];
+                s_sl.c0 = a.chunk_start[sg];
+                s_sl.c1 = a.chunk_start[sg + 1];
+            }
+        }
+        if (w == 0) {
+            if (a.T <= 4 * kWave) one_wave_group<kG, 4>(a.idx, a.slot_rank, a.T, a.L, a.R, d, pick);
+            else if (a.T <= 8 * kWave) one_wave_group<kG, 8>(a.idx, a.slot_rank, a.T, a.L, a.R, d, pick);
+            else one_wave_group<kG, kOneWaveChunks>(a.idx, a.slot_rank, a.T, a.L, a.R, d, pick);
+        }
+        // every wave has the plain arguments in registers before the barrier
+        // (their loads would otherwise sink past it, into the critical chain)
+        asm volatile("" ::"s"(a.x), "s"(a.y), "s"(a.ldx), "s"(a.ldy), "s"(a.part), "s"(a.sync));
+        asm volatile("" ::"s"(a.T), "s"(a.K), "s"(a.S), "s"(a.R), "s"(a.n_kc), "s"(a.max_groups));
+        __syncthreads();
+    }
+    const int s = d.info[0];
+    if (s < 0) return;
+    const int ntok = d.info[2], pos0 = d.info[3], r = d.info[5];
+    const int sg = s_sl.sg;
+    int32_t *err = a.sync + kLine * (a.max_groups * a.S * kSubs);
+
+    if (shrink) {
+        // ---- shrink item (g, kc, sg) ----------------------------------------
+        char *stage = s_union + w * (RR * 128);
+        const uint16_t *abase = uniform_ptr(s_sl.a) + (int64_t)s * a.R * a.K;
+        const int k0 = kc * kKc + w * 64 + 8 * (lane & 7);
+        uint4 v[LPS];
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            // staged row p: x row of token p (p < 32) or lora_a rank row p - 32;
+            // rows past the group or the rank re-read valid rows, dropped below
+            const int p = 8 * i + (lane >> 3);
+            const uint16_t *src = p < kG ? a.x + (int64_t)d.tok[p < ntok ? p : 0] * a.ldx
+                                         : abase + (int64_t)min(p - kG, r - 1) * a.K;
+            v[i] = ldg_as1(src + k0);
+        }
+#pragma unroll
+        for (int i = 0; i < LPS; ++i)
+            *reinterpret_cast<uint4 *>(stage + stage_off(8 * i + (lane >> 3), lane & 7)) = v[i];
+        floatx4_t acc[2][NRB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int b = 0; b < NRB; ++b) acc[t][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint4 xf = *reinterpret_cast<const uint4 *>(stage + stage_off(16 * t + row, 4 * ks + quad));
+#pragma unroll
+                for (int b = 0; b < NRB; ++b) {
+                    const uint4 af = *reinterpret_cast<const uint4 *>(stage + stage_off(kG + 16 * b + row, 4 * ks + quad));
+                    acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag8(xf), frag8(af), acc[t][b], 0, 0, 0);
+                }
+            }
+        __syncthreads();   // every wave is done with the staging (the partials alias it)
+        // acc[t][b][i]: token 16t + 4 quad + i, rank 16b + row
+        float *s_part = reinterpret_cast<float *>(s_union);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int b = 0; b < NRB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s_part[(w * kG + 16 * t + 4 * quad + i) * (RP + 4) + 16 * b + row] = acc[t][b][i];
+        __syncthreads();
+        // the 4 waves' K slices summed in order; ranks past r written as zero
+        float *dst = a.part + ((int64_t)(sg * a.n_kc + kc) * a.T + pos0) * RP;
+#pragma unroll
+        for (int q = 0; q < kG * RP / 2 / kThreads; ++q) {
+            const int e = tid + kThreads * q;
+            const int tk = e / (RP / 2), jp = 2 * (e % (RP / 2));
+            float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                v0 += s_part[(ww * kG + tk) * (RP + 4) + jp];
+                v1 += s_part[(ww * kG + tk) * (RP + 4) + jp + 1];
+            }
+            if (jp >= r) v0 = 0.f;
+            if (jp + 1 >= r) v1 = 0.f;
+            if (tk < ntok) st_coherent(dst + tk * RP + jp, encode2(v0, v1));
+        }
+        return;
+    }
+
+    // ---- expand item (g, chunk, sub) ----------------------------------------
+    const int t0 = sub * kSubTok;
+    if (t0 >= ntok) return;
+    const int ct = min(kSubTok, ntok - t0);
+    const int Ns = (int)s_sl.n;
+    const int n_base = (chunk - s_sl.c0) * kCols;
+    const int n_readers = s_sl.c1 - s_sl.c0;   // one per chunk of the slice
+    const float sc = s_scale[s];
+
+    // loads that do not depend on the shrink: lora_b rows of the wave's 128
+    // columns (one contiguous block) and the y rows of tokens TW w .. TW w + TW - 1
+    const char *bblk = reinterpret_cast<const char *>(uniform_ptr(s_sl.b) + (int64_t)s * Ns * a.R);
+    uint4 bq[BLD];
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
+        bq[i] = ldg_as1(bblk + (int64_t)nr * BROW + byte % BROW);
+    }
+    uint16_t *yrow[TW];
+    uint4 yv[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int tk = TW * w + i;
+        yrow[i] = a.y + (int64_t)d.tok[t0 + (tk < ct ? tk : 0)] * a.ldy + s_sl.off;
+        yv[i] = ldg_nt(yrow[i] + min(n_base + 8 * lane, Ns - 8));
+    }
+
+    int32_t *readers = a.sync + kLine * ((g * a.S + sg) * kSubs + sub);
+    const float *blk = a.part + ((int64_t)sg * a.n_kc * a.T + pos0 + t0) * RP;   // chunk k: + k * T * RP
+    // K-chunk partials of the block's tokens: thread (pair p, K group q) adds chunks
+    // q, q + Q, ... in order; the Q groups are then added in order.  The loads
+    // are the wait: they repeat while any word of the block is still unwritten
+    // (by the time the expand-side loads above have landed, the shrink items
+    // have mostly stored, so one round trip usually suffices).
+    {
+        const int p = tid % PP, q = tid / PP;
+        const int tk = p / (RP / 2), jp = 2 * (p % (RP / 2));
+        const float *src = blk + (tk < ct ? tk : 0) * RP + jp;
+        uint64_t pv[KCQ];
+        for (int n = 0;; ++n) {
+            bool ok = true;
+#pragma unroll
+            for (int c = 0; c < KCQ; ++c)
+                pv[c] = ld_coherent(src + (int64_t)min(q + Q * c, a.n_kc - 1) * a.T * RP);
+#pragma unroll
+            for (int c = 0; c < KCQ; ++c)
+                ok = ok && (uint32_t)pv[c] != 0u && (uint32_t)(pv[c] >> 32) != 0u;
+            if (__syncthreads_and(ok)) break;
+            if (n > kSpin) {
+                if (tid == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < KCQ; ++c)
+            if (q + Q * c < a.n_kc) {
+                v0 += __uint_as_float((uint32_t)pv[c] ^ kReady);
+                v1 += __uint_as_float((uint32_t)(pv[c] >> 32) ^ kReady);
+            }
+        s_red[q][tk][jp] = v0;
+        s_red[q][tk][jp + 1] = v1;
+    }
+    // this work-group has read the block: count it (the last reader clears
+    // it); the count is used only at the end, so its round trip overlaps the
+    // expand
+    int nread = 0;
+    if (tid == 0) nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    for (int i = tid; i < 16 * RP; i += kThreads) {
+        const int tk = i / RP, jj = i - tk * RP;
+        float v = 0.f;
+        if (tk < kSubTok) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) v += s_red[q][tk][jj];
+        }
+        if (jj >= r || tk >= ct) v = 0.f;
+        s_buf[tk][jj] = (uint16_t)f32_to_bf16_rne(v);
+    }
+    // the wave's lora_b rows into its staging area (fragment order below)
+    char *stage = s_union + w * (kColsW * BROW);
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
+    lds_barrier();
+
+    // D[n][t] = B[n][:] . buf[t][:]  (MFMA 16x16x16; tokens past the block are zero)
+    uint2 bfr[NRB];
+#pragma unroll
+    for (int ks = 0; ks < NRB; ++ks) bfr[ks] = *reinterpret_cast<const uint2 *>(&s_buf[row][16 * ks + 4 * quad]);
+    floatx4_t out[kColsW / 16];
+#pragma unroll
+    for (int nb = 0; nb < kColsW / 16; ++nb) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NRB; ++ks) {
+            const uint2 af = *reinterpret_cast<const uint2 *>(stage + (16 * nb + row) * BROW + 32 * ks + 8 * quad);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(af), frag4(bfr[ks]), acc, 0, 0, 0);
+        }
+        out[nb] = acc;
+    }
+    if (tid == 0) s_flag = nread;
+    lds_barrier();   // staging done (the deltas alias it)
+    // lane: token `row`, columns 128 w + 16 nb + 4 quad .. + 3 of the chunk
+    float *s_delta = reinterpret_cast<float *>(s_union);
+    if (row < kSubTok) {
+#pragma unroll
+        for (int nb = 0; nb < kColsW / 16; ++nb)
+            *reinterpret_cast<float4 *>(s_delta + row * (kCols + 4) + w * kColsW + 16 * nb + 4 * quad) =
+                make_float4(sc * out[nb][0], sc * out[nb][1], sc * out[nb][2], sc * out[nb][3]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const int tk = TW * w + i;
+        const int cl = 8 * lane;
+        if (tk < ct && n_base + cl < Ns) {
+            const float4 d0 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl);
+            const float4 d1 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl + 4);
+            const uint4 y0 = yv[i];
+            uint4 o;
+            o.x = pack_bf16x2(bf16_lo(y0.x) + d0.x, bf16_hi(y0.x) + d0.y);
+            o.y = pack_bf16x2(bf16_lo(y0.y) + d0.z, bf16_hi(y0.y) + d0.w);
+            o.z = pack_bf16x2(bf16_lo(y0.z) + d1.x, bf16_hi(y0.z) + d1.y);
+            o.w = pack_bf16x2(bf16_lo(y0.w) + d1.z, bf16_hi(y0.w) + d1.w);
+            stg_nt(yrow[i] + n_base + cl, o);
+        }
+    }
+    // the last reader of the block writes it back to zero for the next call
+    if (s_flag == n_readers - 1) {
+        for (int e = tid; e < a.n_kc * ct * (RP / 2); e += kThreads) {
+            const int k = e / (ct * (RP / 2)), rem = e - k * (ct * (RP / 2));
+            st_coherent(const_cast<float *>(blk) + (int64_t)k * a.T * RP + 2 * rem, 0ull);
+        }
+        if (tid == 0) __hip_atomic_store(readers, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+}  // namespace
+
+int32_t relay_max_groups(int32_t T, int32_t L) {
+    return (T + kRelayGroup - 1) / kRelayGroup + (T < L ? T : L);
+}
+
+int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S) {
+    return kLine * (relay_max_groups(T, L) * S * kSubs + 1);
+}
+
+hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
+                            int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
+                            const int32_t *idx, const int32_t *slot_rank, const float *scale,
+                            float *part, int32_t *sync, hipStream_t st) {
+    RelayArgs a;
+    a.x = static_cast<const uint16_t *>(x); a.ldx = ldx;
+    a.y = static_cast<uint16_t *>(y); a.ldy = ldy;
+    a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
+    a.idx = idx; a.slot_rank = slot_rank; a.scale = scale; a.sl = sl;
+    a.part = part; a.sync = sync;
+    int c = 0;
+    for (int s = 0; s < S; ++s) {
+        a.chunk_start[s] = c;
+        c += (int)((sl.n[s] + kCols - 1) / kCols);
+    }
+    for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
+    a.n_chunks = c;
+    a.n_kc = K / kKc;
+    a.max_groups = relay_max_groups(T, L);
+    a.per_p = (a.max_groups * a.n_kc + 7) / 8 * S;
+    const int per_c = (a.max_groups * c + 7) / 8 * kSubs;
+    dim3 grid((unsigned)(8 * (a.per_p + per_c)));
+    const bool few = a.n_kc <= 16;
+    if (R == 16) {
+        if (few) hipLaunchKernelGGL((k_dec_relay<1, 16>), grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_dec_relay<1, kRelayMaxKc>), grid, dim3(kThreads), 0, st, a);
+    } else {
+        if (few) hipLaunchKernelGGL((k_dec_relay<2, 16>), grid, dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_dec_relay<2, kRelayMaxKc>), grid, dim3(kThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace aa

@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "many", "moe", "logits"])
-    p.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "decode", "prefill"],
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "relay", "grouped", "decode", "prefill"],
                    help="force a decode path (development runs; the headline uses auto)")
     p.add_argument("--moe-tokens", type=int, default=2048,
                    help="tokens of the fused-MoE workload (2048 by default)")
@@ -399,7 +399,8 @@ def main():
     torch.cuda.synchronize()
 
     step_path = {"auto": aa.LORA_PATH_AUTO, "fused": aa.LORA_PATH_FUSED, "prefill": aa.LORA_PATH_PREFILL,
-                 "grouped": aa.LORA_PATH_GROUPED, "decode": aa.LORA_PATH_DECODE}[args.path]
+                 "grouped": aa.LORA_PATH_GROUPED, "decode": aa.LORA_PATH_DECODE,
+                 "relay": aa.LORA_PATH_RELAY}[args.path]
 
     def step(d):
         aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
@@ -413,18 +414,22 @@ def main():
                and c.T // min(c.T, c.L) >= 64)
     rows8 = all(n % 8 == 0 for n in c.N)
     narrow = sum(c.N) <= 16384
-    fused = (not prefill and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
+    # the single-launch kernel with the K-split shrink (the step passes a workspace)
+    relay = (not prefill and c.dtype == "bf16" and c.R in (16, 32) and c.T <= 1024 and c.L <= 64
+             and c.K % 256 == 0 and c.K // 256 <= 32 and rows8 and narrow)
+    fused = (not prefill and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
              and c.T <= 1024 and c.K % 1024 == 0 and rows8 and narrow)
-    grouped = (not prefill and not fused and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
+    grouped = (not prefill and not fused and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
                and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8
                and narrow)
     # auto past those kernels: the prefill (MFMA) kernels, the shrink split over K
-    if (not prefill and not fused and not grouped and c.dtype == "bf16" and c.R in (16, 32, 64, 128)
-            and rows8):
+    if (not prefill and not fused and not grouped and not relay and c.dtype == "bf16"
+            and c.R in (16, 32, 64, 128) and rows8):
         prefill = True
     if args.path != "auto":
         prefill = args.path == "prefill"
         fused, grouped = args.path == "fused", args.path == "grouped"
+        relay = args.path == "relay"
     fold = not prefill and math.ceil(c.K / 256) * c.R <= 512
     part = aa.LORA_FLAG_PARTIAL
     ready = aa.LORA_FLAG_SEGMENTS_READY
@@ -514,8 +519,9 @@ def main():
 
     # ---- per-kernel durations, live, with events around graphs of one kernel
     per_kernel = {}
-    if fused:
-        kernel_calls = [("fused", step)]      # the whole step is one kernel
+    if fused or relay:
+        # the whole step is one kernel
+        kernel_calls = [("relay" if relay else "fused", step)]
     elif grouped:
         kernel_calls = [("segments", segments_only)] if grouped_tab else []
         if grouped_buf:
@@ -549,8 +555,8 @@ def main():
     torch.cuda.synchronize()
 
     ab = algorithmic_bytes(c, args.shared_a)
-    if fused:
-        dom, dom_bytes = "fused", ab["fused"]
+    if fused or relay:
+        dom, dom_bytes = ("relay" if relay else "fused"), ab["fused"]
     else:
         dom = max((k for k in ("shrink", "shrink+reduce", "expand") if k in per_kernel),
                   key=lambda k: per_kernel[k])
@@ -594,7 +600,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": round(per_kernel[dom], 3)},
         "kernels_us": {k: round(v, 3) for k, v in per_kernel.items()},
-        "step_algorithmic_GBps": round((ab["fused"] if fused else
+        "step_algorithmic_GBps": round((ab["fused"] if fused or relay else
                                         ab["shrink"] + ab["expand"] if grouped else ab["total"]) /
                                        (ms_per_step * 1e-3) / 1e9, 1),
         # dense bf16 MFMA work of the step (2 * rank * (K * slices + N_total)

@@ -43,7 +43,9 @@
  *            decode path only).  The intermediate buffer is always fp32.
  *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
  *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
- *            otherwise lora_apply_packed takes FUSED, else GROUPED (when also
+ *            otherwise lora_apply_packed takes RELAY where its shapes allow,
+ *            ws holds lora_workspace_size() bytes and the slices sum to at
+ *            most 16384 columns, else FUSED, else GROUPED (when also
  *            L <= 64 and R <= 64), where the shapes allow and the slices sum
  *            to at most 16384 columns, else PREFILL for
  *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0
@@ -68,8 +70,16 @@
  *            FUSED forces the single-launch decode kernel of
  *            lora_apply_packed (bf16, R % 16 == 0, R <= 32, T <= 1024,
  *            K % 1024 == 0, N, ldy and y_col_offset % 8 == 0; it needs no
- *            workspace).  A forced path that cannot take the arguments
- *            returns LORA_E_PATH.
+ *            workspace);
+ *            RELAY forces the single-launch decode kernel of
+ *            lora_apply_packed whose shrink is split over K chunks of 256
+ *            columns and handed to the expand work-groups of the same launch
+ *            through the workspace (bf16, R == 16 or 32, T <= 1024, L <= 64,
+ *            K % 256 == 0, K <= 8192, N, ldy and y_col_offset % 8 == 0; the
+ *            workspace is required, its partial sums and counters are zero
+ *            again when the kernel ends; lora_shrink / lora_expand reject it).
+ *            A forced path that cannot take the arguments returns
+ *            LORA_E_PATH.
  *   ws       device workspace of at least lora_workspace_size() bytes,
  *            256-byte aligned, owned by the caller.  Calls sharing a
  *            workspace must be ordered on one stream.  The workspace must be
@@ -124,6 +134,7 @@ typedef int32_t lora_status_t;
 #define LORA_PATH_PREFILL  2
 #define LORA_PATH_FUSED    3
 #define LORA_PATH_GROUPED  4
+#define LORA_PATH_RELAY    5
 
 #define LORA_FLAG_SEGMENTS_READY 1u
 #define LORA_FLAG_ACTIVE_ONLY    2u

@@ -112,8 +112,18 @@ def _apply(**kw):
     (dict(path=aa.LORA_PATH_GROUPED, ws=None), aa.LORA_E_NULL),
     (dict(path=aa.LORA_PATH_GROUPED, wsb=1024), aa.LORA_E_WORKSPACE),
     (dict(path=aa.LORA_PATH_FUSED, ldy=6148), aa.LORA_E_PATH),
-    (dict(path=5), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, R=64), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, R=24), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, T=1025), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, L=65), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, K=4104, ldx=4104), aa.LORA_E_PATH),     # K % 256
+    (dict(path=aa.LORA_PATH_RELAY, K=8448, ldx=8448), aa.LORA_E_PATH),     # 33 K chunks
+    (dict(path=aa.LORA_PATH_RELAY, ldy=6148), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
+    (dict(path=aa.LORA_PATH_RELAY, ws=None), aa.LORA_E_NULL),
+    (dict(path=aa.LORA_PATH_RELAY, wsb=1024), aa.LORA_E_WORKSPACE),
     (dict(path=6), aa.LORA_E_PATH),
+    (dict(path=7), aa.LORA_E_PATH),
 ])
 def test_apply_rejects_bad_arguments(kw, code):
     assert _apply(**kw) == code
@@ -137,6 +147,8 @@ def test_shrink_expand_validation():
     # the fused kernel has no separate shrink; the grouped one takes rank <= 64
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
                            aa.LORA_PATH_FUSED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
+                           aa.LORA_PATH_RELAY, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 144, FAKE, None, 1,
                            aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     # the partial-sum hand-off stops at rank 64 on the grouped path

@@ -18,8 +18,8 @@ import synth  # noqa: E402
 from tests import bounds  # noqa: E402
 from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
 
-DEC, PRE, FUS, GRP = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
-                      aa.LORA_PATH_GROUPED)
+DEC, PRE, FUS, GRP, RLY = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
+                           aa.LORA_PATH_GROUPED, aa.LORA_PATH_RELAY)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -78,9 +78,17 @@ def groupable(c):
             and c.K % 64 == 0 and c.K <= 8192 and all(n % 8 == 0 for n in c.N))
 
 
+def relayable(c):
+    """Shapes the single-launch decode kernel with the K-split shrink takes."""
+    return (c.dtype == "bf16" and c.R in (16, 32) and c.T <= 1024 and c.L <= 64
+            and c.K % 256 == 0 and c.K <= 8192 and all(n % 8 == 0 for n in c.N))
+
+
 def skip_unless_path_takes(path, c):
     if path == FUS and not fusable(c):
         pytest.skip("shape outside the single-launch kernel")
+    if path == RLY and not relayable(c):
+        pytest.skip("shape outside the single-launch K-split kernel")
     if path == GRP and not groupable(c):
         pytest.skip("shape outside the slot-grouped kernels")
 
@@ -104,7 +112,7 @@ INTEGER_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY])
 @pytest.mark.parametrize("seed,T,K,N,R,L", INTEGER_CASES)
 def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
@@ -120,7 +128,7 @@ def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY])
 def test_decode_config_qkv(oracle_mod, path):
     """256 tokens, hidden 4096, QKV 4096/1024/1024, rank 16, 8 slots, 10% idx=-1."""
     c = synth.config_decode()
@@ -178,7 +186,7 @@ def test_logits_vocab_32000_every_path(oracle_mod):
     one oracle result."""
     c = synth.config_logits(vocab=32000)
     ref = oracle_y(oracle_mod, c)
-    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP):
+    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY):
         log(f"case logits vocab=32000 path={path}")
         d = LinearOnDevice(c)
         d.apply(path)
@@ -346,7 +354,7 @@ def test_all_tokens_without_adapter_unchanged():
     c = synth.config_decode(T=64)
     c.idx[:] = -1
     d = LinearOnDevice(c)
-    for path in (DEC, PRE, FUS, GRP):
+    for path in (DEC, PRE, FUS, GRP, RLY):
         d.apply(path)
         y = d.y_host()
         assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
@@ -359,7 +367,7 @@ def test_zero_b_identity_and_invalid_slots(oracle_mod):
     c.idx[::11] = 100
     c.slot_rank[3] = 0    # empty slot
     c.B = [np.zeros_like(b) for b in c.B]
-    for path in (DEC, PRE, FUS, GRP):
+    for path in (DEC, PRE, FUS, GRP, RLY):
         d = LinearOnDevice(c)
         d.apply(path)
         y = d.y_host()
@@ -375,7 +383,7 @@ def test_column_offset_and_wide_rows(oracle_mod):
     wide = rng.standard_normal((c.T, 200)).astype(np.float32)
     wide = synth.round_bf16(wide)
     off = 40
-    for path in (DEC, PRE, FUS, GRP):
+    for path in (DEC, PRE, FUS, GRP, RLY):
         yw = dev(wide, torch.bfloat16)
         d = LinearOnDevice(c, guard=False)
         aa.lora_apply_packed(yw, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, y_col_offset=off,
@@ -410,7 +418,7 @@ def test_segments_reused_across_layers(oracle_mod, T, L):
 
 
 @pytest.mark.parametrize("cfg,path", [("many", DEC), ("decode", FUS), ("decode", PRE),
-                                      ("decode", GRP)])
+                                      ("decode", GRP), ("decode", RLY)])
 def test_deterministic_run_twice(cfg, path):
     c = synth.config_many(T=512) if cfg == "many" else synth.config_decode()
     outs = []
@@ -421,7 +429,7 @@ def test_deterministic_run_twice(cfg, path):
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("path", [FUS, GRP])
+@pytest.mark.parametrize("path", [FUS, GRP, RLY])
 def test_fused_skewed_slots(oracle_mod, path):
     """All tokens on one slot (many groups of one slot) and ranks below 16."""
     rng = np.random.default_rng(12)
@@ -438,10 +446,10 @@ def test_fused_skewed_slots(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [FUS, GRP])
+@pytest.mark.parametrize("path", [FUS, GRP, RLY])
 def test_fused_rejects_unsupported(path):
-    # rank 128 is past the single-launch kernel, rank 160 past the grouped ones
-    c = synth.config_many(T=64, R=128 if path == FUS else 160)
+    # rank 128 is past the single-launch kernels, rank 160 past the grouped ones
+    c = synth.config_many(T=64, R=160 if path == GRP else 128)
     d = LinearOnDevice(c, guard=False)
     with pytest.raises(aa.LoraError) as e:
         d.apply(path)
@@ -481,7 +489,7 @@ def on_device_shared_a(c):
     return d
 
 
-@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY])
 @pytest.mark.parametrize("seed,T,K,N,R,L", [
     (51, 600, 1024, [256, 64, 64], 16, 3),     # long runs per slot: auto takes the tile kernels
     (52, 300, 2048, [512, 512], 64, 100),      # 100 slots: auto takes the tile kernels, K split
@@ -523,7 +531,7 @@ def test_shared_lora_a_prefill_shape(oracle_mod):
 MLA_K, MLA_N = 7168, [1536, 576]
 
 
-@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP])
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY])
 @pytest.mark.parametrize("seed,T,R,L", [
     (55, 48, 16, 4),       # decode batch: auto takes the single-launch kernel
     (56, 900, 64, 6),      # long runs per slot: auto takes the tile kernels, one shrink
@@ -566,3 +574,32 @@ def test_zero_tokens_noop():
     aa.lora_apply_packed(y0, x0, d.A, d.B, d.idx[:0], d.rank, d.scale, d.ws)
     torch.cuda.synchronize()
     assert canaries_intact(d.yfull)
+
+
+@pytest.mark.parametrize("T,L,R", [(256, 8, 16), (700, 4, 32), (33, 64, 16), (1024, 64, 32)])
+def test_relay_repeated_calls_leave_counters_zero(oracle_mod, T, L, R):
+    """Calls in a row on one workspace: each equals the first bit for bit and
+    within tolerance of the oracle, and the workspace (partial sums, reader
+    counters, the error word of the bounded waits) is all zero again after
+    every call."""
+    rng = np.random.default_rng(T + L)
+    idx = rng.integers(-1, L, T).astype(np.int32)
+    c = synth.make_linear("relay", T, 2048, [1024, 256, 264], R, L, idx,
+                          rng.choice([R, R // 2, 8], L).astype(np.int32), [2.0] * L, "bf16",
+                          seed=T)
+    d = LinearOnDevice(c, guard=False)
+    assert d.ws.numel() == aa.lora_workspace_size(T, c.K, c.S, c.R, c.L)
+    first = None
+    for call in range(3):
+        log(f"case relay repeat T={T} L={L} R={R} call={call}")
+        d.reset_y()
+        d.apply(RLY)
+        y = d.y_host()
+        nz = int(torch.count_nonzero(d.ws))
+        assert nz == 0, f"{nz} workspace bytes left non-zero"
+        if first is None:
+            first = y
+            bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+            assert_passthrough(c, y)
+        else:
+            assert np.array_equal(y.view(np.uint32), first.view(np.uint32))
