@@ -429,11 +429,12 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
     if (relay) {
-        // one launch; partials and counters in the workspace
+        // one launch; partials and counters in the region at the end of ws
+        const RelayRegion rr = relay_region(ws_bytes, T, K, S, R, L);
         char *w = static_cast<char *>(ws);
         return launched(launch_dec_relay(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale,
-                                         reinterpret_cast<float *>(w + wl.partial),
-                                         reinterpret_cast<int32_t *>(w + wl.sync), st));
+                                         reinterpret_cast<float *>(w + rr.part),
+                                         reinterpret_cast<int32_t *>(w + rr.sync), st));
     }
     if (group) {
         // two launches that derive their token groups from idx, or the

@@ -109,14 +109,39 @@ struct WsLayout {
     SegLayout seg;
     size_t partial;       // fp32 [n_kchunks][T][S*R]
     size_t buf;           // fp32 [S][T][R]
-    size_t sync;          // int32 counters of the single-launch split decode (left at zero)
-    size_t end;
+    size_t relay;         // bytes of the single-launch split decode's region (see relay_region)
+    size_t end;           // the regions above, then the relay region
     int32_t n_kchunks;
 };
 
 int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S);
 
+
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The single-launch split decode's region: its fp32 partials [S][K/256][T][R]
+// and then its counters.  The kernel needs it all zero on entry and leaves it
+// all zero, so nothing else may write there: it sits at the END of the
+// caller's buffer, while every other region starts at offset 0.  Every
+// region grows with each size argument, so a workspace of
+// lora_workspace_size() at the largest sizes a caller uses keeps this region
+// clear of every other call's regions, whatever their shapes.
+struct RelayRegion {
+    size_t part;          // offset of the partials
+    size_t sync;          // offset of the counters
+};
+inline size_t relay_part_bytes(int32_t T, int32_t K, int32_t S, int32_t R) {
+    return align256(sizeof(float) * (size_t)((K + kRelayKc - 1) / kRelayKc) * T * S * R);
+}
+inline size_t relay_bytes(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L) {
+    return relay_part_bytes(T, K, S, R) + align256(sizeof(int32_t) * (size_t)relay_sync_ints(T, L, S));
+}
+inline RelayRegion relay_region(size_t ws_bytes, int32_t T, int32_t K, int32_t S, int32_t R, int32_t L) {
+    RelayRegion r;
+    r.part = (ws_bytes - relay_bytes(T, K, S, R, L)) & ~size_t(255);
+    r.sync = r.part + relay_part_bytes(T, K, S, R);
+    return r;
+}
 
 inline int32_t max_tiles(int32_t T, int32_t L, int32_t tile) {
     // sum over slots of ceil(c_s / tile) <= T / tile + (number of non-empty slots)
@@ -152,8 +177,8 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
     w.n_kchunks = (K + kDecKc - 1) / kDecKc;
     w.partial = o; o = align256(o + sizeof(float) * (size_t)w.n_kchunks * (size_t)T * S * R);
     w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
-    w.sync = o;    o = align256(o + sizeof(int32_t) * (size_t)relay_sync_ints(T, L, S));
-    w.end = o;
+    w.relay = relay_bytes(T, K, S, R, L);
+    w.end = o + w.relay;
     return w;
 }
 
@@ -292,9 +317,9 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
                             hipStream_t st);
 
 int32_t relay_max_groups(int32_t T, int32_t L);
-// part: fp32 [S][K / kRelayKc][T][R]; sync: relay_sync_ints() int32, zero on
-// entry and left at zero (the last int is an error word: set when a wait ran
-// past its bound).
+// part: fp32 [S][K / kRelayKc][T][R]; sync: relay_sync_ints() int32; both zero
+// on entry and left at zero (the last int is an error word: set when a wait
+// ran past its bound).
 hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,

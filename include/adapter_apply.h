@@ -76,8 +76,14 @@
  *            columns and handed to the expand work-groups of the same launch
  *            through the workspace (bf16, R == 16 or 32, T <= 1024, L <= 64,
  *            K % 256 == 0, K <= 8192, N, ldy and y_col_offset % 8 == 0; the
- *            workspace is required, its partial sums and counters are zero
- *            again when the kernel ends; lora_shrink / lora_expand reject it).
+ *            workspace is required: the kernel keeps its partial sums and
+ *            counters in a region at the END of ws (ws_bytes decides where),
+ *            needs that region zero on entry and leaves it zero; the other
+ *            linear calls write only from the start of ws, so a workspace
+ *            shared by calls of several shapes must hold
+ *            lora_workspace_size() at the largest value of each size
+ *            argument, and it must not be shared with the fused-MoE calls;
+ *            lora_shrink / lora_expand reject this path).
  *            A forced path that cannot take the arguments returns
  *            LORA_E_PATH.
  *   ws       device workspace of at least lora_workspace_size() bytes,

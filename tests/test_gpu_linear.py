@@ -603,3 +603,35 @@ def test_relay_repeated_calls_leave_counters_zero(oracle_mod, T, L, R):
             assert_passthrough(c, y)
         else:
             assert np.array_equal(y.view(np.uint32), first.view(np.uint32))
+
+
+def test_relay_after_other_paths_on_one_workspace(oracle_mod):
+    """One workspace, sized for the largest call, serves calls of other paths
+    and shapes that leave split-K partial sums in it; the single-launch K-split
+    kernel keeps its zero-on-entry region at the end of the buffer, clear of
+    every other call's regions, so its results stay exact to tolerance."""
+    rng = np.random.default_rng(77)
+    big = synth.make_linear("big", 1500, 4096, [1024, 264, 256], 16, 100,
+                            rng.integers(-1, 100, 1500).astype(np.int32),
+                            rng.choice([16, 8], 100).astype(np.int32), [1.0] * 100, "bf16", seed=78)
+    ws = aa.alloc_workspace(big.T, big.K, big.S, big.R, big.L)
+    cases = [synth.config_decode(T=256), synth.config_decode(T=64)]
+    for i, c in enumerate(cases):
+        cases[i] = synth.make_linear(f"small{i}", c.T, 4096, big.N, 16, 8, c.idx, c.slot_rank,
+                                     c.scale, "bf16", seed=80 + i)
+    db = LinearOnDevice(big, guard=False)
+    ds = [LinearOnDevice(c, guard=False) for c in cases]
+    for rnd in range(2):
+        for path in (PRE, DEC):
+            log(f"case shared ws round={rnd} big path={path}")
+            db.reset_y()
+            aa.lora_apply_packed(db.y, db.x, db.A, db.B, db.idx, db.rank, db.scale, ws, path=path)
+            torch.cuda.synchronize()
+        for c, d in zip(cases, ds):
+            aa.lora_apply_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, ws, path=DEC)
+            d.reset_y()
+            log(f"case shared ws round={rnd} relay T={c.T}")
+            aa.lora_apply_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, ws, path=RLY)
+            y = d.y_host()
+            bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
+            assert_passthrough(c, y)
