@@ -13,6 +13,8 @@ constexpr int32_t kPrefillMinPerSlot = 64;
 // Decode: the expand adds the shrink's K-chunk partials itself (one launch
 // fewer) while a tile's partials stay small; beyond that a reduce kernel runs.
 constexpr int32_t kFoldMaxChunkRank = 512;   // n_kchunks * R
+// Auto: wide outputs take the single-launch K-split kernel up to this many tokens.
+constexpr int32_t kRelayWideMaxTokens = 256;
 
 inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -383,17 +385,19 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
     int use_prefill = 0;
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
     // Auto takes the single-launch kernel with the K-split shrink for decode
-    // batches of narrow outputs when the workspace is there, else the
-    // single-launch kernel without a workspace.  Auto leaves wide outputs (an
-    // lm_head's vocabulary) to the tile kernels: the persistent expand streams
-    // wide rows faster than either single-launch kernel's expand work-groups
-    // (and the one without a workspace recomputes a group's shrink for every
+    // batches when the workspace is there: for narrow outputs, and for wide
+    // ones (an lm_head's vocabulary) up to 256 tokens, where its 16-token
+    // expand items beat the tile kernels (128256 columns: 44 against 56 us).
+    // Without a workspace narrow outputs take the other single-launch kernel;
+    // past these, wide outputs go to the tile kernels (the single-launch
+    // kernel without a workspace recomputes a group's shrink for every
     // 1024-column chunk).
     const bool narrow = ntot <= kAutoMaxDecodeCols;
     const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
     if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
     const bool relay = path == LORA_PATH_RELAY ||
-                       (path == LORA_PATH_AUTO && !use_prefill && narrow && relay_ok && ws &&
+                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok &&
+                        (narrow || T <= kRelayWideMaxTokens) && ws &&
                         ws_bytes >= ws_layout(T, K, S, R, L).end);
     const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                       (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));

@@ -37,7 +37,6 @@ constexpr int kFusedXcds = 8;
 
 // Single-launch decode with the shrink split over K (relay.hip).
 constexpr int kRelayGroup = 32;        // tokens of one slot per shrink item
-constexpr int kRelaySubTokens = 8;     // tokens per expand item
 constexpr int kRelayKc = 256;          // K columns per shrink item
 constexpr int kRelayCols = 512;        // output columns per expand item
 constexpr int kRelayMaxKc = 32;        // K <= 8192

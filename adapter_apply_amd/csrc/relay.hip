@@ -22,7 +22,7 @@
 // loads with the sc1 bit), so no L2 write-back or invalidate is needed and no
 // counter stands between the data and its reader: an expand work-group loads
 // all its words and repeats while any is still zero.  The last expand work-group to
-// read a block of 8 tokens (a counter per block, each on its own 256-byte line:
+// read a block of tokens (a counter per block, each on its own 256-byte line:
 // counters sharing a line serialise every poll and add of the batch on one
 // memory channel) writes the block back to zero, so the workspace is left as
 // it was found.
@@ -35,8 +35,8 @@
 //     in swizzled LDS and runs v_mfma_f32_16x16x32_bf16 (two 16-token tiles);
 //     the 4 waves are summed in order.  Output: fp32 [S][n_kc][T][R] by
 //     slot-sorted token position.
-//   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g, 512 output columns
-//     of one slice.  lora_b rows and y rows are loaded before the wait; after
+//   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g (16b .. 16b + 15 for
+//     outputs wider than 16384 columns), 512 output columns of one slice.  lora_b rows and y rows are loaded before the wait; after
 //     it the K-chunk partials are summed in a fixed order into a bf16 buffer,
 //     and v_mfma_f32_16x16x16_bf16 forms D[n][t] = B[n][:] . buf[t][:]; y is
 //     read and written 16 bytes per lane along rows (non-temporal).
@@ -52,8 +52,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;     // 4
 constexpr int kG = kRelayGroup;              // tokens per group (32)
-constexpr int kSubTok = kRelaySubTokens;     // tokens per expand work-group
-constexpr int kSubs = kG / kSubTok;          // expand work-groups per (group, chunk)
+constexpr int kMaxSubs = kG / 8;             // expand work-groups per (group, chunk), at most
 constexpr int kKc = kRelayKc;                // K columns per shrink item (256)
 constexpr int kCols = kRelayCols;            // output columns per expand item (512)
 constexpr int kColsW = kCols / kWaves;       // 128 per wave
@@ -139,7 +138,7 @@ __device__ __forceinline__ uint64_t ld_coherent(const float *p) {
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NRB>
+template <int NRB, int kSubTok>
 struct RelaySmem {
     static constexpr int RP = 16 * NRB;                        // padded rank
     static constexpr int RR = kG + RP;                         // staged rows per wave: x then lora_a
@@ -154,10 +153,15 @@ struct RelaySmem {
     static constexpr int Q = kThreads / PP;                    // K-chunk groups of the sum
 };
 
-// NRB: 16-rank blocks of R (1 or 2); MKC: bound on the K chunks (16 or 32).
-template <int NRB, int MKC>
-__global__ __launch_bounds__(kThreads) void k_dec_relay(RelayArgs a) {
-    using SM = RelaySmem<NRB>;
+// NRB: 16-rank blocks of R (1 or 2); MKC: bound on the K chunks (16 or 32);
+// SUB: tokens per expand item (8, or 16 for wide outputs, where fewer expand
+// work-groups re-read each lora_b block; at rank 16 and K <= 4096 an
+// occupancy bound keeps four work-groups per CU without spills).
+template <int NRB, int MKC, int SUB>
+__global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 : 1) void k_dec_relay(RelayArgs a) {
+    constexpr int kSubTok = SUB;
+    constexpr int kSubs = kG / SUB;
+    using SM = RelaySmem<NRB, SUB>;
     constexpr int RP = SM::RP, RR = SM::RR;
     constexpr int LPS = RR / 8;                    // load instructions per wave (8 rows x 128 B)
     constexpr int BROW = RP * 2;                   // bytes of one lora_b row
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_relay(RelayArgs a) {
     if (s < 0) return;
     const int ntok = d.info[2], pos0 = d.info[3], r = d.info[5];
     const int sg = s_sl.sg;
-    int32_t *err = a.sync + kLine * (a.max_groups * a.S * kSubs);
+    int32_t *err = a.sync + kLine * (a.max_groups * a.S * kMaxSubs);
 
     if (shrink) {
         // ---- shrink item (g, kc, sg) ----------------------------------------
@@ -438,7 +442,7 @@ int32_t relay_max_groups(int32_t T, int32_t L) {
 }
 
 int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S) {
-    return kLine * (relay_max_groups(T, L) * S * kSubs + 1);
+    return kLine * (relay_max_groups(T, L) * S * kMaxSubs + 1);
 }
 
 hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
@@ -461,16 +465,22 @@ hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, in
     a.n_kc = K / kKc;
     a.max_groups = relay_max_groups(T, L);
     a.per_p = (a.max_groups * a.n_kc + 7) / 8 * S;
-    const int per_c = (a.max_groups * c + 7) / 8 * kSubs;
+    // wide outputs: 16-token expand items (half the lora_b block reads)
+    int64_t ntot = 0;
+    for (int s = 0; s < S; ++s) ntot += sl.n[s];
+    const bool wide = ntot > kAutoMaxDecodeCols;
+    const int per_c = (a.max_groups * c + 7) / 8 * (wide ? kG / 16 : kG / 8);
     dim3 grid((unsigned)(8 * (a.per_p + per_c)));
     const bool few = a.n_kc <= 16;
+#define AA_RELAY(NRB, MKC, SUB) hipLaunchKernelGGL((k_dec_relay<NRB, MKC, SUB>), grid, dim3(kThreads), 0, st, a)
     if (R == 16) {
-        if (few) hipLaunchKernelGGL((k_dec_relay<1, 16>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_dec_relay<1, kRelayMaxKc>), grid, dim3(kThreads), 0, st, a);
+        if (few) { if (wide) AA_RELAY(1, 16, 16); else AA_RELAY(1, 16, 8); }
+        else { if (wide) AA_RELAY(1, kRelayMaxKc, 16); else AA_RELAY(1, kRelayMaxKc, 8); }
     } else {
-        if (few) hipLaunchKernelGGL((k_dec_relay<2, 16>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_dec_relay<2, kRelayMaxKc>), grid, dim3(kThreads), 0, st, a);
+        if (few) { if (wide) AA_RELAY(2, 16, 16); else AA_RELAY(2, 16, 8); }
+        else { if (wide) AA_RELAY(2, kRelayMaxKc, 16); else AA_RELAY(2, kRelayMaxKc, 8); }
     }
+#undef AA_RELAY
     return hipGetLastError();
 }
 

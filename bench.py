@@ -416,7 +416,7 @@ def main():
     narrow = sum(c.N) <= 16384
     # the single-launch kernel with the K-split shrink (the step passes a workspace)
     relay = (not prefill and c.dtype == "bf16" and c.R in (16, 32) and c.T <= 1024 and c.L <= 64
-             and c.K % 256 == 0 and c.K // 256 <= 32 and rows8 and narrow)
+             and c.K % 256 == 0 and c.K // 256 <= 32 and rows8 and (narrow or c.T <= 256))
     fused = (not prefill and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
              and c.T <= 1024 and c.K % 1024 == 0 and rows8 and narrow)
     grouped = (not prefill and not fused and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64

@@ -44,8 +44,9 @@
  *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
  *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
  *            otherwise lora_apply_packed takes RELAY where its shapes allow,
- *            ws holds lora_workspace_size() bytes and the slices sum to at
- *            most 16384 columns, else FUSED, else GROUPED (when also
+ *            ws holds lora_workspace_size() bytes and either the slices sum
+ *            to at most 16384 columns or T <= 256, else FUSED, else GROUPED
+ *            (when also
  *            L <= 64 and R <= 64), where the shapes allow and the slices sum
  *            to at most 16384 columns, else PREFILL for
  *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0

@@ -576,22 +576,24 @@ def test_zero_tokens_noop():
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("T,L,R", [(256, 8, 16), (700, 4, 32), (33, 64, 16), (1024, 64, 32)])
-def test_relay_repeated_calls_leave_counters_zero(oracle_mod, T, L, R):
+@pytest.mark.parametrize("T,L,R,N", [(256, 8, 16, [1024, 256, 264]), (700, 4, 32, [1024, 256, 264]),
+                                     (33, 64, 16, [1024, 256, 264]), (1024, 64, 32, [1024, 256, 264]),
+                                     (256, 8, 16, [20480]), (200, 5, 32, [16384, 8])])
+def test_relay_repeated_calls_leave_counters_zero(oracle_mod, T, L, R, N):
     """Calls in a row on one workspace: each equals the first bit for bit and
     within tolerance of the oracle, and the workspace (partial sums, reader
     counters, the error word of the bounded waits) is all zero again after
     every call."""
     rng = np.random.default_rng(T + L)
     idx = rng.integers(-1, L, T).astype(np.int32)
-    c = synth.make_linear("relay", T, 2048, [1024, 256, 264], R, L, idx,
+    c = synth.make_linear("relay", T, 2048, N, R, L, idx,
                           rng.choice([R, R // 2, 8], L).astype(np.int32), [2.0] * L, "bf16",
                           seed=T)
     d = LinearOnDevice(c, guard=False)
     assert d.ws.numel() == aa.lora_workspace_size(T, c.K, c.S, c.R, c.L)
     first = None
     for call in range(3):
-        log(f"case relay repeat T={T} L={L} R={R} call={call}")
+        log(f"case relay repeat T={T} L={L} R={R} N={N} call={call}")
         d.reset_y()
         d.apply(RLY)
         y = d.y_host()
