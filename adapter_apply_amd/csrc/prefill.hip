@@ -407,9 +407,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     uint4 yv[NY];
 #pragma unroll
     for (int i = 0; i < NY; ++i) {
+        // rows past the tile's tokens all read one 16-byte unit: an
+        // instruction of padding rows costs one request
         const int q = i * kThreads + tid;
         const int row = q / YU, col = n_base + 8 * (q % YU);
-        yv[i] = ldg_nt(ybase + s_yrow[row] * a.ldy + min(col, Ns - 8));
+        yv[i] = ldg_nt(ybase + s_yrow[row] * a.ldy + (row < ntok ? min(col, Ns - 8) : n_base));
     }
     const char *bblk = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.sl.b[sg]) + grp * Ns * R);
     uint4 bv[NBU];
@@ -612,10 +614,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
         const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
         const uint16_t *ybase = a.y + a.sl.off[c.sg];
+        // rows past the tile's tokens all read one 16-byte unit (of its last
+        // token row), so an instruction of padding rows costs one request
+        const int ntk = tl.z - tl.y;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int q = i * kThreads + tid;
-            yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + min(c.n_base + 8 * (q % YU), c.Ns - 8));
+            const int col = q / YU < ntk ? min(c.n_base + 8 * (q % YU), c.Ns - 8) : c.n_base;
+            yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + col);
         }
         // units q < CW * Ue of the block, Ue = 1 << lgu per row; the rest repeat the last
         const int lgu = lg_units(s_rk[slot]);
