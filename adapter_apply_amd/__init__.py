@@ -245,7 +245,11 @@ def _aligned_ws(n: int, device):
 
 
 def alloc_workspace(T: int, K: int, S: int, R: int, L: int, device="cuda"):
-    """A zero-filled workspace tensor (uint8) of the required size."""
+    """A zero-filled workspace tensor (uint8) of the required size.  A
+    workspace shared by calls of several shapes must be sized with the
+    largest value of each argument (the single-launch K-split decode keeps a
+    zero-on-entry region at its end, clear of the other calls' regions only
+    then)."""
     return _aligned_ws(lora_workspace_size(T, K, S, R, L), device)
 
 
