@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 import adapter_apply_amd as aa
@@ -235,3 +236,26 @@ def test_moe_sizes_and_align_validation():
     assert lib.moe_lora_align(FAKE, FAKE, FAKE, 16, 2, 4, 3, 16, 4, None, None, None, FAKE_WS,
                               16, None) == aa.LORA_E_WORKSPACE
     assert _moe(T=0, y=None, x=None) == aa.LORA_OK
+
+
+def test_workspace_size_grows_with_every_argument():
+    """A workspace shared by calls of several shapes is sized at the largest
+    value of each argument; that keeps the single-launch K-split decode's
+    region (at the end of the buffer) clear of every other call's regions only
+    if the size never shrinks when any one argument grows."""
+    rng = np.random.default_rng(11)
+    lims = dict(T=(1, 1200), K=(8, 9000), S=(1, 8), R=(8, 512), L=(1, 1024))
+    for _ in range(300):
+        args = {k: int(rng.integers(lo, hi + 1)) for k, (lo, hi) in lims.items()}
+        args["K"] -= args["K"] % 8
+        args["R"] -= args["R"] % 8
+        args["K"], args["R"] = max(args["K"], 8), max(args["R"], 8)
+        base = aa.lora_workspace_size(args["T"], args["K"], args["S"], args["R"], args["L"])
+        for k, (lo, hi) in lims.items():
+            step = 8 if k in ("K", "R") else 1
+            bigger = dict(args)
+            bigger[k] = min(hi - (hi % step), args[k] + step * int(rng.integers(1, 64)))
+            if bigger[k] <= args[k]:
+                continue
+            n = aa.lora_workspace_size(bigger["T"], bigger["K"], bigger["S"], bigger["R"], bigger["L"])
+            assert n >= base, (args, k, bigger[k], base, n)

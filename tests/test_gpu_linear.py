@@ -109,6 +109,8 @@ INTEGER_CASES = [
     (33, 64, 1024, [32768], 16, 4),          # one vocabulary-wide slice (lm_head LoRA)
     (34, 150, 1024, [256, 64], 512, 3),      # the largest rank the library takes
     (35, 400, 512, [128, 200], 256, 5),      # rank 256: several 128-rank passes
+    (36, 1024, 8192, [1024, 264], 32, 64),   # the K-split single launch at its largest T, K, L
+    (37, 256, 8192, [20480], 16, 8),         # ... with 16-token expand items over 32 K chunks
 ]
 
 
