@@ -21,8 +21,9 @@
 // agent-scope relaxed atomic stores and loads (on gfx950: global stores and
 // loads with the sc1 bit), so no L2 write-back or invalidate is needed and no
 // counter stands between the data and its reader: an expand work-group loads
-// all its words and repeats while any is still zero.  The last expand work-group to
-// read a block of tokens (a counter per block, each on its own 256-byte line:
+// all its words and repeats while any is still zero.  The last expand
+// work-group to read a block of tokens (a counter per block, each on its own
+// 256-byte line:
 // counters sharing a line serialise every poll and add of the batch on one
 // memory channel) writes the block back to zero, so the workspace is left as
 // it was found.
@@ -36,13 +37,14 @@
 //     the 4 waves are summed in order.  Output: fp32 [S][n_kc][T][R] by
 //     slot-sorted token position.
 //   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g (16b .. 16b + 15 for
-//     outputs wider than 16384 columns), 512 output columns of one slice.  lora_b rows and y rows are loaded before the wait; after
-//     it the K-chunk partials are summed in a fixed order into a bf16 buffer,
-//     and v_mfma_f32_16x16x16_bf16 forms D[n][t] = B[n][:] . buf[t][:]; y is
-//     read and written 16 bytes per lane along rows (non-temporal).
-// XCD placement (block i runs on XCD i % 8): the three slices of a (g, kc)
-// share one XCD (its x rows are read once from HBM), and the four token
-// blocks of a (g, chunk) share one XCD (its lora_b rows are read once).
+//     outputs wider than 16384 columns), 512 output columns of one slice.
+//     lora_b rows and y rows are loaded before the wait; after it the K-chunk
+//     partials are summed in a fixed order into a bf16 buffer, and
+//     v_mfma_f32_16x16x16_bf16 forms D[n][t] = B[n][:] . buf[t][:]; y is read
+//     and written 16 bytes per lane along rows (non-temporal).
+// XCD placement (block i runs on XCD i % 8): the slices of a (g, kc) share
+// one XCD (its x rows are read once from HBM), and the token blocks of a
+// (g, chunk) share one XCD (its lora_b rows are read once).
 #include "discover.hpp"
 
 namespace aa {
@@ -109,9 +111,6 @@ __device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ 
 // it (__syncthreads() also waits for every outstanding global access).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// A load through a pointer read from LDS: the compiler cannot see that it is
-// a global address and would emit a flat load, which also counts against
-// lgkmcnt (every later LDS or scalar wait would then wait for it).
 // A pointer that every lane of the wave holds, moved into scalar registers.
 template <typename P>
 __device__ __forceinline__ P *uniform_ptr(P *p) {
@@ -121,6 +120,9 @@ __device__ __forceinline__ P *uniform_ptr(P *p) {
     return reinterpret_cast<P *>(((uint64_t)hi << 32) | lo);
 }
 
+// A load through a pointer read from LDS: the compiler cannot see that it is
+// a global address and would emit a flat load, which also counts against
+// lgkmcnt (every later LDS or scalar wait would then wait for it).
 __device__ __forceinline__ uint4 ldg_as1(const void *p) {
     const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4_t *>(
         reinterpret_cast<uintptr_t>(p));

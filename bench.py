@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -94,9 +95,17 @@ def algorithmic_bytes(c, shared_a=False):
 def kernel_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "adapter_apply_amd", "csrc"))):
-        with open(os.path.join(ROOT, "adapter_apply_amd", "csrc", f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(ROOT, "adapter_apply_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _code_only(src):
+    """Source text without comments and with whitespace runs collapsed: edits
+    to comments leave the kernels, and so the counters taken on them, valid."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def load_traffic(workload, kernel, khash):
