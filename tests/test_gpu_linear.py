@@ -639,3 +639,31 @@ def test_relay_after_other_paths_on_one_workspace(oracle_mod):
             y = d.y_host()
             bounds.check_bf16_tolerance(y, oracle_y(oracle_mod, c))
             assert_passthrough(c, y)
+
+
+def test_relay_back_to_back_calls_bit_identical(oracle_mod):
+    """300 single-launch K-split calls back to back on one workspace, rotating
+    over three slot assignments (so a partial sum left over from the previous
+    call would be wrong data for the next): every call's output equals the
+    first call of its assignment bit for bit, and that one the oracle."""
+    c = synth.config_decode()
+    rng = np.random.default_rng(21)
+    idxs = [c.idx, rng.permutation(c.idx).astype(np.int32),
+            np.where(rng.random(c.T) < 0.3, -1, rng.integers(0, c.L, c.T)).astype(np.int32)]
+    d = LinearOnDevice(c, guard=False)
+    idx_d = [dev(i) for i in idxs]
+    y0 = d.y.clone()
+    snaps = []
+    for call in range(300):
+        v = call % 3
+        d.y.copy_(y0)
+        aa.lora_apply_packed(d.y, d.x, d.A, d.B, idx_d[v], d.rank, d.scale, d.ws, path=RLY)
+        snaps.append(d.y.clone())
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(d.ws)) == 0
+    for v in range(3):
+        first = host_f32(snaps[v])
+        ref, _ = oracle_mod.lora_apply(c.y0, c.x, c.A, c.B, idxs[v], c.slot_rank, c.scale)
+        bounds.check_bf16_tolerance(first, ref)
+        for call in range(v + 3, 300, 3):
+            assert torch.equal(snaps[call], snaps[v]), f"call {call} (assignment {v}) differs"
