@@ -162,6 +162,72 @@ def _stacked(ts, name, ndim):
             raise ValueError(f"{name} tensors must be contiguous with {ndim} dims")
 
 
+# Argument checks of the wrappers.  The C library checks sizes, alignment and
+# pointers, but it cannot see a tensor's dtype, device or length: an int64
+# idx would be read as pairs of int32, a short idx or y read or written past
+# its end.  So every wrapper checks these here and raises ValueError before
+# the C call (dtypes and shapes first, then the device).
+
+def _need_dtype(t, dtypes, name):
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected " +
+                         " or ".join(str(d) for d in dtypes))
+
+
+def _need_shape(t, shape, name):
+    """shape: a tuple with None for dimensions not checked."""
+    if t.dim() != len(shape) or any(e is not None and t.shape[i] != e for i, e in enumerate(shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}; expected {want}")
+
+
+def _need_vec(t, n, dtype, name):
+    _need_dtype(t, (dtype,), name)
+    if t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of {n} elements "
+                         f"(got shape {list(t.shape)})")
+
+
+def _same_list(ts, name, ndim, dtype, shape_fn=None):
+    if len(ts) < 1:
+        raise ValueError(f"{name} must hold at least one tensor")
+    _stacked(ts, name, ndim)
+    for i, t in enumerate(ts):
+        _need_dtype(t, (dtype,), f"{name}[{i}]")
+        if shape_fn is not None:
+            _need_shape(t, shape_fn(i), f"{name}[{i}]")
+
+
+def _need_device(tensors):
+    """Every tensor on one GPU."""
+    ts = [t for t in tensors if t is not None]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError(f"every tensor must be on a GPU; got one on {t.device}")
+    devs = {t.device for t in ts}
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on several devices: {sorted(str(d) for d in devs)}")
+
+
+def _float_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.float32)
+
+
+def _check_meta(idx, slot_rank, scale, T, L):
+    torch = _torch()
+    _need_vec(idx, T, torch.int32, "idx")
+    if slot_rank is not None:
+        _need_vec(slot_rank, L, torch.int32, "slot_rank")
+    if scale is not None:
+        _need_vec(scale, L, torch.float32, "scale")
+
+
+def _check_ws(ws):
+    if ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous 1-D tensor")
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
@@ -184,6 +250,9 @@ def lora_segment_layout(T: int, L: int) -> dict:
 
 
 def lora_build_segments(idx, slot_rank, L: int, R: int, ws, stream=None):
+    _check_meta(idx, slot_rank, None, idx.shape[0] if idx.dim() == 1 else -1, L)
+    _check_ws(ws)
+    _need_device([idx, slot_rank, ws])
     _check(lib().lora_build_segments(_ptr(idx), _ptr(slot_rank), idx.shape[0], L, R, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)),
            "lora_build_segments")
@@ -192,10 +261,20 @@ def lora_build_segments(idx, slot_rank, L: int, R: int, ws, stream=None):
 def lora_shrink(buf, x, A: Sequence, idx, slot_rank, ws, path: int = LORA_PATH_AUTO,
                 flags: int = 0, stream=None):
     """buf [S, T, R] fp32 (overwritten); x [T, K]; A[s] [L, R, K]."""
+    torch = _torch()
     _rowmajor(x, "x")
-    _stacked(A, "A", 3)
+    _need_dtype(x, _float_types(), "x")
     T, K = x.shape
+    _same_list(A, "A", 3, x.dtype)
     L, R, _ = A[0].shape
+    _same_list(A, "A", 3, x.dtype, lambda i: (L, R, K))
+    _need_dtype(buf, (torch.float32,), "buf")
+    _need_shape(buf, (len(A), T, R), "buf")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check_meta(idx, slot_rank, None, T, L)
+    _check_ws(ws)
+    _need_device([buf, x, *A, idx, slot_rank, ws])
     _check(lib().lora_shrink(_ptr(buf), _ptr(x), x.stride(0), T, K, _ptr_array(A), len(A), L, R,
                              _ptr(idx), _ptr(slot_rank), _dtype_code(x), path, flags, _ptr(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "lora_shrink")
@@ -205,10 +284,22 @@ def lora_expand(y, buf, B: Sequence, idx, slot_rank, scale, ws, y_col_offset: in
                 path: int = LORA_PATH_AUTO, flags: int = 0, stream=None):
     """y [T, >= y_col_offset + sum N] updated in place; buf [S, T, R] fp32;
     B[s] [L, N_s, R]; scale [L] fp32."""
+    torch = _torch()
     _rowmajor(y, "y")
-    _stacked(B, "B", 3)
+    _need_dtype(y, _float_types(), "y")
+    _need_dtype(buf, (torch.float32,), "buf")
+    if buf.dim() != 3 or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous [S, T, R] tensor")
     S, T, R = buf.shape
+    _same_list(B, "B", 3, y.dtype)
     L = B[0].shape[0]
+    if len(B) != S:
+        raise ValueError(f"buf has {S} slices but B holds {len(B)} tensors")
+    _same_list(B, "B", 3, y.dtype, lambda i: (L, None, R))
+    _need_shape(y, (T, None), "y")
+    _check_meta(idx, slot_rank, scale, T, L)
+    _check_ws(ws)
+    _need_device([y, buf, *B, idx, slot_rank, scale, ws])
     N = (_i64 * S)(*[b.shape[1] for b in B])
     _check(lib().lora_expand(_ptr(y), y.stride(0), y_col_offset, _ptr(buf), T, _ptr_array(B), N,
                              S, L, R, _ptr(idx), _ptr(slot_rank), _ptr(scale), _dtype_code(y),
@@ -216,14 +307,30 @@ def lora_expand(y, buf, B: Sequence, idx, slot_rank, scale, ws, y_col_offset: in
                              _stream(stream)), "lora_expand")
 
 
+def _check_packed(y, x, A, B, idx, slot_rank, scale, ws):
+    _rowmajor(x, "x")
+    _rowmajor(y, "y")
+    _need_dtype(x, _float_types(), "x")
+    _need_dtype(y, (x.dtype,), "y")
+    T, K = x.shape
+    _same_list(A, "A", 3, x.dtype)
+    L, R, _ = A[0].shape
+    _same_list(A, "A", 3, x.dtype, lambda i: (L, R, K))
+    if len(B) != len(A):
+        raise ValueError(f"A holds {len(A)} tensors but B holds {len(B)}")
+    _same_list(B, "B", 3, x.dtype, lambda i: (L, None, R))
+    _need_shape(y, (T, None), "y")
+    _check_meta(idx, slot_rank, scale, T, L)
+    if ws is not None:
+        _check_ws(ws)
+    _need_device([y, x, *A, *B, idx, slot_rank, scale, ws])
+
+
 def lora_apply_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
                       y_col_offset: int = 0, path: int = LORA_PATH_AUTO, flags: int = 0,
                       stream=None):
     """y += scale * (x A^T) B^T per slice, in place."""
-    _rowmajor(x, "x")
-    _rowmajor(y, "y")
-    _stacked(A, "A", 3)
-    _stacked(B, "B", 3)
+    _check_packed(y, x, A, B, idx, slot_rank, scale, ws)
     T, K = x.shape
     L, R, _ = A[0].shape
     S = len(A)
@@ -278,7 +385,26 @@ def alloc_moe_workspace(T: int, top_k: int, S: int, R: int, L: int, E: int, devi
 def moe_lora_align(topk_ids, idx, slot_rank, E: int, L: int, R: int, block_m: int, ws,
                    sorted_ids=None, block_expert=None, num_post_padded=None, stream=None):
     """topk_ids [T, top_k] int32; outputs (optional) [L, cap], [L, cap/bm], [L] int32."""
+    torch = _torch()
+    if topk_ids.dim() != 2 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [T, top_k] tensor")
+    _need_dtype(topk_ids, (torch.int32,), "topk_ids")
     T, k = topk_ids.shape
+    _check_meta(idx, slot_rank, None, T, L)
+    outs = (sorted_ids, block_expert, num_post_padded)
+    if any(o is not None for o in outs):
+        if any(o is None for o in outs):
+            raise ValueError("give all three alignment outputs or none")
+        cap = moe_lora_align_capacity(T, k, E, block_m)
+        for o, shape, name in ((sorted_ids, (L, cap), "sorted_ids"),
+                               (block_expert, (L, cap // block_m), "block_expert"),
+                               (num_post_padded, (L,), "num_post_padded")):
+            _need_dtype(o, (torch.int32,), name)
+            _need_shape(o, shape, name)
+            if not o.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    _check_ws(ws)
+    _need_device([topk_ids, idx, slot_rank, ws, *outs])
     _check(lib().moe_lora_align(_ptr(topk_ids), _ptr(idx), _ptr(slot_rank), T, k, E, L, R,
                                 block_m, _ptr(sorted_ids), _ptr(block_expert),
                                 _ptr(num_post_padded), _ptr(ws), ws.numel() * ws.element_size(),
@@ -288,13 +414,37 @@ def moe_lora_align(topk_ids, idx, slot_rank, E: int, L: int, R: int, block_m: in
 def moe_lora_apply(kind: int, y, x, A: Sequence, B: Sequence, topk_ids, topk_w, idx, slot_rank,
                    scale, E: int, ws, reduce_k: bool = False, flags: int = 0, stream=None):
     """A[s] [L, E_a, R, K]; B[s] [L, E_b, N_s, R]; y updated in place."""
+    torch = _torch()
     _rowmajor(x, "x")
     _rowmajor(y, "y")
-    _stacked(A, "A", 4)
-    _stacked(B, "B", 4)
+    _need_dtype(x, _float_types(), "x")
+    _need_dtype(y, (x.dtype,), "y")
+    if topk_ids.dim() != 2 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [T, top_k] tensor")
+    _need_dtype(topk_ids, (torch.int32,), "topk_ids")
     T, k = topk_ids.shape
+    _same_list(A, "A", 4, x.dtype)
     L, E_a, R, K = A[0].shape
+    _same_list(A, "A", 4, x.dtype, lambda i: (L, E_a, R, K))
+    if len(B) != len(A):
+        raise ValueError(f"A holds {len(A)} tensors but B holds {len(B)}")
+    _same_list(B, "B", 4, x.dtype)
     E_b = B[0].shape[1]
+    _same_list(B, "B", 4, x.dtype, lambda i: (L, E_b, None, R))
+    if kind == MOE_LORA_W13:
+        _need_shape(x, (T, K), "x")
+        _need_shape(y, (T * k, None), "y")
+    else:
+        _need_shape(x, (T * k, K), "x")
+        _need_shape(y, (T if reduce_k else T * k, None), "y")
+    if topk_w is not None:
+        _need_dtype(topk_w, (torch.float32,), "topk_w")
+        _need_shape(topk_w, (T, k), "topk_w")
+        if not topk_w.is_contiguous():
+            raise ValueError("topk_w must be contiguous")
+    _check_meta(idx, slot_rank, scale, T, L)
+    _check_ws(ws)
+    _need_device([y, x, *A, *B, topk_ids, topk_w, idx, slot_rank, scale, ws])
     S = len(A)
     N = (_i64 * S)(*[b.shape[2] for b in B])
     _check(lib().moe_lora_apply(kind, _ptr(y), y.stride(0), int(bool(reduce_k)), _ptr(x),

@@ -293,13 +293,20 @@ def config_moe(seed=1005, T=2048, k=8, E=64, K=4096, I=1536, R=16, L=8, shared_o
 # ----------------------------------------------------------------------------
 
 def ternary_sparse(rng, shape, nnz_per_row):
-    """Rows of {-1,0,+1} with at most nnz_per_row non-zeros (last axis)."""
-    out = np.zeros(shape, np.float32)
-    flat = out.reshape(-1, shape[-1])
-    for row in flat:
-        cols = rng.choice(shape[-1], size=min(nnz_per_row, shape[-1]), replace=False)
-        row[cols] = rng.choice(np.array([-1.0, 1.0], np.float32), size=cols.size)
-    return out
+    """Rows of {-1,0,+1} with at most nnz_per_row non-zeros (last axis): each
+    row's non-zero columns are the nnz_per_row smallest of its uniform keys
+    (distinct columns), each with a random sign."""
+    n = shape[-1]
+    nnz = min(nnz_per_row, n)
+    rows = int(np.prod(shape[:-1], dtype=np.int64))
+    out = np.zeros((rows, n), np.float32)
+    if rows and nnz:
+        keys = rng.random((rows, n), dtype=np.float32)
+        cols = np.argpartition(keys, nnz - 1, axis=1)[:, :nnz] if nnz < n else \
+            np.broadcast_to(np.arange(n), (rows, n))
+        signs = rng.choice(np.array([-1.0, 1.0], np.float32), size=(rows, nnz))
+        out[np.arange(rows)[:, None], cols] = signs
+    return out.reshape(shape)
 
 
 def make_integer_linear(T, K, N, R, L, seed, dtype="bf16", p_none=0.15, slot_rank=None,

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 import adapter_apply_amd as aa  # noqa: E402
 import synth  # noqa: E402
-from tests import bounds  # noqa: E402
+from tests import bounds, oracle_par  # noqa: E402
 from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
 
 DEC, PRE, FUS, GRP, RLY = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
@@ -145,24 +145,41 @@ def test_decode_config_qkv(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
-def test_prefill_config_gate_up_sampled(oracle_mod):
-    """8192 tokens in 32 sequences, 16 slots, gate_up 2x14336, rank 64: every
-    output of a sample of 96 tokens (first, last and random ones of every
-    sequence) against the oracle."""
+def test_prefill_config_gate_up_full(oracle_mod):
+    """8192 tokens in 32 sequences, 16 slots, gate_up 2x14336, rank 64, on the
+    auto path (the MFMA tile kernels): all 8192 x 28672 outputs against the
+    oracle (run in token blocks on the host cores)."""
     c = synth.config_prefill()
     log("case prefill_gate_up full size (auto path)")
-    d = LinearOnDevice(c, guard=False)
+    d = LinearOnDevice(c)
     d.apply(aa.LORA_PATH_AUTO)
-    torch.cuda.synchronize()
-    lens = [int(v) for v in c.note.split("=")[1].split(",")]
-    starts = np.cumsum([0] + lens[:-1])
-    rng = np.random.default_rng(0)
-    rows = sorted(set([int(s) for s in starts] + [int(s + l - 1) for s, l in zip(starts, lens)] +
-                      rng.integers(0, c.T, 32).tolist()))
-    y = host_f32(d.y[torch.tensor(rows, device="cuda")])
-    ref = oracle_y(oracle_mod, c, rows)
+    y = d.y_host()
+    assert canaries_intact(d.yfull)
+    ref = oracle_par.lora_apply(oracle_mod, c.y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
     err, rel = bounds.check_bf16_tolerance(y, ref)
-    log(f"  sampled {len(rows)} rows: max abs err {err:.3e} rel {rel:.3e}")
+    log(f"  all {c.T} x {c.Ntot} outputs: max abs err {err:.3e} rel {rel:.3e}")
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, PRE])
+def test_prefill_config_shape_integer_bit_exact(oracle_mod, path):
+    """Integer vectors at exactly the prefill workload's shape (8192 tokens in
+    its 32 sequences, 16 slots, hidden 4096, gate_up 2x14336, rank 64): every
+    output bit-exact, so each of the persistent expand's items (about 30 per
+    work-group here) and each shrink tile is checked at full size."""
+    c0 = synth.config_prefill()
+    c = synth.make_integer_linear(c0.T, c0.K, c0.N, c0.R, c0.L, seed=71, idx=c0.idx,
+                                  slot_rank=np.full(c0.L, c0.R, np.int32))
+    del c0
+    log(f"case prefill-shape integer path={path}")
+    d = LinearOnDevice(c)
+    d.apply(path)
+    y = d.y_host()
+    assert canaries_intact(d.yfull)
+    ref = oracle_par.lora_apply(oracle_mod, c.y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
+    exact = bounds.linear_exact_int_by_slot(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.array_equal(ref, exact.astype(np.float32))
+    bad = np.argwhere(y != ref)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:4].tolist()}"
 
 
 @pytest.mark.parametrize("path", [DEC, PRE])

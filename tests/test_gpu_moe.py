@@ -12,7 +12,7 @@ torch = pytest.importorskip("torch")
 
 import adapter_apply_amd as aa  # noqa: E402
 import synth  # noqa: E402
-from tests import bounds  # noqa: E402
+from tests import bounds, oracle_par  # noqa: E402
 from tests.gpu_util import canaries_intact, dev, guarded, host_f32, log  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
@@ -84,11 +84,13 @@ def test_hand_examples_padded():
             assert np.array_equal(y[:, :n], np.asarray(c["expected_y_reduced"], np.float32))
 
 
-def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
+def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1, full_rank=False,
+                weights=(0.5, 0.25, 1.0)):
     rng = np.random.default_rng(seed)
     idx = rng.integers(0, L, size=T).astype(np.int32)
     idx[rng.random(T) < p_none] = -1
-    rank = rng.integers(1, R + 1, size=L).astype(np.int32)
+    rank = (np.full(L, R, np.int32) if full_rank else
+            rng.integers(1, R + 1, size=L).astype(np.int32))
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     Ea = 1 if shared else E
     x = rng.integers(-1, 2, size=(T, K)).astype(np.float32)
@@ -104,7 +106,7 @@ def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1):
             b[s, :, :, rank[s]:] = 0
         A2[s, :, rank[s]:] = 0
         B2[s, :, :, rank[s]:] = 0
-    w = rng.choice(np.array([0.5, 0.25, 1.0], np.float32), size=(T, k))
+    w = rng.choice(np.array(weights, np.float32), size=(T, k))
     g0 = rng.integers(-8, 9, size=(T * k, 2 * I)).astype(np.float32)
     o0 = rng.integers(-8, 9, size=(T * k, K)).astype(np.float32)
     scale = np.full(L, 2.0, np.float32)
@@ -216,26 +218,60 @@ def oracle_rows(oracle_mod, c, kind, rows, reduce_k=False):
 def test_moe_config_shared_outer(oracle_mod):
     """2048 tokens, 64 experts top-8, d_model 4096, d_mlp 1536, rank 16, 8
     adapters, shared-outer: w13 and w2 (per pair and k-reduced) on the same
-    alignment, every output of a token sample against the oracle."""
+    alignment; every output of every token against the oracle (run in token
+    blocks on the host cores)."""
     c = synth.config_moe()
-    log("case moe config (shared-outer)")
+    log("case moe config (shared-outer), all tokens")
     T, k = c.T, c.k
     ws = aa.alloc_moe_workspace(T, k, 2, c.R, c.L, c.E)
     aa.moe_lora_align(dev(c.topk_ids), dev(c.idx), dev(c.slot_rank), c.E, c.L, c.R, 16, ws)
-    rows = sample_tokens(T, 40)
-    pr = (rows[:, None] * k + np.arange(k)[None, :]).reshape(-1)
     ready = aa.LORA_FLAG_SEGMENTS_READY
     y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
-                c.E, ws=ws, flags=ready, guard=False)
-    err, rel = bounds.check_bf16_tolerance(y[pr], oracle_rows(oracle_mod, c, 0, rows))
-    log(f"  w13 max abs err {err:.3e} rel {rel:.3e}")
+                c.E, ws=ws, flags=ready)
+    ref = oracle_par.moe_lora_apply(oracle_mod, 0, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids,
+                                    None, c.idx, c.slot_rank, c.scale, c.E)
+    err, rel = bounds.check_bf16_tolerance(y, ref)
+    log(f"  w13 all {T * k} pairs: max abs err {err:.3e} rel {rel:.3e}")
     y = run_moe(W2, c.out0, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
-                c.E, ws=ws, flags=ready, guard=False)
-    err, rel = bounds.check_bf16_tolerance(y[pr], oracle_rows(oracle_mod, c, 1, rows))
-    log(f"  w2 max abs err {err:.3e} rel {rel:.3e}")
-    yr = run_moe(W2, np.zeros((T, c.K), np.float32), c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w,
-                 c.idx, c.slot_rank, c.scale, c.E, ws=ws, flags=ready, reduce_k=True, guard=False)
-    bounds.check_bf16_tolerance(yr[rows], oracle_rows(oracle_mod, c, 1, rows, reduce_k=True))
+                c.E, ws=ws, flags=ready)
+    ref = oracle_par.moe_lora_apply(oracle_mod, 1, c.out0, c.h, [c.A2], [c.B2], c.topk_ids,
+                                    c.topk_w, c.idx, c.slot_rank, c.scale, c.E)
+    err, rel = bounds.check_bf16_tolerance(y, ref)
+    log(f"  w2 all {T * k} pairs: max abs err {err:.3e} rel {rel:.3e}")
+    z = np.zeros((T, c.K), np.float32)
+    yr = run_moe(W2, z, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w, c.idx, c.slot_rank, c.scale,
+                 c.E, ws=ws, flags=ready, reduce_k=True)
+    ref = oracle_par.moe_lora_apply(oracle_mod, 1, z, c.h, [c.A2], [c.B2], c.topk_ids, c.topk_w,
+                                    c.idx, c.slot_rank, c.scale, c.E, reduce_k=True)
+    err, rel = bounds.check_bf16_tolerance(yr, ref)
+    log(f"  w2 k-reduced all {T} tokens: max abs err {err:.3e} rel {rel:.3e}")
+
+
+def test_moe_config_shape_integer_bit_exact(oracle_mod):
+    """Integer vectors at exactly the fused-MoE workload's shape (2048 tokens,
+    64 experts top-8, d_model 4096, d_mlp 1536, rank 16, 8 adapters,
+    shared-outer) on the aligned path: w13, w2 per pair and k-reduced w2 equal
+    the oracle bit for bit on every output."""
+    T, k, E, K, I, R, L = 2048, 8, 64, 4096, 1536, 16, 8
+    # weights 1 and 1/2 with scale 2: every per-pair and k-summed result is an
+    # integer far inside bf16's exact range
+    d = integer_moe(81, T, k, E, K, I, R, L, shared=True, p_none=0.0, full_rank=True,
+                    weights=(1.0, 0.5))
+    log("case moe config-shape integer (aligned)")
+    ws = aa.alloc_moe_workspace(T, k, 2, R, L, E)
+    aa.moe_lora_align(dev(d["ids"]), dev(d["idx"]), dev(d["rank"]), E, L, R, 16, ws)
+    ready = aa.LORA_FLAG_SEGMENTS_READY
+    for kind, y0, x, A, B, w, red in ((W13, d["g0"], d["x"], d["A13"], d["B13"], None, False),
+                                      (W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["w"], False),
+                                      (W2, np.zeros((T, K), np.float32), d["h"], [d["A2"]],
+                                       [d["B2"]], d["w"], True)):
+        log(f"  kind={kind} reduce_k={red}")
+        y = run_moe(kind, y0, x, A, B, d["ids"], w, d["idx"], d["rank"], d["scale"], E,
+                    reduce_k=red, ws=ws, flags=ready)
+        ref = oracle_par.moe_lora_apply(oracle_mod, kind, y0, x, A, B, d["ids"], w, d["idx"],
+                                        d["rank"], d["scale"], E, reduce_k=red)
+        bad = np.argwhere(y != ref)
+        assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:4].tolist()}"
 
 
 @pytest.mark.parametrize("T,align", [(4, False), (8, False), (4, True), (8, True), (40, False), (40, True)])
