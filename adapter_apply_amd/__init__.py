@@ -25,6 +25,8 @@ LORA_E_WORKSPACE = 6
 LORA_E_ALIGN = 7
 LORA_E_PATH = 8
 LORA_E_LAUNCH = 9
+LORA_E_TIMEOUT = 10
+LORA_E_RUNTIME = 11
 
 LORA_DT_F32 = 0
 LORA_DT_BF16 = 1
@@ -42,6 +44,7 @@ MOE_LORA_W2 = 1
 LORA_FLAG_SEGMENTS_READY = 1
 LORA_FLAG_ACTIVE_ONLY = 2
 LORA_FLAG_PARTIAL = 4
+LORA_FLAG_RELAY_GIVE_UP = 8   # test hook: the RELAY path's waits give up at once
 
 # Every symbol the header declares, with its ctypes signature.
 _vp = C.c_void_p
@@ -61,6 +64,7 @@ SIGNATURES = {
     "lora_status_string": (C.c_char_p, [_i32]),
     "lora_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)]),
     "lora_workspace_init": (_i32, [_vp, _sz, _vp]),
+    "lora_workspace_check": (_i32, [_vp, _sz, _vp]),
     "lora_segment_layout": (_i32, [_i32, _i32, C.POINTER(SegmentLayout)]),
     "lora_build_segments": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "lora_shrink": (_i32, [_vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _i32,
@@ -69,6 +73,9 @@ SIGNATURES = {
                            _vp, _i32, _i32, _u32, _vp, _sz, _vp]),
     "lora_apply_packed": (_i32, [_vp, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32,
                                  _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "lora_plan_packed": (_i32, [_vp, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32,
+                                _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp, _sz,
+                                C.POINTER(_i32)]),
     "moe_lora_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)]),
     "moe_lora_align_capacity": (_i32, [_i32, _i32, _i32, _i32, C.POINTER(_i32)]),
     "moe_lora_align": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -243,6 +250,15 @@ def lora_workspace_init(ws, stream=None):
            "lora_workspace_init")
 
 
+def lora_workspace_check(ws, stream=None):
+    """Synchronises the stream and raises LoraError(LORA_E_TIMEOUT) if a
+    single-launch K-split decode call on this workspace had a wait give up
+    since the last check (the library has then zero-filled the workspace)."""
+    _check_ws(ws)
+    _check(lib().lora_workspace_check(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "lora_workspace_check")
+
+
 def lora_segment_layout(T: int, L: int) -> dict:
     out = SegmentLayout()
     _check(lib().lora_segment_layout(T, L, C.byref(out)), "lora_segment_layout")
@@ -328,8 +344,9 @@ def _check_packed(y, x, A, B, idx, slot_rank, scale, ws):
 
 def lora_apply_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
                       y_col_offset: int = 0, path: int = LORA_PATH_AUTO, flags: int = 0,
-                      stream=None):
-    """y += scale * (x A^T) B^T per slice, in place."""
+                      stream=None, check: bool = False):
+    """y += scale * (x A^T) B^T per slice, in place.  check=True then runs
+    lora_workspace_check (synchronises; raises if a wait gave up)."""
     _check_packed(y, x, A, B, idx, slot_rank, scale, ws)
     T, K = x.shape
     L, R, _ = A[0].shape
@@ -338,8 +355,33 @@ def lora_apply_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
     _check(lib().lora_apply_packed(_ptr(y), y.stride(0), y_col_offset, _ptr(x), x.stride(0), T, K,
                                    _ptr_array(A), _ptr_array(B), N, S, L, R, _ptr(idx),
                                    _ptr(slot_rank), _ptr(scale), _dtype_code(x), path, flags,
-                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)),
            "lora_apply_packed")
+    if check and ws is not None:
+        lora_workspace_check(ws, stream)
+
+
+def lora_plan_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
+                     y_col_offset: int = 0, path: int = LORA_PATH_AUTO, flags: int = 0) -> int:
+    """The LORA_PATH_* that lora_apply_packed takes for these arguments
+    (nothing is run)."""
+    _check_packed(y, x, A, B, idx, slot_rank, scale, ws)
+    T, K = x.shape
+    L, R, _ = A[0].shape
+    S = len(A)
+    N = (_i64 * S)(*[b.shape[1] for b in B])
+    out = _i32(-1)
+    _check(lib().lora_plan_packed(_ptr(y), y.stride(0), y_col_offset, _ptr(x), x.stride(0), T, K,
+                                  _ptr_array(A), _ptr_array(B), N, S, L, R, _ptr(idx),
+                                  _ptr(slot_rank), _ptr(scale), _dtype_code(x), path, flags,
+                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  C.byref(out)), "lora_plan_packed")
+    return int(out.value)
+
+
+PATH_NAMES = {LORA_PATH_AUTO: "auto", LORA_PATH_DECODE: "decode", LORA_PATH_PREFILL: "prefill",
+              LORA_PATH_FUSED: "fused", LORA_PATH_GROUPED: "grouped", LORA_PATH_RELAY: "relay"}
 
 
 def _aligned_ws(n: int, device):

@@ -198,6 +198,154 @@ Slices make_slices(const void *const *A, const void *const *B, const int64_t *N,
 
 }  // namespace
 
+namespace aa {
+
+// Every check of lora_apply_packed and its choice of path, on the host; it
+// enqueues nothing.  The auto rule, in order:
+//   1. PREFILL when slots carry long token runs (choose_path);
+//   2. RELAY where its shapes allow, a workspace of lora_workspace_size()
+//      bytes is given, and the output is narrow or T <= 256;
+//   3. FUSED where its shapes allow and the output is narrow;
+//   4. GROUPED where its shapes allow, L <= 64, R <= 64 and the output is
+//      narrow;
+//   5. PREFILL for bf16 with R in {16, 32, 64, 128} and rows of 8 columns;
+//   6. DECODE.
+// "Narrow": the slices sum to at most 16384 columns.
+int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void *x, int64_t ldx,
+                    int32_t T, int32_t K, const void *const *A, const void *const *B,
+                    const int64_t *N, int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                    const int32_t *slot_rank, const float *scale, int32_t dtype, int32_t path,
+                    uint32_t flags, const void *ws, size_t ws_bytes, PackedPlan *out) {
+    (void)slot_rank;
+    (void)flags;
+    CHECK(check_sizes(T, S, L, R, dtype));
+    CHECK(check_k(K, ldx));
+    int64_t ntot = 0;
+    CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
+    int use_prefill = 0;
+    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    // Auto takes the single-launch kernel with the K-split shrink for decode
+    // batches when the workspace is there: for narrow outputs, and for wide
+    // ones (an lm_head's vocabulary) up to 256 tokens, where its 16-token
+    // expand items beat the tile kernels (128256 columns: 44 against 56 us).
+    // Without a workspace narrow outputs take the other single-launch kernel;
+    // past these, wide outputs go to the tile kernels (the single-launch
+    // kernel without a workspace recomputes a group's shrink for every
+    // 1024-column chunk).
+    const bool narrow = ntot <= kAutoMaxDecodeCols;
+    const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
+    if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
+    const bool relay = path == LORA_PATH_RELAY ||
+                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok &&
+                        (narrow || T <= kRelayWideMaxTokens) && ws &&
+                        ws_bytes >= ws_layout(T, K, S, R, L).end);
+    const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+                      (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
+    if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
+    // Auto takes the grouped kernels while their in-kernel discovery is the
+    // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
+    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank && narrow;
+    const bool group = !use_prefill && !fuse && !relay && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+                       (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
+    if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
+    // Auto, past the single-launch and discovering grouped kernels (more than
+    // 64 slots, ranks past 64, or wide outputs): the MFMA prefill kernels, the
+    // shrink split over K when its tiles are few, while the persistent expand
+    // takes the rank.
+    if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && !relay && dtype == LORA_DT_BF16 &&
+        (R == 16 || R == 32 || R == 64 || R == 128) && rows_of_8(N, S, ldy, y_col_offset))
+        use_prefill = 1;
+    out->path = relay ? LORA_PATH_RELAY : fuse ? LORA_PATH_FUSED : group ? LORA_PATH_GROUPED
+              : use_prefill ? LORA_PATH_PREFILL : LORA_PATH_DECODE;
+    // One lora_a for every slice (the same pointer in each, as a merged layer
+    // holds when its checkpoint has a single lora_a: [vLLM]
+    // MergedQKVParallelLinearWithLoRA duplicates it per slice).
+    bool shared_a = S > 1 && A;
+    for (int s = 1; s < S && shared_a; ++s) shared_a = A[s] == A[0];
+    out->shared_a = shared_a ? 1 : 0;
+    out->noop = T == 0 ? 1 : 0;
+    if (T == 0) return LORA_OK;
+    if (!y || !x || !idx || !scale) return LORA_E_NULL;
+    CHECK(check_ptrs(A, S));
+    CHECK(check_ptrs(B, S));
+    if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
+    if (!fuse) CHECK(check_ws(ws, ws_bytes, ws_layout(T, K, S, R, L).end));
+    return LORA_OK;
+}
+
+// Enqueues the kernels of a checked plan.
+int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                   int64_t ldx, int32_t T, int32_t K, const void *const *A, const void *const *B,
+                   const int64_t *N, int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                   const int32_t *slot_rank, const float *scale, int32_t dtype, uint32_t flags,
+                   void *ws, size_t ws_bytes, hipStream_t st) {
+    if (p.noop) return LORA_OK;
+    if (p.path == LORA_PATH_FUSED) {
+        // one launch; no workspace and no segments needed
+        const Slices sl = make_slices(A, B, N, S, y_col_offset);
+        return launched(launch_dec_fused(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale, st));
+    }
+    const WsLayout wl = ws_layout(T, K, S, R, L);
+    const SegPtrs seg = seg_ptrs(ws, wl.seg);
+    const Slices sl = make_slices(A, B, N, S, y_col_offset);
+    float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
+    if (p.path == LORA_PATH_RELAY) {
+        // one launch; partials and counters in the region at the end of ws
+        const RelayRegion rr = relay_region(ws_bytes, T, K, S, R, L);
+        char *w = static_cast<char *>(ws);
+        return launched(launch_dec_relay(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale,
+                                         reinterpret_cast<float *>(w + rr.part),
+                                         reinterpret_cast<int32_t *>(w + rr.sync),
+                                         reinterpret_cast<int32_t *>(w + rr.err),
+                                         (flags & LORA_FLAG_RELAY_GIVE_UP) != 0, st));
+    }
+    if (p.path == LORA_PATH_GROUPED) {
+        // two launches that derive their token groups from idx, or the
+        // segment build and launches that read the groups from its table
+        const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
+        if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
+            CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
+        float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+        if (R > kGrpMaxPartialRank) {
+            // large ranks: the K chunks are summed into the token-ordered buffer first
+            int32_t n_kc = 0;
+            CHECK(grp_shrink_part(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
+            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, n_kc, buf, gseg, st)));
+            return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
+                                              nullptr, buf, nullptr, gseg, st));
+        }
+        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
+                                         gseg, st)));
+        return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
+                                          scale, part, nullptr, nullptr, gseg, st));
+    }
+    if (!(flags & LORA_FLAG_SEGMENTS_READY))
+        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
+    if (p.path == LORA_PATH_PREFILL) {
+        // a shared lora_a: the shrink runs once and every slice's expand reads its buffer
+        if (p.shared_a) {
+            const Slices sl1 = make_slices(A, B, N, 1, y_col_offset);
+            CHECK(pre_shrink_buf(x, ldx, T, K, sl1, 1, L, R, idx, slot_rank, seg, wl, ws, buf, st));
+            GroupMap gm;
+            gm.buf_sstride = 0;
+            return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st, gm));
+        }
+        CHECK(pre_shrink_buf(x, ldx, T, K, sl, S, L, R, idx, slot_rank, seg, wl, ws, buf, st));
+        return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
+    }
+    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+    CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
+                                     wl.n_kchunks, st)));
+    if (wl.n_kchunks * R <= kFoldMaxChunkRank)
+        return launched(launch_dec_expand(dtype, y, ldy, nullptr, partial, wl.n_kchunks, T, sl, S,
+                                          L, R, slot_rank, scale, seg, st));
+    CHECK(launched(launch_dec_reduce(T, S, L, R, slot_rank, seg, partial, wl.n_kchunks, buf, st)));
+    return launched(launch_dec_expand(dtype, y, ldy, buf, nullptr, 0, T, sl, S, L, R, slot_rank,
+                                      scale, seg, st));
+}
+
+}  // namespace aa
+
 extern "C" {
 
 const char *lora_status_string(lora_status_t s) {
@@ -212,6 +360,10 @@ const char *lora_status_string(lora_status_t s) {
         case LORA_E_ALIGN: return "pointer or stride alignment not met";
         case LORA_E_PATH: return "the requested path cannot run these arguments";
         case LORA_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case LORA_E_TIMEOUT:
+            return "a hand-over wait of the single-launch K-split decode gave up; the results "
+                   "of the calls since the last check are not valid (the workspace was zero-filled)";
+        case LORA_E_RUNTIME: return "a HIP runtime call failed";
         default: return "unknown status";
     }
 }
@@ -229,6 +381,23 @@ lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     if (!ws) return LORA_E_NULL;
     if (!al(ws, 256)) return LORA_E_ALIGN;
     return launched(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+lora_status_t lora_workspace_check(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return LORA_E_NULL;
+    if (!al(ws, 256)) return LORA_E_ALIGN;
+    if (ws_bytes < 256) return LORA_E_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t word = 0;
+    const char *e = static_cast<const char *>(ws) + err_word_offset(ws_bytes);
+    if (hipMemcpyAsync(&word, e, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return LORA_E_RUNTIME;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_E_RUNTIME;
+    if (word == 0) return LORA_OK;
+    // a wait gave up: late partials may sit in the region, so start over
+    if (launch_fill_zero(ws, ws_bytes, st) != hipSuccess) return LORA_E_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return LORA_E_RUNTIME;
+    return LORA_E_TIMEOUT;
 }
 
 lora_status_t lora_segment_layout(int32_t T, int32_t L, lora_segment_layout_t *out) {
@@ -372,122 +541,31 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
                                       scale, seg, st));
 }
 
+lora_status_t lora_plan_packed(const void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                               int64_t ldx, int32_t T, int32_t K, const void *const *A,
+                               const void *const *B, const int64_t *N, int32_t S, int32_t L,
+                               int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                               const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                               const void *ws, size_t ws_bytes, int32_t *chosen_path) {
+    if (!chosen_path) return LORA_E_NULL;
+    PackedPlan p;
+    CHECK(packed_plan(y, ldy, y_col_offset, x, ldx, T, K, A, B, N, S, L, R, idx, slot_rank, scale,
+                      dtype, path, flags, ws, ws_bytes, &p));
+    *chosen_path = p.path;
+    return LORA_OK;
+}
+
 lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, const void *x,
                                 int64_t ldx, int32_t T, int32_t K, const void *const *A,
                                 const void *const *B, const int64_t *N, int32_t S, int32_t L,
                                 int32_t R, const int32_t *idx, const int32_t *slot_rank,
                                 const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                                 void *ws, size_t ws_bytes, void *stream) {
-    CHECK(check_sizes(T, S, L, R, dtype));
-    CHECK(check_k(K, ldx));
-    int64_t ntot = 0;
-    CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
-    int use_prefill = 0;
-    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
-    // Auto takes the single-launch kernel with the K-split shrink for decode
-    // batches when the workspace is there: for narrow outputs, and for wide
-    // ones (an lm_head's vocabulary) up to 256 tokens, where its 16-token
-    // expand items beat the tile kernels (128256 columns: 44 against 56 us).
-    // Without a workspace narrow outputs take the other single-launch kernel;
-    // past these, wide outputs go to the tile kernels (the single-launch
-    // kernel without a workspace recomputes a group's shrink for every
-    // 1024-column chunk).
-    const bool narrow = ntot <= kAutoMaxDecodeCols;
-    const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
-    if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
-    const bool relay = path == LORA_PATH_RELAY ||
-                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok &&
-                        (narrow || T <= kRelayWideMaxTokens) && ws &&
-                        ws_bytes >= ws_layout(T, K, S, R, L).end);
-    const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
-                      (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
-    if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
-    // Auto takes the grouped kernels while their in-kernel discovery is the
-    // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
-    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank && narrow;
-    const bool group = !use_prefill && !fuse && !relay && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
-                       (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
-    if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
-    // Auto, past the single-launch and discovering grouped kernels (more than
-    // 64 slots, ranks past 64, or wide outputs): the MFMA prefill kernels, the
-    // shrink split over K when its tiles are few, while the persistent expand
-    // takes the rank.
-    if (path == LORA_PATH_AUTO && !use_prefill && !fuse && !group && !relay && dtype == LORA_DT_BF16 &&
-        (R == 16 || R == 32 || R == 64 || R == 128) && rows_of_8(N, S, ldy, y_col_offset))
-        use_prefill = 1;
-    if (T == 0) return LORA_OK;
-    if (!y || !x || !idx || !scale) return LORA_E_NULL;
-    CHECK(check_ptrs(A, S));
-    CHECK(check_ptrs(B, S));
-    if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (fuse) {
-        // one launch; no workspace and no segments needed
-        const Slices sl = make_slices(A, B, N, S, y_col_offset);
-        return launched(launch_dec_fused(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale, st));
-    }
-    const WsLayout wl = ws_layout(T, K, S, R, L);
-    CHECK(check_ws(ws, ws_bytes, wl.end));
-
-    const SegPtrs seg = seg_ptrs(ws, wl.seg);
-    const Slices sl = make_slices(A, B, N, S, y_col_offset);
-    float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
-    if (relay) {
-        // one launch; partials and counters in the region at the end of ws
-        const RelayRegion rr = relay_region(ws_bytes, T, K, S, R, L);
-        char *w = static_cast<char *>(ws);
-        return launched(launch_dec_relay(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale,
-                                         reinterpret_cast<float *>(w + rr.part),
-                                         reinterpret_cast<int32_t *>(w + rr.sync), st));
-    }
-    if (group) {
-        // two launches that derive their token groups from idx, or the
-        // segment build and launches that read the groups from its table
-        const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
-        if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
-            CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
-        float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
-        if (R > kGrpMaxPartialRank) {
-            // large ranks: the K chunks are summed into the token-ordered buffer first
-            int32_t n_kc = 0;
-            CHECK(grp_shrink_part(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
-            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, n_kc, buf, gseg, st)));
-            return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
-                                              nullptr, buf, nullptr, gseg, st));
-        }
-        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
-                                         gseg, st)));
-        return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
-                                          scale, part, nullptr, nullptr, gseg, st));
-    }
-    if (!(flags & LORA_FLAG_SEGMENTS_READY))
-        CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
-    if (use_prefill) {
-        // One lora_a for every slice (the same pointer in each, as a merged
-        // layer holds when its checkpoint has a single lora_a: [vLLM]
-        // MergedQKVParallelLinearWithLoRA duplicates it per slice): the
-        // shrink runs once and every slice's expand reads its buffer.
-        bool shared_a = S > 1;
-        for (int s = 1; s < S && shared_a; ++s) shared_a = A[s] == A[0];
-        if (shared_a) {
-            const Slices sl1 = make_slices(A, B, N, 1, y_col_offset);
-            CHECK(pre_shrink_buf(x, ldx, T, K, sl1, 1, L, R, idx, slot_rank, seg, wl, ws, buf, st));
-            GroupMap gm;
-            gm.buf_sstride = 0;
-            return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st, gm));
-        }
-        CHECK(pre_shrink_buf(x, ldx, T, K, sl, S, L, R, idx, slot_rank, seg, wl, ws, buf, st));
-        return launched(launch_pre_expand(y, ldy, buf, T, sl, S, L, R, slot_rank, scale, seg, st));
-    }
-    float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
-    CHECK(launched(launch_dec_shrink(dtype, x, ldx, T, K, sl, S, L, R, slot_rank, seg, partial,
-                                     wl.n_kchunks, st)));
-    if (wl.n_kchunks * R <= kFoldMaxChunkRank)
-        return launched(launch_dec_expand(dtype, y, ldy, nullptr, partial, wl.n_kchunks, T, sl, S,
-                                          L, R, slot_rank, scale, seg, st));
-    CHECK(launched(launch_dec_reduce(T, S, L, R, slot_rank, seg, partial, wl.n_kchunks, buf, st)));
-    return launched(launch_dec_expand(dtype, y, ldy, buf, nullptr, 0, T, sl, S, L, R, slot_rank,
-                                      scale, seg, st));
+    PackedPlan p;
+    CHECK(packed_plan(y, ldy, y_col_offset, x, ldx, T, K, A, B, N, S, L, R, idx, slot_rank, scale,
+                      dtype, path, flags, ws, ws_bytes, &p));
+    return packed_run(p, y, ldy, y_col_offset, x, ldx, T, K, A, B, N, S, L, R, idx, slot_rank,
+                      scale, dtype, flags, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

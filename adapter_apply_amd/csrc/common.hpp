@@ -109,7 +109,7 @@ struct WsLayout {
     size_t partial;       // fp32 [n_kchunks][T][S*R]
     size_t buf;           // fp32 [S][T][R]
     size_t relay;         // bytes of the single-launch split decode's region (see relay_region)
-    size_t end;           // the regions above, then the relay region
+    size_t end;           // the regions above, the relay region, the error word's line
     int32_t n_kchunks;
 };
 
@@ -118,16 +118,24 @@ int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S);
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The error word of the single-launch split decode's bounded waits: the first
+// int32 of the workspace's last 256-byte line (inside the buffer whatever
+// ws_bytes is).  Set when a wait gives up; read and cleared by
+// lora_workspace_check.  No kernel writes anything else to that line.
+inline size_t err_word_offset(size_t ws_bytes) { return (ws_bytes - sizeof(int32_t)) & ~size_t(255); }
+
 // The single-launch split decode's region: its fp32 partials [S][K/256][T][R]
 // and then its counters.  The kernel needs it all zero on entry and leaves it
 // all zero, so nothing else may write there: it sits at the END of the
-// caller's buffer, while every other region starts at offset 0.  Every
-// region grows with each size argument, so a workspace of
-// lora_workspace_size() at the largest sizes a caller uses keeps this region
-// clear of every other call's regions, whatever their shapes.
+// caller's buffer, just before the error word's line, while every other
+// region starts at offset 0.  Every region grows with each size argument, so
+// a workspace of lora_workspace_size() at the largest sizes a caller uses
+// keeps this region clear of every other call's regions, whatever their
+// shapes.
 struct RelayRegion {
     size_t part;          // offset of the partials
     size_t sync;          // offset of the counters
+    size_t err;           // offset of the error word
 };
 inline size_t relay_part_bytes(int32_t T, int32_t K, int32_t S, int32_t R) {
     return align256(sizeof(float) * (size_t)((K + kRelayKc - 1) / kRelayKc) * T * S * R);
@@ -137,7 +145,8 @@ inline size_t relay_bytes(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
 }
 inline RelayRegion relay_region(size_t ws_bytes, int32_t T, int32_t K, int32_t S, int32_t R, int32_t L) {
     RelayRegion r;
-    r.part = (ws_bytes - relay_bytes(T, K, S, R, L)) & ~size_t(255);
+    r.err = err_word_offset(ws_bytes);
+    r.part = (r.err - relay_bytes(T, K, S, R, L)) & ~size_t(255);
     r.sync = r.part + relay_part_bytes(T, K, S, R);
     return r;
 }
@@ -177,7 +186,7 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
     w.partial = o; o = align256(o + sizeof(float) * (size_t)w.n_kchunks * (size_t)T * S * R);
     w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
     w.relay = relay_bytes(T, K, S, R, L);
-    w.end = o + w.relay;
+    w.end = o + w.relay + 256;   // the relay region, then the error word's line
     return w;
 }
 
@@ -206,7 +215,7 @@ inline MoeWsLayout moe_ws_layout(int32_t T, int32_t k, int32_t S, int32_t R, int
     m.part = align256(m.buf + sizeof(float) * (size_t)S * T * k * R);
     const int64_t items = (int64_t)T * k < kMoeSplitItems ? (int64_t)T * k : kMoeSplitItems;
     m.part_bytes = sizeof(float) * (size_t)kMoeSplitChunks * items * S * R;
-    m.end = align256(m.part + m.part_bytes);
+    m.end = align256(m.part + m.part_bytes) + 256;   // error word's line: never written
     return m;
 }
 
@@ -260,6 +269,25 @@ hipError_t launch_moe_small(void *y, int64_t ldy, const void *x, int64_t ldx, in
                             const float *coef, const int32_t *idx, const int32_t *slot_rank,
                             const float *scale, hipStream_t st);
 
+
+// lora_apply_packed in two steps (abi.hip): packed_plan runs every argument
+// check and chooses the path without enqueueing anything; packed_run enqueues
+// the plan's kernels.  Both return a LORA_* status.
+struct PackedPlan {
+    int32_t path;       // LORA_PATH_RELAY, FUSED, GROUPED, PREFILL or DECODE
+    int32_t shared_a;   // every slice passes the same lora_a pointer
+    int32_t noop;       // T == 0
+};
+int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void *x, int64_t ldx,
+                    int32_t T, int32_t K, const void *const *A, const void *const *B,
+                    const int64_t *N, int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                    const int32_t *slot_rank, const float *scale, int32_t dtype, int32_t path,
+                    uint32_t flags, const void *ws, size_t ws_bytes, PackedPlan *out);
+int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                   int64_t ldx, int32_t T, int32_t K, const void *const *A, const void *const *B,
+                   const int64_t *N, int32_t S, int32_t L, int32_t R, const int32_t *idx,
+                   const int32_t *slot_rank, const float *scale, int32_t dtype, uint32_t flags,
+                   void *ws, size_t ws_bytes, hipStream_t st);
 
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
@@ -317,12 +345,13 @@ hipError_t launch_dec_fused(void *y, int64_t ldy, const void *x, int64_t ldx, in
 
 int32_t relay_max_groups(int32_t T, int32_t L);
 // part: fp32 [S][K / kRelayKc][T][R]; sync: relay_sync_ints() int32; both zero
-// on entry and left at zero (the last int is an error word: set when a wait
-// ran past its bound).
+// on entry and left at zero.  err: set to 1 when a wait runs past its bound
+// (or at once with give_up, a test hook); never cleared by the kernel.
 hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,
-                            float *part, int32_t *sync, hipStream_t st);
+                            float *part, int32_t *sync, int32_t *err, bool give_up,
+                            hipStream_t st);
 
 int32_t grp_max_groups(int32_t T, int32_t L);
 int32_t grp_kchunks(int32_t K);

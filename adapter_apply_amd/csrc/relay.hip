@@ -8,11 +8,14 @@
 // expand work-group of that (group, slice) adds the chunks' partials.
 //
 // Roles.  Blocks [0, 8 * per_p) shrink, the rest expand.  Work-groups are
-// dispatched in block order, so when an expand work-group starts waiting, every
-// shrink work-group has already been dispatched; shrink work-groups wait for
-// nothing, so every wait ends.  The waits are bounded all the same: past kSpin
-// polls the work-group sets the error word of the workspace and goes on
-// (results are then not valid; nothing hangs).
+// dispatched in block order (observed on gfx950: the XCC_ID register reads back
+// block % 8 for every block, in order; the programming model does not promise
+// it), so when an expand work-group starts waiting, every shrink work-group has
+// already been dispatched; shrink work-groups wait for nothing, so every wait
+// ends.  The waits are bounded all the same: past kSpin polls the work-group
+// sets the error word of the workspace and goes on (nothing hangs; that call's
+// results are not valid, and late partials may be left in the region).
+// lora_workspace_check reports the error and zero-fills the workspace.
 //
 // Hand-over.  A partial is stored as its fp32 bit pattern XOR kReady, a quiet
 // NaN whose payload has non-zero low bits: no sum of bf16 products yields it
@@ -81,8 +84,9 @@ struct RelayArgs {
     Slices sl;
     int32_t chunk_start[kMaxSlices + 1];
     float *part;         // fp32 [S][n_kc][T][R]
-    int32_t *sync;       // per (group, slice, token block) reader count, then the error word;
-                         // kLine int32 apart
+    int32_t *sync;       // per (group, slice, token block) reader count, kLine int32 apart
+    int32_t *err;        // error word: set when a wait gives up
+    int32_t give_up;     // test hook: every wait gives up after its first poll
 };
 
 struct RelayDisc {
@@ -232,7 +236,6 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
     if (s < 0) return;
     const int ntok = d.info[2], pos0 = d.info[3], r = d.info[5];
     const int sg = s_sl.sg;
-    int32_t *err = a.sync + kLine * (a.max_groups * a.S * kMaxSubs);
 
     if (shrink) {
         // ---- shrink item (g, kc, sg) ----------------------------------------
@@ -346,9 +349,9 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
 #pragma unroll
             for (int c = 0; c < KCQ; ++c)
                 ok = ok && (uint32_t)pv[c] != 0u && (uint32_t)(pv[c] >> 32) != 0u;
-            if (__syncthreads_and(ok)) break;
-            if (n > kSpin) {
-                if (tid == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__syncthreads_and(ok) && !a.give_up) break;
+            if (n >= (a.give_up ? 0 : kSpin)) {
+                if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(4);
@@ -444,19 +447,20 @@ int32_t relay_max_groups(int32_t T, int32_t L) {
 }
 
 int32_t relay_sync_ints(int32_t T, int32_t L, int32_t S) {
-    return kLine * (relay_max_groups(T, L) * S * kMaxSubs + 1);
+    return kLine * (relay_max_groups(T, L) * S * kMaxSubs);
 }
 
 hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
                             const int32_t *idx, const int32_t *slot_rank, const float *scale,
-                            float *part, int32_t *sync, hipStream_t st) {
+                            float *part, int32_t *sync, int32_t *err, bool give_up,
+                            hipStream_t st) {
     RelayArgs a;
     a.x = static_cast<const uint16_t *>(x); a.ldx = ldx;
     a.y = static_cast<uint16_t *>(y); a.ldy = ldy;
     a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
     a.idx = idx; a.slot_rank = slot_rank; a.scale = scale; a.sl = sl;
-    a.part = part; a.sync = sync;
+    a.part = part; a.sync = sync; a.err = err; a.give_up = give_up ? 1 : 0;
     int c = 0;
     for (int s = 0; s < S; ++s) {
         a.chunk_start[s] = c;

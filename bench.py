@@ -415,30 +415,16 @@ def main():
         aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
                              d["ws"], path=step_path)
 
-    # Kernel-by-kernel calls that launch exactly the kernels of one step: the
-    # decode path folds the K-chunk reduction into the expand while
-    # ceil(K/256) * R <= 512 (the library's rule), else a reduce kernel runs.
-    # the library's auto rule for lora_apply_packed (abi.hip: choose_path, can_group)
-    prefill = (c.dtype == "bf16" and c.R % 16 == 0 and c.T >= 512
-               and c.T // min(c.T, c.L) >= 64)
-    rows8 = all(n % 8 == 0 for n in c.N)
-    narrow = sum(c.N) <= 16384
-    # the single-launch kernel with the K-split shrink (the step passes a workspace)
-    relay = (not prefill and c.dtype == "bf16" and c.R in (16, 32) and c.T <= 1024 and c.L <= 64
-             and c.K % 256 == 0 and c.K // 256 <= 32 and rows8 and (narrow or c.T <= 256))
-    fused = (not prefill and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 32
-             and c.T <= 1024 and c.K % 1024 == 0 and rows8 and narrow)
-    grouped = (not prefill and not fused and not relay and c.dtype == "bf16" and c.R % 16 == 0 and c.R <= 64
-               and c.L <= 64 and c.T <= 4096 and c.K % 64 == 0 and math.ceil(c.K / 512) <= 16 and rows8
-               and narrow)
-    # auto past those kernels: the prefill (MFMA) kernels, the shrink split over K
-    if (not prefill and not fused and not grouped and not relay and c.dtype == "bf16"
-            and c.R in (16, 32, 64, 128) and rows8):
-        prefill = True
-    if args.path != "auto":
-        prefill = args.path == "prefill"
-        fused, grouped = args.path == "fused", args.path == "grouped"
-        relay = args.path == "relay"
+    # The path the step takes, as the library reports it (lora_plan_packed runs
+    # the same checks and choice as lora_apply_packed); the kernel-by-kernel
+    # calls below launch exactly that path's kernels.
+    d0 = insts[0]
+    taken = aa.lora_plan_packed(d0["y"], d0["x"], d0["A"], d0["B"], d0["idx"], d0["rank"],
+                                d0["scale"], d0["ws"], path=step_path)
+    relay, fused = taken == aa.LORA_PATH_RELAY, taken == aa.LORA_PATH_FUSED
+    grouped, prefill = taken == aa.LORA_PATH_GROUPED, taken == aa.LORA_PATH_PREFILL
+    # the decode path folds the K-chunk reduction into the expand while
+    # ceil(K/256) * R <= 512, else a reduce kernel runs
     fold = not prefill and math.ceil(c.K / 256) * c.R <= 512
     part = aa.LORA_FLAG_PARTIAL
     ready = aa.LORA_FLAG_SEGMENTS_READY

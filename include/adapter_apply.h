@@ -41,57 +41,68 @@
  *            element of the expand ([SGL] prepare_lora_batch scalings).
  *   dtype    LORA_DT_BF16 (x, A, B, y all bf16) or LORA_DT_F32 (all fp32;
  *            decode path only).  The intermediate buffer is always fp32.
- *   path     LORA_PATH_AUTO chooses per call: PREFILL when slots carry long
- *            token runs (T >= 512 and T / min(T, L) >= 64, bf16, R % 16 == 0);
- *            otherwise lora_apply_packed takes RELAY where its shapes allow,
- *            ws holds lora_workspace_size() bytes and either the slices sum
- *            to at most 16384 columns or T <= 256, else FUSED, else GROUPED
- *            (when also
- *            L <= 64 and R <= 64), where the shapes allow and the slices sum
- *            to at most 16384 columns, else PREFILL for
- *            bf16 with R in {16, 32, 64, 128} and N, ldy, y_col_offset % 8 == 0
- *            (batches of many slots or high ranks: the MFMA kernels, the
- *            shrink split over K when its tiles are few), and DECODE
- *            elsewhere; lora_shrink / lora_expand take PREFILL for bf16
- *            batches with L > 64 or R > 64 (R in {16, 32, 64, 128}; the
- *            expand also needs N, ldy, y_col_offset % 8 == 0) and DECODE
- *            otherwise, and DECODE whenever LORA_FLAG_PARTIAL is set (a
- *            shrink and an expand called apart exchange the token-ordered
- *            buffer, which every path writes and reads alike).
- *            DECODE forces the split (segments, VALU shrink, expand) decode
- *            path; PREFILL forces the MFMA path (bf16, R % 16 == 0 only);
- *            GROUPED forces the slot-grouped decode kernels (split-K MFMA
- *            shrink, MFMA expand; each work-group finds its token group from
- *            idx while L <= 64 and T <= 1024, past that the call builds the
- *            segments (or takes them with LORA_FLAG_SEGMENTS_READY) and the
- *            kernels read the groups from them: bf16, R % 16 == 0,
- *            R <= 128, T <= 4096, and for the shrink K % 64 == 0, K <= 8192,
- *            for the expand N % 8 == 0, ldy % 8 == 0, y_col_offset % 8 == 0;
- *            LORA_FLAG_PARTIAL only for R <= 64);
- *            FUSED forces the single-launch decode kernel of
- *            lora_apply_packed (bf16, R % 16 == 0, R <= 32, T <= 1024,
- *            K % 1024 == 0, N, ldy and y_col_offset % 8 == 0; it needs no
- *            workspace);
- *            RELAY forces the single-launch decode kernel of
- *            lora_apply_packed whose shrink is split over K chunks of 256
- *            columns and handed to the expand work-groups of the same launch
- *            through the workspace (bf16, R == 16 or 32, T <= 1024, L <= 64,
- *            K % 256 == 0, K <= 8192, N, ldy and y_col_offset % 8 == 0; the
- *            workspace is required: the kernel keeps its partial sums and
- *            counters in a region at the END of ws (ws_bytes decides where),
- *            needs that region zero on entry and leaves it zero; the other
- *            linear calls write only from the start of ws, so a workspace
- *            shared by calls of several shapes must hold
- *            lora_workspace_size() at the largest value of each size
- *            argument, and it must not be shared with the fused-MoE calls;
- *            lora_shrink / lora_expand reject this path).
- *            A forced path that cannot take the arguments returns
- *            LORA_E_PATH.
+ *   path     The kernels a call runs.  LORA_PATH_AUTO chooses; any other
+ *            value forces that path and returns LORA_E_PATH when its shapes
+ *            do not allow the arguments.  lora_plan_packed reports the path
+ *            lora_apply_packed takes, without running it.
+ *
+ *            Paths and the shapes each takes ("rows of 8": every N[s], ldy
+ *            and y_col_offset % 8 == 0):
+ *              RELAY    lora_apply_packed only.  One launch; the shrink is
+ *                       split over K chunks of 256 columns and handed to the
+ *                       expand work-groups of the same launch through a
+ *                       region at the END of ws.  bf16, R in {16, 32},
+ *                       T <= 1024, L <= 64, K % 256 == 0, K <= 8192, rows
+ *                       of 8; needs ws (see ws below).
+ *              FUSED    lora_apply_packed only.  One launch, no workspace;
+ *                       each work-group recomputes its group's shrink.
+ *                       bf16, R % 16 == 0, R <= 32, T <= 1024,
+ *                       K % 1024 == 0, rows of 8.
+ *              GROUPED  slot-grouped split-K MFMA shrink, MFMA expand (two
+ *                       launches; groups found from idx inside the kernels
+ *                       while L <= 64 and T <= 1024, else from the segment
+ *                       table).  bf16, R % 16 == 0, R <= 128, T <= 4096;
+ *                       shrink: K % 64 == 0, K <= 8192; expand: rows of 8;
+ *                       LORA_FLAG_PARTIAL only for R <= 64.
+ *              PREFILL  segments, MFMA tile shrink (split over K when its
+ *                       tiles are few), MFMA tile expand.  bf16, R % 16 == 0
+ *                       (the persistent expand: R in {16, 32, 64, 128} and
+ *                       rows of 8).
+ *              DECODE   segments, VALU split-K shrink, VALU expand.  Every
+ *                       shape and dtype the call accepts (the only fp32 path).
+ *
+ *            LORA_PATH_AUTO in lora_apply_packed ("narrow": the slices sum
+ *            to at most 16384 columns; the first row that holds wins):
+ *              | condition                                        | path    |
+ *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |
+ *              | RELAY's shapes, ws of lora_workspace_size(),     | RELAY   |
+ *              |   narrow or T <= 256                             |         |
+ *              | FUSED's shapes, narrow                           | FUSED   |
+ *              | GROUPED's shapes, L <= 64, R <= 64, narrow       | GROUPED |
+ *              | bf16, R in {16, 32, 64, 128}, rows of 8          | PREFILL |
+ *              | otherwise                                        | DECODE  |
+ *            LORA_PATH_AUTO in lora_shrink / lora_expand (RELAY and FUSED
+ *            are not theirs):
+ *              | condition                                        | path    |
+ *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |
+ *              | no LORA_FLAG_PARTIAL, bf16, L > 64 or R > 64,    | PREFILL |
+ *              |   R in {16, 32, 64, 128} (expand: rows of 8)     |         |
+ *              | otherwise                                        | DECODE  |
+ *            A shrink and an expand called apart exchange the token-ordered
+ *            buffer, which every path writes and reads alike, so the two
+ *            calls need not take the same path (with LORA_FLAG_PARTIAL they
+ *            must).
  *   ws       device workspace of at least lora_workspace_size() bytes,
  *            256-byte aligned, owned by the caller.  Calls sharing a
  *            workspace must be ordered on one stream.  The workspace must be
  *            zero-filled before its first use (lora_workspace_init); the
- *            library leaves its counters at zero after every call.
+ *            library leaves its counters at zero after every call.  RELAY
+ *            keeps its partial sums and counters in a region at the END of ws
+ *            (ws_bytes decides where) that must be zero on entry and is left
+ *            zero; every other region starts at offset 0.  So a workspace
+ *            shared by calls of several shapes must hold
+ *            lora_workspace_size() at the largest value of each size
+ *            argument, and it must not be shared with the fused-MoE calls.
  *   flags    LORA_FLAG_SEGMENTS_READY: the workspace already holds the
  *            segments of this (idx, slot_rank, T, L) from lora_build_segments
  *            (built once per batch and shared by every LoRA layer, as [SGL]
@@ -132,6 +143,8 @@ typedef int32_t lora_status_t;
 #define LORA_E_ALIGN      7  /* pointer or stride alignment not met               */
 #define LORA_E_PATH       8  /* forced path cannot run these arguments            */
 #define LORA_E_LAUNCH     9  /* the HIP runtime rejected a launch                 */
+#define LORA_E_TIMEOUT   10  /* lora_workspace_check: a RELAY hand-over wait gave up */
+#define LORA_E_RUNTIME   11  /* lora_workspace_check: a HIP runtime call failed   */
 
 #define LORA_DT_F32   0
 #define LORA_DT_BF16  1
@@ -146,6 +159,7 @@ typedef int32_t lora_status_t;
 #define LORA_FLAG_SEGMENTS_READY 1u
 #define LORA_FLAG_ACTIVE_ONLY    2u
 #define LORA_FLAG_PARTIAL        4u
+#define LORA_FLAG_RELAY_GIVE_UP  8u   /* test hook, see lora_workspace_check */
 
 #define LORA_MAX_SLICES 8
 #define LORA_MAX_RANK   512
@@ -161,6 +175,29 @@ lora_status_t lora_workspace_size(int32_t T, int32_t K, int32_t S, int32_t R, in
 
 /* Zero-fill a workspace (a fill kernel on `stream`, no memset node). */
 lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Status of the calls made on a workspace since its last check, for the one
+ * path whose kernels wait on each other: RELAY hands partial sums from shrink
+ * to expand work-groups of one launch, and each wait is bounded (it ends
+ * because work-groups start in block order; the bound only guards against a
+ * dispatcher that does not).  A wait that gives up sets an error word in the
+ * first int32 of the workspace's last 256-byte line and lets the kernel
+ * finish; that call's y is then not valid, and late partial sums may be left
+ * in the workspace where the next RELAY call would take them for its own.
+ * This call synchronises `stream`, reads the word and returns LORA_OK when it
+ * is zero; otherwise it zero-fills the whole workspace (so the next call
+ * starts clean; segments built with lora_build_segments must be built again),
+ * synchronises again and returns LORA_E_TIMEOUT.  ([SGL] reports failures of
+ * its control-plane calls explicitly, LoRAUpdateOutput(success,
+ * error_message); this is the data path's counterpart.)  Blocking: not for
+ * graph capture.  LORA_FLAG_RELAY_GIVE_UP (a test hook) makes every wait of a
+ * RELAY call give up after its first poll, so the error path can be forced
+ * from the host while every kernel still ends normally.
+ * The fused-MoE workspace keeps the same line free, so the check returns
+ * LORA_OK on it.
+ */
+lora_status_t lora_workspace_check(void *ws, size_t ws_bytes, void *stream);
 
 /* Byte offsets, inside the workspace, of the segment arrays written by
  * lora_build_segments, so callers and tests can read them back:
@@ -231,6 +268,19 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
                                 int32_t R, const int32_t *idx, const int32_t *slot_rank,
                                 const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The path lora_apply_packed would take for these arguments (one of
+ * LORA_PATH_RELAY, FUSED, GROUPED, PREFILL, DECODE), after the same checks,
+ * without enqueueing anything.  Returns what lora_apply_packed would return
+ * for a bad argument.
+ */
+lora_status_t lora_plan_packed(const void *y, int64_t ldy, int64_t y_col_offset, const void *x,
+                               int64_t ldx, int32_t T, int32_t K, const void *const *A,
+                               const void *const *B, const int64_t *N, int32_t S, int32_t L,
+                               int32_t R, const int32_t *idx, const int32_t *slot_rank,
+                               const float *scale, int32_t dtype, int32_t path, uint32_t flags,
+                               const void *ws, size_t ws_bytes, int32_t *chosen_path);
 
 /* ------------------------------------------------------------------------
  * Fused-MoE LoRA ([vLLM] FusedMoEWithLoRA; shared-outer layout from [PR]

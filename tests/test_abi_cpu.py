@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 12):
         assert aa.status_string(code)
     assert aa.status_string(99) == "unknown status"
 
@@ -259,3 +259,69 @@ def test_workspace_size_grows_with_every_argument():
                 continue
             n = aa.lora_workspace_size(bigger["T"], bigger["K"], bigger["S"], bigger["R"], bigger["L"])
             assert n >= base, (args, k, bigger[k], base, n)
+
+
+def test_workspace_check_rejects_before_any_runtime_call():
+    lib = aa.lib()
+    assert lib.lora_workspace_check(None, 1 << 20, None) == aa.LORA_E_NULL
+    assert lib.lora_workspace_check(FAKE_WS + 16, 1 << 20, None) == aa.LORA_E_ALIGN
+    assert lib.lora_workspace_check(FAKE_WS, 255, None) == aa.LORA_E_WORKSPACE
+
+
+def _plan(**kw):
+    a = dict(y=FAKE, ldy=6144, off=0, x=FAKE, ldx=4096, T=256, K=4096, A=_ptrs(3), B=_ptrs(3),
+             N=(C.c_int64 * 3)(4096, 1024, 1024), S=3, L=8, R=16, idx=FAKE, rank=FAKE,
+             scale=FAKE, dt=aa.LORA_DT_BF16, path=0, flags=0, ws=FAKE_WS, wsb=1 << 40)
+    a.update(kw)
+    out = C.c_int32(-1)
+    st = aa.lib().lora_plan_packed(a["y"], a["ldy"], a["off"], a["x"], a["ldx"], a["T"], a["K"],
+                                   a["A"], a["B"], a["N"], a["S"], a["L"], a["R"], a["idx"],
+                                   a["rank"], a["scale"], a["dt"], a["path"], a["flags"],
+                                   a["ws"], a["wsb"], C.byref(out))
+    return st, out.value
+
+
+def _ws_size(T, K, S, R, L):
+    n = C.c_size_t(0)
+    assert aa.lib().lora_workspace_size(T, K, S, R, L, C.byref(n)) == 0
+    return n.value
+
+
+@pytest.mark.parametrize("kw,path", [
+    # decode QKV with a workspace: the single-launch K-split kernel
+    (dict(), aa.LORA_PATH_RELAY),
+    # ... with a workspace one byte short of lora_workspace_size(): the other single launch
+    (dict(path=aa.LORA_PATH_AUTO, wsb=_ws_size(256, 4096, 3, 16, 8) - 1, ws=None),
+     aa.LORA_PATH_FUSED),
+    (dict(ws=None, wsb=0), aa.LORA_PATH_FUSED),
+    # long runs per slot (8192 tokens over 16 slots): the tile kernels
+    (dict(T=8192, L=16, R=64, S=2, N=(C.c_int64 * 2)(14336, 14336), ldy=28672), aa.LORA_PATH_PREFILL),
+    # 128 slots at rank 128: the tile kernels
+    (dict(T=1024, L=128, R=128, S=1, K=8192, ldx=8192, N=(C.c_int64 * 1)(8192), ldy=8192),
+     aa.LORA_PATH_PREFILL),
+    # rank 64 with few slots and a short batch: the grouped kernels
+    (dict(T=64, R=64), aa.LORA_PATH_GROUPED),
+    # lm_head vocabulary at 256 tokens: single launch; at 512 tokens: tile kernels
+    (dict(S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
+    (dict(T=512, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    # fp32: the VALU path only
+    (dict(dt=aa.LORA_DT_F32, R=16), aa.LORA_PATH_DECODE),
+    # rows not in 8-column units: the VALU path
+    (dict(N=(C.c_int64 * 3)(4096, 1020, 1028)), aa.LORA_PATH_DECODE),
+    # forced paths are reported as such
+    (dict(path=aa.LORA_PATH_GROUPED), aa.LORA_PATH_GROUPED),
+    (dict(path=aa.LORA_PATH_DECODE), aa.LORA_PATH_DECODE),
+])
+def test_plan_reports_the_path(kw, path):
+    st, got = _plan(**kw)
+    assert st == aa.LORA_OK
+    assert got == path, (got, path)
+
+
+@pytest.mark.parametrize("kw", [dict(R=0), dict(N=None), dict(y=FAKE + 4), dict(path=99),
+                                dict(path=aa.LORA_PATH_FUSED, R=128), dict(wsb=1024, path=1)])
+def test_plan_fails_as_the_call_would(kw):
+    st, _ = _plan(**kw)
+    ap = {k: v for k, v in kw.items()}
+    assert st != aa.LORA_OK
+    assert st == _apply(**ap)

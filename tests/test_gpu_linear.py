@@ -684,3 +684,32 @@ def test_relay_back_to_back_calls_bit_identical(oracle_mod):
         bounds.check_bf16_tolerance(first, ref)
         for call in range(v + 3, 300, 3):
             assert torch.equal(snaps[call], snaps[v]), f"call {call} (assignment {v}) differs"
+
+
+def test_relay_forced_give_up_reported_and_repaired(oracle_mod):
+    """The host forces every hand-over wait of a RELAY call to give up after its
+    first poll (LORA_FLAG_RELAY_GIVE_UP; every kernel still ends normally):
+    lora_workspace_check reports LORA_E_TIMEOUT and zero-fills the workspace,
+    after which a normal call on the same workspace equals a call on a fresh
+    workspace bit for bit, and the check reports LORA_OK again."""
+    c = synth.config_decode()
+    d = LinearOnDevice(c, guard=False)
+    fresh = LinearOnDevice(c, guard=False)
+    fresh.apply(RLY)
+    want = fresh.y_host()
+    bounds.check_bf16_tolerance(want, oracle_y(oracle_mod, c))
+    aa.lora_workspace_check(d.ws)                      # nothing to report yet
+    for rnd in range(3):
+        log(f"case relay forced give-up round={rnd}")
+        d.reset_y()
+        d.apply(RLY, flags=aa.LORA_FLAG_RELAY_GIVE_UP)
+        with pytest.raises(aa.LoraError) as e:
+            aa.lora_workspace_check(d.ws)
+        assert e.value.code == aa.LORA_E_TIMEOUT
+        assert int(torch.count_nonzero(d.ws)) == 0
+        d.reset_y()
+        d.apply(RLY)
+        got = d.y_host()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        aa.lora_workspace_check(d.ws)
+        assert int(torch.count_nonzero(d.ws)) == 0
