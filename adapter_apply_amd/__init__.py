@@ -27,6 +27,8 @@ LORA_E_PATH = 8
 LORA_E_LAUNCH = 9
 LORA_E_TIMEOUT = 10
 LORA_E_RUNTIME = 11
+LORA_E_SCRATCH = 12
+LORA_STATIC_SCRATCH_BYTES = 32 << 20
 
 LORA_DT_F32 = 0
 LORA_DT_BF16 = 1
@@ -76,6 +78,8 @@ SIGNATURES = {
     "lora_plan_packed": (_i32, [_vp, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32,
                                 _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp, _sz,
                                 C.POINTER(_i32)]),
+    "lora_apply_packed_noalloc": (_i32, [_vp, _i64, _i64, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
+                                         _i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp]),
     "moe_lora_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)]),
     "moe_lora_align_capacity": (_i32, [_i32, _i32, _i32, _i32, C.POINTER(_i32)]),
     "moe_lora_align": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -382,6 +386,30 @@ def lora_plan_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
 
 PATH_NAMES = {LORA_PATH_AUTO: "auto", LORA_PATH_DECODE: "decode", LORA_PATH_PREFILL: "prefill",
               LORA_PATH_FUSED: "fused", LORA_PATH_GROUPED: "grouped", LORA_PATH_RELAY: "relay"}
+
+
+def lora_apply_packed_noalloc(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale,
+                              y_col_offset: int = 0, path: int = LORA_PATH_AUTO, flags: int = 0,
+                              stream=None):
+    """lora_apply_packed with the library's static per-GPU scratch instead of
+    a workspace: allocates nothing.  Calls overlapping in time on one GPU
+    race (they share the array)."""
+    _check_packed(y, x, A, B, idx, slot_rank, scale, None)
+    T, K = x.shape
+    L, R, _ = A[0].shape
+    S = len(A)
+    N = (_i64 * S)(*[b.shape[1] for b in B])
+    _check(lib().lora_apply_packed_noalloc(_ptr(y), y.stride(0), y_col_offset, _ptr(x),
+                                           x.stride(0), T, K, _ptr_array(A), _ptr_array(B), N, S,
+                                           L, R, _ptr(idx), _ptr(slot_rank), _ptr(scale),
+                                           _dtype_code(x), path, flags, _stream(stream)),
+           "lora_apply_packed_noalloc")
+
+
+def lora_static_scratch_check(stream=None):
+    """lora_workspace_check on the static scratch of lora_apply_packed_noalloc
+    (current device)."""
+    _check(lib().lora_workspace_check(None, 0, _stream(stream)), "lora_workspace_check")
 
 
 def _aligned_ws(n: int, device):

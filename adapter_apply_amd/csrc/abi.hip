@@ -364,6 +364,8 @@ const char *lora_status_string(lora_status_t s) {
             return "a hand-over wait of the single-launch K-split decode gave up; the results "
                    "of the calls since the last check are not valid (the workspace was zero-filled)";
         case LORA_E_RUNTIME: return "a HIP runtime call failed";
+        case LORA_E_SCRATCH:
+            return "the call needs more scratch than lora_apply_packed_noalloc's static array holds";
         default: return "unknown status";
     }
 }
@@ -384,6 +386,7 @@ lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream) {
 }
 
 lora_status_t lora_workspace_check(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws && ws_bytes == 0) return static_scratch_check(static_cast<hipStream_t>(stream));
     if (!ws) return LORA_E_NULL;
     if (!al(ws, 256)) return LORA_E_ALIGN;
     if (ws_bytes < 256) return LORA_E_WORKSPACE;

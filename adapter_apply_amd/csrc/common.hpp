@@ -289,6 +289,10 @@ int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offs
                    const int32_t *slot_rank, const float *scale, int32_t dtype, uint32_t flags,
                    void *ws, size_t ws_bytes, hipStream_t st);
 
+// lora_workspace_check on lora_apply_packed_noalloc's array of the current
+// device (static_scratch.hip): LORA_OK, or LORA_E_TIMEOUT after zero-filling it.
+int32_t static_scratch_check(hipStream_t st);
+
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_segments(const int32_t *idx, const int32_t *slot_rank, int32_t T, int32_t L,
                            int32_t R, const SegPtrs &seg, hipStream_t st);

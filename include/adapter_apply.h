@@ -144,7 +144,9 @@ typedef int32_t lora_status_t;
 #define LORA_E_PATH       8  /* forced path cannot run these arguments            */
 #define LORA_E_LAUNCH     9  /* the HIP runtime rejected a launch                 */
 #define LORA_E_TIMEOUT   10  /* lora_workspace_check: a RELAY hand-over wait gave up */
-#define LORA_E_RUNTIME   11  /* lora_workspace_check: a HIP runtime call failed   */
+#define LORA_E_RUNTIME   11  /* a HIP runtime call (not a launch) failed          */
+#define LORA_E_SCRATCH   12  /* lora_apply_packed_noalloc: the call needs more
+                                scratch than LORA_STATIC_SCRATCH_BYTES holds      */
 
 #define LORA_DT_F32   0
 #define LORA_DT_BF16  1
@@ -198,6 +200,8 @@ lora_status_t lora_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * LORA_OK on it.
  */
 lora_status_t lora_workspace_check(void *ws, size_t ws_bytes, void *stream);
+/* ws == NULL with ws_bytes == 0 checks (and repairs) the current device's
+ * static scratch of lora_apply_packed_noalloc instead. */
 
 /* Byte offsets, inside the workspace, of the segment arrays written by
  * lora_build_segments, so callers and tests can read them back:
@@ -281,6 +285,34 @@ lora_status_t lora_plan_packed(const void *y, int64_t ldy, int64_t y_col_offset,
                                int32_t R, const int32_t *idx, const int32_t *slot_rank,
                                const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                                const void *ws, size_t ws_bytes, int32_t *chosen_path);
+
+/*
+ * lora_apply_packed without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and calls no
+ * allocating routine.  Its scratch is one file-scope device array of
+ * LORA_STATIC_SCRATCH_BYTES per GPU (held until the process ends), zero-filled
+ * by the first call on each device (a fill kernel on `stream`).  Same
+ * arguments and results as lora_apply_packed, with these differences:
+ *   - a call whose workspace regions do not fit (lora_workspace_size() less
+ *     its end region must fit in half the array, and the end region in the
+ *     other half) returns LORA_E_SCRATCH before anything is enqueued; decode
+ *     batches up to T 1024, K 8192, 3 slices, R 32 fit;
+ *   - LORA_FLAG_SEGMENTS_READY is ignored: every call builds its segments;
+ *   - every call on a GPU shares that GPU's array and leaves it as the next
+ *     call needs it, so calls that overlap in time on one GPU (on different
+ *     streams, or from different host threads) race; order them on one
+ *     stream;
+ *   - lora_workspace_check(NULL, 0, stream) reports a RELAY give-up in it.
+ */
+#define LORA_STATIC_SCRATCH_BYTES (32u << 20)
+lora_status_t lora_apply_packed_noalloc(void *y, int64_t ldy, int64_t y_col_offset,
+                                        const void *x, int64_t ldx, int32_t T, int32_t K,
+                                        const void *const *A, const void *const *B,
+                                        const int64_t *N, int32_t S, int32_t L, int32_t R,
+                                        const int32_t *idx, const int32_t *slot_rank,
+                                        const float *scale, int32_t dtype, int32_t path,
+                                        uint32_t flags, void *stream);
 
 /* ------------------------------------------------------------------------
  * Fused-MoE LoRA ([vLLM] FusedMoEWithLoRA; shared-outer layout from [PR]

@@ -325,3 +325,12 @@ def test_plan_fails_as_the_call_would(kw):
     ap = {k: v for k, v in kw.items()}
     assert st != aa.LORA_OK
     assert st == _apply(**ap)
+
+
+def test_noalloc_rejects_sizes_past_its_scratch():
+    lib = aa.lib()
+    args = [FAKE, 28672, 0, FAKE, 4096, 8192, 4096, _ptrs(2), _ptrs(2), (C.c_int64 * 2)(14336, 14336),
+            2, 16, 64, FAKE, FAKE, FAKE, aa.LORA_DT_BF16, 0, 0, None]
+    assert lib.lora_apply_packed_noalloc(*args) == aa.LORA_E_SCRATCH
+    args[16] = 9                                  # a bad dtype is reported first
+    assert lib.lora_apply_packed_noalloc(*args) == aa.LORA_E_DTYPE
