@@ -301,23 +301,28 @@ int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offs
     }
     if (p.path == LORA_PATH_GROUPED) {
         // two launches that derive their token groups from idx, or the
-        // segment build and launches that read the groups from its table
+        // segment build and launches that read the groups from its table;
+        // a shared lora_a is shrunk once (slice 0) and every slice's expand
+        // adds that shrink
         const SegPtrs *gseg = grp_discovers(T, L) ? nullptr : &seg;
         if (gseg && !(flags & LORA_FLAG_SEGMENTS_READY))
             CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));
         float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.partial);
+        const int32_t Ssh = p.shared_a ? 1 : S;
+        const Slices slsh = p.shared_a ? make_slices(A, B, N, 1, y_col_offset) : sl;
+        const bool sh = p.shared_a != 0;
         if (R > kGrpMaxPartialRank) {
             // large ranks: the K chunks are summed into the token-ordered buffer first
             int32_t n_kc = 0;
-            CHECK(grp_shrink_part(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
-            CHECK(launched(launch_grp_reduce(T, S, L, R, idx, slot_rank, part, n_kc, buf, gseg, st)));
+            CHECK(grp_shrink_part(x, ldx, T, K, slsh, Ssh, L, R, idx, slot_rank, part, wl, gseg, st, &n_kc));
+            CHECK(launched(launch_grp_reduce(T, Ssh, L, R, idx, slot_rank, part, n_kc, buf, gseg, st)));
             return launched(launch_grp_expand(y, ldy, T, 1, sl, S, L, R, idx, slot_rank, scale,
-                                              nullptr, buf, nullptr, gseg, st));
+                                              nullptr, buf, nullptr, gseg, st, sh));
         }
-        CHECK(launched(launch_grp_shrink(x, ldx, T, K, sl, S, L, R, idx, slot_rank, part, nullptr,
+        CHECK(launched(launch_grp_shrink(x, ldx, T, K, slsh, Ssh, L, R, idx, slot_rank, part, nullptr,
                                          gseg, st)));
         return launched(launch_grp_expand(y, ldy, T, grp_kchunks(K), sl, S, L, R, idx, slot_rank,
-                                          scale, part, nullptr, nullptr, gseg, st));
+                                          scale, part, nullptr, nullptr, gseg, st, sh));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
         CHECK(launched(launch_segments(idx, slot_rank, T, L, R, seg, st)));

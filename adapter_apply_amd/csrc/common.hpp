@@ -371,12 +371,13 @@ hipError_t launch_grp_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
                              const int32_t *slot_rank, float *part, int32_t *n_kc_out,
                              const SegPtrs *seg, hipStream_t st);
 // Adds the partials (n_kc chunks, or the count at n_kc_in capped at n_kc) or,
-// when buf is given, the token-ordered buffer [S][T][R].
+// when buf is given, the token-ordered buffer [S][T][R]; shared_a: every slice
+// adds slice 0's (the shrink of one lora_a shared by all slices).
 hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, const Slices &sl,
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *scale, const float *part,
                              const float *buf, const int32_t *n_kc_in, const SegPtrs *seg,
-                             hipStream_t st);
+                             hipStream_t st, bool shared_a = false);
 // With a segment table of keyed tiles (slot * ekey + expert), pass ekey; T is
 // the number of items (positions of the partials, rows of buf).
 hipError_t launch_grp_reduce(int32_t T, int32_t S, int32_t L, int32_t R, const int32_t *idx,

@@ -242,6 +242,7 @@ struct GrpExpandArgs {
     const float *part;       // [S][n_kc][T][R] rows by slot-sorted position, or
     const float *buf;        // [S][T][R] rows by token (then n_kc = 1)
     const int32_t *n_kc_in;  // or null: chunk count written by the shrink, at most n_kc
+    int32_t shared;          // every slice reads slice 0's partials / buffer (one lora_a)
     Slices sl;
     int32_t chunk_start[kMaxSlices + 1];
     GrpTable tab;
@@ -323,8 +324,9 @@ __global__ __launch_bounds__(kThreads) void k_grp_expand(GrpExpandArgs a) {
     for (int v = 0; v < NQ; ++v) {
         const int q = min(tid % Q + kThreads * v, Q - 1);
         const int pt = min(q / (R / 4), ntok - 1);
-        const float *pbase = a.buf ? a.buf + ((int64_t)sg * a.T + tokl[pt]) * R + 4 * (q % (R / 4))
-                                   : a.part + ((int64_t)sg * n_kc * a.T + pos0 + pt) * R + 4 * (q % (R / 4));
+        const int sp = a.shared ? 0 : sg;
+        const float *pbase = a.buf ? a.buf + ((int64_t)sp * a.T + tokl[pt]) * R + 4 * (q % (R / 4))
+                                   : a.part + ((int64_t)sp * n_kc * a.T + pos0 + pt) * R + 4 * (q % (R / 4));
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
             const int kcl = min(h + H * i, n_kc - 1);
@@ -534,8 +536,9 @@ hipError_t launch_grp_expand(void *y, int64_t ldy, int32_t T, int32_t n_kc, cons
                              int32_t S, int32_t L, int32_t R, const int32_t *idx,
                              const int32_t *slot_rank, const float *scale, const float *part,
                              const float *buf, const int32_t *n_kc_in, const SegPtrs *seg,
-                             hipStream_t st) {
+                             hipStream_t st, bool shared_a) {
     GrpExpandArgs a;
+    a.shared = shared_a ? 1 : 0;
     a.tab = grp_table(seg);
     a.y = static_cast<uint16_t *>(y); a.ldy = ldy;
     a.T = T; a.S = S; a.L = L; a.R = R;

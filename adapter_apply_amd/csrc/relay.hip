@@ -38,7 +38,10 @@
 //     lora_a rows line by line (8 rows x 128 B per instruction), stages them
 //     in swizzled LDS and runs v_mfma_f32_16x16x32_bf16 (two 16-token tiles);
 //     the 4 waves are summed in order.  Output: fp32 [S][n_kc][T][R] by
-//     slot-sorted token position.
+//     slot-sorted token position.  When every slice passes the same lora_a
+//     ([vLLM] MergedQKVParallelLinearWithLoRA copies one checkpoint lora_a
+//     into every slice) only slice 0's shrink items run, and the expand items
+//     of every slice add slice 0's partials.
 //   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g (16b .. 16b + 15 for
 //     outputs wider than 16384 columns), 512 output columns of one slice.
 //     lora_b rows and y rows are loaded before the wait; after it the K-chunk
@@ -78,6 +81,8 @@ struct RelayArgs {
     int32_t n_chunks;    // 512-column chunks over all slices
     int32_t max_groups;
     int32_t per_p;       // shrink blocks per XCD
+    int32_t S_shrink;    // slices with a shrink of their own: S, or 1 when every slice
+                         // shares one lora_a (the expands of all slices read slice 0's)
     const int32_t *idx;
     const int32_t *slot_rank;
     const float *scale;
@@ -152,19 +157,23 @@ struct RelaySmem {
     static constexpr int kPart = kWaves * kG * (RP + 4) * 4;   // aliases the staging
     static constexpr int kProd = kStage > kPart ? kStage : kPart;
     static constexpr int kBStage = kWaves * kColsW * RP * 2;   // expand: lora_b rows
-    static constexpr int kDelta = kSubTok * (kCols + 4) * 4;   // expand: fp32 deltas (aliases)
-    static constexpr int kCons = kBStage > kDelta ? kBStage : kDelta;
+    static constexpr int kDelta = kSubTok * (kCols + 4) * 4;   // expand: fp32 deltas
+    // the deltas get an LDS area of their own where that keeps the work-group
+    // under 40 KB (four per CU), else they alias the staging after a barrier
+    static constexpr bool kDeltaAliases = kBStage + kSubTok * (kCols + 4) * 4 > 40 * 1024;
+    static constexpr int kDeltaOff = kDeltaAliases ? 0 : kBStage;
+    static constexpr int kCons = kDeltaOff + kDelta > kBStage ? kDeltaOff + kDelta : kBStage;
     static constexpr int kUnion = kProd > kCons ? kProd : kCons;
     static constexpr int PP = kSubTok * RP / 2;                // partial pairs per K chunk
-    static constexpr int Q = kThreads / PP;                    // K-chunk groups of the sum
+    static_assert(PP % kWave == 0 && PP <= kThreads, "pairs of a block fill whole waves");
 };
 
 // NRB: 16-rank blocks of R (1 or 2); MKC: bound on the K chunks (16 or 32);
 // SUB: tokens per expand item (8, or 16 for wide outputs, where fewer expand
-// work-groups re-read each lora_b block; at rank 16 and K <= 4096 an
-// occupancy bound keeps four work-groups per CU without spills).
+// work-groups re-read each lora_b block).  At rank 16 and K <= 4096 an
+// occupancy bound keeps four work-groups per CU without spills.
 template <int NRB, int MKC, int SUB>
-__global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 : 1) void k_dec_relay(RelayArgs a) {
+__global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_dec_relay(RelayArgs a) {
     constexpr int kSubTok = SUB;
     constexpr int kSubs = kG / SUB;
     using SM = RelaySmem<NRB, SUB>;
@@ -172,15 +181,13 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
     constexpr int LPS = RR / 8;                    // load instructions per wave (8 rows x 128 B)
     constexpr int BROW = RP * 2;                   // bytes of one lora_b row
     constexpr int BLD = kColsW * BROW / 1024;      // load instructions for a wave's lora_b rows
-    constexpr int PP = SM::PP, Q = SM::Q;
-    constexpr int KCQ = MKC / Q;                     // K chunks per summing thread, at most
+    constexpr int PP = SM::PP;
     constexpr int TW = kSubTok / kWaves;             // y rows per wave
 
     __shared__ __attribute__((aligned(16))) char s_union[SM::kUnion];
-    __shared__ __attribute__((aligned(16))) float s_red[Q][kSubTok][RP];
     __shared__ __attribute__((aligned(16))) uint16_t s_buf[16][RP + 8];   // MFMA tile: 16 tokens
     __shared__ RelayDisc d;
-    __shared__ int s_flag;
+    __shared__ int s_last[1];
     __shared__ float s_scale[kWave];
     __shared__ RelaySlice s_sl;
 
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
     const bool shrink = j < a.per_p;
     int g, kc = 0, chunk = 0, sub = 0;
     if (shrink) {
-        const int u = (j / a.S) * 8 + xcd;
+        const int u = (j / a.S_shrink) * 8 + xcd;
         g = u / a.n_kc;
         kc = u % a.n_kc;
     } else {
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
             s_scale[lane] = a.scale[min(lane, a.L - 1)];
             if (lane == 0) {
                 int sg = 0;
-                if (shrink) sg = j % a.S;
+                if (shrink) sg = j % a.S_shrink;
                 else
                     while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
                 s_sl.sg = sg;
@@ -307,7 +314,10 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
     const int ct = min(kSubTok, ntok - t0);
     const int Ns = (int)s_sl.n;
     const int n_base = (chunk - s_sl.c0) * kCols;
-    const int n_readers = s_sl.c1 - s_sl.c0;   // one per chunk of the slice
+    // readers of a block of partials: one per chunk of the slice, or of every
+    // slice when they share the shrink
+    const int n_readers = a.S_shrink == 1 && a.S > 1 ? a.n_chunks : s_sl.c1 - s_sl.c0;
+    const int sp = a.S_shrink == 1 ? 0 : sg;   // the slice whose partials this item adds
     const float sc = s_scale[s];
 
     // loads that do not depend on the shrink: lora_b rows of the wave's 128
@@ -329,64 +339,71 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
         yv[i] = ldg_nt(yrow[i] + min(n_base + 8 * lane, Ns - 8));
     }
 
-    int32_t *readers = a.sync + kLine * ((g * a.S + sg) * kSubs + sub);
-    const float *blk = a.part + ((int64_t)sg * a.n_kc * a.T + pos0 + t0) * RP;   // chunk k: + k * T * RP
-    // K-chunk partials of the block's tokens: thread (pair p, K group q) adds chunks
-    // q, q + Q, ... in order; the Q groups are then added in order.  The loads
-    // are the wait: they repeat while any word of the block is still unwritten
-    // (by the time the expand-side loads above have landed, the shrink items
-    // have mostly stored, so one round trip usually suffices).
-    {
-        const int p = tid % PP, q = tid / PP;
-        const int tk = p / (RP / 2), jp = 2 * (p % (RP / 2));
+    int32_t *readers = a.sync + kLine * ((g * a.S + sp) * kSubs + sub);
+    const float *blk = a.part + ((int64_t)sp * a.n_kc * a.T + pos0 + t0) * RP;   // chunk k: + k * T * RP
+
+    // Each wave stages its lora_b rows (fragment order below): the waves that
+    // do not poll at once, the polling ones when their data is in (their
+    // first poll must not wait for the lora_b loads).  The buffer's padding
+    // token rows are zeroed before the wait, so that after it only the buffer
+    // itself stands between the partials and the MFMA.
+    char *stage = s_union + w * (kColsW * BROW);
+    const auto stage_b = [&]() {
+#pragma unroll
+        for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
+    };
+    stage_b();
+    for (int i = tid; i < (16 - kSubTok) * RP; i += kThreads)
+        s_buf[kSubTok + i / RP][i % RP] = 0;
+
+    // K-chunk partials of the block's tokens: the first PP threads (whole
+    // waves) each own one pair of rank entries of one token and add its
+    // n_kc chunks in order.  The loads are the wait: a wave repeats them while
+    // any of its words is still unwritten; the other waves go on to the
+    // barrier.  (By the time the expand-side loads above have landed, the
+    // shrink items have mostly stored, so one round trip usually suffices.)
+    if (tid < PP) {
+        const int tk = tid / (RP / 2), jp = 2 * (tid % (RP / 2));
         const float *src = blk + (tk < ct ? tk : 0) * RP + jp;
-        uint64_t pv[KCQ];
+        uint64_t pv[MKC];
         for (int n = 0;; ++n) {
             bool ok = true;
 #pragma unroll
-            for (int c = 0; c < KCQ; ++c)
-                pv[c] = ld_coherent(src + (int64_t)min(q + Q * c, a.n_kc - 1) * a.T * RP);
+            for (int c = 0; c < MKC; ++c)
+                pv[c] = ld_coherent(src + (int64_t)min(c, a.n_kc - 1) * a.T * RP);
 #pragma unroll
-            for (int c = 0; c < KCQ; ++c)
+            for (int c = 0; c < MKC; ++c)
                 ok = ok && (uint32_t)pv[c] != 0u && (uint32_t)(pv[c] >> 32) != 0u;
-            if (__syncthreads_and(ok) && !a.give_up) break;
+            if (__all(ok) && !a.give_up) break;
             if (n >= (a.give_up ? 0 : kSpin)) {
-                if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(4);
         }
         float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < KCQ; ++c)
-            if (q + Q * c < a.n_kc) {
+        for (int c = 0; c < MKC; ++c)
+            if (c < a.n_kc) {
                 v0 += __uint_as_float((uint32_t)pv[c] ^ kReady);
                 v1 += __uint_as_float((uint32_t)(pv[c] >> 32) ^ kReady);
             }
-        s_red[q][tk][jp] = v0;
-        s_red[q][tk][jp + 1] = v1;
+        if (jp >= r || tk >= ct) v0 = 0.f;
+        if (jp + 1 >= r || tk >= ct) v1 = 0.f;
+        *reinterpret_cast<uint32_t *>(&s_buf[tk][jp]) = pack_bf16x2(v0, v1);
     }
-    // this work-group has read the block: count it (the last reader clears
-    // it); the count is used only at the end, so its round trip overlaps the
-    // expand
-    int nread = 0;
-    if (tid == 0) nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();
-    for (int i = tid; i < 16 * RP; i += kThreads) {
-        const int tk = i / RP, jj = i - tk * RP;
-        float v = 0.f;
-        if (tk < kSubTok) {
-#pragma unroll
-            for (int q = 0; q < Q; ++q) v += s_red[q][tk][jj];
-        }
-        if (jj >= r || tk >= ct) v = 0.f;
-        s_buf[tk][jj] = (uint16_t)f32_to_bf16_rne(v);
-    }
-    // the wave's lora_b rows into its staging area (fragment order below)
-    char *stage = s_union + w * (kColsW * BROW);
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
-    lds_barrier();
+    // The block is read: count it, one count per work-group (a block has as
+    // many readers as its slice has column chunks, all adding to one counter).
+    // With one polling wave it counts right after its poll, so the round trip
+    // overlaps the barrier and the expand; with several, after the barrier
+    // that follows all their reads.  The work-group that makes the last count
+    // clears the block.
+    int nread = -1;
+    if (PP == kWave && tid == 0)
+        nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();   // the buffer is complete, the lora_b rows are staged
+    if (PP > kWave && tid == 0)
+        nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // D[n][t] = B[n][:] . buf[t][:]  (MFMA 16x16x16; tokens past the block are zero)
     uint2 bfr[NRB];
@@ -403,16 +420,18 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
         }
         out[nb] = acc;
     }
-    if (tid == 0) s_flag = nread;
-    lds_barrier();   // staging done (the deltas alias it)
+    if (SM::kDeltaAliases) lds_barrier();   // every wave is done with the staging
+    float *s_delta = reinterpret_cast<float *>(s_union + SM::kDeltaOff);
     // lane: token `row`, columns 128 w + 16 nb + 4 quad .. + 3 of the chunk
-    float *s_delta = reinterpret_cast<float *>(s_union);
     if (row < kSubTok) {
 #pragma unroll
         for (int nb = 0; nb < kColsW / 16; ++nb)
             *reinterpret_cast<float4 *>(s_delta + row * (kCols + 4) + w * kColsW + 16 * nb + 4 * quad) =
                 make_float4(sc * out[nb][0], sc * out[nb][1], sc * out[nb][2], sc * out[nb][3]);
     }
+    // the count is needed before the y stores: a wait on it after them would
+    // also wait for the stores (vmcnt counts both)
+    if (tid == 0) s_last[0] = nread == n_readers - 1;
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(kThreads, (SUB == 16 && NRB == 1 && MKC == 16) ? 4 
         }
     }
     // the last reader of the block writes it back to zero for the next call
-    if (s_flag == n_readers - 1) {
+    if (s_last[0]) {
         for (int e = tid; e < a.n_kc * ct * (RP / 2); e += kThreads) {
             const int k = e / (ct * (RP / 2)), rem = e - k * (ct * (RP / 2));
             st_coherent(const_cast<float *>(blk) + (int64_t)k * a.T * RP + 2 * rem, 0ull);
@@ -470,7 +489,11 @@ hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, in
     a.n_chunks = c;
     a.n_kc = K / kKc;
     a.max_groups = relay_max_groups(T, L);
-    a.per_p = (a.max_groups * a.n_kc + 7) / 8 * S;
+    // one lora_a for every slice (the same pointer): one shrink for all
+    bool shared_a = S > 1;
+    for (int s = 1; s < S && shared_a; ++s) shared_a = sl.a[s] == sl.a[0];
+    a.S_shrink = shared_a ? 1 : S;
+    a.per_p = (a.max_groups * a.n_kc + 7) / 8 * a.S_shrink;
     // wide outputs: 16-token expand items (half the lora_b block reads)
     int64_t ntot = 0;
     for (int s = 0; s < S; ++s) ntot += sl.n[s];

@@ -713,3 +713,31 @@ def test_relay_forced_give_up_reported_and_repaired(oracle_mod):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
         aa.lora_workspace_check(d.ws)
         assert int(torch.count_nonzero(d.ws)) == 0
+
+
+@pytest.mark.parametrize("path", [RLY, GRP])
+def test_shared_lora_a_decode_config_repeated(oracle_mod, path):
+    """The decode QKV workload with one lora_a for every slice: the shrink runs
+    once (slice 0's) and the expands of all three slices add it.  Three calls in
+    a row on one workspace equal each other bit for bit and the oracle within
+    tolerance, and the K-split region is all zero after each call (the last of
+    the readers over every slice clears the shared partials)."""
+    c = shared_a_case(synth.config_decode())
+    d = on_device_shared_a(c)
+    ref = oracle_y(oracle_mod, c)
+    first = None
+    for call in range(3):
+        log(f"case shared lora_a decode config path={path} call={call}")
+        d.reset_y()
+        d.apply(path)
+        y = d.y_host()
+        if path == RLY:
+            assert int(torch.count_nonzero(d.ws)) == 0
+        if first is None:
+            first = y
+            err, rel = bounds.check_bf16_tolerance(y, ref)
+            log(f"  max abs err {err:.3e} rel {rel:.3e}")
+            assert_passthrough(c, y)
+        else:
+            assert np.array_equal(y.view(np.uint32), first.view(np.uint32))
+    assert canaries_intact(d.yfull)
