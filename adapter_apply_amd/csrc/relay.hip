@@ -7,12 +7,15 @@
 // of a (group, slice) is done once, split over K chunks of 256 columns; every
 // expand work-group of that (group, slice) adds the chunks' partials.
 //
-// Roles.  Blocks [0, 8 * per_p) shrink, the rest expand.  Work-groups are
+// Roles.  The grid has two parts, the groups a batch usually fills and then
+// the rest (a group's count is known only after the discovery), each part its
+// shrink blocks first, then its expand blocks; so idle work-groups of the
+// second part do not hold slots ahead of working ones.  Work-groups are
 // dispatched in block order (observed on gfx950: the XCC_ID register reads back
 // block % 8 for every block, in order; the programming model does not promise
-// it), so when an expand work-group starts waiting, every shrink work-group has
-// already been dispatched; shrink work-groups wait for nothing, so every wait
-// ends.  The waits are bounded all the same: past kSpin polls the work-group
+// it), so when an expand work-group starts waiting, every shrink work-group of
+// its group has already been dispatched; shrink work-groups wait for nothing,
+// so every wait ends.  The waits are bounded all the same: past kSpin polls the work-group
 // sets the error word of the workspace and goes on (nothing hangs; that call's
 // results are not valid, and late partials may be left in the region).
 // lora_workspace_check reports the error and zero-fills the workspace.
@@ -80,7 +83,8 @@ struct RelayArgs {
     int32_t n_kc;        // K / kKc
     int32_t n_chunks;    // 512-column chunks over all slices
     int32_t max_groups;
-    int32_t per_p;       // shrink blocks per XCD
+    int32_t n_first;     // groups in the first part of the grid
+    int32_t pstart[4];   // first block of: part 1 expand, part 2 shrink, part 2 expand, the end
     int32_t S_shrink;    // slices with a shrink of their own: S, or 1 when every slice
                          // shares one lora_a (the expands of all slices read slice 0's)
     const int32_t *idx;
@@ -193,21 +197,27 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
-    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
-    const bool shrink = j < a.per_p;
+    // Two parts, each its shrink items then its expand items: the groups a
+    // batch usually fills, then the rest (known only after the discovery),
+    // so that idle work-groups do not hold slots ahead of working ones.
+    const int b = blockIdx.x;
+    const bool second = b >= a.pstart[1];
+    const int g0 = second ? a.n_first : 0, gn = second ? a.max_groups : a.n_first;
+    const bool shrink = b < a.pstart[0] || (second && b < a.pstart[2]);
+    const int rel = b - (shrink ? (second ? a.pstart[1] : 0) : (second ? a.pstart[2] : a.pstart[0]));
+    const int xcd = rel % 8, j = rel / 8;
     int g, kc = 0, chunk = 0, sub = 0;
     if (shrink) {
         const int u = (j / a.S_shrink) * 8 + xcd;
-        g = u / a.n_kc;
+        g = g0 + u / a.n_kc;
         kc = u % a.n_kc;
     } else {
-        const int jc = j - a.per_p;
-        const int v = (jc / kSubs) * 8 + xcd;
-        sub = jc % kSubs;
-        g = v / a.n_chunks;
+        const int v = (j / kSubs) * 8 + xcd;
+        sub = j % kSubs;
+        g = g0 + v / a.n_chunks;
         chunk = v % a.n_chunks;
     }
-    if (g >= a.max_groups) g = -1;
+    if (g >= gn) g = -1;
     {
         const auto pick = [=](int n) { return g < n ? g : -1; };
         // wave 1 fetches the slot scales (L <= 64) and the item's slice
@@ -493,13 +503,27 @@ hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, in
     bool shared_a = S > 1;
     for (int s = 1; s < S && shared_a; ++s) shared_a = sl.a[s] == sl.a[0];
     a.S_shrink = shared_a ? 1 : S;
-    a.per_p = (a.max_groups * a.n_kc + 7) / 8 * a.S_shrink;
+    // The first part holds the groups a batch usually fills: the larger of
+    // T/32 plus half the slots, and the expected number of slots with tokens
+    // (slots drawn uniformly) plus two.
+    {
+        const int tl = T < L ? T : L;
+        const int dense = (T + kG - 1) / kG + (tl + 1) / 2;
+        const int sparse = (int)ceil(L * (1.0 - exp(-(double)T / L))) + 2;
+        a.n_first = min(a.max_groups, dense > sparse ? dense : sparse);
+    }
     // wide outputs: 16-token expand items (half the lora_b block reads)
     int64_t ntot = 0;
     for (int s = 0; s < S; ++s) ntot += sl.n[s];
     const bool wide = ntot > kAutoMaxDecodeCols;
-    const int per_c = (a.max_groups * c + 7) / 8 * (wide ? kG / 16 : kG / 8);
-    dim3 grid((unsigned)(8 * (a.per_p + per_c)));
+    const int subs = wide ? kG / 16 : kG / 8;
+    const auto sblocks = [&](int groups) { return 8 * ((groups * a.n_kc + 7) / 8 * a.S_shrink); };
+    const auto eblocks = [&](int groups) { return 8 * ((groups * c + 7) / 8 * subs); };
+    a.pstart[0] = sblocks(a.n_first);
+    a.pstart[1] = a.pstart[0] + eblocks(a.n_first);
+    a.pstart[2] = a.pstart[1] + sblocks(a.max_groups - a.n_first);
+    a.pstart[3] = a.pstart[2] + eblocks(a.max_groups - a.n_first);
+    dim3 grid((unsigned)a.pstart[3]);
     const bool few = a.n_kc <= 16;
 #define AA_RELAY(NRB, MKC, SUB) hipLaunchKernelGGL((k_dec_relay<NRB, MKC, SUB>), grid, dim3(kThreads), 0, st, a)
     if (R == 16) {
