@@ -24,10 +24,12 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source flags.  relay.hip: one thread's atomic add whose result is used
-# much later; the atomic optimizer would rewrite it into a wave-wide add whose
-# result every lane reads at once, stalling the work-group for the round trip.
-EXTRA = {"relay.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# Per-source flags.  relay.hip, segments.hip: one thread's atomic add whose
+# result is used much later; the atomic optimizer would rewrite it into a
+# wave-wide add whose result every lane reads at once, stalling the work-group
+# for the round trip.
+EXTRA = {"relay.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+         "segments.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:

@@ -286,7 +286,10 @@ int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offs
         return launched(launch_dec_fused(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale, st));
     }
     const WsLayout wl = ws_layout(T, K, S, R, L);
-    const SegPtrs seg = seg_ptrs(ws, wl.seg);
+    SegPtrs seg = seg_ptrs(ws, wl.seg);
+    // the single-launch segment build's region in the end area, above this
+    // call's own regions
+    attach_seg_x(seg, ws, ws_bytes, T, L, 0, wl.buf + align256(sizeof(float) * (size_t)S * T * R));
     const Slices sl = make_slices(A, B, N, S, y_col_offset);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + wl.buf);
     if (p.path == LORA_PATH_RELAY) {
@@ -430,8 +433,9 @@ lora_status_t lora_build_segments(const int32_t *idx, const int32_t *slot_rank, 
     if (T > 0 && !idx) return LORA_E_NULL;
     const SegLayout l = seg_layout(T, L);
     CHECK(check_ws(ws, ws_bytes, l.end));
-    return launched(launch_segments(idx, slot_rank, T, L, R, seg_ptrs(ws, l),
-                                    static_cast<hipStream_t>(stream)));
+    SegPtrs seg = seg_ptrs(ws, l);
+    attach_seg_x(seg, ws, ws_bytes, T, L, 0, l.end);
+    return launched(launch_segments(idx, slot_rank, T, L, R, seg, static_cast<hipStream_t>(stream)));
 }
 
 lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int32_t K,

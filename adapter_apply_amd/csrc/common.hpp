@@ -98,7 +98,7 @@ struct SegLayout {
     size_t perm;          // int32[T]
     size_t tiles_dec;     // int4[max_tiles_dec]: slot, begin, end, 0
     size_t tiles_pre;     // int4[max_tiles_pre]
-    size_t counts;        // int32[ceil(T / kSegThreads)][L + 1]: split build, per work-group
+    size_t counts;        // int32[ceil(T / kSegThreads)][L + 1]: two-launch build, per work-group
     size_t end;
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
@@ -151,6 +151,24 @@ inline RelayRegion relay_region(size_t ws_bytes, int32_t T, int32_t K, int32_t S
     return r;
 }
 
+// The single-launch segment build (more than kSegSplitItems items, at most
+// kSegOneMaxWg work-groups) exchanges its work-groups' per-key counts through
+// a region that, like the relay region, must be zero on entry and is left
+// zero: [counts int32 [n_wg][keys + 1]][one 256-byte line: done counter].  It
+// sits at the end of the workspace, just below the error word's line (it may
+// overlap the relay region: both are zero between calls).  Past
+// kSegOneMaxWg work-groups the build takes two launches, but the region stays
+// reserved, so that the size grows with every argument.  (A lone build of at
+// most kSegSplitItems items runs in one work-group and does not use it; the
+// token job of the fused-MoE alignment, built beside the pair job, does.)
+constexpr int kSegOneMaxWg = 16;
+inline size_t seg_x_bytes(int32_t n_items, int32_t nkeys) {
+    int64_t n_wg = ((int64_t)n_items + kSegThreads - 1) / kSegThreads;
+    if (n_wg < 1) n_wg = 1;
+    if (n_wg > kSegOneMaxWg) n_wg = kSegOneMaxWg;
+    return align256(sizeof(int32_t) * (size_t)n_wg * (nkeys + 1)) + 256;
+}
+
 inline int32_t max_tiles(int32_t T, int32_t L, int32_t tile) {
     // sum over slots of ceil(c_s / tile) <= T / tile + (number of non-empty slots)
     int64_t m = (int64_t)T / tile + (T < L ? T : L) + 1;
@@ -186,7 +204,10 @@ inline WsLayout ws_layout(int32_t T, int32_t K, int32_t S, int32_t R, int32_t L)
     w.partial = o; o = align256(o + sizeof(float) * (size_t)w.n_kchunks * (size_t)T * S * R);
     w.buf = o;     o = align256(o + sizeof(float) * (size_t)S * T * R);
     w.relay = relay_bytes(T, K, S, R, L);
-    w.end = o + w.relay + 256;   // the relay region, then the error word's line
+    // the end area (relay region and the single-launch segment build's
+    // region, which may overlap), then the error word's line
+    const size_t x = seg_x_bytes(T, L);
+    w.end = o + (w.relay > x ? w.relay : x) + 256;
     return w;
 }
 
@@ -215,7 +236,9 @@ inline MoeWsLayout moe_ws_layout(int32_t T, int32_t k, int32_t S, int32_t R, int
     m.part = align256(m.buf + sizeof(float) * (size_t)S * T * k * R);
     const int64_t items = (int64_t)T * k < kMoeSplitItems ? (int64_t)T * k : kMoeSplitItems;
     m.part_bytes = sizeof(float) * (size_t)kMoeSplitChunks * items * S * R;
-    m.end = align256(m.part + m.part_bytes) + 256;   // error word's line: never written
+    // the single-launch segment build's regions of the pair and token jobs,
+    // then the error word's line
+    m.end = align256(m.part + m.part_bytes) + seg_x_bytes(T * k, L * E) + seg_x_bytes(T, L) + 256;
     return m;
 }
 
@@ -232,6 +255,9 @@ struct SegPtrs {
     int4 *tiles_dec;
     int4 *tiles_pre;
     int32_t *counts;
+    int32_t *xcounts;     // single-launch build's region (see seg_x_bytes), or null:
+    int32_t *xdone;       //   the build takes two launches
+    int32_t *err;         // the workspace's error word (a wait of the build gave up)
     int32_t max_tiles_dec;
     int32_t max_tiles_pre;
 };
@@ -245,9 +271,26 @@ inline SegPtrs seg_ptrs(void *ws, const SegLayout &l) {
     p.tiles_dec = reinterpret_cast<int4 *>(b + l.tiles_dec);
     p.tiles_pre = reinterpret_cast<int4 *>(b + l.tiles_pre);
     p.counts = reinterpret_cast<int32_t *>(b + l.counts);
+    p.xcounts = p.xdone = p.err = nullptr;
     p.max_tiles_dec = l.max_tiles_dec;
     p.max_tiles_pre = l.max_tiles_pre;
     return p;
+}
+
+// Gives `seg` the single-launch build's region of (n_items, nkeys) at the end
+// of a workspace of ws_bytes, `below` bytes under the error word's line, when
+// the build takes one launch and the region stays above byte `floor` (the
+// caller's own regions).  Otherwise the build keeps two launches.
+inline void attach_seg_x(SegPtrs &seg, void *ws, size_t ws_bytes, int32_t n_items, int32_t nkeys,
+                         size_t below, size_t floor) {
+    const size_t xb = seg_x_bytes(n_items, nkeys);
+    const size_t err = err_word_offset(ws_bytes);
+    const int64_t n_wg = ((int64_t)n_items + kSegThreads - 1) / kSegThreads;
+    if (n_wg > kSegOneMaxWg || err < below + xb || err - below - xb < floor) return;
+    char *b = static_cast<char *>(ws);
+    seg.xcounts = reinterpret_cast<int32_t *>(b + err - below - xb);
+    seg.xdone = reinterpret_cast<int32_t *>(b + err - below - 256);
+    seg.err = reinterpret_cast<int32_t *>(b + err);
 }
 
 // Per-slice pointers and widths passed by value to kernels.

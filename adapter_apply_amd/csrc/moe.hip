@@ -112,16 +112,22 @@ lora_status_t moe_check_meta(int32_t T, int32_t k, int32_t E, int32_t L, int32_t
 
 lora_status_t moe_segments(const int32_t *topk_ids, const int32_t *idx, const int32_t *slot_rank,
                            int32_t T, int32_t k, int32_t E, int32_t L, int32_t R,
-                           const MoeWsLayout &ml, void *ws, hipStream_t st) {
+                           const MoeWsLayout &ml, void *ws, size_t ws_bytes, hipStream_t st) {
     if (T == 0) {
         CHECK(launched(launch_segments_keyed(idx, slot_rank, nullptr, 1, 1, T, L, R,
                                              seg_ptrs(ws, ml.tok), st)));
         return launched(launch_segments_keyed(idx, slot_rank, topk_ids, k, E, T * k, L, R,
                                               seg_ptrs(ws, ml.pair), st));
     }
-    // the token and the (token, k) pair segments in one pair of launches
-    const SegJob jobs[2] = {seg_job_of(nullptr, 1, 1, T, seg_ptrs(ws, ml.tok)),
-                            seg_job_of(topk_ids, k, E, T * k, seg_ptrs(ws, ml.pair))};
+    // the token and the (token, k) pair segments together: one launch when
+    // their exchange regions fit in the end area (above the buffers), else a
+    // pair of launches
+    SegPtrs tok = seg_ptrs(ws, ml.tok), pair = seg_ptrs(ws, ml.pair);
+    const size_t xp = seg_x_bytes(T * k, L * E), xt = seg_x_bytes(T, L);
+    const size_t floor = ml.end - xp - xt - 256;
+    attach_seg_x(pair, ws, ws_bytes, T * k, L * E, 0, floor);
+    attach_seg_x(tok, ws, ws_bytes, T, L, xp, floor);
+    const SegJob jobs[2] = {seg_job_of(nullptr, 1, 1, T, tok), seg_job_of(topk_ids, k, E, T * k, pair)};
     return launched(launch_segments_split(idx, slot_rank, L, R, jobs, 2, st));
 }
 
@@ -160,7 +166,7 @@ lora_status_t moe_lora_align(const int32_t *topk_ids, const int32_t *idx, const 
     const MoeWsLayout ml = moe_ws_layout(T, top_k, 1, R, L, E);
     if (ws_bytes < ml.pair.end) return LORA_E_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    CHECK(moe_segments(topk_ids, idx, slot_rank, T, top_k, E, L, R, ml, ws, st));
+    CHECK(moe_segments(topk_ids, idx, slot_rank, T, top_k, E, L, R, ml, ws, ws_bytes, st));
     if (!want_out) return LORA_OK;
     return launched(launch_moe_align_out(seg_ptrs(ws, ml.pair), T, top_k, E, L, block_m, sorted_ids,
                                          block_expert, num_post_padded, st));
@@ -219,7 +225,7 @@ lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_
                                          slot_rank, scale, st));
     }
     if (!(flags & LORA_FLAG_SEGMENTS_READY))
-        CHECK(moe_segments(topk_ids, idx, slot_rank, T, top_k, E, L, R, ml, ws, st));
+        CHECK(moe_segments(topk_ids, idx, slot_rank, T, top_k, E, L, R, ml, ws, ws_bytes, st));
     const SegPtrs tok = seg_ptrs(ws, ml.tok), pair = seg_ptrs(ws, ml.pair);
     float *buf = reinterpret_cast<float *>(static_cast<char *>(ws) + ml.buf);
     Slices sl{};

@@ -762,9 +762,12 @@ hipError_t launch_pre_shrink(const void *x, int64_t ldx, int32_t T, int32_t K, c
     a.R = R; a.slot_rank = slot_rank; a.seg = seg; a.sl = sl; a.buf = buf;
     a.gm = gm;
     if (a.gm.buf_rows == 0) a.gm.buf_rows = T;
-    // columns per work-group: all of S * R up to 128, in blocks of 32
+    // columns per work-group, in blocks of 32: all of S * R up to 64; past
+    // that 128 when the shrink is split over K (many short tiles), else 64
+    // (long tiles: twice the work-groups for the CUs, and half the LDS reads
+    // per stage of the waves that compute)
     const int sr = S * R;
-    const int ncb = sr <= 32 ? 1 : sr <= 64 ? 2 : 4;
+    const int ncb = sr <= 32 ? 1 : (sr <= 64 || !part) ? 2 : 4;
     a.n_cb = (sr + 32 * ncb - 1) / (32 * ncb);
     // K splits: every split gets at least one stage; the count actually used
     // goes back to the caller (the partials hold that many chunks)

@@ -71,19 +71,49 @@ __device__ __forceinline__ void scatter_step(int s, int t, int nbits, int lane, 
     }
 }
 
+constexpr int kSegSpin = 1 << 20;
+
+__device__ __forceinline__ void st_co32(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_co32(const int32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// block_exclusive_scan with barriers that wait for LDS only
+__device__ int block_exclusive_scan_lds(int v, int *total, int *wsum) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wsum[w] = incl;
+    lds_sync();
+    if (w == 0) {
+        const int s = lane < kSegWaves ? wsum[lane] : 0;
+        const int si = wave_incl_scan(s);
+        if (lane < kSegWaves) wsum[kSegWaves + lane] = si - s;
+        if (lane == kSegWaves - 1) wsum[2 * kSegWaves] = si;
+    }
+    lds_sync();
+    int r = wsum[kSegWaves + w] + incl - v;
+    *total = wsum[2 * kSegWaves];
+    lds_sync();
+    return r;
+}
+
 constexpr int kRegSteps = 16;  // 64-item steps per wave held in registers (<= 16384 items)
 
 // Work tiles of both paths (key-major, item ranges of at most the tile size)
 // and the header.  Thread tid stands for key tid: cnt items from `start`.
-// Every thread of the block calls it.
+// Every thread of the block calls it.  Its scans use LDS barriers, which do
+// not wait for the scatter's stores still in flight.
 __device__ void emit_tiles(int cnt, int start, int n_active, int n_invalid, const SegPtrs &seg,
                            int *wsum) {
     const int tid = threadIdx.x;
     int n_dec = 0, n_pre = 0;
     const int td = (cnt + kDecTile - 1) / kDecTile;
     const int tp = (cnt + kPreTile - 1) / kPreTile;
-    const int od = block_exclusive_scan(td, &n_dec, wsum);
-    const int op = block_exclusive_scan(tp, &n_pre, wsum);
+    const int od = block_exclusive_scan_lds(td, &n_dec, wsum);
+    const int op = block_exclusive_scan_lds(tp, &n_pre, wsum);
     for (int q = 0; q < td; ++q)
         seg.tiles_dec[od + q] = make_int4(tid, start + q * kDecTile,
                                           min(start + (q + 1) * kDecTile, start + cnt), 0);
@@ -323,6 +353,118 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_place(SegJobs a) {
     emit_tiles(tid < nkeys ? tot : 0, start, n_active, n_inv, seg, wsum);
 }
 
+// ---- single-launch build for up to kSegOneMaxWg work-groups per job -------
+// The two passes above in one launch: each work-group counts its 1024 items
+// per key, publishes the counts (stored plus one, so that zero means "not
+// written yet", through agent-scope relaxed atomic stores), then reads every
+// work-group's counts (the loads repeat while any is zero, bounded: past
+// kSegSpin polls the workspace's error word is set and the build goes on),
+// and places its items as the second pass does.  The last work-group to have
+// read them (a done counter) writes the counts and the counter back to zero.
+// Every work-group waits for all of its job's work-groups, so a launch has at
+// most 2 * kSegOneMaxWg work-groups of 1024 threads, resident together on any
+// GPU that is not full.  After the counts are published only LDS barriers
+// are used (a block barrier would also wait for the stores).
+
+__global__ __launch_bounds__(kSegThreads) void k_seg_one(SegJobs a) {
+    extern __shared__ int32_t lds[];
+    int b = 0;
+    const SegJob jb = seg_job(a, &b);
+    const int L = a.L;
+    const int nkeys = jb.topk ? L * jb.E : L;  // <= kSegThreads
+    const int n_wg = jb.n_wg;                  // <= kSegOneMaxWg
+    const SegPtrs &seg = jb.seg;
+    int32_t *wcnt = lds;                       // [kSegWaves][nkeys]
+    int32_t *srank = lds + kSegWaves * nkeys;  // [L]
+    __shared__ int32_t wsum[2 * kSegWaves + 1];
+    __shared__ int32_t s_invalid, s_last;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nbits = nkeys > 1 ? 32 - __clz(nkeys - 1) : 0;
+    const int t = b * kSegThreads + tid;
+    const bool in = t < jb.n_items;
+    const int v = in ? a.idx[jb.topk ? t / jb.k : t] : -1;
+    const int e = (in && jb.topk) ? jb.topk[t] : 0;
+    for (int i = tid; i < L; i += kSegThreads) srank[i] = a.slot_rank ? a.slot_rank[i] : a.R;
+    for (int i = tid; i < kSegWaves * nkeys; i += kSegThreads) wcnt[i] = 0;
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+    int inv = 0;
+    const int key = filt_key(v, e, srank, jb.topk != nullptr, jb.E, L, &inv);
+    int32_t *mycnt = wcnt + w * nkeys;
+    count_step(key, nbits, lane, mycnt);
+    if (inv) atomicAdd(&s_invalid, inv);
+    __syncthreads();
+
+    // publish this work-group's counts per key, and its slot ids past L
+    const int stride = nkeys + 1;
+    for (int kk = tid; kk < nkeys; kk += kSegThreads) {
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < kSegWaves; ++q) c += wcnt[q * nkeys + kk];
+        st_co32(seg.xcounts + (int64_t)b * stride + kk, c + 1);
+    }
+    if (tid == 0) st_co32(seg.xcounts + (int64_t)b * stride + nkeys, s_invalid + 1);
+
+    // Column col of every work-group's counts: the sum over all, and over
+    // those before this one.
+    auto col_sums = [&](int col, int &all, int &pre) {
+        int c[kSegOneMaxWg];
+        for (int n = 0;; ++n) {
+            bool ok = true;
+#pragma unroll
+            for (int u = 0; u < kSegOneMaxWg; ++u) {
+                c[u] = ld_co32(seg.xcounts + (int64_t)min(u, n_wg - 1) * stride + col);
+                ok = ok && c[u] != 0;
+            }
+            if (ok) break;
+            if (n >= kSegSpin) {
+                st_co32(seg.err, 1);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        all = 0; pre = 0;
+#pragma unroll
+        for (int u = 0; u < kSegOneMaxWg; ++u)
+            if (u < n_wg) { all += c[u] - 1; pre += u < b ? c[u] - 1 : 0; }
+    };
+    int tot = 0, before = 0, n_inv = 0, unused = 0;
+    if (tid < nkeys) col_sums(tid, tot, before);
+    if (tid == 0 && b == 0) col_sums(nkeys, n_inv, unused);
+    lds_sync();
+    // every thread of this work-group has read the counts; the count of such
+    // work-groups is used only at the end
+    int done = 0;
+    if (tid == 0) done = __hip_atomic_fetch_add(seg.xdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    int n_active = 0;
+    const int start = block_exclusive_scan_lds(tid < nkeys ? tot : 0, &n_active, wsum);
+    if (tid < nkeys) {
+        int run = start + before;
+        for (int q = 0; q < kSegWaves; ++q) {
+            const int c = wcnt[q * nkeys + tid];
+            wcnt[q * nkeys + tid] = run;
+            run += c;
+        }
+        if (b == 0) seg.slot_start[tid] = start;
+    }
+    if (b == 0 && tid == 0) seg.slot_start[nkeys] = n_active;
+    lds_sync();
+    scatter_step(key, t, nbits, lane, mycnt, seg.perm);
+    if (b == 0) {
+        // work-group 0 of the job: the tail of perm, the tiles and the header
+        for (int i = n_active + tid; i < jb.n_items; i += kSegThreads) seg.perm[i] = -1;
+        emit_tiles(tid < nkeys ? tot : 0, start, n_active, n_inv, seg, wsum);
+    }
+    // the last work-group to have read the counts zeroes them for the next call
+    if (tid == 0) s_last = done == n_wg - 1;
+    lds_sync();
+    if (s_last) {
+        for (int i = tid; i < n_wg * stride; i += kSegThreads) st_co32(seg.xcounts + i, 0);
+        if (tid == 0) st_co32(seg.xdone, 0);
+    }
+}
+
 __global__ void k_fill_zero(uint4 *__restrict__ p, size_t n16, uint8_t *__restrict__ tail,
                             size_t ntail) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -389,6 +531,21 @@ hipError_t launch_segments_split(const int32_t *idx, const int32_t *slot_rank, i
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
+    }
+    // one launch when every job has its exchange region (and so at most
+    // kSegOneMaxWg work-groups), else count and place apart
+    bool one = true;
+    for (int j = 0; j < n_jobs; ++j)
+        one = one && jobs[j].seg.xcounts && jobs[j].seg.xdone && jobs[j].seg.err &&
+              jobs[j].n_wg <= kSegOneMaxWg;
+    if (one) {
+        if (lds > 48 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_seg_one),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(k_seg_one, dim3(n_wg), dim3(kSegThreads), lds, st, a);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL(k_seg_count, dim3(n_wg), dim3(kSegThreads), lds, st, a);
     hipLaunchKernelGGL(k_seg_place, dim3(n_wg), dim3(kSegThreads), lds, st, a);

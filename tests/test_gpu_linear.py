@@ -348,8 +348,13 @@ def test_segments_bit_exact(oracle_mod, seed, T, L):
     rank = rng.integers(0, 3, size=L).astype(np.int32) * 8
     log(f"case segments T={T} L={L}")
     ws = aa.alloc_workspace(T, 64, 1, 16, L)
-    aa.lora_build_segments(dev(idx), dev(rank), L, 16, ws)
+    for _ in range(3):      # a build leaves its exchange region zero for the next one
+        aa.lora_build_segments(dev(idx), dev(rank), L, 16, ws)
     torch.cuda.synchronize()
+    # the end area (exchange regions of the single-launch build): zero again
+    n_wg = -(-T // 1024)
+    xb = 0 if T <= 4096 else (-(-4 * min(n_wg, 16) * (L + 1) // 256) * 256 + 256)
+    assert int(torch.count_nonzero(ws[ws.numel() - 256 - xb:])) == 0
     lay = aa.lora_segment_layout(T, L)
     w = ws.cpu().numpy()
 
