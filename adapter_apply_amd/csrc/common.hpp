@@ -88,6 +88,11 @@ __device__ __forceinline__ void stg_nt(E *p, const uint4 &v) {
     __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t *>(p));
 }
 
+// Work-group barrier for LDS traffic only: global loads, stores and atomics
+// stay in flight across it (__syncthreads() may also wait for every
+// outstanding global access, which puts a memory round trip on the path).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Workspace layout (all offsets 256-byte aligned).
 // ---------------------------------------------------------------------------

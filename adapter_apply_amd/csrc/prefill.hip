@@ -74,11 +74,12 @@ __device__ __forceinline__ int swz(int n, int u, int U) {
 // Shrink: work-group = (64-item tile, block of 32 * NCB buffer columns), 8
 // waves.  K advances in stages of 64 columns: a stage is the tile's x rows and
 // the block's lora_a rows, 128 bytes each, loaded row-contiguously (one wave
-// instruction = 8 whole rows), with NPF stages in flight in registers and two
-// LDS buffers (one barrier per stage).  Wave w owns the 32 x 32 output block
-// (token block w & 1, column block w >> 1) and runs v_mfma_f32_32x32x16_bf16
-// over the stage.  Writes fp32 buf[s][t][j] for every column of the block that
-// exists (zeros for j >= rank); K % 8 == 0, any rank.
+// instruction = 8 whole rows), with 4 stages in flight in registers and two
+// LDS buffers (one barrier per stage, LDS traffic only).  The 2 * NCB output
+// blocks of 32 x 32 are shared by the 8 waves, each block's K steps split
+// over 4 / NCB waves (v_mfma_f32_32x32x16_bf16).  Writes fp32 buf[s][t][j]
+// for every column of the block that exists (zeros for j >= rank);
+// K % 8 == 0, any rank.
 constexpr int kShThreads = 512;
 constexpr int kShStageK = 64;          // K columns per stage (128 bytes of a row)
 constexpr int kShNpf = 4;              // stages in flight
@@ -88,7 +89,11 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
     constexpr int ROWS = 64 + 32 * NCB;                // x rows, then lora_a rows
     constexpr int UNITS = ROWS * 8;                    // 16-byte units per stage
     constexpr int NU = (UNITS + kShThreads - 1) / kShThreads;
-    __shared__ __attribute__((aligned(16))) char s_stage[2][ROWS * 128];
+    // every thread stores all NU of its units (rows past ROWS are never read),
+    // so no store of a stage sits under a branch
+    __shared__ __attribute__((aligned(16))) char s_stage[2][NU * kShThreads * 16];
+    static_assert((4 / NCB - 1) * 2 * NCB * 16 * 64 * 4 <= 2 * NU * kShThreads * 16,
+                  "the staging area holds the K parts summed after the last stage");
     __shared__ int64_t s_brow[64];
 
     // Work-group i runs on XCD i % 8; XCD x takes a contiguous range of the
@@ -143,50 +148,83 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
             ring[slot][v] = ldg<uint4>(rowp[v] + k);
         }
     };
+    // The store takes the loaded value through a mask, not a select: a select
+    // of a load result becomes a branch, and the compiler waits for every
+    // load in flight (the prefetched stages included) before it.
     auto put = [&](int slot, int st, char *buf) {
 #pragma unroll
         for (int v = 0; v < NU; ++v) {
             const int q = v * kShThreads + tid;
-            if (q < UNITS) {
-                // stages past this split's last (padding to a multiple of
-                // kShNpf) belong to the next split or lie past K: zeros
-                const bool kin = st < nst && (sb + st) * kShStageK + uoff[v] < a.K;
-                *reinterpret_cast<uint4 *>(buf + swz(q >> 3, q & 7, 8)) = kin ? ring[slot][v] : make_uint4(0, 0, 0, 0);
-            }
+            // stages past this split's last (padding to a multiple of
+            // kShNpf) belong to the next split or lie past K: zeros
+            const bool kin = st < nst && (sb + st) * kShStageK + uoff[v] < a.K;
+            const uint32_t m = 0u - (uint32_t)kin;
+            const uint4 u = ring[slot][v];
+            *reinterpret_cast<uint4 *>(buf + swz(q >> 3, q & 7, 8)) = make_uint4(u.x & m, u.y & m, u.z & m, u.w & m);
         }
     };
-    const int tb = w & 1, cbk = w >> 1;
+    // Every wave computes: wave w takes the 32 x 32 block (token block w & 1,
+    // column block cbk) over KSW of the stage's 4 K steps (part kp); the
+    // KSPLIT parts of a block are summed in order after the last stage.  A
+    // wave reads all its fragments of a stage before its first MFMA.
+    constexpr int KSPLIT = 4 / NCB, KSW = kShStageK / 16 / KSPLIT;
+    const int tb = w & 1, cbk = (w >> 1) % NCB, kp = (w >> 1) / NCB;
     floatx16_t acc = {};
     auto mma = [&](const char *buf) {
-        if (cbk < NCB) {
+        uint4 xf[KSW], af[KSW];
 #pragma unroll
-            for (int ks = 0; ks < kShStageK / 16; ++ks) {
-                const int u = 2 * ks + half;
-                const uint4 xf = *reinterpret_cast<const uint4 *>(buf + swz(32 * tb + l32, u, 8));
-                const uint4 af = *reinterpret_cast<const uint4 *>(buf + swz(64 + 32 * cbk + l32, u, 8));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xf), as_frag(af), acc, 0, 0, 0);
-            }
+        for (int i = 0; i < KSW; ++i) {
+            const int u = 2 * (kp * KSW + i) + half;
+            xf[i] = *reinterpret_cast<const uint4 *>(buf + swz(32 * tb + l32, u, 8));
+            af[i] = *reinterpret_cast<const uint4 *>(buf + swz(64 + 32 * cbk + l32, u, 8));
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < KSW; ++i)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(xf[i]), as_frag(af[i]), acc, 0, 0, 0);
     };
     // Stages past the split's last one (padding to a multiple of kShNpf) stage
     // zeros.  No branch around the loads.
+    // The prologue issues the stages in ring order, as the loop refills them
+    // (kept by scheduling barriers): the loop's first store then waits only
+    // for its own stage.  Issued in another order, the loads of stage 0 could
+    // be the youngest in flight when the loop is entered, and the wait at the
+    // loop's head would drain every stage on each pass.
 #pragma unroll
-    for (int u = 0; u < kShNpf; ++u) issue(u, min(u, nst - 1));
+    for (int u = 0; u < kShNpf; ++u) {
+        issue(u, min(u, nst - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int st0 = 0; st0 < nst; st0 += kShNpf) {
 #pragma unroll
         for (int u = 0; u < kShNpf; ++u) {
             const int st = st0 + u;
             char *buf = s_stage[st & 1];
             put(u, st, buf);
-            __syncthreads();
+            lds_barrier();
             issue(u, min(st + kShNpf, nst - 1));   // refill the slot just consumed
             mma(buf);
         }
     }
     __syncthreads();   // s_brow visible (and every stage consumed)
+    if (KSPLIT > 1) {
+        // parts 1 .. KSPLIT-1 of each block through the (now free) staging
+        // area, added to part 0 in order
+        float *s_red = reinterpret_cast<float *>(&s_stage[0][0]);
+        const int blk = tb + 2 * cbk;
+        if (kp > 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s_red[(((kp - 1) * 2 * NCB + blk) * 16 + i) * 64 + lane] = acc[i];
+        }
+        __syncthreads();
+        if (kp > 0) return;
+#pragma unroll
+        for (int q = 1; q < KSPLIT; ++q)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] += s_red[(((q - 1) * 2 * NCB + blk) * 16 + i) * 64 + lane];
+    }
 
     // acc[i]: token 32*tb + 8*(i/4) + 4*half + (i%4), column 32*(NCB*cb + cbk) + l32
-    if (cbk >= NCB) return;
     const int c = cb * 32 * NCB + 32 * cbk + l32;
     if (c >= SRf) return;
     const int sg = c / a.R, j = c - sg * a.R;
@@ -801,7 +839,8 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     for (int s = 0; s < S; ++s)
         aligned = aligned && sl.n[s] % 8 == 0 && sl.off[s] % 8 == 0;
     // the persistent kernel: ranks 16, 32, 64, 128 (power-of-two rows), no
-    // per-item factor; the per-launch kernel: ranks up to 64; else the generic one
+    // per-item factor (its load would hang off the token index, inside the
+    // item pipeline); the per-launch kernel: ranks up to 64; else the generic one
     const bool pipe = aligned && (R == 16 || R == 32 || R == 64 || R == 128) && !a.gm.coef && !a.gm.ksum;
     const bool rows = aligned && R <= 64;
     const int cols = pipe ? (R <= 64 ? kRowCols : kRowCols / 2) : rows ? kRowCols : kExpGroupCols;
@@ -815,8 +854,11 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     a.per_xcd = (c + kXcds - 1) / kXcds;
     dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
     if (pipe) {
-        // two work-groups per CU, 32 CUs per XCD
-        const dim3 pgrid(kXcds * 64);
+        // 32 CUs per XCD; two work-groups per CU, three at rank 16 (whose
+        // 44 KB of LDS leave room for a third: more items in flight to cover
+        // the fixed cost of the small ones, e.g. the half-full (slot, expert)
+        // tiles of a fused-MoE call)
+        const dim3 pgrid(kXcds * (R == 16 ? 96 : 64));
         switch (R / 16) {
             case 1: hipLaunchKernelGGL((k_pre_expand_pipe<1, kRowCols>), pgrid, dim3(kThreads), 0, st, a); break;
             case 2: hipLaunchKernelGGL((k_pre_expand_pipe<2, kRowCols>), pgrid, dim3(kThreads), 0, st, a); break;

@@ -120,10 +120,6 @@ __device__ __forceinline__ short4_t frag4(const uint2 &u) { return __builtin_bit
 // the unit XOR-swizzled with the row (fragment reads of 8 rows hit 8 bank groups).
 __device__ __forceinline__ int stage_off(int r, int u) { return r * 128 + ((u ^ (r & 7)) << 4); }
 
-// Barrier for LDS traffic only: global loads and atomics stay in flight across
-// it (__syncthreads() also waits for every outstanding global access).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // A pointer that every lane of the wave holds, moved into scalar registers.
 template <typename P>
 __device__ __forceinline__ P *uniform_ptr(P *p) {

@@ -79,24 +79,23 @@ __device__ __forceinline__ void st_co32(int32_t *p, int32_t v) {
 __device__ __forceinline__ int32_t ld_co32(const int32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // block_exclusive_scan with barriers that wait for LDS only
 __device__ int block_exclusive_scan_lds(int v, int *total, int *wsum) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int incl = wave_incl_scan(v);
     if (lane == 63) wsum[w] = incl;
-    lds_sync();
+    lds_barrier();
     if (w == 0) {
         const int s = lane < kSegWaves ? wsum[lane] : 0;
         const int si = wave_incl_scan(s);
         if (lane < kSegWaves) wsum[kSegWaves + lane] = si - s;
         if (lane == kSegWaves - 1) wsum[2 * kSegWaves] = si;
     }
-    lds_sync();
+    lds_barrier();
     int r = wsum[kSegWaves + w] + incl - v;
     *total = wsum[2 * kSegWaves];
-    lds_sync();
+    lds_barrier();
     return r;
 }
 
@@ -431,7 +430,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_one(SegJobs a) {
     int tot = 0, before = 0, n_inv = 0, unused = 0;
     if (tid < nkeys) col_sums(tid, tot, before);
     if (tid == 0 && b == 0) col_sums(nkeys, n_inv, unused);
-    lds_sync();
+    lds_barrier();
     // every thread of this work-group has read the counts; the count of such
     // work-groups is used only at the end
     int done = 0;
@@ -449,7 +448,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_one(SegJobs a) {
         if (b == 0) seg.slot_start[tid] = start;
     }
     if (b == 0 && tid == 0) seg.slot_start[nkeys] = n_active;
-    lds_sync();
+    lds_barrier();
     scatter_step(key, t, nbits, lane, mycnt, seg.perm);
     if (b == 0) {
         // work-group 0 of the job: the tail of perm, the tiles and the header
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(kSegThreads) void k_seg_one(SegJobs a) {
     }
     // the last work-group to have read the counts zeroes them for the next call
     if (tid == 0) s_last = done == n_wg - 1;
-    lds_sync();
+    lds_barrier();
     if (s_last) {
         for (int i = tid; i < n_wg * stride; i += kSegThreads) st_co32(seg.xcounts + i, 0);
         if (tid == 0) st_co32(seg.xdone, 0);
