@@ -447,6 +447,12 @@ struct GroupMap {
                                    // 0: every slice reads slice 0, the shrink of a shared lora_a)
     const float *coef = nullptr;   // per-item factor (routing weight), or null
     int32_t ksum = 0;              // expand: buffer row of token t = sum_j coef[t*ksum+j] * buf[t*ksum+j]
+    // expand, pair view (pair_k = k > 0): the segments are token tiles keyed
+    // by slot, and the items are their (token, k) pairs, 64 to a tile; a pair
+    // whose expert pair_ids[p] lies outside [0, pair_E) carries no delta
+    int32_t pair_k = 0;
+    const int32_t *pair_ids = nullptr;
+    int32_t pair_E = 0;
 };
 
 // K splits of the row-oriented MFMA shrink.  A batch with few 64-token tiles

@@ -249,6 +249,14 @@ lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_
             // sum_j w[t,j] * buf[t*k + j], expanded once per token with the shared lora_b
             ex.Ekey = 1; ex.Ew = 1; ex.buf_rows = P; ex.coef = topk_w; ex.ksum = top_k;
             ex_seg = &tok;
+        } else if (kind == MOE_LORA_W2 && E_b == 1) {
+            // one lora_b for every expert ([PR] shared-outer): the expand
+            // needs the pairs grouped by slot only, and a token's pairs share
+            // its slot, so it walks full runs of 64 pairs of the token tiles
+            // instead of the (slot, expert) tiles, half empty on average
+            ex.Ekey = 1; ex.Ew = 1; ex.buf_rows = P; ex.coef = topk_w;
+            ex.pair_k = top_k; ex.pair_ids = topk_ids; ex.pair_E = E;
+            ex_seg = &tok;
         } else {
             ex.Ekey = E; ex.Ew = E_b; ex.buf_rows = P;
             ex.coef = kind == MOE_LORA_W2 ? topk_w : nullptr;

@@ -244,6 +244,31 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
     }
 }
 
+// The tiles an expand walks.  Normally the segment table's prefill tiles; in
+// the pair view (gm.pair_k = k > 0) the table holds token tiles keyed by slot
+// and expand tile j is the (j % k)-th run of kPreTile (token, k) pairs of
+// token tile j / k: position p of a token tile's pair run is pair
+// perm[p / k] * k + p % k (the pairs of a token share its slot).  A run past
+// the token tile's pairs is empty.
+__device__ __forceinline__ int exp_n_tiles(const PreExpandArgs &a) {
+    return a.seg.header[3] * (a.gm.pair_k ? a.gm.pair_k : 1);
+}
+__device__ __forceinline__ int4 exp_tile(const PreExpandArgs &a, int j) {
+    const int k = a.gm.pair_k;
+    if (!k) return a.seg.tiles_pre[j];
+    const int4 t = a.seg.tiles_pre[j / k];
+    const int b = t.y * k + kPreTile * (j % k);
+    return make_int4(t.x, b, min(t.z * k, b + kPreTile), 0);
+}
+__device__ __forceinline__ int exp_perm(const PreExpandArgs &a, int p) {
+    const int k = a.gm.pair_k;
+    return k ? a.seg.perm[p / k] * k + p % k : a.seg.perm[p];
+}
+// whether an item of a tile carries a delta (pair view: its expert in range)
+__device__ __forceinline__ bool exp_live(const PreExpandArgs &a, int item) {
+    return !a.gm.pair_k || (uint32_t)a.gm.pair_ids[item] < (uint32_t)a.gm.pair_E;
+}
+
 // Per-lane view of one token block of an expand tile: the item, its y row, its
 // scale factor and the 8 buffer values of rank group jj (k-summed if asked).
 struct ExpItem {
@@ -256,8 +281,9 @@ struct ExpItem {
 __device__ __forceinline__ ExpItem exp_item(const PreExpandArgs &a, int p0, int row, int ntok,
                                             float sc) {
     ExpItem it;
-    it.ok = row < ntok;
-    it.item = a.seg.perm[p0 + (it.ok ? row : 0)];   // clamped: never stored
+    const bool in = row < ntok;
+    it.item = exp_perm(a, p0 + (in ? row : 0));   // clamped: never stored
+    it.ok = in && exp_live(a, it.item);
     it.yrow = it.item / a.gm.y_div;
     const float cf = (a.gm.coef && !a.gm.ksum) ? a.gm.coef[it.item] : 1.0f;
     it.scl = sc * cf;
@@ -301,8 +327,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
     const int tile = local / a.per_xcd;
     const int cg = (local - tile * a.per_xcd) * kXcds + xcd;
     if (cg >= a.n_cg) return;
-    if (tile >= a.seg.header[3]) return;
-    const int4 tl = a.seg.tiles_pre[tile];
+    if (tile >= exp_n_tiles(a)) return;
+    const int4 tl = exp_tile(a, tile);
+    if (tl.z <= tl.y) return;
     const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
     const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
@@ -412,14 +439,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     __shared__ __attribute__((aligned(16))) char s_buf[kRowTok * U * 16];
     __shared__ int64_t s_yrow[kRowTok];
     __shared__ float s_scl[kRowTok];
+    __shared__ int s_live[kRowTok];
 
     const int xcd = blockIdx.x % kXcds;
     const int local = blockIdx.x / kXcds;
     const int tile = local / a.per_xcd;
     const int cg = (local - tile * a.per_xcd) * kXcds + xcd;
     if (cg >= a.n_cg) return;
-    if (tile >= a.seg.header[3]) return;
-    const int4 tl = a.seg.tiles_pre[tile];
+    if (tile >= exp_n_tiles(a)) return;
+    const int4 tl = exp_tile(a, tile);
+    if (tl.z <= tl.y) return;
     const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey, p0 = tl.y, ntok = tl.z - tl.y;
     const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
     const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
@@ -434,9 +463,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     // ---- per-token row, scale and buffer item (tokens past the tile: clamped)
     if (tid < kRowTok) {
         const int row = tid < ntok ? tid : 0;
-        const int item = a.seg.perm[p0 + row];
+        const int item = exp_perm(a, p0 + row);
         s_yrow[tid] = item / a.gm.y_div;
         s_scl[tid] = sc * ((a.gm.coef && !a.gm.ksum) ? a.gm.coef[item] : 1.0f);
+        s_live[tid] = tid < ntok && exp_live(a, item);
     }
     __syncthreads();
 
@@ -467,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
         const int t = q / (R / 4), j = 4 * (q % (R / 4));
         frow[i] = t;
         const int row = t < ntok ? t : 0;
-        const int item = a.seg.perm[p0 + row];
+        const int item = exp_perm(a, p0 + row);
         if (!a.gm.ksum) {
             fv[i] = ldg<float4>(a.buf + ((int64_t)sg * a.gm.buf_sstride + item / a.gm.buf_div) * R + j);
         } else {
@@ -545,12 +575,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
     }
     __syncthreads();
 
-    // ---- write the tile back, row by row ----------------------------------
+    // ---- write the tile back, row by row (rows that carry a delta) ---------
 #pragma unroll
     for (int i = 0; i < NY; ++i) {
         const int q = i * kThreads + tid;
         const int row = q / YU, col = n_base + 8 * (q % YU);
-        if (row < ntok && col < Ns)
+        if (s_live[row] && col < Ns)
             stg_nt(ybase + s_yrow[row] * a.ldy + col,
                    *reinterpret_cast<const uint4 *>(&s_y[row * kRowYStride + 8 * (q % YU)]));
     }
@@ -841,7 +871,8 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     // the persistent kernel: ranks 16, 32, 64, 128 (power-of-two rows), no
     // per-item factor (its load would hang off the token index, inside the
     // item pipeline); the per-launch kernel: ranks up to 64; else the generic one
-    const bool pipe = aligned && (R == 16 || R == 32 || R == 64 || R == 128) && !a.gm.coef && !a.gm.ksum;
+    const bool pipe = aligned && (R == 16 || R == 32 || R == 64 || R == 128) && !a.gm.coef && !a.gm.ksum &&
+                      !a.gm.pair_k;
     const bool rows = aligned && R <= 64;
     const int cols = pipe ? (R <= 64 ? kRowCols : kRowCols / 2) : rows ? kRowCols : kExpGroupCols;
     int c = 0;
@@ -852,7 +883,8 @@ hipError_t launch_pre_expand(void *y, int64_t ldy, const float *buf, int32_t T, 
     for (int s = S; s <= kMaxSlices; ++s) a.group_start[s] = c;
     a.n_cg = c;
     a.per_xcd = (c + kXcds - 1) / kXcds;
-    dim3 grid((unsigned)(seg.max_tiles_pre * a.per_xcd * kXcds));
+    const int64_t max_tiles = (int64_t)seg.max_tiles_pre * (gm.pair_k ? gm.pair_k : 1);
+    dim3 grid((unsigned)(max_tiles * a.per_xcd * kXcds));
     if (pipe) {
         // 32 CUs per XCD; two work-groups per CU, three at rank 16 (whose
         // 44 KB of LDS leave room for a third: more items in flight to cover

@@ -198,6 +198,29 @@ def test_small_batch_invalid_experts_and_empty_slots(oracle_mod, align):
         assert np.array_equal(y[dead], y0[dead])
 
 
+def test_w2_shared_lora_b_pair_runs_invalid_experts(oracle_mod):
+    """w2 with one lora_b for every expert walks runs of 64 (token, k) pairs of
+    the token tiles: several runs per slot, a top_k that does not divide 64, and
+    pairs whose expert lies outside [0, E) inside full runs stay untouched; bit
+    for bit against the oracle."""
+    T, k, E, K, I, R, L = 700, 6, 16, 256, 128, 16, 3
+    d = integer_moe(11, T, k, E, K, I, R, L, shared=True, p_none=0.1)
+    rng = np.random.default_rng(12)
+    ids = d["ids"].copy()
+    bad = rng.random(ids.shape) < 0.05
+    ids[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E + 3)
+    log("case moe w2 pair runs with invalid experts")
+    y = run_moe(W2, d["o0"], d["h"], [d["A2"]], [d["B2"]], ids, d["w"], d["idx"], d["rank"],
+                d["scale"], E)
+    ref = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], ids, d["w"],
+                                    d["idx"], d["rank"], d["scale"], E)
+    assert np.array_equal(y, ref), np.max(np.abs(y - ref))
+    t_of = np.arange(T * k) // k
+    dead = (ids.reshape(-1) < 0) | (ids.reshape(-1) >= E) | (d["idx"][t_of] < 0)
+    assert dead.sum() > 100
+    assert np.array_equal(y[dead], d["o0"][dead])
+
+
 def sample_tokens(T, n, seed=0):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, n)])).astype(np.int64)
