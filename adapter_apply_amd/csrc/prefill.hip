@@ -587,14 +587,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
 }
 
 // Persistent, software-pipelined form of k_pre_expand_rows for the common case
-// (no per-item factor, no k-reduction): two work-groups per CU, each walking a
-// strided list of (tile, column group) items of its XCD.  The y / lora_b /
-// buffer loads of item k+1 are in flight while item k is multiplied, added
-// and stored; the per-item token lists (tile descriptor -> perm gather -> y
-// and buffer rows) run two and three items ahead in registers and reach the
-// loads through double-buffered LDS slots, so no dependent load sits on the
-// critical path.  Items are ordered column group first, so an XCD's
-// work-groups share a few column groups of lora_b in its L2 at any time.
+// (no per-item factor, no k-reduction): two or three work-groups per CU, each
+// walking a strided list of (tile, column group) items of its XCD.  The y /
+// lora_b / buffer loads of item k+1 are in flight while item k is multiplied,
+// added and stored; the per-item token lists (tile descriptor -> perm gather
+// -> y and buffer rows) run two and three items ahead in registers and reach
+// the loads through double-buffered LDS slots, so no dependent load sits on
+// the critical path.  Items are ordered tile first: the work-groups of an XCD
+// work at any time on a few consecutive (slot-ordered) tiles with all the
+// XCD's column groups, so each tile's buffer rows and the few slots' lora_b
+// blocks are fetched into its L2 once (ordered column group first, the
+// lora_b blocks of a slot were evicted between its tiles and fetched again:
+// about one more pass over lora_b on the prefill gate_up workload).
 // Ranks up to 128 (R = 16 * NKS); CW output columns per item (256 up to rank
 // 64, 128 above, so that two work-groups still fit a CU's LDS).  Of each
 // lora_b row only the first 2 * ceil(r / 16) units (rounded up to a power of
@@ -634,11 +638,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     // item k of this work-group (clamped to its last one): tile and column group
     auto tile_of = [&](int k) {
         const int j = lw + min(k, cnt - 1) * nw;
-        return j % n_tiles;
+        return j / a.per_xcd;
     };
     auto cg_of = [&](int k) {
         const int j = lw + min(k, cnt - 1) * nw;
-        return (j / n_tiles) * kXcds + xcd;
+        return (j % a.per_xcd) * kXcds + xcd;
     };
     struct Col { int sg, Ns, n_base; bool ok; };
     auto col_of = [&](int k) {
