@@ -279,6 +279,37 @@ def measure_copy_gbps(torch, dev, nbytes=1 << 30, reps=10):
     return gbps
 
 
+def measure_gemm_tflops(torch, dev, n=8192, reps=10):
+    """Rate of a large dense bf16 matrix product through torch (hipBLASLt):
+    the practical MFMA ceiling of this machine beside the 2.5 PFLOP/s nominal
+    (the copy rate above plays the same part for HBM)."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return tflops
+
+
+# measured once per run by main(); reported in every entry's "mfma"
+GEMM_TFLOPS = [None]
+
+
+def _gemm_fields(achieved):
+    g = GEMM_TFLOPS[0]
+    return {} if g is None else {"gemm_TFLOPs": round(g, 1), "frac_of_gemm": round(achieved / g, 5)}
+
+
 class Rotation:
     """Graph capture and timing over n_inst distinct instances."""
 
@@ -502,6 +533,7 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
         "mfma": {"achieved": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                 **_gemm_fields(ab["flops"] / (ms_per_step * 1e-3) / 1e12),
                  "executed_frac": (None if mfma_exec is None else
                                    round(mfma_exec / (ms_per_step * 1e-3) / 1e12 /
                                          MFMA_BF16_PEAK_TFLOPS, 5))},
@@ -603,7 +635,8 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
         "step_algorithmic_GBps": round(ab["total"] / (ms_per_step * 1e-3) / 1e9, 1),
         "mfma": {"achieved": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+                 "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                 **_gemm_fields(ab["flops"] / (ms_per_step * 1e-3) / 1e12)},
         "cpu_baseline": None if args.no_cpu_baseline else moe_cpu_baseline(c, cpu_seconds),
         "wall_s": round(wall, 3),
     }
@@ -631,6 +664,8 @@ def headline_line(entry, name, steps, warmup, copy_gbps, khash):
     e.pop("warmup", None)
     out.update(e)
     out["copy_GBps"] = round(copy_gbps, 1)
+    if GEMM_TFLOPS[0] is not None:
+        out["gemm_TFLOPs"] = round(GEMM_TFLOPS[0], 1)
     out["kernel_hash"] = khash
     return out
 
@@ -653,6 +688,7 @@ def main():
         return
     t0 = time.perf_counter()
     copy_gbps = measure_copy_gbps(torch, torch.device("cuda:0"))
+    GEMM_TFLOPS[0] = measure_gemm_tflops(torch, torch.device("cuda:0"))
     khash = kernel_hash()
     if name == "moe":
         entry = moe_entry(args, steps, warmup, args.cpu_seconds, copy_gbps)
