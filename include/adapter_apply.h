@@ -117,8 +117,10 @@
  *            them (one launch fewer); buf is then neither written nor read.
  *            The prefill path ignores the flag and goes through buf.
  *
- * Alignment: x, y, A[s], B[s] 16-byte aligned; ldx % 8 == 0; ldy and
- * y_col_offset % 4 == 0; buf 16-byte aligned.  Violations -> LORA_E_ALIGN.
+ * Alignment: x, y, A[s], B[s] 16-byte aligned; K and ldx % 8 == 0; every
+ * N[s], ldy and y_col_offset % 4 == 0; R % 8 == 0 for bf16 and R % 4 == 0
+ * for fp32 (whole 16-byte units per lora_b row); buf 16-byte aligned.
+ * Violations -> LORA_E_ALIGN.
  * Aliasing of y with x, A, B, buf or ws is not allowed.
  */
 #ifndef ADAPTER_APPLY_H
