@@ -686,14 +686,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
         const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
         const uint16_t *ybase = a.y + a.sl.off[c.sg];
-        // rows past the tile's tokens all read one 16-byte unit (of its last
-        // token row), so an instruction of padding rows costs one request
+        // the work-group's load instructions past the tile's tokens are
+        // skipped (a uniform branch; the registers are read only after the
+        // next pass's drain); padding rows inside an instruction read one
+        // 16-byte unit (of the last token row): one request
         const int ntk = tl.z - tl.y;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int q = i * kThreads + tid;
             const int col = q / YU < ntk ? min(c.n_base + 8 * (q % YU), c.Ns - 8) : c.n_base;
-            yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + col);
+            if (i * (kThreads / YU) < ntk)   // the work-group's instruction i holds a token row
+                yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + col);
         }
         // units q < CW * Ue of the block, Ue = 1 << lgu per row; the rest repeat the last
         const int lgu = lg_units(s_rk[slot]);
@@ -761,7 +764,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         // 2. loads of item k+1, metadata of item k+2, descriptor of item k+3
         const float sc = s_sc[slot];
         const Col ck = c0;
-        data_load(tl1, c1, nslot);
+        if (k + 1 < cnt) data_load(tl1, c1, nslot);   // the last item has none (a reload of it
+                                                      // would fetch its y rows once more)
         const Meta m2 = meta_load(tl2);
         const int4 tl3 = ldg<int4>(&a.seg.tiles_pre[tile_of(k + 3)]);
         // 3. D[n][t] for item k over its slot's rank steps, added into the y tile
