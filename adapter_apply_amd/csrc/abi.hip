@@ -1,5 +1,7 @@
 // C-ABI entry points: argument checks (all before any launch), workspace
 // carving and path dispatch.  Declarations and contracts: include/adapter_apply.h.
+#include <cmath>
+
 #include "../../include/adapter_apply.h"
 #include "common.hpp"
 
@@ -15,6 +17,10 @@ constexpr int32_t kPrefillMinPerSlot = 64;
 constexpr int32_t kFoldMaxChunkRank = 512;   // n_kchunks * R
 // Auto: wide outputs take the single-launch K-split kernel up to this many tokens.
 constexpr int32_t kRelayWideMaxTokens = 256;
+// Auto's K-split single launch for narrow outputs: expected 32-token groups at
+// most this many, or at least this many tokens per slot that draws any.
+constexpr double kRelayFewGroups = 12.0;
+constexpr double kRelayMinPerSlot = 24.0;
 
 inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -235,10 +241,28 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     const bool narrow = ntot <= kAutoMaxDecodeCols;
     const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
     if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
+    // The K-split single launch runs a fixed set of work-groups per 32-token
+    // slot group (at the QKV shape 16 K chunks x 3 slices of shrink and 12
+    // column chunks x 4 token blocks of expand), however few tokens the group
+    // holds; the other single-launch kernel recomputes the shrink of each
+    // 8-token group per 1024-column chunk.  So for narrow outputs auto takes
+    // the K-split launch when the expected groups are few or full: at most
+    // kRelayFewGroups of them, or at least kRelayMinPerSlot tokens per slot
+    // that draws any (slots drawn uniformly).  Measured (QKV shape, rank 16):
+    // 8 slots, 1 to 1024 tokens, it is the faster one (T 512: 12.9 against
+    // 16.7 us; T 1024: 24.2 against 26.1); 64 slots at T 64 and 256, and 32
+    // slots at T 512, the other (10.5, 18.3, 17.1 against 20.2, 31.0, 19.9 us).
+    const double used = L * (1.0 - exp(-(double)T / L));
+    const bool relay_batch = used + T / (double)kRelayGroup <= kRelayFewGroups ||
+                             T >= kRelayMinPerSlot * used;
+    const bool relay_ws = ws && ws_bytes >= ws_layout(T, K, S, R, L).end;
+    // Decode-sized batches of long slot runs take it too, before the tile
+    // kernels (8 slots, T 512: 12.9 against 27.1 us; T 1024: 24.2 against 30.3).
+    if (path == LORA_PATH_AUTO && use_prefill && relay_ok && narrow && relay_ws && relay_batch)
+        use_prefill = 0;
     const bool relay = path == LORA_PATH_RELAY ||
-                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok &&
-                        (narrow || T <= kRelayWideMaxTokens) && ws &&
-                        ws_bytes >= ws_layout(T, K, S, R, L).end);
+                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok && relay_ws &&
+                        ((narrow && relay_batch) || (!narrow && T <= kRelayWideMaxTokens)));
     const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
                       (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;

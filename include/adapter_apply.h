@@ -72,11 +72,13 @@
  *                       shape and dtype the call accepts (the only fp32 path).
  *
  *            LORA_PATH_AUTO in lora_apply_packed ("narrow": the slices sum
- *            to at most 16384 columns; the first row that holds wins):
+ *            to at most 16384 columns; "a relay batch": with
+ *            U = L (1 - exp(-T / L)) the slots expected to draw tokens,
+ *            U + T / 32 <= 12 or T >= 24 U; the first row that holds wins):
  *              | condition                                        | path    |
- *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |
  *              | RELAY's shapes, ws of lora_workspace_size(),     | RELAY   |
- *              |   narrow or T <= 256                             |         |
+ *              |   narrow and a relay batch, or T <= 256          |         |
+ *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |
  *              | FUSED's shapes, narrow                           | FUSED   |
  *              | GROUPED's shapes, L <= 64, R <= 64, narrow       | GROUPED |
  *              | bf16, R in {16, 32, 64, 128}, rows of 8          | PREFILL |

@@ -294,6 +294,17 @@ def _ws_size(T, K, S, R, L):
     (dict(path=aa.LORA_PATH_AUTO, wsb=_ws_size(256, 4096, 3, 16, 8) - 1, ws=None),
      aa.LORA_PATH_FUSED),
     (dict(ws=None, wsb=0), aa.LORA_PATH_FUSED),
+    # decode-sized batches of long slot runs: the single launch (8 slots, 512
+    # and 1024 tokens); past its 1024 tokens, the tile kernels
+    (dict(T=512), aa.LORA_PATH_RELAY),
+    (dict(T=1024), aa.LORA_PATH_RELAY),
+    (dict(T=2048), aa.LORA_PATH_PREFILL),
+    # many slots of a few tokens each: the other single launch
+    (dict(T=64, L=64), aa.LORA_PATH_FUSED),
+    (dict(T=256, L=64), aa.LORA_PATH_FUSED),
+    (dict(T=512, L=32), aa.LORA_PATH_FUSED),
+    # a few tokens over a few slots: the K-split single launch
+    (dict(T=8), aa.LORA_PATH_RELAY),
     # long runs per slot (8192 tokens over 16 slots): the tile kernels
     (dict(T=8192, L=16, R=64, S=2, N=(C.c_int64 * 2)(14336, 14336), ldy=28672), aa.LORA_PATH_PREFILL),
     # 128 slots at rank 128: the tile kernels
