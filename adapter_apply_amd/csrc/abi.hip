@@ -21,6 +21,8 @@ constexpr int32_t kRelayWideMaxTokens = 256;
 // most this many, or at least this many tokens per slot that draws any.
 constexpr double kRelayFewGroups = 12.0;
 constexpr double kRelayMinPerSlot = 24.0;
+// Auto: the grouped kernels at rank 16 for narrow outputs up to this many tokens.
+constexpr int32_t kGrpR16MaxTokens = 4096;
 
 inline bool al(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -263,13 +265,23 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     const bool relay = path == LORA_PATH_RELAY ||
                        (path == LORA_PATH_AUTO && !use_prefill && relay_ok && relay_ws &&
                         ((narrow && relay_batch) || (!narrow && T <= kRelayWideMaxTokens)));
+    // The other single launch up to 64 slots: past that each of many small
+    // groups streams its slot's lora_a once per column chunk (1024 tokens over
+    // 128 slots at rank 32: 95.6 us against 64.1 for the tile kernels).
     const bool fuse = !use_prefill && !relay && can_fuse(T, K, R, N, S, ldy, y_col_offset, dtype) &&
-                      (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow));
+                      (path == LORA_PATH_FUSED || (path == LORA_PATH_AUTO && narrow && L <= 64));
     if (path == LORA_PATH_FUSED && !fuse) return LORA_E_PATH;
     // Auto takes the grouped kernels while their in-kernel discovery is the
-    // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself.
-    const bool group_auto = L <= 64 && R <= kGrpMaxPartialRank && narrow;
-    const bool group = !use_prefill && !fuse && !relay && can_group(T, K, R, N, S, ldy, y_col_offset, dtype) &&
+    // one-wave kind (L <= 64) and the expand sums the K-chunk partials itself;
+    // and at rank 16 for narrow outputs up to 4096 tokens and 128 slots, also
+    // before the tile kernels (QKV shape: 2048 tokens over 16 slots 36.8
+    // against 40.1 us, 1536 over 128 slots 44.2 against 51.9; at ranks 32 and
+    // 64 the tile kernels are faster).
+    const bool group_r16 = R == 16 && narrow && T <= kGrpR16MaxTokens && L <= 128;
+    const bool group_auto = (L <= 64 && R <= kGrpMaxPartialRank && narrow) || group_r16;
+    const bool group_ok = can_group(T, K, R, N, S, ldy, y_col_offset, dtype);
+    if (path == LORA_PATH_AUTO && use_prefill && !relay && group_r16 && group_ok) use_prefill = 0;
+    const bool group = !use_prefill && !fuse && !relay && group_ok &&
                        (path == LORA_PATH_GROUPED || (path == LORA_PATH_AUTO && group_auto));
     if (path == LORA_PATH_GROUPED && !group) return LORA_E_PATH;
     // Auto, past the single-launch and discovering grouped kernels (more than

@@ -78,8 +78,10 @@
  *              | condition                                        | path    |
  *              | RELAY's shapes, ws of lora_workspace_size(),     | RELAY   |
  *              |   narrow and a relay batch, or T <= 256          |         |
+ *              | GROUPED's shapes, R == 16, T <= 4096, L <= 128,  | GROUPED |
+ *              |   narrow                                         |         |
  *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |
- *              | FUSED's shapes, narrow                           | FUSED   |
+ *              | FUSED's shapes, narrow, L <= 64                  | FUSED   |
  *              | GROUPED's shapes, L <= 64, R <= 64, narrow       | GROUPED |
  *              | bf16, R in {16, 32, 64, 128}, rows of 8          | PREFILL |
  *              | otherwise                                        | DECODE  |

@@ -295,10 +295,16 @@ def _ws_size(T, K, S, R, L):
      aa.LORA_PATH_FUSED),
     (dict(ws=None, wsb=0), aa.LORA_PATH_FUSED),
     # decode-sized batches of long slot runs: the single launch (8 slots, 512
-    # and 1024 tokens); past its 1024 tokens, the tile kernels
+    # and 1024 tokens); past its 1024 tokens at rank 16, the grouped kernels
+    # (narrow outputs, up to 4096 tokens); at higher ranks the tile kernels
     (dict(T=512), aa.LORA_PATH_RELAY),
     (dict(T=1024), aa.LORA_PATH_RELAY),
-    (dict(T=2048), aa.LORA_PATH_PREFILL),
+    (dict(T=2048), aa.LORA_PATH_GROUPED),
+    (dict(T=2048, L=16), aa.LORA_PATH_GROUPED),
+    (dict(T=8192, L=16), aa.LORA_PATH_PREFILL),
+    (dict(T=2048, R=32), aa.LORA_PATH_PREFILL),
+    # many slots at rank 32: the tile kernels, not the single launch
+    (dict(T=1024, L=128, R=32), aa.LORA_PATH_PREFILL),
     # many slots of a few tokens each: the other single launch
     (dict(T=64, L=64), aa.LORA_PATH_FUSED),
     (dict(T=256, L=64), aa.LORA_PATH_FUSED),
