@@ -15,8 +15,9 @@ constexpr int32_t kPrefillMinPerSlot = 64;
 // Decode: the expand adds the shrink's K-chunk partials itself (one launch
 // fewer) while a tile's partials stay small; beyond that a reduce kernel runs.
 constexpr int32_t kFoldMaxChunkRank = 512;   // n_kchunks * R
-// Auto: wide outputs take the single-launch K-split kernel up to this many tokens.
-constexpr int32_t kRelayWideMaxTokens = 256;
+// Auto: wide outputs take the single-launch K-split kernel up to this many
+// output elements (256 tokens of a 128256-column vocabulary).
+constexpr int64_t kRelayWideMaxElems = 256LL * 128256;
 // Auto's K-split single launch for narrow outputs: expected 32-token groups at
 // most this many, or at least this many tokens per slot that draws any.
 constexpr double kRelayFewGroups = 12.0;
@@ -234,8 +235,8 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
     // Auto takes the single-launch kernel with the K-split shrink for decode
     // batches when the workspace is there: for narrow outputs, and for wide
-    // ones (an lm_head's vocabulary) up to 256 tokens, where its 16-token
-    // expand items beat the tile kernels (128256 columns: 44 against 56 us).
+    // ones (an lm_head's vocabulary) up to a bound on T times the width, where
+    // its 16-token expand items beat the tile kernels.
     // Without a workspace narrow outputs take the other single-launch kernel;
     // past these, wide outputs go to the tile kernels (the single-launch
     // kernel without a workspace recomputes a group's shrink for every
@@ -258,13 +259,17 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     const bool relay_batch = used + T / (double)kRelayGroup <= kRelayFewGroups ||
                              T >= kRelayMinPerSlot * used;
     const bool relay_ws = ws && ws_bytes >= ws_layout(T, K, S, R, L).end;
+    // Wide outputs (an lm_head's vocabulary): while its expand grid (groups x
+    // 512-column chunks) stays within what 256 tokens of a 128256-column
+    // vocabulary make (there 44 against 52 us for the tile kernels; 512 tokens
+    // of 32000 columns 28.1 against 35.6; 384 of 128256 columns 70.8 against
+    // 61.5, 256 over 64 slots 208 against 154 us for the tile kernels).
+    const bool relay_wide = !narrow && relay_batch && (int64_t)T * ntot <= kRelayWideMaxElems;
+    const bool relay_auto = relay_ok && relay_ws && ((narrow && relay_batch) || relay_wide);
     // Decode-sized batches of long slot runs take it too, before the tile
     // kernels (8 slots, T 512: 12.9 against 27.1 us; T 1024: 24.2 against 30.3).
-    if (path == LORA_PATH_AUTO && use_prefill && relay_ok && narrow && relay_ws && relay_batch)
-        use_prefill = 0;
-    const bool relay = path == LORA_PATH_RELAY ||
-                       (path == LORA_PATH_AUTO && !use_prefill && relay_ok && relay_ws &&
-                        ((narrow && relay_batch) || (!narrow && T <= kRelayWideMaxTokens)));
+    if (path == LORA_PATH_AUTO && use_prefill && relay_auto) use_prefill = 0;
+    const bool relay = path == LORA_PATH_RELAY || (path == LORA_PATH_AUTO && !use_prefill && relay_auto);
     // The other single launch up to 64 slots: past that each of many small
     // groups streams its slot's lora_a once per column chunk (1024 tokens over
     // 128 slots at rank 32: 95.6 us against 64.1 for the tile kernels).

@@ -76,8 +76,8 @@
  *            U = L (1 - exp(-T / L)) the slots expected to draw tokens,
  *            U + T / 32 <= 12 or T >= 24 U; the first row that holds wins):
  *              | condition                                        | path    |
- *              | RELAY's shapes, ws of lora_workspace_size(),     | RELAY   |
- *              |   narrow and a relay batch, or T <= 256          |         |
+ *              | RELAY's shapes, ws of lora_workspace_size(), a   | RELAY   |
+ *              |   relay batch, narrow or T * sum(N) <= 256*128256|         |
  *              | GROUPED's shapes, R == 16, T <= 4096, L <= 128,  | GROUPED |
  *              |   narrow                                         |         |
  *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |

@@ -321,6 +321,10 @@ def _ws_size(T, K, S, R, L):
     # lm_head vocabulary at 256 tokens: single launch; at 512 tokens: tile kernels
     (dict(S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
     (dict(T=512, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    (dict(T=384, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    (dict(T=256, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    # a 32000-column vocabulary: the single launch up to 1024 tokens
+    (dict(T=1024, L=16, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_RELAY),
     # fp32: the VALU path only
     (dict(dt=aa.LORA_DT_F32, R=16), aa.LORA_PATH_DECODE),
     # rows not in 8-column units: the VALU path
