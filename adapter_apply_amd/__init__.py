@@ -82,6 +82,7 @@ SIGNATURES = {
                                          _i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _u32, _vp]),
     "moe_lora_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, C.POINTER(_sz)]),
     "moe_lora_align_capacity": (_i32, [_i32, _i32, _i32, _i32, C.POINTER(_i32)]),
+    "moe_lora_plan": (_i32, [_i32, _i32, _i32, _i32, C.POINTER(_i32)]),
     "moe_lora_align": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                               _vp, _sz, _vp]),
     "moe_lora_apply": (_i32, [_i32, _vp, _i64, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _vp,
@@ -446,6 +447,14 @@ def moe_lora_align_capacity(T: int, top_k: int, E: int, block_m: int) -> int:
     _check(lib().moe_lora_align_capacity(T, top_k, E, block_m, C.byref(c)),
            "moe_lora_align_capacity")
     return int(c.value)
+
+
+def moe_lora_plan(T: int, top_k: int, R: int, reduce_k: bool = False) -> bool:
+    """True when moe_lora_apply without LORA_FLAG_SEGMENTS_READY skips the
+    alignment for these sizes (the library's own rule)."""
+    u = _i32(0)
+    _check(lib().moe_lora_plan(T, top_k, R, int(bool(reduce_k)), C.byref(u)), "moe_lora_plan")
+    return bool(u.value)
 
 
 def alloc_moe_workspace(T: int, top_k: int, S: int, R: int, L: int, E: int, device="cuda"):

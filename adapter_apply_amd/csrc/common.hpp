@@ -309,7 +309,7 @@ struct Slices {
 // A fused-MoE call of at most this many (token, k) pairs, rank 16, without
 // the k-reduction and without a prebuilt alignment skips the alignment
 // (moe_small.hip).
-constexpr int kMoeSmallPairs = 256;
+constexpr int kMoeSmallPairs = 1024;
 bool moe_small_takes(int32_t pairs, int32_t R, int32_t reduce_k);
 hipError_t launch_moe_small(void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T, int32_t top_k,
                             int32_t K, const Slices &sl, int32_t S, int32_t E, int32_t L, int32_t R,

@@ -152,6 +152,15 @@ lora_status_t moe_lora_align_capacity(int32_t T, int32_t top_k, int32_t E, int32
     return LORA_OK;
 }
 
+lora_status_t moe_lora_plan(int32_t T, int32_t top_k, int32_t R, int32_t reduce_k,
+                            int32_t *unsorted) {
+    if (!unsorted) return LORA_E_NULL;
+    if (T < 0 || top_k < 1) return LORA_E_SHAPE;
+    *unsorted = moe_small_takes((int32_t)std::min<int64_t>((int64_t)T * top_k, INT32_MAX), R,
+                                reduce_k) ? 1 : 0;
+    return LORA_OK;
+}
+
 lora_status_t moe_lora_align(const int32_t *topk_ids, const int32_t *idx, const int32_t *slot_rank,
                              int32_t T, int32_t top_k, int32_t E, int32_t L, int32_t R,
                              int32_t block_m, int32_t *sorted_ids, int32_t *block_expert,

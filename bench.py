@@ -575,8 +575,8 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
     del base
     torch.cuda.synchronize()
     ready = aa.LORA_FLAG_SEGMENTS_READY
-    # a call of at most 256 pairs (rank 16) skips the alignment (the library's rule)
-    small = c.T * c.k <= 256 and c.R == 16
+    # whether a call of this size skips the alignment (the library's own rule)
+    small = aa.moe_lora_plan(c.T, c.k, c.R)
 
     def align(d):
         aa.moe_lora_align(d["ids"], d["idx"], d["rank"], c.E, c.L, c.R, 16, d["ws"])

@@ -338,6 +338,15 @@ lora_status_t moe_lora_workspace_size(int32_t T, int32_t top_k, int32_t S, int32
 lora_status_t moe_lora_align_capacity(int32_t T, int32_t top_k, int32_t E, int32_t block_m,
                                       int32_t *cap);
 
+/* Whether moe_lora_apply, called without LORA_FLAG_SEGMENTS_READY for T
+ * tokens, top_k, rank R and reduce_k, takes the path without alignment
+ * (*unsorted = 1; see moe_lora_apply) or builds the alignment in its
+ * workspace (*unsorted = 0).  The same rule as moe_lora_apply; launches
+ * nothing.  LORA_E_SHAPE when T < 0 or top_k < 1, LORA_E_NULL when unsorted
+ * is NULL. */
+lora_status_t moe_lora_plan(int32_t T, int32_t top_k, int32_t R, int32_t reduce_k,
+                            int32_t *unsorted);
+
 /*
  * Alignment ([vLLM] FusedMoEWithLoRA, the moe_lora_align_block_size call
  * and its per-slot views): groups the pairs of every slot by expert, experts
@@ -368,10 +377,11 @@ lora_status_t moe_lora_align(const int32_t *topk_ids, const int32_t *idx, const 
  *   topk_ids device int32 [T][top_k]; topk_w device float [T][top_k] or NULL.
  * ws: moe_lora_workspace_size() bytes; flags: LORA_FLAG_SEGMENTS_READY when
  * ws holds this batch's alignment (moe_lora_align or a previous apply).
- * Without that flag, a call of at most 256 pairs at R == 16 without reduce_k
+ * Without that flag, a call of at most 1024 pairs at R == 16 without reduce_k
  * skips the alignment ([vLLM] FusedMoEWithLoRA's naive regime for small
- * batches): one work-group per (pair, 1024 output columns).  Small batches
- * that are aligned run their shrink split over K.
+ * batches): one work-group per (pair, chunk of 512, 1024 or 2048 output
+ * columns of a slice); moe_lora_plan reports which.  Small batches that are
+ * aligned run their shrink split over K.
  */
 lora_status_t moe_lora_apply(int32_t kind, void *y, int64_t ldy, int32_t reduce_k, const void *x,
                              int64_t ldx, int32_t T, int32_t top_k, int32_t K,

@@ -238,6 +238,23 @@ def test_moe_sizes_and_align_validation():
     assert _moe(T=0, y=None, x=None) == aa.LORA_OK
 
 
+def test_moe_plan_reports_the_unsorted_rule():
+    """moe_lora_plan: at most 1024 (token, k) pairs at rank 16 without the
+    k-reduction skip the alignment; anything else builds it."""
+    assert aa.moe_lora_plan(128, 8, 16)                  # 1024 pairs
+    assert aa.moe_lora_plan(1, 1, 16)
+    assert aa.moe_lora_plan(0, 8, 16)
+    assert not aa.moe_lora_plan(129, 8, 16)              # 1032 pairs
+    assert not aa.moe_lora_plan(4, 8, 32)                # another rank
+    assert not aa.moe_lora_plan(4, 8, 16, reduce_k=True)
+    assert not aa.moe_lora_plan(1 << 28, 16, 16)         # pair count past int32
+    lib = aa.lib()
+    out = aa._i32(0)
+    assert lib.moe_lora_plan(-1, 8, 16, 0, aa.C.byref(out)) == aa.LORA_E_SHAPE
+    assert lib.moe_lora_plan(4, 0, 16, 0, aa.C.byref(out)) == aa.LORA_E_SHAPE
+    assert lib.moe_lora_plan(4, 8, 16, 0, None) == aa.LORA_E_NULL
+
+
 def test_workspace_size_grows_with_every_argument():
     """A workspace shared by calls of several shapes is sized at the largest
     value of each argument; that keeps the single-launch K-split decode's

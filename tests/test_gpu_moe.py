@@ -130,7 +130,7 @@ def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L
     ref2 = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
                                      d["idx"], d["rank"], d["scale"], E)
     # both paths where a call is small enough for the one without alignment
-    for align in ((False, True) if T * k <= 256 else (False,)):
+    for align in ((False, True) if aa.moe_lora_plan(T, k, R) else (False,)):
         log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L} align={align}")
         y = run_moe(W13, d["g0"], d["x"], d["A13"], d["B13"], d["ids"], None, d["idx"], d["rank"],
                     d["scale"], E, align=align)
@@ -297,15 +297,17 @@ def test_moe_config_shape_integer_bit_exact(oracle_mod):
         assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("T,align", [(4, False), (8, False), (4, True), (8, True), (40, False), (40, True)])
+@pytest.mark.parametrize("T,align", [(4, False), (8, False), (12, False), (24, False), (4, True),
+                                     (8, True), (40, False), (40, True)])
 def test_moe_config_small_batch(oracle_mod, T, align):
     """The fused-MoE workload's shapes at decode-sized batches (d_model 4096,
-    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): up to 256 pairs (32
-    tokens) the call skips the alignment; aligned, the few tiles make both
+    d_mlp 1536, 64 experts top-8, rank 16, 8 adapters): a call of few pairs
+    skips the alignment (4 and 8 tokens: one output column per thread; 12
+    tokens: two for w2; 24 tokens: four); aligned, the few tiles make both
     shrinks run split over K."""
     c = synth.config_moe(T=T)
     rows = np.arange(T)
-    log(f"case moe small batch T={T} align={align}")
+    log(f"case moe small batch T={T} align={align} unsorted={aa.moe_lora_plan(T, c.k, c.R)}")
     y = run_moe(W13, c.gate_up0, c.x, c.A13, c.B13, c.topk_ids, None, c.idx, c.slot_rank, c.scale,
                 c.E, align=align)
     bounds.check_bf16_tolerance(y, oracle_rows(oracle_mod, c, 0, rows))

@@ -121,7 +121,7 @@ def test_moe_sweep_bit_exact(oracle_mod, case):
     rank = d["rank"].copy()
     if L > 1:
         rank[0] = 0
-    aligns = (False, True) if T * k <= 256 else (False,)
+    aligns = (False, True) if aa.moe_lora_plan(T, k, R) else (False,)
     log(f"case moe sweep {case}: T={T} k={k} E={E} K={K} I={I} R={R} L={L} shared={shared}")
     ref13 = oracle_mod.moe_lora_apply(0, d["g0"], d["x"], d["A13"], d["B13"], ids, None, d["idx"],
                                       rank, d["scale"], E)
