@@ -39,6 +39,7 @@ LORA_PATH_PREFILL = 2
 LORA_PATH_FUSED = 3
 LORA_PATH_GROUPED = 4
 LORA_PATH_RELAY = 5
+LORA_PATH_TOKEN = 6
 
 MOE_LORA_W13 = 0
 MOE_LORA_W2 = 1
@@ -386,7 +387,8 @@ def lora_plan_packed(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale, ws,
 
 
 PATH_NAMES = {LORA_PATH_AUTO: "auto", LORA_PATH_DECODE: "decode", LORA_PATH_PREFILL: "prefill",
-              LORA_PATH_FUSED: "fused", LORA_PATH_GROUPED: "grouped", LORA_PATH_RELAY: "relay"}
+              LORA_PATH_FUSED: "fused", LORA_PATH_GROUPED: "grouped", LORA_PATH_RELAY: "relay",
+              LORA_PATH_TOKEN: "token"}
 
 
 def lora_apply_packed_noalloc(y, x, A: Sequence, B: Sequence, idx, slot_rank, scale,

@@ -154,6 +154,27 @@ lora_status_t grp_shrink_part(const void *x, int64_t ldx, int32_t T, int32_t K, 
                                       gseg, st));
 }
 
+// TOKEN's grid is T x (256-column chunks); each work-group reads its slot's
+// K x R lora_a block.  It fits while a work-group reads at most 1 MB of
+// lora_a and the rounds of 1024 work-groups (four per CU) times the 16-row
+// passes of the rank stay within 4; auto takes it while the lora_a bytes of
+// all work-groups stay within the dtype's bound.
+// The grid's work-groups, or -1 past what one launch takes (2^31 - 1).
+int64_t token_wgs(int32_t T, const int64_t *N, int32_t S) {
+    int64_t c = 0;
+    for (int s = 0; s < S; ++s) {
+        c += (N[s] + kTokenCols - 1) / kTokenCols;
+        if (c > INT32_MAX) return -1;
+    }
+    const int64_t w = (int64_t)T * c;
+    return w > INT32_MAX ? -1 : w;
+}
+bool token_fits(int64_t wgs, int32_t K, int32_t R, int32_t dtype) {
+    const int64_t a_wg = (int64_t)K * R * (dtype == LORA_DT_BF16 ? 2 : 4);
+    const int64_t rounds = (wgs + kTokenRound - 1) / kTokenRound;
+    return wgs >= 0 && a_wg <= kTokenMaxWgBytes && rounds * ((R + 15) / 16) <= kTokenMaxRoundPasses;
+}
+
 lora_status_t choose_path(int32_t path, int32_t T, int32_t L, int32_t R, int32_t dtype,
                           int *use_prefill) {
     const bool can_prefill = dtype == LORA_DT_BF16 && R % 16 == 0;
@@ -210,15 +231,17 @@ Slices make_slices(const void *const *A, const void *const *B, const int64_t *N,
 namespace aa {
 
 // Every check of lora_apply_packed and its choice of path, on the host; it
-// enqueues nothing.  The auto rule, in order:
-//   1. PREFILL when slots carry long token runs (choose_path);
-//   2. RELAY where its shapes allow, a workspace of lora_workspace_size()
-//      bytes is given, and the output is narrow or T <= 256;
-//   3. FUSED where its shapes allow and the output is narrow;
-//   4. GROUPED where its shapes allow, L <= 64, R <= 64 and the output is
+// enqueues nothing.  The auto rule, the first that holds:
+//   1. TOKEN while its work-groups' recomputed shrinks read little lora_a;
+//   2. RELAY for relay batches with a workspace of lora_workspace_size()
+//      bytes, narrow outputs or T x width up to 256 x 128256;
+//   3. GROUPED at rank 16 for narrow outputs up to 4096 tokens and 128 slots;
+//   4. PREFILL when slots carry long token runs (choose_path);
+//   5. FUSED where its shapes allow, the output is narrow and L <= 64;
+//   6. GROUPED where its shapes allow, L <= 64, R <= 64 and the output is
 //      narrow;
-//   5. PREFILL for bf16 with R in {16, 32, 64, 128} and rows of 8 columns;
-//   6. DECODE.
+//   7. PREFILL for bf16 with R in {16, 32, 64, 128} and rows of 8 columns;
+//   8. DECODE.
 // "Narrow": the slices sum to at most 16384 columns.
 int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void *x, int64_t ldx,
                     int32_t T, int32_t K, const void *const *A, const void *const *B,
@@ -231,8 +254,35 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     CHECK(check_k(K, ldx));
     int64_t ntot = 0;
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
+    // TOKEN (one work-group per token and 256 columns, each recomputing its
+    // token's shrink) while the lora_a bytes those shrinks read stay small:
+    // measured against RELAY on bf16 (QKV shape: 1 to 16 tokens 4.3-5.5
+    // against 6.0-6.6 us, 32 tokens 7.3 against 7.0; a 32000-column lm_head
+    // at 4 tokens 5.9 against 7.0, 16 tokens 12.0 against 7.9; rank-64
+    // gate_up at 1 token 11.9 against 21.5), and against DECODE's three
+    // launches on fp32 (QKV shape 80 tokens 28.3 against 31.1, 96 tokens 33.6
+    // against 31.4; hidden 64, 4096 tokens 8.0 against 22.0).
+    const int64_t tok_wgs = token_wgs(T, N, S);
+    if (path == LORA_PATH_TOKEN && tok_wgs < 0) return LORA_E_PATH;
+    // (token_fits bounds the work-groups to 4096 and each one's lora_a bytes
+    // to 1 MB, so the product below stays far inside int64)
+    const bool token = path == LORA_PATH_TOKEN ||
+                       (path == LORA_PATH_AUTO && token_fits(tok_wgs, K, R, dtype) &&
+                        tok_wgs * K * R * (dtype == LORA_DT_BF16 ? 2 : 4) <=
+                            (dtype == LORA_DT_BF16 ? kTokenMaxBytesBf16 : kTokenMaxBytesF32));
     int use_prefill = 0;
-    CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (!token) CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
+    if (token) {
+        out->path = LORA_PATH_TOKEN;
+        out->shared_a = 0;
+        out->noop = T == 0 ? 1 : 0;
+        if (T == 0) return LORA_OK;
+        if (!y || !x || !idx || !scale) return LORA_E_NULL;
+        CHECK(check_ptrs(A, S));
+        CHECK(check_ptrs(B, S));
+        if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
+        return LORA_OK;   // no workspace needed
+    }
     // Auto takes the single-launch kernel with the K-split shrink for decode
     // batches when the workspace is there: for narrow outputs, and for wide
     // ones (an lm_head's vocabulary) up to a bound on T times the width, where
@@ -325,6 +375,12 @@ int32_t packed_run(const PackedPlan &p, void *y, int64_t ldy, int64_t y_col_offs
         // one launch; no workspace and no segments needed
         const Slices sl = make_slices(A, B, N, S, y_col_offset);
         return launched(launch_dec_fused(y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank, scale, st));
+    }
+    if (p.path == LORA_PATH_TOKEN) {
+        // one launch; no workspace and no segments needed
+        const Slices sl = make_slices(A, B, N, S, y_col_offset);
+        return launched(launch_dec_token(dtype, y, ldy, x, ldx, T, K, sl, S, L, R, idx, slot_rank,
+                                         scale, st));
     }
     const WsLayout wl = ws_layout(T, K, S, R, L);
     SegPtrs seg = seg_ptrs(ws, wl.seg);
@@ -483,7 +539,8 @@ lora_status_t lora_shrink(float *buf, const void *x, int64_t ldx, int32_t T, int
                           const void *const *A, int32_t S, int32_t L, int32_t R,
                           const int32_t *idx, const int32_t *slot_rank, int32_t dtype,
                           int32_t path, uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
-    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY) return LORA_E_PATH;
+    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY || path == LORA_PATH_TOKEN)
+        return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     CHECK(check_k(K, ldx));
     int use_prefill = 0;
@@ -537,7 +594,8 @@ lora_status_t lora_expand(void *y, int64_t ldy, int64_t y_col_offset, const floa
                           int32_t L, int32_t R, const int32_t *idx, const int32_t *slot_rank,
                           const float *scale, int32_t dtype, int32_t path, uint32_t flags,
                           void *ws, size_t ws_bytes, void *stream) {
-    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY) return LORA_E_PATH;
+    if (path == LORA_PATH_FUSED || path == LORA_PATH_RELAY || path == LORA_PATH_TOKEN)
+        return LORA_E_PATH;
     CHECK(check_sizes(T, S, L, R, dtype));
     int64_t ntot = 0;
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));

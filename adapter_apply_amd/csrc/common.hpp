@@ -379,6 +379,17 @@ hipError_t launch_dec_reduce(int32_t T, int32_t S, int32_t L, int32_t R,
                              int32_t n_kchunks, float *buf, hipStream_t st);
 // buf == nullptr: the expand sums the K-chunk partials itself (count read from
 // the segment header, at most n_kchunks).
+// TOKEN: one launch, work-group = (token, kTokenCols output columns) (k_dec_token).
+constexpr int kTokenCols = 256;
+constexpr int64_t kTokenRound = 1024;                 // work-groups resident at once (4 per CU)
+constexpr int64_t kTokenMaxRoundPasses = 4;
+constexpr int64_t kTokenMaxWgBytes = 1 << 20;         // lora_a bytes per work-group
+constexpr int64_t kTokenMaxBytesBf16 = 72LL << 20;    // auto: lora_a bytes of all work-groups
+constexpr int64_t kTokenMaxBytesF32 = 512LL << 20;
+hipError_t launch_dec_token(int dtype, void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
+                            int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
+                            const int32_t *idx, const int32_t *slot_rank, const float *scale,
+                            hipStream_t st);
 hipError_t launch_dec_expand(int dtype, void *y, int64_t ldy, const float *buf,
                              const float *partial, int32_t n_kchunks, int32_t T,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,

@@ -330,7 +330,173 @@ __global__ __launch_bounds__(kThreads) void k_dec_expand(ExpandArgs a) {
     }
 }
 
+// Single launch for tiny batches: work-group = (token, 256 output columns of
+// one slice).  Each work-group computes its token's shrink for its slice,
+// x[t] . A[s][j]^T for the slot's r rank rows (wave w takes rows w, w + 4, ...,
+// four at a time; lanes over K, 16 bytes each, then a fixed-order wave sum),
+// into LDS; then
+// each thread adds one column, y[t][n] += scale[s] * sum_j buf[j] * B[s][n][j]
+// (j ascending).  The y value and the first lora_b vectors of the column are
+// loaded before the shrink.  No segment build, no workspace: the shrink is
+// recomputed by every column chunk of a token, which the host allows only
+// for a few tokens and a small K * R.
+constexpr int kTokCols = kTokenCols;   // output columns per work-group, one per thread
+static_assert(kTokCols == kThreads, "one column per thread");
+constexpr int kTokPreVecs = 2;         // lora_b vectors per column loaded before the shrink
+constexpr int kTokRows = 4;            // rank rows a wave's shrink takes at once
+
+struct TokenArgs {
+    void *y;
+    int64_t ldy;
+    const void *x;
+    int64_t ldx;
+    int32_t K, L, R, S, n_chunks;
+    const int32_t *idx;
+    const int32_t *slot_rank;
+    const float *scale;
+    Slices sl;
+    int32_t chunk_start[kMaxSlices + 1];
+};
+
+__device__ __forceinline__ float vec_elt(const uint4 &v, int i) {
+    const uint32_t w = i < 4 ? (i < 2 ? v.x : v.y) : (i < 6 ? v.z : v.w);
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+__device__ __forceinline__ float vec_elt(const float4 &v, int i) {
+    return i < 2 ? (i ? v.y : v.x) : (i == 2 ? v.z : v.w);
+}
+__device__ __forceinline__ float elt_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float elt_f32(float v) { return v; }
+__device__ __forceinline__ void elt_store(uint16_t *p, float v) { *p = (uint16_t)f32_to_bf16_rne(v); }
+__device__ __forceinline__ void elt_store(float *p, float v) { *p = v; }
+
+// Sum over the 64 lanes of a wave, the same value on every lane: DPP sums
+// within each 16-lane row (quad swaps, then half-row and row mirrors), then
+// the four row sums in row order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_f32<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror
+    v += dpp_f32<0x140>(v);   // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dec_token(TokenArgs a) {
+    typedef typename Elt<BF16>::T E;
+    typedef typename std::conditional<BF16, uint4, float4>::type V;
+    constexpr int EPV = Elt<BF16>::kPerVec;
+    __shared__ float s_tb[kMaxRank];
+    const int t = blockIdx.x / a.n_chunks;
+    const int chunk = blockIdx.x - t * a.n_chunks;
+    const int s = a.idx[t];
+    if (s < 0 || s >= a.L) return;                       // uniform: no adapter
+    const int r = a.slot_rank ? min(a.slot_rank[s], a.R) : a.R;
+    if (r <= 0) return;
+    int sg = 0;
+    while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
+    const int Ns = (int)a.sl.n[sg];
+    const int n = (chunk - a.chunk_start[sg]) * kTokCols + threadIdx.x;
+    const bool live = n < Ns;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+
+    // the column's y value and first lora_b vectors (clamped: column 0, and
+    // the row's last vector needed)
+    E *yp = static_cast<E *>(a.y) + (int64_t)t * a.ldy + a.sl.off[sg] + (live ? n : 0);
+    const E y0 = *yp;
+    const E *br = static_cast<const E *>(a.sl.b[sg]) + ((int64_t)s * Ns + (live ? n : 0)) * a.R;
+    const int nvec = (r + EPV - 1) / EPV;
+    V bpre[kTokPreVecs];
+#pragma unroll
+    for (int q = 0; q < kTokPreVecs; ++q) bpre[q] = ldg<V>(br + EPV * min(q, nvec - 1));
+
+    // ---- shrink --------------------------------------------------------
+    const E *xr = static_cast<const E *>(a.x) + (int64_t)t * a.ldx;
+    const E *ar = static_cast<const E *>(a.sl.a[sg]) + (int64_t)s * a.R * a.K;
+    // wave w takes rank rows w + 4 i, kTokRows at a time (one x load feeds
+    // them; rows past r repeat row r - 1 and are not written)
+    for (int j0 = w; j0 < r; j0 += kTokRows * kWavesPerWg) {
+        const E *arow[kTokRows];
+        float acc[kTokRows];
+#pragma unroll
+        for (int i = 0; i < kTokRows; ++i) {
+            arow[i] = ar + (int64_t)min(j0 + i * kWavesPerWg, r - 1) * a.K;
+            acc[i] = 0.0f;
+        }
+#pragma unroll 4
+        for (int k0 = EPV * lane; k0 < a.K; k0 += EPV * kWave) {
+            const V xv = ldg<V>(xr + k0);
+            V av[kTokRows];
+#pragma unroll
+            for (int i = 0; i < kTokRows; ++i) av[i] = ldg<V>(arow[i] + k0);
+#pragma unroll
+            for (int i = 0; i < kTokRows; ++i) acc[i] = dot_vec(xv, av[i], acc[i], 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kTokRows; ++i) {
+            const int j = j0 + i * kWavesPerWg;
+            if (j < r) {                                 // uniform over the wave
+                const float v = wave_sum_f32(acc[i]);
+                if (lane == 0) s_tb[j] = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- expand: one column per thread ------------------------------------
+    if (!live) return;
+    float d = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kTokPreVecs; ++q)
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            const int j = EPV * q + i;
+            if (j < r) d = fmaf(s_tb[j], vec_elt(bpre[q], i), d);
+        }
+    for (int q = kTokPreVecs; q < nvec; ++q) {
+        const V bv = ldg<V>(br + EPV * q);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            const int j = EPV * q + i;
+            if (j < r) d = fmaf(s_tb[j], vec_elt(bv, i), d);
+        }
+    }
+    elt_store(yp, elt_f32(y0) + a.scale[s] * d);
+}
+
 }  // namespace
+
+hipError_t launch_dec_token(int dtype, void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
+                            int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,
+                            const int32_t *idx, const int32_t *slot_rank, const float *scale,
+                            hipStream_t st) {
+    TokenArgs a{};
+    a.y = y; a.ldy = ldy; a.x = x; a.ldx = ldx; a.K = K; a.L = L; a.R = R; a.S = S;
+    a.idx = idx; a.slot_rank = slot_rank; a.scale = scale; a.sl = sl;
+    int c = 0;
+    for (int s = 0; s < S; ++s) {
+        a.chunk_start[s] = c;
+        c += (int)((sl.n[s] + kTokCols - 1) / kTokCols);
+    }
+    for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
+    a.n_chunks = c;
+    const int64_t grid = (int64_t)T * c;
+    if (grid <= 0) return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(k_dec_token<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_dec_token<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_dec_shrink(int dtype, const void *x, int64_t ldx, int32_t T, int32_t K,
                              const Slices &sl, int32_t S, int32_t L, int32_t R,

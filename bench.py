@@ -61,7 +61,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="all", choices=["all", *LINEAR, "moe"],
                    help="all: the headline decode line with every other configuration nested")
-    p.add_argument("--path", default="auto", choices=["auto", "fused", "relay", "grouped", "decode", "prefill"],
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "relay", "grouped", "decode", "prefill",
+                                                     "token"],
                    help="force a decode path (development runs; the headline uses auto)")
     p.add_argument("--moe-tokens", type=int, default=2048,
                    help="tokens of the fused-MoE workload (2048 by default)")
@@ -413,7 +414,8 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
 
     step_path = {"auto": aa.LORA_PATH_AUTO, "fused": aa.LORA_PATH_FUSED,
                  "prefill": aa.LORA_PATH_PREFILL, "grouped": aa.LORA_PATH_GROUPED,
-                 "decode": aa.LORA_PATH_DECODE, "relay": aa.LORA_PATH_RELAY}[args.path]
+                 "decode": aa.LORA_PATH_DECODE, "relay": aa.LORA_PATH_RELAY,
+                 "token": aa.LORA_PATH_TOKEN}[args.path]
 
     def step(d):
         aa.lora_apply_packed(d["y"], d["x"], d["A"], d["B"], d["idx"], d["rank"], d["scale"],
@@ -426,6 +428,9 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
     taken = aa.lora_plan_packed(d0["y"], d0["x"], d0["A"], d0["B"], d0["idx"], d0["rank"],
                                 d0["scale"], d0["ws"], path=step_path)
     relay, fused = taken == aa.LORA_PATH_RELAY, taken == aa.LORA_PATH_FUSED
+    # the paths that are one kernel for the whole step
+    single = {aa.LORA_PATH_RELAY: "relay", aa.LORA_PATH_FUSED: "fused",
+              aa.LORA_PATH_TOKEN: "token"}.get(taken)
     grouped, prefill = taken == aa.LORA_PATH_GROUPED, taken == aa.LORA_PATH_PREFILL
     # the decode path folds the K-chunk reduction into the expand while
     # ceil(K/256) * R <= 512, else a reduce kernel runs
@@ -456,7 +461,7 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
     if args.profile:
         for i in range(max(steps, 1)):
             step(insts[i % n_inst])
-        if not (fused or relay):
+        if not single:
             for fn in ((segments_only, shrink_reduce, expand_only) if grouped_buf else
                        (segments_only, shrink_reduce, shrink_only, expand_only)):
                 for i in range(n_inst):
@@ -474,8 +479,8 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
     ms_per_step, wall = rot.time_steps(step, steps, warmup)
 
     # ---- per-kernel durations, live: median over replays of one-kernel graphs
-    if fused or relay:
-        kernel_calls = [("relay" if relay else "fused", step)]   # the whole step is one kernel
+    if single:
+        kernel_calls = [(single, step)]   # the whole step is one kernel
     elif grouped:
         kernel_calls = [("segments", segments_only)] if grouped_tab else []
         kernel_calls += ([("shrink+reduce", shrink_reduce), ("expand", expand_only)] if grouped_buf
@@ -494,8 +499,8 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
     torch.cuda.synchronize()
 
     ab = algorithmic_bytes(c, args.shared_a)
-    if fused or relay:
-        dom, dom_bytes = ("relay" if relay else "fused"), ab["fused"]
+    if single:
+        dom, dom_bytes = single, ab["fused"]
     else:
         dom = max((k for k in ("shrink", "shrink+reduce", "expand") if k in per_kernel),
                   key=lambda k: per_kernel[k])
@@ -505,7 +510,7 @@ def linear_entry(name, args, steps, warmup, cpu_seconds, copy_gbps):
     counted = args.path == "auto" and not args.shared_a
     traffic = load_traffic(name, dom, khash) if counted else None
     mfma_exec = load_mfma_counters(name, khash) if counted else None
-    step_bytes = (ab["fused"] if fused or relay else
+    step_bytes = (ab["fused"] if single else
                   ab["shrink"] + ab["expand"] if grouped else ab["total"])
     entry = {
         "workload": DESC[name] + (", one lora_a for every slice" if args.shared_a else ""),

@@ -68,14 +68,25 @@
  *                       tiles are few), MFMA tile expand.  bf16, R % 16 == 0
  *                       (the persistent expand: R in {16, 32, 64, 128} and
  *                       rows of 8).
+ *              TOKEN    lora_apply_packed only.  One launch, no workspace;
+ *                       work-group = (token, 256 output columns of a slice),
+ *                       each recomputing its token's shrink (VALU).  Every
+ *                       shape and dtype the call accepts whose grid
+ *                       (T x the slices' 256-column chunks) is at most
+ *                       2^31 - 1 work-groups.
  *              DECODE   segments, VALU split-K shrink, VALU expand.  Every
- *                       shape and dtype the call accepts (the only fp32 path).
+ *                       shape and dtype the call accepts.
  *
  *            LORA_PATH_AUTO in lora_apply_packed ("narrow": the slices sum
  *            to at most 16384 columns; "a relay batch": with
  *            U = L (1 - exp(-T / L)) the slots expected to draw tokens,
- *            U + T / 32 <= 12 or T >= 24 U; the first row that holds wins):
+ *            U + T / 32 <= 12 or T >= 24 U; W = T * sum ceil(N[s] / 256),
+ *            TOKEN's work-groups; e = 2 (bf16) or 4 (fp32) bytes; the first
+ *            row that holds wins):
  *              | condition                                        | path    |
+ *              | ceil(W / 1024) * ceil(R / 16) <= 4,              | TOKEN   |
+ *              |   K*R*e <= 1 MB, W*K*R*e <= 72 MB (bf16) or      |         |
+ *              |   512 MB (fp32)                                  |         |
  *              | RELAY's shapes, ws of lora_workspace_size(), a   | RELAY   |
  *              |   relay batch, narrow or T * sum(N) <= 256*128256|         |
  *              | GROUPED's shapes, R == 16, T <= 4096, L <= 128,  | GROUPED |
@@ -163,6 +174,7 @@ typedef int32_t lora_status_t;
 #define LORA_PATH_FUSED    3
 #define LORA_PATH_GROUPED  4
 #define LORA_PATH_RELAY    5
+#define LORA_PATH_TOKEN    6
 
 #define LORA_FLAG_SEGMENTS_READY 1u
 #define LORA_FLAG_ACTIVE_ONLY    2u
@@ -281,7 +293,7 @@ lora_status_t lora_apply_packed(void *y, int64_t ldy, int64_t y_col_offset, cons
 
 /*
  * The path lora_apply_packed would take for these arguments (one of
- * LORA_PATH_RELAY, FUSED, GROUPED, PREFILL, DECODE), after the same checks,
+ * LORA_PATH_TOKEN, RELAY, FUSED, GROUPED, PREFILL, DECODE), after the same checks,
  * without enqueueing anything.  Returns what lora_apply_packed would return
  * for a bad argument.
  */

@@ -123,8 +123,10 @@ def _apply(**kw):
     (dict(path=aa.LORA_PATH_RELAY, dt=aa.LORA_DT_F32), aa.LORA_E_PATH),
     (dict(path=aa.LORA_PATH_RELAY, ws=None), aa.LORA_E_NULL),
     (dict(path=aa.LORA_PATH_RELAY, wsb=1024), aa.LORA_E_WORKSPACE),
-    (dict(path=6), aa.LORA_E_PATH),
+    # TOKEN takes every shape whose grid one launch holds
+    (dict(path=aa.LORA_PATH_TOKEN, S=1, N=(C.c_int64 * 1)(1 << 40), ldy=1 << 40), aa.LORA_E_PATH),
     (dict(path=7), aa.LORA_E_PATH),
+    (dict(path=99), aa.LORA_E_PATH),
 ])
 def test_apply_rejects_bad_arguments(kw, code):
     assert _apply(**kw) == code
@@ -150,6 +152,8 @@ def test_shrink_expand_validation():
                            aa.LORA_PATH_FUSED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
                            aa.LORA_PATH_RELAY, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
+    assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 16, FAKE, None, 1,
+                           aa.LORA_PATH_TOKEN, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     assert lib.lora_shrink(FAKE, FAKE, 64, 16, 64, A, 2, 3, 144, FAKE, None, 1,
                            aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     # the partial-sum hand-off stops at rank 64 on the grouped path
@@ -162,6 +166,8 @@ def test_shrink_expand_validation():
     assert lib.lora_expand(FAKE, 136, 0, FAKE, 16, A, Ng, 2, 3, 16, FAKE, None, FAKE, 1,
                            aa.LORA_PATH_GROUPED, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     N = (C.c_int64 * 2)(64, 64)
+    assert lib.lora_expand(FAKE, 128, 0, FAKE, 16, A, N, 2, 3, 16, FAKE, None, FAKE, 1,
+                           aa.LORA_PATH_TOKEN, 0, FAKE_WS, ok_ws, None) == aa.LORA_E_PATH
     assert lib.lora_expand(FAKE, 128, 0, None, 16, A, N, 2, 3, 8, FAKE, None, FAKE, 0, 0, 0,
                            FAKE_WS, ok_ws, None) == aa.LORA_E_NULL
     assert lib.lora_expand(FAKE, 100, 0, FAKE, 16, A, N, 2, 3, 8, FAKE, None, FAKE, 0, 0, 0,
@@ -326,8 +332,31 @@ def _ws_size(T, K, S, R, L):
     (dict(T=64, L=64), aa.LORA_PATH_FUSED),
     (dict(T=256, L=64), aa.LORA_PATH_FUSED),
     (dict(T=512, L=32), aa.LORA_PATH_FUSED),
-    # a few tokens over a few slots: the K-split single launch
-    (dict(T=8), aa.LORA_PATH_RELAY),
+    # a few tokens: one work-group per token and 256 columns while the lora_a
+    # its shrinks re-read stays within 72 MB (bf16): 8 tokens x 24 chunks x
+    # 128 KB = 25 MB; at 32 tokens (100 MB) the K-split single launch
+    (dict(T=8), aa.LORA_PATH_TOKEN),
+    (dict(T=1), aa.LORA_PATH_TOKEN),
+    (dict(T=32), aa.LORA_PATH_RELAY),
+    (dict(T=8, ws=None, wsb=0), aa.LORA_PATH_TOKEN),           # needs no workspace
+    # a 32000-column lm_head: 4 tokens (500 work-groups, 66 MB) TOKEN, 16 RELAY
+    (dict(T=4, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_TOKEN),
+    (dict(T=16, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_RELAY),
+    # rank 64 at one token: 4 passes of 16 rows, one round of work-groups
+    (dict(T=1, R=64), aa.LORA_PATH_TOKEN),
+    (dict(T=16, R=64), aa.LORA_PATH_GROUPED),                  # 384 x 512 KB past 72 MB
+    # fp32 (the split VALU path otherwise): up to 512 MB of lora_a re-reads
+    # and 4 rounds x passes; the fp32 workload at hidden 64
+    (dict(dt=aa.LORA_DT_F32, R=16, T=64), aa.LORA_PATH_TOKEN),
+    (dict(dt=aa.LORA_DT_F32, R=16, T=96), aa.LORA_PATH_DECODE),
+    (dict(dt=aa.LORA_DT_F32, R=4, T=16, K=64, ldx=64, L=3, S=1, N=(C.c_int64 * 1)(64), ldy=64),
+     aa.LORA_PATH_TOKEN),
+    (dict(dt=aa.LORA_DT_F32, R=4, T=4096, K=64, ldx=64, L=3, S=1, N=(C.c_int64 * 1)(64), ldy=64),
+     aa.LORA_PATH_TOKEN),
+    (dict(dt=aa.LORA_DT_F32, R=4, T=4097, K=64, ldx=64, L=3, S=1, N=(C.c_int64 * 1)(64), ldy=64),
+     aa.LORA_PATH_DECODE),                                     # 5 rounds of 1024 work-groups
+    (dict(dt=aa.LORA_DT_F32, R=64, T=1, K=8192, ldx=8192, S=1, N=(C.c_int64 * 1)(64), ldy=64),
+     aa.LORA_PATH_DECODE),                                     # 2 MB of lora_a per work-group
     # long runs per slot (8192 tokens over 16 slots): the tile kernels
     (dict(T=8192, L=16, R=64, S=2, N=(C.c_int64 * 2)(14336, 14336), ldy=28672), aa.LORA_PATH_PREFILL),
     # 128 slots at rank 128: the tile kernels
@@ -349,6 +378,8 @@ def _ws_size(T, K, S, R, L):
     # forced paths are reported as such
     (dict(path=aa.LORA_PATH_GROUPED), aa.LORA_PATH_GROUPED),
     (dict(path=aa.LORA_PATH_DECODE), aa.LORA_PATH_DECODE),
+    (dict(path=aa.LORA_PATH_TOKEN), aa.LORA_PATH_TOKEN),
+    (dict(path=aa.LORA_PATH_TOKEN, dt=aa.LORA_DT_F32, R=4, T=8192), aa.LORA_PATH_TOKEN),
 ])
 def test_plan_reports_the_path(kw, path):
     st, got = _plan(**kw)

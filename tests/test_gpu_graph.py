@@ -41,7 +41,7 @@ def metadata_sets(c):
 
 
 @pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, aa.LORA_PATH_GROUPED, aa.LORA_PATH_PREFILL,
-                                  aa.LORA_PATH_DECODE, aa.LORA_PATH_RELAY])
+                                  aa.LORA_PATH_DECODE, aa.LORA_PATH_RELAY, aa.LORA_PATH_TOKEN])
 def test_graph_replays_read_current_metadata(oracle_mod, path):
     c = synth.config_decode()
     d = LinearOnDevice(c, guard=False)

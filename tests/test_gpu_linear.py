@@ -18,8 +18,8 @@ import synth  # noqa: E402
 from tests import bounds, oracle_par  # noqa: E402
 from tests.gpu_util import LinearOnDevice, canaries_intact, dev, host_f32, log  # noqa: E402
 
-DEC, PRE, FUS, GRP, RLY = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
-                           aa.LORA_PATH_GROUPED, aa.LORA_PATH_RELAY)
+DEC, PRE, FUS, GRP, RLY, TOK = (aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
+                                aa.LORA_PATH_GROUPED, aa.LORA_PATH_RELAY, aa.LORA_PATH_TOKEN)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -53,16 +53,40 @@ def oracle_y(oracle_mod, c, rows=None):
 
 # ---------------------------------------------------------------------------
 
-def test_tiny_fp32_decode(oracle_mod):
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, TOK])
+def test_tiny_fp32_decode(oracle_mod, path):
     c = synth.config_tiny()
-    log(f"case tiny fp32 T={c.T}")
+    log(f"case tiny fp32 T={c.T} path={path}")
     d = LinearOnDevice(c)
-    d.apply(DEC)
+    d.apply(path)
     y = d.y_host()
     ref = oracle_y(oracle_mod, c)
     M = bounds.linear_magnitude(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
     assert np.all(np.abs(y - ref) <= bounds.fp32_bound(M, c.K, c.R))
     assert_passthrough(c, y)
+    assert canaries_intact(d.yfull)
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, TOK])
+@pytest.mark.parametrize("seed,T,K,N,R,L", [
+    (61, 16, 64, [64], 4, 3),                      # the fp32 workload's shape
+    (62, 64, 4096, [4096, 1024, 1024], 16, 8),     # QKV at 64 tokens: auto takes TOKEN
+    (63, 300, 520, [36, 1028], 12, 5),             # ragged columns, rank 12: one 16-row pass
+    (64, 1, 8, [4], 4, 1),                         # one token, K 8, one 4-column slice
+    (65, 40, 1024, [300], 40, 3),                  # rank 40: three passes of the token shrink
+])
+def test_fp32_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
+    """fp32 on the paths that take it (the split VALU kernels, the one-launch
+    token kernel and auto's choice between them): integer vectors, bit for bit."""
+    c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="f32")
+    log(f"case fp32 integer path={path} T={T} K={K} N={N} R={R} L={L}")
+    d = LinearOnDevice(c)
+    d.apply(path)
+    y = d.y_host()
+    ref = oracle_y(oracle_mod, c)
+    exact = bounds.linear_exact_int(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.array_equal(ref, exact.astype(np.float32))
+    assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
     assert canaries_intact(d.yfull)
 
 
@@ -114,7 +138,7 @@ INTEGER_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY, TOK])
 @pytest.mark.parametrize("seed,T,K,N,R,L", INTEGER_CASES)
 def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
@@ -130,7 +154,7 @@ def test_integer_vectors_bit_exact(oracle_mod, path, seed, T, K, N, R, L):
     assert canaries_intact(d.yfull)
 
 
-@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY])
+@pytest.mark.parametrize("path", [DEC, PRE, FUS, GRP, RLY, TOK])
 def test_decode_config_qkv(oracle_mod, path):
     """256 tokens, hidden 4096, QKV 4096/1024/1024, rank 16, 8 slots, 10% idx=-1."""
     c = synth.config_decode()
@@ -205,7 +229,7 @@ def test_logits_vocab_32000_every_path(oracle_mod):
     one oracle result."""
     c = synth.config_logits(vocab=32000)
     ref = oracle_y(oracle_mod, c)
-    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY):
+    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK):
         log(f"case logits vocab=32000 path={path}")
         d = LinearOnDevice(c)
         d.apply(path)
@@ -378,7 +402,7 @@ def test_all_tokens_without_adapter_unchanged():
     c = synth.config_decode(T=64)
     c.idx[:] = -1
     d = LinearOnDevice(c)
-    for path in (DEC, PRE, FUS, GRP, RLY):
+    for path in (DEC, PRE, FUS, GRP, RLY, TOK):
         d.apply(path)
         y = d.y_host()
         assert np.array_equal(y.view(np.uint32), c.y0.view(np.uint32))
@@ -391,7 +415,7 @@ def test_zero_b_identity_and_invalid_slots(oracle_mod):
     c.idx[::11] = 100
     c.slot_rank[3] = 0    # empty slot
     c.B = [np.zeros_like(b) for b in c.B]
-    for path in (DEC, PRE, FUS, GRP, RLY):
+    for path in (DEC, PRE, FUS, GRP, RLY, TOK):
         d = LinearOnDevice(c)
         d.apply(path)
         y = d.y_host()
@@ -407,7 +431,7 @@ def test_column_offset_and_wide_rows(oracle_mod):
     wide = rng.standard_normal((c.T, 200)).astype(np.float32)
     wide = synth.round_bf16(wide)
     off = 40
-    for path in (DEC, PRE, FUS, GRP, RLY):
+    for path in (DEC, PRE, FUS, GRP, RLY, TOK):
         yw = dev(wide, torch.bfloat16)
         d = LinearOnDevice(c, guard=False)
         aa.lora_apply_packed(yw, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, y_col_offset=off,
@@ -513,7 +537,7 @@ def on_device_shared_a(c):
     return d
 
 
-@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY])
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK])
 @pytest.mark.parametrize("seed,T,K,N,R,L", [
     (51, 600, 1024, [256, 64, 64], 16, 3),     # long runs per slot: auto takes the tile kernels
     (52, 300, 2048, [512, 512], 64, 100),      # 100 slots: auto takes the tile kernels, K split
@@ -555,7 +579,7 @@ def test_shared_lora_a_prefill_shape(oracle_mod):
 MLA_K, MLA_N = 7168, [1536, 576]
 
 
-@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY])
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK])
 @pytest.mark.parametrize("seed,T,R,L", [
     (55, 48, 16, 4),       # decode batch: auto takes the single-launch kernel
     (56, 900, 64, 6),      # long runs per slot: auto takes the tile kernels, one shrink

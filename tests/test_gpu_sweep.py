@@ -26,7 +26,7 @@ from tests.gpu_util import canaries_intact, dev, guarded, host_f32, log  # noqa:
 from tests.test_gpu_moe import W13, W2, integer_moe, run_moe  # noqa: E402
 
 PATHS = [aa.LORA_PATH_AUTO, aa.LORA_PATH_DECODE, aa.LORA_PATH_PREFILL, aa.LORA_PATH_FUSED,
-         aa.LORA_PATH_GROUPED, aa.LORA_PATH_RELAY]
+         aa.LORA_PATH_GROUPED, aa.LORA_PATH_RELAY, aa.LORA_PATH_TOKEN]
 
 
 @pytest.fixture(scope="module", autouse=True)
