@@ -370,26 +370,6 @@ __device__ __forceinline__ float elt_f32(float v) { return v; }
 __device__ __forceinline__ void elt_store(uint16_t *p, float v) { *p = (uint16_t)f32_to_bf16_rne(v); }
 __device__ __forceinline__ void elt_store(float *p, float v) { *p = v; }
 
-// Sum over the 64 lanes of a wave, the same value on every lane: DPP sums
-// within each 16-lane row (quad swaps, then half-row and row mirrors), then
-// the four row sums in row order.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xf, 0xf, false));
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-    v += dpp_f32<0xb1>(v);    // quad_perm [1, 0, 3, 2]
-    v += dpp_f32<0x4e>(v);    // quad_perm [2, 3, 0, 1]
-    v += dpp_f32<0x141>(v);   // row_half_mirror
-    v += dpp_f32<0x140>(v);   // row_mirror
-    const int b = __builtin_bit_cast(int, v);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
-           __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-}
-
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_dec_token(TokenArgs a) {
     typedef typename Elt<BF16>::T E;

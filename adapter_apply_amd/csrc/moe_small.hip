@@ -8,8 +8,8 @@
 // loads the y values and (up to 2 columns per thread) the lora_b rows of its
 // CPT adjacent columns, which do not depend on the shrink, then computes its
 // part of the pair's shrink x[row] . A[slot][ea]^T (8 elements of K per
-// thread and step, every rank row, fp32), which a wave butterfly and an
-// ordered sum over the 8 waves complete;
+// thread and step, every rank row, fp32), which a wave sum and an ordered
+// sum over the 8 waves complete;
 // then y[p][off + n] = RNE(y + scale[slot] * coef[p] * sum_j buf[j] * B[n][j]).
 // The shrink is recomputed by each column chunk of a pair; the host picks the
 // smallest CPT (1, 2 or 4) whose grid holds at most one work-group per CU,
@@ -134,14 +134,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int q = 0; q < 2 * CPT; ++q) bv[q] = ldg<uint4>(br + 8 * q);
     }
-    // wave butterfly (the same order on every lane), then the waves in order
+    // wave sums (a fixed order), then the waves in order
 #pragma unroll
-    for (int j = 0; j < kRank; ++j) {
-        float v = acc[j];
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-        acc[j] = v;
-    }
+    for (int j = 0; j < kRank; ++j) acc[j] = wave_sum_f32(acc[j]);
     if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < kRank; ++j) s_part[w][j] = acc[j];
