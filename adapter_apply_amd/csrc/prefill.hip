@@ -598,7 +598,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
 // XCD's column groups, so each tile's buffer rows and the few slots' lora_b
 // blocks are fetched into its L2 once (ordered column group first, the
 // lora_b blocks of a slot were evicted between its tiles and fetched again:
-// about one more pass over lora_b on the prefill gate_up workload).
+// about one more pass over lora_b on the prefill gate_up workload).  Item
+// f = tile * n_cg + cg runs on XCD f % 8: with n_cg a multiple of 8 each XCD
+// keeps the same column groups for every tile (its lora_b columns stay in its
+// L2); otherwise the XCDs still get equal shares and no item is empty.
 // Ranks up to 128 (R = 16 * NKS); CW output columns per item (256 up to rank
 // 64, 128 above, so that two work-groups still fit a CU's LDS).  Of each
 // lora_b row only the first 2 * ceil(r / 16) units (rounded up to a power of
@@ -629,21 +632,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     const int lw = blockIdx.x / kXcds;
     const int nw = gridDim.x / kXcds;
     const int n_tiles = a.seg.header[3];
-    const int n_x = n_tiles * a.per_xcd;
+    // items f = tile * n_cg + cg, dealt round-robin to the XCDs (f % 8)
+    const int64_t n_items = (int64_t)n_tiles * a.n_cg;
+    const int n_x = n_items > xcd ? (int)((n_items - xcd + kXcds - 1) / kXcds) : 0;
     const int cnt = lw < n_x ? (n_x - lw + nw - 1) / nw : 0;
     if (cnt == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
 
     // item k of this work-group (clamped to its last one): tile and column group
-    auto tile_of = [&](int k) {
-        const int j = lw + min(k, cnt - 1) * nw;
-        return j / a.per_xcd;
-    };
-    auto cg_of = [&](int k) {
-        const int j = lw + min(k, cnt - 1) * nw;
-        return (j % a.per_xcd) * kXcds + xcd;
-    };
+    auto item_of = [&](int k) { return (int64_t)(lw + min(k, cnt - 1) * nw) * kXcds + xcd; };
+    auto tile_of = [&](int k) { return (int)(item_of(k) / a.n_cg); };
+    auto cg_of = [&](int k) { return (int)(item_of(k) % a.n_cg); };
     struct Col { int sg, Ns, n_base; bool ok; };
     auto col_of = [&](int k) {
         const int cg0 = cg_of(k);
