@@ -50,7 +50,7 @@ DESC = {
 # (timed steps, warmup steps) of a configuration timed alone, and nested
 DEFAULTS = {"decode": (4000, 400), "tiny": (2000, 200), "prefill": (200, 20), "many": (1000, 100),
             "moe": (200, 20), "logits": (1000, 100)}
-NESTED_STEPS = {"tiny": (500, 50), "prefill": (200, 20), "many": (200, 20), "moe": (200, 20),
+NESTED_STEPS = {"tiny": (2000, 200), "prefill": (200, 20), "many": (200, 20), "moe": (200, 20),
                 "logits": (200, 20)}
 
 
