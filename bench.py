@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "fused", "relay", "grouped", "decode", "prefill",
                                                      "token"],
                    help="force a decode path (development runs; the headline uses auto)")
+    p.add_argument("--moe-reduce-k", action="store_true",
+                   help="fused-MoE: the w2 delta summed over the token's k pairs into [T][d_model]")
     p.add_argument("--moe-tokens", type=int, default=2048,
                    help="tokens of the fused-MoE workload (2048 by default)")
     p.add_argument("--shared-a", action="store_true",
@@ -113,12 +115,13 @@ def algorithmic_bytes(c, shared_a=False):
                 active_slots=len(slots))
 
 
-def moe_algorithmic_bytes(c):
+def moe_algorithmic_bytes(c, reduce_k=False):
     """Bytes the fused-MoE step must move for the realised routing: w13 reads
     the x rows of tokens with an adapter, the shared lora_a of their slots, the
     lora_b of every (slot, expert) pair used, and read-modify-writes their
     gate_up rows; w2 reads the h rows, lora_a of every (slot, expert) pair
-    used, the shared lora_b, and read-modify-writes the w2 output rows."""
+    used, the shared lora_b, and read-modify-writes the w2 output rows (one
+    per pair, or one per token when the delta is summed over the k pairs)."""
     el = 2
     act = [t for t in range(c.T) if 0 <= c.idx[t] < c.L and c.slot_rank[c.idx[t]] > 0]
     slots = sorted({int(c.idx[t]) for t in act})
@@ -129,7 +132,8 @@ def moe_algorithmic_bytes(c):
     w13 = (len(act) * c.K * el + 2 * sum(rk(s) for s in slots) * c.K * el
            + 2 * sum(rk(s) for s, _ in used) * c.I * el + n_pairs * 2 * c.I * el * 2)
     w2 = (n_pairs * c.I * el + sum(rk(s) for s, _ in used) * c.I * el
-          + sum(rk(s) for s in slots) * c.K * el + n_pairs * c.K * el * 2)
+          + sum(rk(s) for s in slots) * c.K * el
+          + (len(act) if reduce_k else n_pairs) * c.K * el * 2)
     flops = 2 * (2 * sum(rk(int(c.idx[t])) for t in act) * c.K
                  + sum(rk(s) for s, _ in pairs) * 2 * c.I
                  + sum(rk(s) for s, _ in pairs) * (c.I + c.K))
@@ -243,17 +247,26 @@ def linear_cpu_baseline(c, seconds):
                         c.T, seconds, "the same batch")
 
 
-def moe_cpu_baseline(c, seconds):
+def moe_cpu_baseline(c, seconds, reduce_k=False):
     import oracle
     oracle.build(force=False)
+    out_red = moe_reduced_out(c) if reduce_k else None
 
     def run(lo, hi):
         pr = slice(lo * c.k, hi * c.k)
         oracle.moe_lora_apply(0, c.gate_up0[pr], c.x[lo:hi], c.A13, c.B13, c.topk_ids[lo:hi],
                               None, c.idx[lo:hi], c.slot_rank, c.scale, c.E)
-        oracle.moe_lora_apply(1, c.out0[pr], c.h[pr], [c.A2], [c.B2], c.topk_ids[lo:hi],
-                              c.topk_w[lo:hi], c.idx[lo:hi], c.slot_rank, c.scale, c.E)
-    return oracle_rates(run, c.T, seconds, "the same batch, w13 and w2 per (token, k) pair")
+        oracle.moe_lora_apply(1, out_red[lo:hi] if reduce_k else c.out0[pr], c.h[pr], [c.A2], [c.B2],
+                              c.topk_ids[lo:hi], c.topk_w[lo:hi], c.idx[lo:hi], c.slot_rank, c.scale,
+                              c.E, reduce_k=reduce_k)
+    return oracle_rates(run, c.T, seconds, "the same batch, w13 per (token, k) pair and w2 " +
+                        ("summed over each token's pairs" if reduce_k else "per (token, k) pair"))
+
+
+def moe_reduced_out(c):
+    """The w2 output for the k-reduced form, [T][d_model]: the first pair row
+    of each token of the seeded per-pair output."""
+    return c.out0.reshape(c.T, c.k, -1)[:, 0, :].copy()
 
 
 # ---------------------------------------------------------------------------
@@ -562,12 +575,14 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
     import synth
     dev = torch.device("cuda:0")
     c = synth.config_moe(T=args.moe_tokens)
+    red = getattr(args, "moe_reduce_k", False)   # w2 delta summed over each token's pairs
     bf = torch.bfloat16
     to = lambda a, d=None: (torch.from_numpy(np.ascontiguousarray(a)).to(d) if d is not None
                             else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     base = dict(x=to(c.x, bf), h=to(c.h, bf), A13=[to(a, bf) for a in c.A13],
                 B13=[to(b, bf) for b in c.B13], A2=[to(c.A2, bf)], B2=[to(c.B2, bf)],
-                g=to(c.gate_up0, bf), o=to(c.out0, bf), ids=to(c.topk_ids), w=to(c.topk_w),
+                g=to(c.gate_up0, bf), o=to(moe_reduced_out(c) if red else c.out0, bf),
+                ids=to(c.topk_ids), w=to(c.topk_w),
                 idx=to(c.idx), rank=to(c.slot_rank), scale=to(c.scale))
     inst_bytes = sum((t.numel() * t.element_size()) for k, v in base.items()
                      for t in (v if isinstance(v, list) else [v]))
@@ -580,8 +595,8 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
     del base
     torch.cuda.synchronize()
     ready = aa.LORA_FLAG_SEGMENTS_READY
-    # whether a call of this size skips the alignment (the library's own rule)
-    small = aa.moe_lora_plan(c.T, c.k, c.R)
+    # whether the calls of this size skip the alignment (the library's own rule)
+    small = aa.moe_lora_plan(c.T, c.k, c.R) and aa.moe_lora_plan(c.T, c.k, c.R, red)
 
     def align(d):
         aa.moe_lora_align(d["ids"], d["idx"], d["rank"], c.E, c.L, c.R, 16, d["ws"])
@@ -592,7 +607,8 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
 
     def w2(d):
         aa.moe_lora_apply(aa.MOE_LORA_W2, d["o"], d["h"], d["A2"], d["B2"], d["ids"], d["w"],
-                          d["idx"], d["rank"], d["scale"], c.E, d["ws"], flags=0 if small else ready)
+                          d["idx"], d["rank"], d["scale"], c.E, d["ws"], reduce_k=red,
+                          flags=0 if small else ready)
 
     calls = (("w13", w13), ("w2", w2)) if small else (("align", align), ("w13", w13), ("w2", w2))
 
@@ -614,7 +630,7 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
     rot = Rotation(torch, insts)
     ms_per_step, wall = rot.time_steps(step, steps, warmup)
     per_call = {k: rot.median_us(fn, min_launches=200) for k, fn in calls}
-    ab = moe_algorithmic_bytes(c)
+    ab = moe_algorithmic_bytes(c, red)
     dom = max(("w13", "w2"), key=lambda k: per_call[k])
     achieved = ab[dom] / (per_call[dom] * 1e-6) / 1e9
     khash = kernel_hash()
@@ -622,6 +638,7 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
         "workload": (f"fused-MoE LoRA: {c.T} tokens, 64 experts top-8, d_model 4096, d_mlp 1536, "
                      "rank 16, 8 adapters, shared-outer; " +
                      ("w13 + w2 per (token, k), no alignment (few pairs)" if small else
+                      "align + w13 per (token, k) + w2 summed over each token's k pairs" if red else
                       "align + w13 + w2 per (token, k)")),
         "value": round(c.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
         "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup, "dtype": "bf16",
@@ -633,7 +650,7 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
         "roofline": {"bound": "hbm", "kernel": dom + " (shrink + expand launches)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic("moe", dom, khash),
+                     "traffic": None if red else load_traffic("moe", dom, khash),
                      "algorithmic_bytes": ab[dom], "kernel_us": round(per_call[dom], 3),
                      "copy_GBps": round(copy_gbps, 1),
                      "frac_of_copy": round(achieved / copy_gbps, 4)},
@@ -642,7 +659,7 @@ def moe_entry(args, steps, warmup, cpu_seconds, copy_gbps):
                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(ab["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
                  **_gemm_fields(ab["flops"] / (ms_per_step * 1e-3) / 1e12)},
-        "cpu_baseline": None if args.no_cpu_baseline else moe_cpu_baseline(c, cpu_seconds),
+        "cpu_baseline": None if args.no_cpu_baseline else moe_cpu_baseline(c, cpu_seconds, red),
         "wall_s": round(wall, 3),
     }
     del insts, rot
