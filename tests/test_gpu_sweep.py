@@ -8,7 +8,8 @@ slice or not) and runs lora_apply_packed on auto and on every path that takes
 the shape (the library's own lora_plan_packed decides which).  x, A, B are in
 {-1, 0, 1} and y0 is an integer, so every partial sum is exact and each path
 must equal the oracle exactly; the columns of y outside the slices and the
-canary bands around y stay untouched.  The fused-MoE half draws
+canary bands around y stay untouched; an fp32 part does the same on the
+paths that take fp32.  The fused-MoE half draws
 (T, top_k, E, K, I, rank, slots) with out-of-range experts, one lora_a / lora_b
 shared by the experts or not, the aligned path or the one without alignment,
 and the k-reduced w2."""
@@ -99,6 +100,53 @@ def test_linear_sweep_bit_exact(oracle_mod, case):
         assert canaries_intact(yfull)
         ran.append(aa.PATH_NAMES[taken])
     aa.lora_workspace_check(ws)                      # raises if a hand-over wait gave up
+    log(f"  paths {ran}")
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_fp32_sweep_bit_exact(oracle_mod, case):
+    """fp32 on the paths that take it (auto, DECODE, TOKEN): random shapes,
+    ranks in steps of 4, slots switched off, out-of-range slots and a column
+    offset, bit for bit against the oracle."""
+    rng = np.random.default_rng(9800 + case)
+    T = int(np.exp(rng.uniform(0.0, np.log(600.0))))
+    K = int(rng.choice([8, 64, 520, 1024, 4096]))
+    S = int(rng.integers(1, 4))
+    N = [int(rng.choice([4, 64, 252, 256, 1028, 4096])) for _ in range(S)]
+    R = int(rng.choice([4, 8, 12, 16, 32, 64]))
+    L = int(rng.choice([1, 3, 8, 40]))
+    c = synth.make_integer_linear(T, K, N, R, L, seed=9900 + case, dtype="f32",
+                                  p_none=float(rng.choice([0.0, 0.2])))
+    rank = c.slot_rank.copy()
+    rank[rng.random(L) < 0.2] = 0
+    idx = c.idx.copy()
+    idx[rng.random(T) < 0.05] = L + 1
+    for b in c.B:
+        for sl in range(L):
+            b[sl, :, rank[sl]:] = 0
+    ncol = int(sum(N))
+    off = int(rng.choice([0, 4, 12]))
+    y_host = rng.integers(-8, 9, size=(T, off + ncol + 4)).astype(np.float32)
+    ref = oracle_mod.lora_apply(y_host[:, off:off + ncol].copy(), c.x, c.A, c.B, idx, rank, c.scale)[0]
+    f32 = torch.float32
+    x = dev(c.x, f32)
+    Ad, Bd = [dev(a, f32) for a in c.A], [dev(b, f32) for b in c.B]
+    idx_d, rank_d, scale_d = dev(idx), dev(rank), dev(c.scale)
+    ws = aa.alloc_workspace(T, K, len(N), R, L)
+    log(f"case fp32 sweep {case}: T={T} K={K} N={N} R={R} L={L} off={off}")
+    ran = []
+    for path in (aa.LORA_PATH_AUTO, aa.LORA_PATH_DECODE, aa.LORA_PATH_TOKEN):
+        yfull, y = guarded(y_host, f32)
+        taken = aa.lora_plan_packed(y, x, Ad, Bd, idx_d, rank_d, scale_d, ws, y_col_offset=off,
+                                    path=path)
+        aa.lora_apply_packed(y, x, Ad, Bd, idx_d, rank_d, scale_d, ws, y_col_offset=off, path=path)
+        got = host_f32(y)
+        assert np.array_equal(got[:, off:off + ncol], ref), \
+            f"path {aa.PATH_NAMES[taken]}: max diff {np.max(np.abs(got[:, off:off + ncol] - ref))}"
+        assert np.array_equal(got[:, :off], y_host[:, :off])
+        assert np.array_equal(got[:, off + ncol:], y_host[:, off + ncol:])
+        assert canaries_intact(yfull)
+        ran.append(aa.PATH_NAMES[taken])
     log(f"  paths {ran}")
 
 
