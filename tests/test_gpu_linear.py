@@ -614,6 +614,30 @@ def test_mla_two_partition_lora_b_tolerance(oracle_mod):
     assert canaries_intact(d.yfull)
 
 
+@pytest.mark.parametrize("N", [[64, 128, 8, 256, 32, 1024, 16, 512],          # rows of 8
+                               [12, 36, 4, 1028, 64, 20, 8, 300]])             # ragged widths
+def test_max_slices_bit_exact(oracle_mod, N):
+    """LORA_MAX_SLICES (8) slices of different widths, integer vectors, on auto
+    and every path lora_plan_packed accepts for the shape, bit for bit."""
+    c = synth.make_integer_linear(300, 1024, N, 16, 5, seed=71, dtype="bf16")
+    ref = oracle_y(oracle_mod, c)
+    ran = []
+    for path in (aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK):
+        d = LinearOnDevice(c)
+        try:
+            taken = aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+        except aa.LoraError as e:
+            assert path != aa.LORA_PATH_AUTO and e.code == aa.LORA_E_PATH, str(e)
+            continue
+        log(f"case max slices N={N} path={aa.PATH_NAMES[taken]}")
+        d.apply(path)
+        y = d.y_host()
+        assert np.array_equal(y, ref), f"path {aa.PATH_NAMES[taken]}: {np.max(np.abs(y - ref))}"
+        assert canaries_intact(d.yfull)
+        ran.append(aa.PATH_NAMES[taken])
+    assert len(ran) >= 3, ran
+
+
 def test_zero_tokens_noop():
     c = synth.config_decode(T=8)
     d = LinearOnDevice(c)
