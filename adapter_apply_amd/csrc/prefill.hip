@@ -290,9 +290,10 @@ __device__ __forceinline__ ExpItem exp_item(const PreExpandArgs &a, int p0, int 
     return it;
 }
 
-// 8 buffer values (ranks jj .. jj+7) of an item for slice sg, as two float4;
-// ranks at or past r are zeroed (an expand-only caller may leave them arbitrary).
-__device__ __forceinline__ void buf_vals(const PreExpandArgs &a, int sg, int item, int jj, int r,
+// 8 buffer values (ranks jj .. jj+7) of an item for slice sg, as two float4
+// (the caller zeroes ranks at or past the slot's rank when it packs them: an
+// expand-only caller may leave them arbitrary).
+__device__ __forceinline__ void buf_vals(const PreExpandArgs &a, int sg, int item, int jj,
                                          float4 &v0, float4 &v1) {
     if (a.gm.ksum) {
         v0 = make_float4(0, 0, 0, 0);
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_expand(PreExpandArgs a) {
                 uint4 f = make_uint4(0, 0, 0, 0);
                 if (ks < nk) {
                     float4 v0, v1;
-                    buf_vals(a, sg, it[tb].item, jj, r, v0, v1);
+                    buf_vals(a, sg, it[tb].item, jj, v0, v1);
                     f = pack_frag(v0, v1, jj, r);
                 }
                 bfrag[tb][ks] = f;
