@@ -35,7 +35,8 @@ def run_pair(c, path):
 
 
 @pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, aa.LORA_PATH_RELAY, aa.LORA_PATH_GROUPED,
-                                  aa.LORA_PATH_PREFILL, aa.LORA_PATH_DECODE])
+                                  aa.LORA_PATH_PREFILL, aa.LORA_PATH_DECODE, aa.LORA_PATH_FUSED,
+                                  aa.LORA_PATH_TOKEN])
 def test_noalloc_equals_workspace_call(oracle_mod, path):
     big = synth.config_decode()                  # 256 tokens, QKV 4096/1024/1024
     small = synth.config_decode(seed=77, T=40)   # then a smaller batch on the same array
