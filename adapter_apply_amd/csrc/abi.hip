@@ -15,9 +15,6 @@ constexpr int32_t kPrefillMinPerSlot = 64;
 // Decode: the expand adds the shrink's K-chunk partials itself (one launch
 // fewer) while a tile's partials stay small; beyond that a reduce kernel runs.
 constexpr int32_t kFoldMaxChunkRank = 512;   // n_kchunks * R
-// Auto: wide outputs take the single-launch K-split kernel up to this many
-// output elements (256 tokens of a 128256-column vocabulary).
-constexpr int64_t kRelayWideMaxElems = 256LL * 128256;
 // Auto's K-split single launch for narrow outputs: expected 32-token groups at
 // most this many, or at least this many tokens per slot that draws any.
 constexpr double kRelayFewGroups = 12.0;
@@ -233,8 +230,8 @@ namespace aa {
 // Every check of lora_apply_packed and its choice of path, on the host; it
 // enqueues nothing.  The auto rule, the first that holds:
 //   1. TOKEN while its work-groups' recomputed shrinks read little lora_a;
-//   2. RELAY for relay batches with a workspace of lora_workspace_size()
-//      bytes, narrow outputs or T x width up to 256 x 128256;
+//   2. RELAY with a workspace of lora_workspace_size() bytes: for relay
+//      batches of narrow outputs, and for every wide output it takes;
 //   3. GROUPED at rank 16 for narrow outputs up to 4096 tokens and 128 slots;
 //   4. PREFILL when slots carry long token runs (choose_path);
 //   5. FUSED where its shapes allow, the output is narrow and L <= 64;
@@ -283,14 +280,14 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
         if (!al(y, 16) || !al(x, 16)) return LORA_E_ALIGN;
         return LORA_OK;   // no workspace needed
     }
-    // Auto takes the single-launch kernel with the K-split shrink for decode
-    // batches when the workspace is there: for narrow outputs, and for wide
-    // ones (an lm_head's vocabulary) up to a bound on T times the width, where
-    // its 16-token expand items beat the tile kernels.
-    // Without a workspace narrow outputs take the other single-launch kernel;
-    // past these, wide outputs go to the tile kernels (the single-launch
-    // kernel without a workspace recomputes a group's shrink for every
-    // 1024-column chunk).
+    // Auto takes the single-launch kernel with the K-split shrink when the
+    // workspace is there: for decode batches of narrow outputs, and for every
+    // wide output (an lm_head's vocabulary) it takes, where its 16-token
+    // expand items of up to four column chunks beat the tile kernels.
+    // Without a workspace narrow outputs take the other single-launch kernel,
+    // and wide outputs go to the tile kernels (the single-launch kernel
+    // without a workspace recomputes a group's shrink for every 1024-column
+    // chunk).
     const bool narrow = ntot <= kAutoMaxDecodeCols;
     const bool relay_ok = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype);
     if (path == LORA_PATH_RELAY && !relay_ok) return LORA_E_PATH;
@@ -309,12 +306,13 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     const bool relay_batch = used + T / (double)kRelayGroup <= kRelayFewGroups ||
                              T >= kRelayMinPerSlot * used;
     const bool relay_ws = ws && ws_bytes >= ws_layout(T, K, S, R, L).end;
-    // Wide outputs (an lm_head's vocabulary): while its expand grid (groups x
-    // 512-column chunks) stays within what 256 tokens of a 128256-column
-    // vocabulary make (there 44 against 52 us for the tile kernels; 512 tokens
-    // of 32000 columns 28.1 against 35.6; 384 of 128256 columns 70.8 against
-    // 61.5, 256 over 64 slots 208 against 154 us for the tile kernels).
-    const bool relay_wide = !narrow && relay_batch && (int64_t)T * ntot <= kRelayWideMaxElems;
+    // Wide outputs (an lm_head's vocabulary) take it wherever it runs: measured
+    // against the tile kernels on vocabularies of 32000 to 256000 columns, 64
+    // to 1024 tokens over 8 to 64 slots, ranks 16 and 32, it is the faster
+    // (128256 columns: 256 tokens 36.0 against 50.3 us, 1024 tokens 104.8
+    // against 117.6, 256 tokens over 64 slots 118.4 against 153.0; 1024
+    // tokens of 32000 columns over 64 slots 52.8 against 64.4).
+    const bool relay_wide = !narrow;
     const bool relay_auto = relay_ok && relay_ws && ((narrow && relay_batch) || relay_wide);
     // Decode-sized batches of long slot runs take it too, before the tile
     // kernels (8 slots, T 512: 12.9 against 27.1 us; T 1024: 24.2 against 30.3).

@@ -45,15 +45,19 @@
 //     ([vLLM] MergedQKVParallelLinearWithLoRA copies one checkpoint lora_a
 //     into every slice) only slice 0's shrink items run, and the expand items
 //     of every slice add slice 0's partials.
-//   expand (g, chunk, b): tokens 8b .. 8b + 7 of group g (16b .. 16b + 15 for
-//     outputs wider than 16384 columns), 512 output columns of one slice.
-//     lora_b rows and y rows are loaded before the wait; after it the K-chunk
-//     partials are summed in a fixed order into a bf16 buffer, and
-//     v_mfma_f32_16x16x16_bf16 forms D[n][t] = B[n][:] . buf[t][:]; y is read
-//     and written 16 bytes per lane along rows (non-temporal).
+//   expand (g, item, b): tokens 8b .. 8b + 7 of group g (16b .. 16b + 15 for
+//     outputs wider than 16384 columns), CPI consecutive 512-column chunks
+//     of one slice (one chunk; up to four on wide outputs, as many as keep
+//     about four expand work-groups per CU).  The first chunk's lora_b rows,
+//     read straight into MFMA fragments, and its y rows are loaded before the
+//     wait; after it the K-chunk partials are summed in a fixed order into a
+//     bf16 buffer, and v_mfma_f32_16x16x16_bf16 (16x16x32 at rank 32) forms
+//     D[n][t] = B[n][:] . buf[t][:] chunk by chunk, the next chunk's loads in
+//     flight meanwhile; y is read and written 16 bytes per lane along rows
+//     (non-temporal).
 // XCD placement (block i runs on XCD i % 8): the slices of a (g, kc) share
 // one XCD (its x rows are read once from HBM), and the token blocks of a
-// (g, chunk) share one XCD (its lora_b rows are read once).
+// (g, item) share one XCD (its lora_b rows are read once).
 #include "discover.hpp"
 
 namespace aa {
@@ -63,13 +67,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;     // 4
 constexpr int kG = kRelayGroup;              // tokens per group (32)
-constexpr int kMaxSubs = kG / 8;             // expand work-groups per (group, chunk), at most
+constexpr int kMaxSubs = kG / 8;             // expand work-groups per (group, item), at most
 constexpr int kKc = kRelayKc;                // K columns per shrink item (256)
 constexpr int kCols = kRelayCols;            // output columns per expand item (512)
 constexpr int kColsW = kCols / kWaves;       // 128 per wave
 constexpr int kSpin = 1 << 20;
 constexpr uint32_t kReady = 0x7fc0deadu;   // stored word = fp32 bits ^ kReady (never 0)
 constexpr int kLine = 64;                  // int32 per counter: one 256-byte line each
+constexpr int kRelayMaxCpi = 4;            // 512-column chunks per expand item, at most (1, 2 or 4)
+constexpr int kRelayMinItems = 1024;       // expand work-groups to keep (four per CU)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
@@ -81,7 +87,7 @@ struct RelayArgs {
     int64_t ldy;
     int32_t T, K, S, L, R;
     int32_t n_kc;        // K / kKc
-    int32_t n_chunks;    // 512-column chunks over all slices
+    int32_t n_items;     // expand items per (group, token block) over all slices
     int32_t max_groups;
     int32_t n_first;     // groups in the first part of the grid
     int32_t pstart[4];   // first block of: part 1 expand, part 2 shrink, part 2 expand, the end
@@ -91,7 +97,8 @@ struct RelayArgs {
     const int32_t *slot_rank;
     const float *scale;
     Slices sl;
-    int32_t chunk_start[kMaxSlices + 1];
+    int32_t chunk_start[kMaxSlices + 1];   // first 512-column chunk of each slice
+    int32_t item_start[kMaxSlices + 1];    // first expand item of each slice
     float *part;         // fp32 [S][n_kc][T][R]
     int32_t *sync;       // per (group, slice, token block) reader count, kLine int32 apart
     int32_t *err;        // error word: set when a wait gives up
@@ -110,11 +117,19 @@ struct RelaySlice {
     const uint16_t *a;
     const uint16_t *b;
     int64_t n, off;
-    int32_t sg, c0, c1;
+    int32_t sg, c0, c1, i0, i1;
 };
 
 __device__ __forceinline__ bf16x8_t frag8(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ short4_t frag4(const uint2 &u) { return __builtin_bit_cast(short4_t, u); }
+
+// D += A . B over one 16-rank block (4 ranks per lane) or two (8 per lane)
+__device__ __forceinline__ floatx4_t mfma_rank(const uint2 &a, const uint2 &b, floatx4_t acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(a), frag4(b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_t mfma_rank(const uint4 &a, const uint4 &b, floatx4_t acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag8(a), frag8(b), acc, 0, 0, 0);
+}
 
 // Byte offset of 16-byte unit u of row r in a staging area of 128-byte rows,
 // the unit XOR-swizzled with the row (fragment reads of 8 rows hit 8 bank groups).
@@ -137,6 +152,13 @@ __device__ __forceinline__ uint4 ldg_as1(const void *p) {
         reinterpret_cast<uintptr_t>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ldg_as1(const void *p, uint2 &out) {
+    const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(1))) u32x2_t *>(
+        reinterpret_cast<uintptr_t>(p));
+    out = make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void ldg_as1(const void *p, uint4 &out) { out = ldg_as1(p); }
 
 __device__ __forceinline__ void st_coherent(float *p, uint64_t v) {
     __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -156,23 +178,19 @@ struct RelaySmem {
     static constexpr int kStage = kWaves * RR * 128;
     static constexpr int kPart = kWaves * kG * (RP + 4) * 4;   // aliases the staging
     static constexpr int kProd = kStage > kPart ? kStage : kPart;
-    static constexpr int kBStage = kWaves * kColsW * RP * 2;   // expand: lora_b rows
     static constexpr int kDelta = kSubTok * (kCols + 4) * 4;   // expand: fp32 deltas
-    // the deltas get an LDS area of their own where that keeps the work-group
-    // under 40 KB (four per CU), else they alias the staging after a barrier
-    static constexpr bool kDeltaAliases = kBStage + kSubTok * (kCols + 4) * 4 > 40 * 1024;
-    static constexpr int kDeltaOff = kDeltaAliases ? 0 : kBStage;
-    static constexpr int kCons = kDeltaOff + kDelta > kBStage ? kDeltaOff + kDelta : kBStage;
-    static constexpr int kUnion = kProd > kCons ? kProd : kCons;
+    static constexpr int kUnion = kProd > kDelta ? kProd : kDelta;
     static constexpr int PP = kSubTok * RP / 2;                // partial pairs per K chunk
     static_assert(PP % kWave == 0 && PP <= kThreads, "pairs of a block fill whole waves");
 };
 
 // NRB: 16-rank blocks of R (1 or 2); MKC: bound on the K chunks (16 or 32);
 // SUB: tokens per expand item (8, or 16 for wide outputs, where fewer expand
-// work-groups re-read each lora_b block).  At rank 16 and K <= 4096 an
+// work-groups re-read each lora_b block); CPI: 512-column chunks per expand
+// item (several for wide outputs, so that the group discovery and the wait
+// for the partials are paid once for them).  At rank 16 and K <= 4096 an
 // occupancy bound keeps four work-groups per CU without spills.
-template <int NRB, int MKC, int SUB>
+template <int NRB, int MKC, int SUB, int CPI>
 __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_dec_relay(RelayArgs a) {
     constexpr int kSubTok = SUB;
     constexpr int kSubs = kG / SUB;
@@ -180,7 +198,8 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
     constexpr int RP = SM::RP, RR = SM::RR;
     constexpr int LPS = RR / 8;                    // load instructions per wave (8 rows x 128 B)
     constexpr int BROW = RP * 2;                   // bytes of one lora_b row
-    constexpr int BLD = kColsW * BROW / 1024;      // load instructions for a wave's lora_b rows
+    constexpr int kNB = kColsW / 16;               // 16-column MFMA blocks per wave
+    using BFrag = typename std::conditional<NRB == 1, uint2, uint4>::type;   // a lane's ranks of one row
     constexpr int PP = SM::PP;
     constexpr int TW = kSubTok / kWaves;             // y rows per wave
 
@@ -202,7 +221,7 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
     const bool shrink = b < a.pstart[0] || (second && b < a.pstart[2]);
     const int rel = b - (shrink ? (second ? a.pstart[1] : 0) : (second ? a.pstart[2] : a.pstart[0]));
     const int xcd = rel % 8, j = rel / 8;
-    int g, kc = 0, chunk = 0, sub = 0;
+    int g, kc = 0, item = 0, sub = 0;
     if (shrink) {
         const int u = (j / a.S_shrink) * 8 + xcd;
         g = g0 + u / a.n_kc;
@@ -210,8 +229,8 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
     } else {
         const int v = (j / kSubs) * 8 + xcd;
         sub = j % kSubs;
-        g = g0 + v / a.n_chunks;
-        chunk = v % a.n_chunks;
+        g = g0 + v / a.n_items;
+        item = v % a.n_items;
     }
     if (g >= gn) g = -1;
     {
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
                 int sg = 0;
                 if (shrink) sg = j % a.S_shrink;
                 else
-                    while (sg + 1 < a.S && chunk >= a.chunk_start[sg + 1]) ++sg;
+                    while (sg + 1 < a.S && item >= a.item_start[sg + 1]) ++sg;
                 s_sl.sg = sg;
                 s_sl.a = static_cast<const uint16_t *>(a.sl.a[sg]);
                 s_sl.b = static_cast<const uint16_t *>(a.sl.b[sg]);
@@ -232,6 +251,8 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
                 s_sl.off = a.sl.off[sg];
                 s_sl.c0 = a.chunk_start[sg];
                 s_sl.c1 = a.chunk_start[sg + 1];
+                s_sl.i0 = a.item_start[sg];
+                s_sl.i1 = a.item_start[sg + 1];
             }
         }
         if (w == 0) {
@@ -314,51 +335,56 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
         return;
     }
 
-    // ---- expand item (g, chunk, sub) ----------------------------------------
+    // ---- expand item (g, item, sub) -----------------------------------------
     const int t0 = sub * kSubTok;
     if (t0 >= ntok) return;
     const int ct = min(kSubTok, ntok - t0);
     const int Ns = (int)s_sl.n;
-    const int n_base = (chunk - s_sl.c0) * kCols;
-    // readers of a block of partials: one per chunk of the slice, or of every
+    // the item's chunks: cfirst .. cfirst + nc - 1 of its slice
+    const int cfirst = s_sl.c0 + (item - s_sl.i0) * CPI;
+    const int nc = min(CPI, s_sl.c1 - cfirst);
+    const int n_base = (cfirst - s_sl.c0) * kCols;
+    // readers of a block of partials: one per item of the slice, or of every
     // slice when they share the shrink
-    const int n_readers = a.S_shrink == 1 && a.S > 1 ? a.n_chunks : s_sl.c1 - s_sl.c0;
+    const int n_readers = a.S_shrink == 1 && a.S > 1 ? a.n_items : s_sl.i1 - s_sl.i0;
     const int sp = a.S_shrink == 1 ? 0 : sg;   // the slice whose partials this item adds
     const float sc = s_scale[s];
 
-    // loads that do not depend on the shrink: lora_b rows of the wave's 128
-    // columns (one contiguous block) and the y rows of tokens TW w .. TW w + TW - 1
+    // lora_b in MFMA fragment order, straight from memory: for column block
+    // nb the lane reads row 16 nb + row of the wave's 128 columns, ranks
+    // 4 quad .. 4 quad + 3 (8 bytes; at rank 32, 8 quad .. 8 quad + 7), so one
+    // wave instruction reads 16 whole rows.  The buffer fragment below takes
+    // the same ranks of its token.
     const char *bblk = reinterpret_cast<const char *>(uniform_ptr(s_sl.b) + (int64_t)s * Ns * a.R);
-    uint4 bq[BLD];
+    const auto load_b = [&](BFrag(&bq)[kNB], int nb0) {
 #pragma unroll
-    for (int i = 0; i < BLD; ++i) {
-        const int byte = 1024 * i + 16 * lane;
-        const int nr = min(n_base + w * kColsW + byte / BROW, Ns - 1);
-        bq[i] = ldg_as1(bblk + (int64_t)nr * BROW + byte % BROW);
-    }
+        for (int nb = 0; nb < kNB; ++nb) {
+            const int nr = min(nb0 + w * kColsW + 16 * nb + row, Ns - 1);
+            ldg_as1(bblk + (int64_t)nr * BROW + (int)sizeof(BFrag) * quad, bq[nb]);
+        }
+    };
+    // y rows of tokens TW w .. TW w + TW - 1, 8 columns per lane
     uint16_t *yrow[TW];
-    uint4 yv[TW];
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
         const int tk = TW * w + i;
         yrow[i] = a.y + (int64_t)d.tok[t0 + (tk < ct ? tk : 0)] * a.ldy + s_sl.off;
-        yv[i] = ldg_nt(yrow[i] + min(n_base + 8 * lane, Ns - 8));
     }
+    const auto load_y = [&](uint4(&yv)[TW], int nb0) {
+#pragma unroll
+        for (int i = 0; i < TW; ++i) yv[i] = ldg_nt(yrow[i] + min(nb0 + 8 * lane, Ns - 8));
+    };
+    // the first chunk's loads do not depend on the shrink: issued before the wait
+    BFrag bq[CPI][kNB];
+    uint4 yv[CPI][TW];
+    load_b(bq[0], n_base);
+    load_y(yv[0], n_base);
 
     int32_t *readers = a.sync + kLine * ((g * a.S + sp) * kSubs + sub);
     const float *blk = a.part + ((int64_t)sp * a.n_kc * a.T + pos0 + t0) * RP;   // chunk k: + k * T * RP
 
-    // Each wave stages its lora_b rows (fragment order below): the waves that
-    // do not poll at once, the polling ones when their data is in (their
-    // first poll must not wait for the lora_b loads).  The buffer's padding
-    // token rows are zeroed before the wait, so that after it only the buffer
-    // itself stands between the partials and the MFMA.
-    char *stage = s_union + w * (kColsW * BROW);
-    const auto stage_b = [&]() {
-#pragma unroll
-        for (int i = 0; i < BLD; ++i) *reinterpret_cast<uint4 *>(stage + 1024 * i + 16 * lane) = bq[i];
-    };
-    stage_b();
+    // The buffer's padding token rows are zeroed before the wait, so that
+    // after it only the buffer itself stands between the partials and the MFMA.
     for (int i = tid; i < (16 - kSubTok) * RP; i += kThreads)
         s_buf[kSubTok + i / RP][i % RP] = 0;
 
@@ -407,52 +433,54 @@ __global__ __launch_bounds__(kThreads, (NRB == 1 && MKC == 16) ? 4 : 1) void k_d
     int nread = -1;
     if (PP == kWave && tid == 0)
         nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();   // the buffer is complete, the lora_b rows are staged
+    lds_barrier();   // the buffer is complete
     if (PP > kWave && tid == 0)
         nread = __hip_atomic_fetch_add(readers, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // D[n][t] = B[n][:] . buf[t][:]  (MFMA 16x16x16; tokens past the block are zero)
-    uint2 bfr[NRB];
+    // D[n][t] = B[n][:] . buf[t][:] per chunk (MFMA; tokens past the block are
+    // zero).  Chunk c + 1's lora_b and y rows are loaded while chunk c is
+    // multiplied and written; items with fewer than CPI chunks repeat their
+    // last chunk's loads and skip its stores.
+    const BFrag bfr = *reinterpret_cast<const BFrag *>(&s_buf[row][(int)sizeof(BFrag) / 2 * quad]);
+    float *s_delta = reinterpret_cast<float *>(s_union);
 #pragma unroll
-    for (int ks = 0; ks < NRB; ++ks) bfr[ks] = *reinterpret_cast<const uint2 *>(&s_buf[row][16 * ks + 4 * quad]);
-    floatx4_t out[kColsW / 16];
+    for (int c = 0; c < CPI; ++c) {
+        const int nb0 = n_base + min(c, nc - 1) * kCols;
+        floatx4_t out[kNB];
 #pragma unroll
-    for (int nb = 0; nb < kColsW / 16; ++nb) {
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NRB; ++ks) {
-            const uint2 af = *reinterpret_cast<const uint2 *>(stage + (16 * nb + row) * BROW + 32 * ks + 8 * quad);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(frag4(af), frag4(bfr[ks]), acc, 0, 0, 0);
+        for (int nb = 0; nb < kNB; ++nb) out[nb] = mfma_rank(bq[c][nb], bfr, floatx4_t{0.f, 0.f, 0.f, 0.f});
+        if (c + 1 < CPI) {
+            const int nb1 = n_base + min(c + 1, nc - 1) * kCols;
+            load_b(bq[c + 1], nb1);
+            load_y(yv[c + 1], nb1);
         }
-        out[nb] = acc;
-    }
-    if (SM::kDeltaAliases) lds_barrier();   // every wave is done with the staging
-    float *s_delta = reinterpret_cast<float *>(s_union + SM::kDeltaOff);
-    // lane: token `row`, columns 128 w + 16 nb + 4 quad .. + 3 of the chunk
-    if (row < kSubTok) {
+        if (c > 0) lds_barrier();   // every wave has read the previous chunk's deltas
+        // lane: token `row`, columns 128 w + 16 nb + 4 quad .. + 3 of the chunk
+        if (row < kSubTok) {
 #pragma unroll
-        for (int nb = 0; nb < kColsW / 16; ++nb)
-            *reinterpret_cast<float4 *>(s_delta + row * (kCols + 4) + w * kColsW + 16 * nb + 4 * quad) =
-                make_float4(sc * out[nb][0], sc * out[nb][1], sc * out[nb][2], sc * out[nb][3]);
-    }
-    // the count is needed before the y stores: a wait on it after them would
-    // also wait for the stores (vmcnt counts both)
-    if (tid == 0) s_last[0] = nread == n_readers - 1;
-    lds_barrier();
+            for (int nb = 0; nb < kNB; ++nb)
+                *reinterpret_cast<float4 *>(s_delta + row * (kCols + 4) + w * kColsW + 16 * nb + 4 * quad) =
+                    make_float4(sc * out[nb][0], sc * out[nb][1], sc * out[nb][2], sc * out[nb][3]);
+        }
+        // the count is needed before the y stores: a wait on it after them would
+        // also wait for the stores (vmcnt counts both)
+        if (c == 0 && tid == 0) s_last[0] = nread == n_readers - 1;
+        lds_barrier();
 #pragma unroll
-    for (int i = 0; i < TW; ++i) {
-        const int tk = TW * w + i;
-        const int cl = 8 * lane;
-        if (tk < ct && n_base + cl < Ns) {
-            const float4 d0 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl);
-            const float4 d1 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl + 4);
-            const uint4 y0 = yv[i];
-            uint4 o;
-            o.x = pack_bf16x2(bf16_lo(y0.x) + d0.x, bf16_hi(y0.x) + d0.y);
-            o.y = pack_bf16x2(bf16_lo(y0.y) + d0.z, bf16_hi(y0.y) + d0.w);
-            o.z = pack_bf16x2(bf16_lo(y0.z) + d1.x, bf16_hi(y0.z) + d1.y);
-            o.w = pack_bf16x2(bf16_lo(y0.w) + d1.z, bf16_hi(y0.w) + d1.w);
-            stg_nt(yrow[i] + n_base + cl, o);
+        for (int i = 0; i < TW; ++i) {
+            const int tk = TW * w + i;
+            const int cl = 8 * lane;
+            if (c < nc && tk < ct && nb0 + cl < Ns) {
+                const float4 d0 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl);
+                const float4 d1 = *reinterpret_cast<const float4 *>(s_delta + tk * (kCols + 4) + cl + 4);
+                const uint4 y0 = yv[c][i];
+                uint4 o;
+                o.x = pack_bf16x2(bf16_lo(y0.x) + d0.x, bf16_hi(y0.x) + d0.y);
+                o.y = pack_bf16x2(bf16_lo(y0.y) + d0.z, bf16_hi(y0.y) + d0.w);
+                o.z = pack_bf16x2(bf16_lo(y0.z) + d1.x, bf16_hi(y0.z) + d1.y);
+                o.w = pack_bf16x2(bf16_lo(y0.w) + d1.z, bf16_hi(y0.w) + d1.w);
+                stg_nt(yrow[i] + nb0 + cl, o);
+            }
         }
     }
     // the last reader of the block writes it back to zero for the next call
@@ -486,13 +514,6 @@ hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, in
     a.T = T; a.K = K; a.S = S; a.L = L; a.R = R;
     a.idx = idx; a.slot_rank = slot_rank; a.scale = scale; a.sl = sl;
     a.part = part; a.sync = sync; a.err = err; a.give_up = give_up ? 1 : 0;
-    int c = 0;
-    for (int s = 0; s < S; ++s) {
-        a.chunk_start[s] = c;
-        c += (int)((sl.n[s] + kCols - 1) / kCols);
-    }
-    for (int s = S; s <= kMaxSlices; ++s) a.chunk_start[s] = c;
-    a.n_chunks = c;
     a.n_kc = K / kKc;
     a.max_groups = relay_max_groups(T, L);
     // one lora_a for every slice (the same pointer): one shrink for all
@@ -513,22 +534,51 @@ hipError_t launch_dec_relay(void *y, int64_t ldy, const void *x, int64_t ldx, in
     for (int s = 0; s < S; ++s) ntot += sl.n[s];
     const bool wide = ntot > kAutoMaxDecodeCols;
     const int subs = wide ? kG / 16 : kG / 8;
+    int n_chunks = 0;
+    for (int s = 0; s < S; ++s) n_chunks += (int)((sl.n[s] + kCols - 1) / kCols);
+    // chunks per expand item: as many as keep the expected expand items at
+    // four work-groups per CU or more
+    int cpi = 1;
+    if (wide)
+        while (cpi < kRelayMaxCpi && a.n_first * ((n_chunks + 2 * cpi - 1) / (2 * cpi)) * subs >= kRelayMinItems)
+            cpi *= 2;
+    int c = 0, it = 0;
+    for (int s = 0; s < S; ++s) {
+        a.chunk_start[s] = c;
+        a.item_start[s] = it;
+        const int ch = (int)((sl.n[s] + kCols - 1) / kCols);
+        c += ch;
+        it += (ch + cpi - 1) / cpi;
+    }
+    for (int s = S; s <= kMaxSlices; ++s) {
+        a.chunk_start[s] = c;
+        a.item_start[s] = it;
+    }
+    a.n_items = it;
     const auto sblocks = [&](int groups) { return 8 * ((groups * a.n_kc + 7) / 8 * a.S_shrink); };
-    const auto eblocks = [&](int groups) { return 8 * ((groups * c + 7) / 8 * subs); };
+    const auto eblocks = [&](int groups) { return 8 * ((groups * it + 7) / 8 * subs); };
     a.pstart[0] = sblocks(a.n_first);
     a.pstart[1] = a.pstart[0] + eblocks(a.n_first);
     a.pstart[2] = a.pstart[1] + sblocks(a.max_groups - a.n_first);
     a.pstart[3] = a.pstart[2] + eblocks(a.max_groups - a.n_first);
     dim3 grid((unsigned)a.pstart[3]);
     const bool few = a.n_kc <= 16;
-#define AA_RELAY(NRB, MKC, SUB) hipLaunchKernelGGL((k_dec_relay<NRB, MKC, SUB>), grid, dim3(kThreads), 0, st, a)
+#define AA_RELAY(NRB, MKC, SUB, CPI) hipLaunchKernelGGL((k_dec_relay<NRB, MKC, SUB, CPI>), grid, dim3(kThreads), 0, st, a)
+#define AA_RELAY_SUB(NRB, MKC)                                                       \
+    do {                                                                             \
+        if (!wide) AA_RELAY(NRB, MKC, 8, 1);                                         \
+        else if (cpi == 1) AA_RELAY(NRB, MKC, 16, 1);                                \
+        else if (cpi == 2) AA_RELAY(NRB, MKC, 16, 2);                                \
+        else AA_RELAY(NRB, MKC, 16, 4);                                              \
+    } while (0)
     if (R == 16) {
-        if (few) { if (wide) AA_RELAY(1, 16, 16); else AA_RELAY(1, 16, 8); }
-        else { if (wide) AA_RELAY(1, kRelayMaxKc, 16); else AA_RELAY(1, kRelayMaxKc, 8); }
+        if (few) AA_RELAY_SUB(1, 16);
+        else AA_RELAY_SUB(1, kRelayMaxKc);
     } else {
-        if (few) { if (wide) AA_RELAY(2, 16, 16); else AA_RELAY(2, 16, 8); }
-        else { if (wide) AA_RELAY(2, kRelayMaxKc, 16); else AA_RELAY(2, kRelayMaxKc, 8); }
+        if (few) AA_RELAY_SUB(2, 16);
+        else AA_RELAY_SUB(2, kRelayMaxKc);
     }
+#undef AA_RELAY_SUB
 #undef AA_RELAY
     return hipGetLastError();
 }

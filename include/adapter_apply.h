@@ -87,8 +87,8 @@
  *              | ceil(W / 1024) * ceil(R / 16) <= 4,              | TOKEN   |
  *              |   K*R*e <= 1 MB, W*K*R*e <= 72 MB (bf16) or      |         |
  *              |   512 MB (fp32)                                  |         |
- *              | RELAY's shapes, ws of lora_workspace_size(), a   | RELAY   |
- *              |   relay batch, narrow or T * sum(N) <= 256*128256|         |
+ *              | RELAY's shapes, ws of lora_workspace_size(), and | RELAY   |
+ *              |   not narrow, or narrow and a relay batch        |         |
  *              | GROUPED's shapes, R == 16, T <= 4096, L <= 128,  | GROUPED |
  *              |   narrow                                         |         |
  *              | T >= 512, T / min(T, L) >= 64, bf16, R % 16 == 0 | PREFILL |

@@ -364,11 +364,14 @@ def _ws_size(T, K, S, R, L):
      aa.LORA_PATH_PREFILL),
     # rank 64 with few slots and a short batch: the grouped kernels
     (dict(T=64, R=64), aa.LORA_PATH_GROUPED),
-    # lm_head vocabulary at 256 tokens: single launch; at 512 tokens: tile kernels
+    # an lm_head vocabulary: the K-split single launch wherever it runs (up to
+    # 1024 tokens and 64 slots, with its workspace); past that the tile kernels
     (dict(S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
-    (dict(T=512, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
-    (dict(T=384, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
-    (dict(T=256, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    (dict(T=512, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
+    (dict(T=384, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
+    (dict(T=1024, L=64, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_RELAY),
+    (dict(T=1025, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
+    (dict(T=256, L=65, S=1, N=(C.c_int64 * 1)(128256), ldy=128256), aa.LORA_PATH_PREFILL),
     # a 32000-column vocabulary: the single launch up to 1024 tokens
     (dict(T=1024, L=16, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_RELAY),
     # fp32: the VALU path only
