@@ -242,7 +242,8 @@ def test_logits_vocab_32000_every_path(oracle_mod):
 
 def test_logits_vocab_128256_auto(oracle_mod):
     """The lm_head workload at its measured size (vocabulary 128256) on the
-    auto path, which takes the tile kernels for outputs this wide."""
+    auto path, which takes the K-split single launch (expand items of four
+    512-column chunks) for outputs this wide."""
     c = synth.config_logits()
     log("case logits vocab=128256 auto")
     d = LinearOnDevice(c)
@@ -636,6 +637,42 @@ def test_max_slices_bit_exact(oracle_mod, N):
         assert canaries_intact(d.yfull)
         ran.append(aa.PATH_NAMES[taken])
     assert len(ran) >= 3, ran
+
+
+@pytest.mark.parametrize("seed,T,K,N,R,L,shared", [
+    # two chunks per expand item: 36 expected groups x 28 items x 2 token blocks
+    (81, 1024, 1024, [14336, 14336], 16, 8, False),
+    (81, 1024, 1024, [14336, 14336], 16, 8, True),
+    # four chunks per item over three slices of 79, 48 and 17 chunks: each
+    # slice's last item is short, the last chunk of the third holds 8 columns
+    (82, 512, 1024, [40000, 24576, 8200], 16, 8, False),
+    (82, 512, 1024, [40000, 24576, 8200], 16, 8, True),
+    (83, 512, 1024, [40000, 24576, 8200], 32, 8, False),
+    (83, 512, 1024, [40000, 24576, 8200], 32, 8, True),
+    # vocabularies: rank 32 at 64 tokens, and K = 8192 (32 K chunks)
+    (84, 64, 1024, [128256], 32, 8, False),
+    (85, 256, 8192, [128256], 16, 8, False),
+])
+def test_relay_wide_items_bit_exact(oracle_mod, seed, T, K, N, R, L, shared):
+    """Wide outputs on the K-split single launch, whose expand work-groups walk
+    up to four consecutive column chunks of one slice: integer vectors bit
+    for bit on RELAY and on auto (which takes it), with one lora_a for every
+    slice too (every item of every slice then reads slice 0's partials); the
+    workspace is all zero after each call."""
+    c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
+    if shared:
+        c = shared_a_case(c)
+    ref = oracle_y(oracle_mod, c)
+    for path in (aa.LORA_PATH_AUTO, RLY):
+        d = on_device_shared_a(c) if shared else LinearOnDevice(c)
+        taken = aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+        log(f"case relay wide T={T} K={K} N={N} R={R} shared={shared} path={aa.PATH_NAMES[path]}")
+        assert taken == RLY, aa.PATH_NAMES[taken]
+        d.apply(path)
+        y = d.y_host()
+        assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
+        assert canaries_intact(d.yfull)
+        assert int(torch.count_nonzero(d.ws)) == 0
 
 
 def test_zero_tokens_noop():
