@@ -79,7 +79,12 @@ __device__ __forceinline__ int swz(int n, int u, int U) {
 // blocks of 32 x 32 are shared by the 8 waves, each block's K steps split
 // over 4 / NCB waves (v_mfma_f32_32x32x16_bf16).  Writes fp32 buf[s][t][j]
 // for every column of the block that exists (zeros for j >= rank);
-// K % 8 == 0, any rank.
+// K % 8 == 0, any rank.  With one column block (S * R <= 32) a tile's x rows
+// are read by one work-group only and are loaded non-temporally, so that
+// they do not push the lora_a rows other tiles reuse out of the L2 (the
+// fused-MoE step 153 -> 147 us); with more blocks the work-groups of a tile
+// share its x rows through the L2 (non-temporal there: prefill shrink 37 ->
+// 45 us).
 constexpr int kShThreads = 512;
 constexpr int kShStageK = 64;          // K columns per stage (128 bytes of a row)
 constexpr int kShNpf = 4;              // stages in flight
@@ -145,7 +150,10 @@ __global__ __launch_bounds__(kShThreads) void k_pre_shrink_rows(PreShrinkArgs a)
 #pragma unroll
         for (int v = 0; v < NU; ++v) {
             const int k = min((sb + st) * kShStageK + uoff[v], a.K - 8);
-            ring[slot][v] = ldg<uint4>(rowp[v] + k);
+            // unit 0 of every thread is an x row (64 rows x 8 units = the
+            // first 512); with one column block its rows are read by this
+            // work-group only, and are streamed so as not to evict lora_a rows
+            ring[slot][v] = NCB == 1 && v == 0 ? ldg_nt(rowp[v] + k) : ldg<uint4>(rowp[v] + k);
         }
     };
     // The store takes the loaded value through a mask, not a select: a select
