@@ -43,7 +43,18 @@ def metadata_sets(c):
 @pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, aa.LORA_PATH_GROUPED, aa.LORA_PATH_PREFILL,
                                   aa.LORA_PATH_DECODE, aa.LORA_PATH_RELAY, aa.LORA_PATH_TOKEN])
 def test_graph_replays_read_current_metadata(oracle_mod, path):
-    c = synth.config_decode()
+    replay_check(oracle_mod, synth.config_decode(), path)
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, aa.LORA_PATH_RELAY, aa.LORA_PATH_PREFILL])
+def test_graph_replays_wide_output(oracle_mod, path):
+    """The lm_head shape (256 tokens, a 128256-column vocabulary): auto and
+    RELAY take the K-split single launch with expand items of four column
+    chunks, PREFILL the tile kernels."""
+    replay_check(oracle_mod, synth.config_logits(), path)
+
+
+def replay_check(oracle_mod, c, path):
     d = LinearOnDevice(c, guard=False)
     y0 = d.y.clone()
     # warm-up on a side stream, then capture one call
