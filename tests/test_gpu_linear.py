@@ -639,26 +639,31 @@ def test_max_slices_bit_exact(oracle_mod, N):
     assert len(ran) >= 3, ran
 
 
-@pytest.mark.parametrize("seed,T,K,N,R,L,shared", [
+@pytest.mark.parametrize("seed,T,K,N,R,L,shared,auto_path", [
     # two chunks per expand item: 36 expected groups x 28 items x 2 token blocks
-    (81, 1024, 1024, [14336, 14336], 16, 8, False),
-    (81, 1024, 1024, [14336, 14336], 16, 8, True),
+    (81, 1024, 1024, [14336, 14336], 16, 8, False, RLY),
+    (81, 1024, 1024, [14336, 14336], 16, 8, True, RLY),
     # four chunks per item over three slices of 79, 48 and 17 chunks: each
     # slice's last item is short, the last chunk of the third holds 8 columns
-    (82, 512, 1024, [40000, 24576, 8200], 16, 8, False),
-    (82, 512, 1024, [40000, 24576, 8200], 16, 8, True),
-    (83, 512, 1024, [40000, 24576, 8200], 32, 8, False),
-    (83, 512, 1024, [40000, 24576, 8200], 32, 8, True),
+    (82, 512, 1024, [40000, 24576, 8200], 16, 8, False, RLY),
+    (82, 512, 1024, [40000, 24576, 8200], 16, 8, True, RLY),
+    (83, 512, 1024, [40000, 24576, 8200], 32, 8, False, RLY),
+    (83, 512, 1024, [40000, 24576, 8200], 32, 8, True, RLY),
     # vocabularies: rank 32 at 64 tokens, and K = 8192 (32 K chunks)
-    (84, 64, 1024, [128256], 32, 8, False),
-    (85, 256, 8192, [128256], 16, 8, False),
+    (84, 64, 1024, [128256], 32, 8, False, RLY),
+    (85, 256, 8192, [128256], 16, 8, False, RLY),
+    # a few tokens (two chunks per item): a vocabulary at 4 tokens (auto:
+    # TOKEN, whose 2004 work-groups re-read 66 MB of lora_a), two wide slices
+    # at 12 tokens and rank 32
+    (86, 4, 1024, [128256], 16, 8, False, TOK),
+    (87, 12, 1024, [40000, 24576], 32, 8, False, RLY),
 ])
-def test_relay_wide_items_bit_exact(oracle_mod, seed, T, K, N, R, L, shared):
+def test_relay_wide_items_bit_exact(oracle_mod, seed, T, K, N, R, L, shared, auto_path):
     """Wide outputs on the K-split single launch, whose expand work-groups walk
     up to four consecutive column chunks of one slice: integer vectors bit
-    for bit on RELAY and on auto (which takes it), with one lora_a for every
-    slice too (every item of every slice then reads slice 0's partials); the
-    workspace is all zero after each call."""
+    for bit on RELAY and on auto (which takes it, or TOKEN for a few tokens),
+    with one lora_a for every slice too (every item of every slice then
+    reads slice 0's partials); the workspace is all zero after each call."""
     c = synth.make_integer_linear(T, K, N, R, L, seed=seed, dtype="bf16")
     if shared:
         c = shared_a_case(c)
@@ -667,7 +672,7 @@ def test_relay_wide_items_bit_exact(oracle_mod, seed, T, K, N, R, L, shared):
         d = on_device_shared_a(c) if shared else LinearOnDevice(c)
         taken = aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
         log(f"case relay wide T={T} K={K} N={N} R={R} shared={shared} path={aa.PATH_NAMES[path]}")
-        assert taken == RLY, aa.PATH_NAMES[taken]
+        assert taken == (auto_path if path == aa.LORA_PATH_AUTO else RLY), aa.PATH_NAMES[taken]
         d.apply(path)
         y = d.y_host()
         assert np.array_equal(y, ref), f"max diff {np.max(np.abs(y - ref))}"
