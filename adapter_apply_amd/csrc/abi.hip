@@ -252,21 +252,27 @@ int32_t packed_plan(const void *y, int64_t ldy, int64_t y_col_offset, const void
     int64_t ntot = 0;
     CHECK(check_n(N, S, ldy, y_col_offset, &ntot));
     // TOKEN (one work-group per token and 256 columns, each recomputing its
-    // token's shrink) while the lora_a bytes those shrinks read stay small:
-    // measured against RELAY on bf16 (QKV shape: 1 to 16 tokens 4.3-5.5
-    // against 6.0-6.6 us, 32 tokens 7.3 against 7.0; a 32000-column lm_head
-    // at 4 tokens 5.9 against 7.0, 16 tokens 12.0 against 7.9; rank-64
-    // gate_up at 1 token 11.9 against 21.5), and against DECODE's three
-    // launches on fp32 (QKV shape 80 tokens 28.3 against 31.1, 96 tokens 33.6
-    // against 31.4; hidden 64, 4096 tokens 8.0 against 22.0).
+    // token's shrink) while the lora_a bytes those shrinks read stay small.
+    // Measured with the inputs in HBM against RELAY on bf16: QKV shape 1 to
+    // 12 tokens 5.5-6.9 against 6.3-7.3 us, 16 tokens 8.1 against 7.4, 24
+    // tokens 9.4 against 7.5 (so narrow outputs that RELAY could take keep a
+    // lower bound); a 32000-column lm_head at 4 tokens 7.4 against 7.6, 8
+    // tokens 10.1 against 9.0; rank-64 gate_up at 1 token 11.9 against 21.5
+    // for the grouped kernels (RELAY takes ranks 16 and 32 only).  Against
+    // DECODE's three launches on fp32: QKV shape 80 tokens 28.3 against 31.1,
+    // 96 tokens 33.6 against 31.4; hidden 64, 4096 tokens 8.0 against 22.0.
     const int64_t tok_wgs = token_wgs(T, N, S);
     if (path == LORA_PATH_TOKEN && tok_wgs < 0) return LORA_E_PATH;
+    const bool relay_fits = can_relay(T, K, R, L, N, S, ldy, y_col_offset, dtype) && ws &&
+                            ws_bytes >= ws_layout(T, K, S, R, L).end;
+    const int64_t tok_max = dtype != LORA_DT_BF16             ? kTokenMaxBytesF32
+                            : ntot <= kAutoMaxDecodeCols && relay_fits ? kTokenMaxBytesNarrow
+                                                                    : kTokenMaxBytesBf16;
     // (token_fits bounds the work-groups to 4096 and each one's lora_a bytes
     // to 1 MB, so the product below stays far inside int64)
     const bool token = path == LORA_PATH_TOKEN ||
                        (path == LORA_PATH_AUTO && token_fits(tok_wgs, K, R, dtype) &&
-                        tok_wgs * K * R * (dtype == LORA_DT_BF16 ? 2 : 4) <=
-                            (dtype == LORA_DT_BF16 ? kTokenMaxBytesBf16 : kTokenMaxBytesF32));
+                        tok_wgs * K * R * (dtype == LORA_DT_BF16 ? 2 : 4) <= tok_max);
     int use_prefill = 0;
     if (!token) CHECK(choose_path(path, T, L, R, dtype, &use_prefill));
     if (token) {

@@ -405,6 +405,7 @@ constexpr int64_t kTokenRound = 1024;                 // work-groups resident at
 constexpr int64_t kTokenMaxRoundPasses = 4;
 constexpr int64_t kTokenMaxWgBytes = 1 << 20;         // lora_a bytes per work-group
 constexpr int64_t kTokenMaxBytesBf16 = 72LL << 20;    // auto: lora_a bytes of all work-groups
+constexpr int64_t kTokenMaxBytesNarrow = 44LL << 20;  // the same, bf16 outputs that RELAY could take
 constexpr int64_t kTokenMaxBytesF32 = 512LL << 20;
 hipError_t launch_dec_token(int dtype, void *y, int64_t ldy, const void *x, int64_t ldx, int32_t T,
                             int32_t K, const Slices &sl, int32_t S, int32_t L, int32_t R,

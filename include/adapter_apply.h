@@ -85,7 +85,8 @@
  *            row that holds wins):
  *              | condition                                        | path    |
  *              | ceil(W / 1024) * ceil(R / 16) <= 4,              | TOKEN   |
- *              |   K*R*e <= 1 MB, W*K*R*e <= 72 MB (bf16) or      |         |
+ *              |   K*R*e <= 1 MB, W*K*R*e <= 44 MB (bf16, narrow, |         |
+ *              |   RELAY's shapes and ws), 72 MB (other bf16) or  |         |
  *              |   512 MB (fp32)                                  |         |
  *              | RELAY's shapes, ws of lora_workspace_size(), and | RELAY   |
  *              |   not narrow, or narrow and a relay batch        |         |

@@ -333,12 +333,17 @@ def _ws_size(T, K, S, R, L):
     (dict(T=256, L=64), aa.LORA_PATH_FUSED),
     (dict(T=512, L=32), aa.LORA_PATH_FUSED),
     # a few tokens: one work-group per token and 256 columns while the lora_a
-    # its shrinks re-read stays within 72 MB (bf16): 8 tokens x 24 chunks x
-    # 128 KB = 25 MB; at 32 tokens (100 MB) the K-split single launch
+    # its shrinks re-read stays within 44 MB (bf16, narrow, RELAY possible):
+    # 12 tokens x 24 chunks x 128 KB = 36 MB; at 16 tokens (48 MB) the K-split
+    # single launch; without a workspace for it the bound is 72 MB
     (dict(T=8), aa.LORA_PATH_TOKEN),
     (dict(T=1), aa.LORA_PATH_TOKEN),
+    (dict(T=12), aa.LORA_PATH_TOKEN),
+    (dict(T=16), aa.LORA_PATH_RELAY),
     (dict(T=32), aa.LORA_PATH_RELAY),
     (dict(T=8, ws=None, wsb=0), aa.LORA_PATH_TOKEN),           # needs no workspace
+    (dict(T=16, ws=None, wsb=0), aa.LORA_PATH_TOKEN),
+    (dict(T=32, ws=None, wsb=0), aa.LORA_PATH_FUSED),
     # a 32000-column lm_head: 4 tokens (500 work-groups, 66 MB) TOKEN, 16 RELAY
     (dict(T=4, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_TOKEN),
     (dict(T=16, S=1, N=(C.c_int64 * 1)(32000), ldy=32000), aa.LORA_PATH_RELAY),
