@@ -616,8 +616,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_rows(PreExpandArgs a
 // lora_b row only the first 2 * ceil(r / 16) units (rounded up to a power of
 // two) are read, r the item's slot rank: slots of low rank in a tensor padded
 // to a high rank do not pay for the padding.
+// A load at a wave-uniform address of data no work-group of the launch
+// writes, through the scalar cache (s_load: counted by lgkmcnt, so waits for
+// the vector loads in flight do not depend on it).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4 ldg_uniform(const int4 *p) {
+    const i32x4_t v = *reinterpret_cast<const __attribute__((address_space(4))) i32x4_t *>(
+        reinterpret_cast<uintptr_t>(p));
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
 template <int NKS, int CW>
-__global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a) {
+__global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(PreExpandArgs a) {
     constexpr int R = 16 * NKS;
     constexpr int U = R / 8;                       // 16-byte units per lora_b row (power of two)
     constexpr int LGU = U == 2 ? 1 : U == 4 ? 2 : U == 8 ? 3 : 4;
@@ -628,6 +638,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     constexpr int NFU = kRowTok * (R / 4) / kThreads;
     constexpr int WC = CW / 4;                     // columns per wave
     constexpr int NB = WC / 32;                    // 32-column MFMA blocks per wave
+    // Ranks 32 to 128 take the loop whose every pass issues the same memory
+    // operations (below); rank 16 keeps the one with skipped loads and stores,
+    // which needs fewer registers (165 against 184), so that three
+    // work-groups fit a CU as its grid assumes.
+    constexpr bool kStatic = NKS > 1;
     static_assert((U & (U - 1)) == 0 && U <= 16, "lora_b rows of 2, 4, 8 or 16 units");
     __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * YS];
     __shared__ __attribute__((aligned(16))) char s_b[CW * U * 16];
@@ -653,12 +668,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     auto item_of = [&](int k) { return (int64_t)(lw + min(k, cnt - 1) * nw) * kXcds + xcd; };
     auto tile_of = [&](int k) { return (int)(item_of(k) / a.n_cg); };
     auto cg_of = [&](int k) { return (int)(item_of(k) % a.n_cg); };
-    struct Col { int sg, Ns, n_base; bool ok; };
+    struct Col { int sg, Ns, n_base; };
     auto col_of = [&](int k) {
-        const int cg0 = cg_of(k);
+        const int cg = cg_of(k);
         Col c;
-        c.ok = cg0 < a.n_cg;
-        const int cg = c.ok ? cg0 : a.n_cg - 1;
         c.sg = 0;
         while (c.sg + 1 < a.S && cg >= a.group_start[c.sg + 1]) ++c.sg;
         c.Ns = (int)a.sl.n[c.sg];
@@ -674,7 +687,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         const int ntok = tl.z - tl.y;
         m.item = a.seg.perm[tl.y + min(tid & 63, ntok - 1)];
         const int sl = tl.x / a.gm.Ekey;
-        m.rank = a.slot_rank ? a.slot_rank[sl] : a.R;
+        // through the global address space (a select between slot_rank and
+        // the argument R would make it a FLAT load, which the compiler's
+        // waits treat as unordered: every wait after it would be for zero)
+        const int32_t *rk = a.slot_rank ? a.slot_rank + sl : reinterpret_cast<const int32_t *>(a.scale + sl);
+        const int32_t rv = *reinterpret_cast<const __attribute__((address_space(1))) int32_t *>(
+            reinterpret_cast<uintptr_t>(rk));
+        m.rank = a.slot_rank ? rv : a.R;
         m.sc = a.scale[sl];
         return m;
     };
@@ -695,16 +714,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
         const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
         const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
         const uint16_t *ybase = a.y + a.sl.off[c.sg];
-        // the work-group's load instructions past the tile's tokens are
-        // skipped (a uniform branch; the registers are read only after the
-        // next pass's drain); padding rows inside an instruction read one
-        // 16-byte unit (of the last token row): one request
+        // padding rows read one 16-byte unit of the last token row (its row
+        // in s_yrow): one request per instruction.  At ranks 32 to 128 no
+        // load sits under a branch, so the count of memory operations in
+        // flight is the same on every pass and each wait covers only what it
+        // needs; at rank 16 the work-group's instructions past the tile's
+        // tokens are skipped.
         const int ntk = tl.z - tl.y;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int q = i * kThreads + tid;
             const int col = q / YU < ntk ? min(c.n_base + 8 * (q % YU), c.Ns - 8) : c.n_base;
-            if (i * (kThreads / YU) < ntk)   // the work-group's instruction i holds a token row
+            if (kStatic || i * (kThreads / YU) < ntk)   // rank 16: instruction i holds a token row
                 yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + col);
         }
         // units q < CW * Ue of the block, Ue = 1 << lgu per row; the rest repeat the last
@@ -729,110 +750,223 @@ __global__ __launch_bounds__(kThreads, 2) void k_pre_expand_pipe(PreExpandArgs a
     };
 
     // ---- prologue: items 0, 1, 2 ------------------------------------------
-    int4 tl0 = ldg<int4>(&a.seg.tiles_pre[tile_of(0)]);
-    int4 tl1 = ldg<int4>(&a.seg.tiles_pre[tile_of(1)]);
-    int4 tl2 = ldg<int4>(&a.seg.tiles_pre[tile_of(2)]);
+    int4 tl0 = ldg_uniform(&a.seg.tiles_pre[tile_of(0)]);
+    int4 tl1 = ldg_uniform(&a.seg.tiles_pre[tile_of(1)]);
+    int4 tl2 = ldg_uniform(&a.seg.tiles_pre[tile_of(2)]);
     meta_put(meta_load(tl0), 0);
     Meta m1 = meta_load(tl1);
     Col c0 = col_of(0), c1 = col_of(1);
     __syncthreads();
     data_load(tl0, c0, 0);
 
-    for (int k = 0; k < cnt; ++k) {
-        const int slot = k & 1, nslot = slot ^ 1;
-        const int ntok = tl0.z - tl0.y;
-        const int r = s_rk[slot];
-        const int nks = (r + 15) >> 4;
-        // 1. item k into LDS; item k+1's metadata into its slot
-        {
+    if constexpr (!kStatic) {
+        for (int k = 0; k < cnt; ++k) {
+            const int slot = k & 1, nslot = slot ^ 1;
+            const int ntok = tl0.z - tl0.y;
+            const int r = s_rk[slot];
+            const int nks = (r + 15) >> 4;
+            // 1. item k into LDS; item k+1's metadata into its slot
+            {
 #pragma unroll
-            for (int i = 0; i < NY; ++i) {
-                const int q = i * kThreads + tid;
-                *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
+                for (int i = 0; i < NY; ++i) {
+                    const int q = i * kThreads + tid;
+                    *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
+                }
+                const int lgu = lg_units(r);
+#pragma unroll
+                for (int i = 0; i < NBU; ++i) {
+                    const int q = i * kThreads + tid;
+                    if (q < (CW << lgu))
+                        *reinterpret_cast<uint4 *>(s_b + swz(q >> lgu, q & ((1 << lgu) - 1), U)) = bv[i];
+                }
+#pragma unroll
+                for (int i = 0; i < NFU; ++i) {
+                    const int q = i * kThreads + tid;
+                    const int t = q / (R / 4), j = 4 * (q % (R / 4));
+                    const bool ok = t < ntok;
+                    uint2 o;
+                    o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
+                    o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
+                    *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
+                }
+                meta_put(m1, nslot);
             }
-            const int lgu = lg_units(r);
+            __syncthreads();
+            // 2. loads of item k+1, metadata of item k+2, descriptor of item k+3
+            const float sc = s_sc[slot];
+            const Col ck = c0;
+            if (k + 1 < cnt) data_load(tl1, c1, nslot);   // the last item has none (a reload of it
+                                                          // would fetch its y rows once more)
+            const Meta m2 = meta_load(tl2);
+            const int4 tl3 = ldg<int4>(&a.seg.tiles_pre[tile_of(k + 3)]);
+            // 3. D[n][t] for item k over its slot's rank steps, added into the y tile
+            {
+                floatx16_t acc[NB][2];
 #pragma unroll
-            for (int i = 0; i < NBU; ++i) {
-                const int q = i * kThreads + tid;
-                if (q < (CW << lgu))
-                    *reinterpret_cast<uint4 *>(s_b + swz(q >> lgu, q & ((1 << lgu) - 1), U)) = bv[i];
-            }
+                for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = floatx16_t{};
 #pragma unroll
-            for (int i = 0; i < NFU; ++i) {
-                const int q = i * kThreads + tid;
-                const int t = q / (R / 4), j = 4 * (q % (R / 4));
-                const bool ok = t < ntok;
-                uint2 o;
-                o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
-                o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
-                *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
-            }
-            meta_put(m1, nslot);
-        }
-        __syncthreads();
-        // 2. loads of item k+1, metadata of item k+2, descriptor of item k+3
-        const float sc = s_sc[slot];
-        const Col ck = c0;
-        if (k + 1 < cnt) data_load(tl1, c1, nslot);   // the last item has none (a reload of it
-                                                      // would fetch its y rows once more)
-        const Meta m2 = meta_load(tl2);
-        const int4 tl3 = ldg<int4>(&a.seg.tiles_pre[tile_of(k + 3)]);
-        // 3. D[n][t] for item k over its slot's rank steps, added into the y tile
-        if (ck.ok) {
-            floatx16_t acc[NB][2];
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if (ks < nks) {
+                        const int u = 2 * ks + half;
+                        uint4 bfr[2];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = floatx16_t{};
+                        for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                if (ks < nks) {
-                    const int u = 2 * ks + half;
-                    uint4 bfr[2];
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(WC * w + 32 * nb + l32, u, U));
 #pragma unroll
-                    for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
+                            for (int tb = 0; tb < 2; ++tb)
+                                acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                        }
+                    }
+                }
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(WC * w + 32 * nb + l32, u, U));
+                for (int tb = 0; tb < 2; ++tb) {
+                    const int t = 32 * tb + l32;
+                    if (t < ntok) {
 #pragma unroll
-                        for (int tb = 0; tb < 2; ++tb)
-                            acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * YS + WC * w + 32 * nb + 8 * g + 4 * half]);
+                                const uint2 y0 = *yp;
+                                uint2 o;
+                                o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + sc * acc[nb][tb][4 * g + 1]);
+                                o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[nb][tb][4 * g + 2], bf16_hi(y0.y) + sc * acc[nb][tb][4 * g + 3]);
+                                *yp = o;
+                            }
                     }
                 }
             }
+            __syncthreads();
+            // 4. item k back to y, row by row
+            {
+                uint16_t *ybase = a.y + a.sl.off[ck.sg];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int t = 32 * tb + l32;
-                if (t < ntok) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * YS + WC * w + 32 * nb + 8 * g + 4 * half]);
-                            const uint2 y0 = *yp;
-                            uint2 o;
-                            o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + sc * acc[nb][tb][4 * g + 1]);
-                            o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[nb][tb][4 * g + 2], bf16_hi(y0.y) + sc * acc[nb][tb][4 * g + 3]);
-                            *yp = o;
-                        }
+                for (int i = 0; i < NY; ++i) {
+                    const int q = i * kThreads + tid;
+                    const int row = q / YU, col = ck.n_base + 8 * (q % YU);
+                    if (row < ntok && col < ck.Ns)
+                        stg_nt(ybase + s_yrow[slot][row] * a.ldy + col,
+                               *reinterpret_cast<const uint4 *>(&s_y[row * YS + 8 * (q % YU)]));
                 }
             }
+            __syncthreads();
+            tl0 = tl1; tl1 = tl2; tl2 = tl3;
+            m1 = m2;
+            c0 = c1; c1 = col_of(k + 2);
         }
-        __syncthreads();
-        // 4. item k back to y, row by row
-        if (ck.ok) {
-            uint16_t *ybase = a.y + a.sl.off[ck.sg];
+    } else {
+        // One item (k): the last has no prefetch; every other pass issues the
+        // same memory operations, so the wait at its head is for item k's data only.
+        auto item = [&](int k, auto prefetch) {
+            constexpr bool kPrefetch = decltype(prefetch)::value;
+            const int slot = k & 1, nslot = slot ^ 1;
+            // descriptor of item k+3 through the scalar cache, issued before the
+            // wait for item k's data
+            const int4 tl3 = ldg_uniform(&a.seg.tiles_pre[tile_of(k + 3)]);
+            const int ntok = tl0.z - tl0.y;
+            const int r = s_rk[slot];
+            const int nks = (r + 15) >> 4;
+            // 1. item k into LDS; item k+1's metadata into its slot
+            {
 #pragma unroll
-            for (int i = 0; i < NY; ++i) {
-                const int q = i * kThreads + tid;
-                const int row = q / YU, col = ck.n_base + 8 * (q % YU);
-                if (row < ntok && col < ck.Ns)
-                    stg_nt(ybase + s_yrow[slot][row] * a.ldy + col,
-                           *reinterpret_cast<const uint4 *>(&s_y[row * YS + 8 * (q % YU)]));
+                for (int i = 0; i < NY; ++i) {
+                    const int q = i * kThreads + tid;
+                    *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
+                }
+                const int lgu = lg_units(r);
+#pragma unroll
+                for (int i = 0; i < NBU; ++i) {
+                    const int q = i * kThreads + tid;
+                    if (q < (CW << lgu))
+                        *reinterpret_cast<uint4 *>(s_b + swz(q >> lgu, q & ((1 << lgu) - 1), U)) = bv[i];
+                }
+#pragma unroll
+                for (int i = 0; i < NFU; ++i) {
+                    const int q = i * kThreads + tid;
+                    const int t = q / (R / 4), j = 4 * (q % (R / 4));
+                    const bool ok = t < ntok;
+                    uint2 o;
+                    o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
+                    o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
+                    *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
+                }
+                meta_put(m1, nslot);
             }
+            __syncthreads();
+            // 2. loads of item k+1, metadata of item k+2
+            const float sc = s_sc[slot];
+            const Col ck = c0;
+            if constexpr (kPrefetch) data_load(tl1, c1, nslot);   // the last item has none
+            const Meta m2 = meta_load(tl2);
+            // 3. D[n][t] for item k over its slot's rank steps, added into the y tile
+            {
+                floatx16_t acc[NB][2];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = floatx16_t{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if (ks < nks) {
+                        const int u = 2 * ks + half;
+                        uint4 bfr[2];
+#pragma unroll
+                        for (int tb = 0; tb < 2; ++tb) bfr[tb] = *reinterpret_cast<const uint4 *>(s_buf + swz(32 * tb + l32, u, U));
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const uint4 af = *reinterpret_cast<const uint4 *>(s_b + swz(WC * w + 32 * nb + l32, u, U));
+#pragma unroll
+                            for (int tb = 0; tb < 2; ++tb)
+                                acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af), as_frag(bfr[tb]), acc[nb][tb], 0, 0, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const int t = 32 * tb + l32;
+                    if (t < ntok) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                uint2 *yp = reinterpret_cast<uint2 *>(&s_y[t * YS + WC * w + 32 * nb + 8 * g + 4 * half]);
+                                const uint2 y0 = *yp;
+                                uint2 o;
+                                o.x = pack_bf16x2(bf16_lo(y0.x) + sc * acc[nb][tb][4 * g + 0], bf16_hi(y0.x) + sc * acc[nb][tb][4 * g + 1]);
+                                o.y = pack_bf16x2(bf16_lo(y0.y) + sc * acc[nb][tb][4 * g + 2], bf16_hi(y0.y) + sc * acc[nb][tb][4 * g + 3]);
+                                *yp = o;
+                            }
+                    }
+                }
+            }
+            __syncthreads();
+            // 4. item k back to y, row by row.  Every lane stores: rows past the
+            // tile's tokens and columns past the slice store the last token row's
+            // (or the last column unit's) final value again, the same bytes to the
+            // same place, so no store sits under a branch.
+            {
+                uint16_t *ybase = a.y + a.sl.off[ck.sg];
+#pragma unroll
+                for (int i = 0; i < NY; ++i) {
+                    const int q = i * kThreads + tid;
+                    const int row = min(q / YU, ntok - 1);
+                    const int cu = min(8 * (q % YU), ck.Ns - 8 - ck.n_base);
+                    stg_nt(ybase + s_yrow[slot][row] * a.ldy + ck.n_base + cu,
+                           *reinterpret_cast<const uint4 *>(&s_y[row * YS + cu]));
+                }
+            }
+            __syncthreads();
+            tl0 = tl1; tl1 = tl2; tl2 = tl3;
+            m1 = m2;
+            c0 = c1; c1 = col_of(k + 2);
+        };
+        // the first item is peeled too, so that the loop is entered with the
+        // same operations in flight as its back edge carries
+        if (cnt > 1) {
+            item(0, std::true_type{});
+            for (int k = 1; k + 1 < cnt; ++k) item(k, std::true_type{});
         }
-        __syncthreads();
-        tl0 = tl1; tl1 = tl2; tl2 = tl3;
-        m1 = m2;
-        c0 = c1; c1 = col_of(k + 2);
+        item(cnt - 1, std::false_type{});
     }
 }
 
