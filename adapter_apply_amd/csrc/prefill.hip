@@ -714,18 +714,22 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
         const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
         const int64_t grp = (int64_t)s * a.gm.Ew + (a.gm.Ew == 1 ? 0 : e);
         const uint16_t *ybase = a.y + a.sl.off[c.sg];
-        // padding rows read one 16-byte unit of the last token row (its row
-        // in s_yrow): one request per instruction.  At ranks 32 to 128 no
-        // load sits under a branch, so the count of memory operations in
-        // flight is the same on every pass and each wait covers only what it
-        // needs; at rank 16 the work-group's instructions past the tile's
-        // tokens are skipped.
+        // At ranks 32 to 128 each load is masked per lane to the units that
+        // exist (token rows of the tile, units of the slot's rank, buffer
+        // entries below it): an instruction with no lane left is skipped, the
+        // others address only their useful lanes (the texture addresser's
+        // time per instruction goes with its lanes: 20 full instructions per
+        // item were most of an item's time), and the compiler still counts
+        // every load, so each wait covers only what it needs.  Lanes left out
+        // keep stale registers that nothing reads.  At rank 16 the
+        // work-group's y instructions past the tile's tokens are skipped and
+        // padding rows read one 16-byte unit of the last token row.
         const int ntk = tl.z - tl.y;
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const int q = i * kThreads + tid;
             const int col = q / YU < ntk ? min(c.n_base + 8 * (q % YU), c.Ns - 8) : c.n_base;
-            if (kStatic || i * (kThreads / YU) < ntk)   // rank 16: instruction i holds a token row
+            if (kStatic ? q / YU < ntk : i * (kThreads / YU) < ntk)   // rank 16: instruction i holds a token row
                 yv[i] = ldg_nt(ybase + s_yrow[slot][q / YU] * a.ldy + col);
         }
         // units q < CW * Ue of the block, Ue = 1 << lgu per row; the rest repeat the last
@@ -736,7 +740,8 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
         for (int i = 0; i < NBU; ++i) {
             const int q = min(i * kThreads + tid, last);
             const int n = min(c.n_base + (q >> lgu), c.Ns - 1);
-            bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + (q & ((1 << lgu) - 1))) * 16));
+            if (!kStatic || i * kThreads + tid <= last)
+                bv[i] = ldg<uint4>(reinterpret_cast<const uint4 *>(bblk + ((int64_t)n * U + (q & ((1 << lgu) - 1))) * 16));
         }
         // buffer rows: entries j >= r are dropped, so their loads repeat the
         // last needed float4 of the row (no extra cache lines)
@@ -745,7 +750,8 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
         for (int i = 0; i < NFU; ++i) {
             const int q = i * kThreads + tid;
             const int t = q / (R / 4), j = 4 * (q % (R / 4));
-            fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_sstride + s_brow[slot][t]) * R + min(j, jmax));
+            if (!kStatic || (t < ntk && j <= jmax))
+                fv[i] = ldg<float4>(a.buf + ((int64_t)c.sg * a.gm.buf_sstride + s_brow[slot][t]) * R + min(j, jmax));
         }
     };
 
