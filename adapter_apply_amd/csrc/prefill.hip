@@ -707,8 +707,15 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
             s_sc[slot] = m.sc;
         }
     };
+    // (zero at the start: lanes whose loads are masked off keep them)
     uint4 yv[NY], bv[NBU];
     float4 fv[NFU];
+#pragma unroll
+    for (int i = 0; i < NY; ++i) yv[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < NBU; ++i) bv[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < NFU; ++i) fv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     // data loads of item k (its metadata in LDS slot k & 1)
     auto data_load = [&](const int4 &tl, const Col &c, int slot) {
         const int s = tl.x / a.gm.Ekey, e = tl.x - s * a.gm.Ekey;
