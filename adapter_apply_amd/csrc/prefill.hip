@@ -643,6 +643,7 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
     // which needs fewer registers (165 against 184), so that three
     // work-groups fit a CU as its grid assumes.
     constexpr bool kStatic = NKS > 1;
+    constexpr bool kPutLive = NKS >= 8;
     static_assert((U & (U - 1)) == 0 && U <= 16, "lora_b rows of 2, 4, 8 or 16 units");
     __shared__ __attribute__((aligned(16))) uint16_t s_y[kRowTok * YS];
     __shared__ __attribute__((aligned(16))) char s_b[CW * U * 16];
@@ -883,10 +884,18 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
             const int nks = (r + 15) >> 4;
             // 1. item k into LDS; item k+1's metadata into its slot
             {
+                // at rank 128 only the rows and rank entries that are read: the
+                // tile's token rows (the y tile's others are never stored back,
+                // and the buffer's only reach discarded products) and the
+                // buffer entries of the slot's rank steps (zero past r); the
+                // LDS writes of a tile of a few tokens were a sixth of an item's
+                // time in batches of many slots (at lower ranks the masks cost
+                // more than they save)
 #pragma unroll
                 for (int i = 0; i < NY; ++i) {
                     const int q = i * kThreads + tid;
-                    *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
+                    if (!kPutLive || q / YU < ntok)
+                        *reinterpret_cast<uint4 *>(&s_y[(q / YU) * YS + 8 * (q % YU)]) = yv[i];
                 }
                 const int lgu = lg_units(r);
 #pragma unroll
@@ -899,11 +908,12 @@ __global__ __launch_bounds__(kThreads, NKS == 1 ? 3 : 2) void k_pre_expand_pipe(
                 for (int i = 0; i < NFU; ++i) {
                     const int q = i * kThreads + tid;
                     const int t = q / (R / 4), j = 4 * (q % (R / 4));
-                    const bool ok = t < ntok;
+                    const bool ok = kPutLive || t < ntok;
                     uint2 o;
                     o.x = pack_bf16x2(ok && j < r ? fv[i].x : 0.f, ok && j + 1 < r ? fv[i].y : 0.f);
                     o.y = pack_bf16x2(ok && j + 2 < r ? fv[i].z : 0.f, ok && j + 3 < r ? fv[i].w : 0.f);
-                    *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
+                    if (!kPutLive || (t < ntok && j < 16 * nks))
+                        *reinterpret_cast<uint2 *>(s_buf + swz(t, j >> 3, U) + ((j & 4) << 1)) = o;
                 }
                 meta_put(m1, nslot);
             }
