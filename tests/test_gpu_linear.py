@@ -269,6 +269,33 @@ def test_many_adapter_config(oracle_mod, path):
     assert canaries_intact(d.yfull)
 
 
+def test_many_adapter_shape_integer_bit_exact(oracle_mod):
+    """Integer vectors at exactly the many-adapter workload's shape (1024
+    tokens, 128 slots with Zipf(1.1) popularity and its slot ranks {8..128}
+    padded to 128, hidden and output 8192) on auto and PREFILL, which take the
+    tile kernels: the shrink split over K and its ordered reduce, and the
+    rank-128 persistent expand with its loads masked to the rows and rank
+    units that exist and its LDS writes limited to them.  Every output bit
+    for bit."""
+    m = synth.config_many()
+    c = synth.make_integer_linear(m.T, m.K, m.N, m.R, m.L, seed=1010, idx=m.idx,
+                                  slot_rank=m.slot_rank)
+    del m
+    ref = oracle_par.lora_apply(oracle_mod, c.y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
+    exact = bounds.linear_exact_int_by_slot(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.array_equal(ref, exact.astype(np.float32))
+    for path in (aa.LORA_PATH_AUTO, PRE):
+        d = LinearOnDevice(c)
+        taken = aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+        log(f"case many-adapter-shape integer path={aa.PATH_NAMES[path]}")
+        assert taken == PRE, aa.PATH_NAMES[taken]
+        d.apply(path)
+        y = d.y_host()
+        assert canaries_intact(d.yfull)
+        bad = np.argwhere(y != ref)
+        assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:4].tolist()}"
+
+
 def test_many_adapter_separate_calls_auto(oracle_mod):
     """lora_shrink then lora_expand on auto, apart, for the many-slot batch:
     both take the tile kernels and exchange the token-ordered buffer."""
