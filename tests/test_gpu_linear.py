@@ -707,6 +707,31 @@ def test_relay_wide_items_bit_exact(oracle_mod, seed, T, K, N, R, L, shared, aut
         assert int(torch.count_nonzero(d.ws)) == 0
 
 
+def test_relay_largest_shape_bit_exact(oracle_mod):
+    """The largest call the K-split single launch takes: 1024 tokens, K = 8192
+    (32 K chunks), rank 32, and a 257024-column vocabulary (the widest the
+    logits layer lists), 8 slots; integer vectors on RELAY and on auto (which
+    takes it), every output bit for bit, the workspace zero afterwards."""
+    T, K, N, R, L = 1024, 8192, [257024], 32, 8
+    c = synth.make_integer_linear(T, K, N, R, L, seed=91, dtype="bf16")
+    ref = oracle_par.lora_apply(oracle_mod, c.y0, c.x, c.A, c.B, c.idx, c.slot_rank, c.scale)
+    exact = bounds.linear_exact_int_by_slot(c.x, c.A, c.B, c.idx, c.slot_rank, c.scale, c.y0)
+    assert np.array_equal(ref, exact.astype(np.float32))
+    del exact
+    for path in (aa.LORA_PATH_AUTO, RLY):
+        d = LinearOnDevice(c)
+        taken = aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+        log(f"case relay largest shape path={aa.PATH_NAMES[path]}")
+        assert taken == RLY, aa.PATH_NAMES[taken]
+        d.apply(path)
+        y = d.y_host()
+        assert canaries_intact(d.yfull)
+        bad = np.argwhere(y != ref)
+        assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:4].tolist()}"
+        assert int(torch.count_nonzero(d.ws)) == 0
+        del d, y
+
+
 def test_zero_tokens_noop():
     c = synth.config_decode(T=8)
     d = LinearOnDevice(c)
