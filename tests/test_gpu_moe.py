@@ -122,6 +122,8 @@ def integer_moe(seed, T, k, E, K, I, R, L, shared, p_none=0.1, full_rank=False,
     (4, 300, 4, 64, 128, 64, 16, 16),     # L * E = 1024 keys
     (5, 40, 4, 8, 2048, 1024, 16, 3),     # small batch, long K: the shrinks split over K
     (6, 30, 2, 4, 256, 128, 512, 2),      # the largest rank the library takes
+    (7, 128, 8, 16, 256, 96, 16, 4),      # 1024 pairs: the most the unaligned path takes
+    (8, 129, 8, 16, 256, 96, 16, 4),      # 1032 pairs: aligned only
 ])
 def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L):
     d = integer_moe(seed, T, k, E, K, I, R, L, shared)
@@ -129,6 +131,7 @@ def test_integer_vectors_bit_exact(oracle_mod, shared, seed, T, k, E, K, I, R, L
                                       d["idx"], d["rank"], d["scale"], E)
     ref2 = oracle_mod.moe_lora_apply(1, d["o0"], d["h"], [d["A2"]], [d["B2"]], d["ids"], d["w"],
                                      d["idx"], d["rank"], d["scale"], E)
+    assert aa.moe_lora_plan(T, k, R) == (T * k <= 1024 and R == 16)
     # both paths where a call is small enough for the one without alignment
     for align in ((False, True) if aa.moe_lora_plan(T, k, R) else (False,)):
         log(f"case moe integer shared={shared} T={T} k={k} E={E} L={L} align={align}")
