@@ -888,3 +888,27 @@ def test_shared_lora_a_decode_config_repeated(oracle_mod, path):
         else:
             assert np.array_equal(y.view(np.uint32), first.view(np.uint32))
     assert canaries_intact(d.yfull)
+
+
+@pytest.mark.parametrize("nbytes", [0, 1, 15, 16, 17, 4096 + 7, (1 << 20) + 3, (70 << 20) + 13])
+def test_workspace_init_exact_range(nbytes):
+    """lora_workspace_init zero-fills exactly ws_bytes bytes from a 256-byte
+    aligned start, whole 16-byte units and a ragged tail alike, and leaves
+    the bytes past the end as they were."""
+    log(f"case workspace init bytes={nbytes}")
+    pad = 4096
+    raw = torch.empty(nbytes + pad + 256, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    buf = raw[off:off + nbytes + pad]
+    buf.fill_(0xAB)
+    rc = aa.lib().lora_workspace_init(aa.C.c_void_p(buf.data_ptr()), nbytes, None)
+    torch.cuda.synchronize()
+    assert rc == aa.LORA_OK
+    assert int(torch.count_nonzero(buf[:nbytes])) == 0
+    assert bool(torch.all(buf[nbytes:] == 0xAB))
+    if nbytes:
+        # a start that is not 256-byte aligned is refused before any launch
+        rc = aa.lib().lora_workspace_init(aa.C.c_void_p(buf.data_ptr() + 16), nbytes, None)
+        assert rc == aa.LORA_E_ALIGN
+        torch.cuda.synchronize()
+        assert bool(torch.all(buf[nbytes:] == 0xAB))
