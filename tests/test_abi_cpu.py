@@ -232,6 +232,18 @@ def test_moe_apply_rejects_bad_arguments(kw, code):
 def test_moe_sizes_and_align_validation():
     n = aa.moe_lora_workspace_size(2048, 8, 2, 16, 8, 64)
     assert n > 2048 * 8 * 16 * 2 * 4
+    assert aa.moe_lora_workspace_size(4096, 8, 2, 16, 8, 64) > n      # more tokens
+    assert aa.moe_lora_workspace_size(2048, 8, 2, 32, 8, 64) > n      # higher rank
+    assert aa.moe_lora_workspace_size(2048, 8, 3, 16, 8, 64) > n      # more slices
+    out = aa.C.c_size_t(0)
+    size = aa.lib().moe_lora_workspace_size
+    assert size(16, 2, 0, 16, 4, 4, aa.C.byref(out)) == aa.LORA_E_SLICES
+    assert size(16, 2, 9, 16, 4, 4, aa.C.byref(out)) == aa.LORA_E_SLICES
+    assert size(16, 2, 1, 16, 41, 25, aa.C.byref(out)) == aa.LORA_E_SHAPE   # 1025 slot-expert keys
+    assert size(16, 2, 1, 0, 4, 4, aa.C.byref(out)) == aa.LORA_E_RANK
+    assert size(-1, 2, 1, 16, 4, 4, aa.C.byref(out)) == aa.LORA_E_SHAPE
+    assert size(16, 2, 1, 16, 4, 4, None) == aa.LORA_E_NULL
+    assert size(0, 2, 1, 16, 4, 4, aa.C.byref(out)) == aa.LORA_OK
     assert aa.moe_lora_align_capacity(2, 2, 2, 4) == 12
     assert aa.moe_lora_align_capacity(2, 2, 2, 2) == 6
     lib = aa.lib()
