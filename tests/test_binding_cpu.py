@@ -2,6 +2,7 @@
 ValueError before it calls into the library (CPU tensors: the dtype and
 shape checks run before the device check, and a well-formed call on CPU
 tensors is refused for its device)."""
+import os
 import pytest
 import torch
 
@@ -154,3 +155,16 @@ def test_moe_align_rejects():
         aa.moe_lora_align(ids, idx, None, E, L, R, 16, ws, torch.zeros(L, cap, dtype=I32))
     with pytest.raises(ValueError, match="GPU"):
         aa.moe_lora_align(ids, idx, None, E, L, R, 16, ws)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU only: --gpus above 1 exits with status 2 and a
+    message, before anything touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
