@@ -1,7 +1,7 @@
 """The Python binding rejects tensors of the wrong dtype, shape or device with
 ValueError before it calls into the library (CPU tensors: the dtype and
 shape checks run before the device check, and a well-formed call on CPU
-tensors is refused for its device)."""
+tensors is refused for its device); bench.py refuses a multi-GPU run."""
 import os
 import pytest
 import torch
