@@ -912,3 +912,29 @@ def test_workspace_init_exact_range(nbytes):
         assert rc == aa.LORA_E_ALIGN
         torch.cuda.synchronize()
         assert bool(torch.all(buf[nbytes:] == 0xAB))
+
+
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK])
+def test_side_stream_equals_default_stream(oracle_mod, path):
+    """A call on a stream of its own (the stream argument, with the default
+    stream current) gives the same bits as the call on the default stream:
+    every launch of the call, fills included, goes to the stream it is given."""
+    c = synth.config_decode()
+    d = LinearOnDevice(c, guard=False)
+    try:
+        aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+    except aa.LoraError:
+        pytest.skip("the path does not take this shape")
+    log(f"case side stream path={path}")
+    d.apply(path)
+    want = d.y_host()
+    bounds.check_bf16_tolerance(want, oracle_y(oracle_mod, c))
+    s = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for rnd in range(3):
+        d.reset_y()
+        s.wait_stream(main)
+        aa.lora_apply_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path, stream=s)
+        main.wait_stream(s)
+        got = d.y_host()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), rnd
