@@ -368,3 +368,44 @@ def test_moe_passthrough_and_zero_b(oracle_mod):
     Bz = [np.zeros_like(b) for b in c.B13]
     y = run_moe(W13, c.gate_up0, c.x, c.A13, Bz, c.topk_ids, None, c.idx, c.slot_rank, c.scale, c.E)
     assert np.array_equal(y.view(np.uint32), c.gate_up0.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,align", [(64, False), (64, True), (2048, True)])
+def test_side_stream_equals_default_stream(T, align):
+    """The fused-MoE calls (the alignment, w13 and w2) on a stream of their own,
+    with the default stream current, give the same bits as on the default
+    stream, without alignment and with it."""
+    c = synth.config_moe(T=T)
+    ids, idx, rank, scale = dev(c.topk_ids), dev(c.idx), dev(c.slot_rank), dev(c.scale)
+    tw = dev(c.topk_w)
+    x, h = dev(c.x, BF), dev(c.h, BF)
+    A13, B13 = [dev(a, BF) for a in c.A13], [dev(b, BF) for b in c.B13]
+    A2, B2 = [dev(c.A2, BF)], [dev(c.B2, BF)]
+    L, R = c.A13[0].shape[0], c.A13[0].shape[2]
+    ws = aa.alloc_moe_workspace(T, c.k, 2, R, L, c.E)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def call(stream):
+        g, o = dev(c.gate_up0, BF), dev(c.out0, BF)
+        flags = 0
+        if stream is not None:
+            stream.wait_stream(main)
+        if align:
+            aa.moe_lora_align(ids, idx, rank, c.E, L, R, 16, ws, stream=stream)
+            flags = aa.LORA_FLAG_SEGMENTS_READY
+        aa.moe_lora_apply(W13, g, x, A13, B13, ids, None, idx, rank, scale, c.E, ws, flags=flags,
+                          stream=stream)
+        aa.moe_lora_apply(W2, o, h, A2, B2, ids, tw, idx, rank, scale, c.E, ws, flags=flags,
+                          stream=stream)
+        if stream is not None:
+            main.wait_stream(stream)
+        torch.cuda.synchronize()
+        return host_f32(g), host_f32(o)
+
+    log(f"case moe side stream T={T} align={align}")
+    want = call(None)
+    for rnd in range(2):
+        got = call(side)
+        for w_, g_ in zip(want, got):
+            assert np.array_equal(g_.view(np.uint32), w_.view(np.uint32)), rnd
