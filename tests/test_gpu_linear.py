@@ -938,3 +938,39 @@ def test_side_stream_equals_default_stream(oracle_mod, path):
         main.wait_stream(s)
         got = d.y_host()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), rnd
+
+
+def strided_rows(t, lead, tail):
+    """The same values as the 2-D tensor t, as a column window of a wider
+    tensor (row stride K + lead + tail) whose other columns hold large values
+    that would show in y if a kernel read them."""
+    T, K = t.shape
+    wide = torch.full((T, lead + K + tail), 1024.0, dtype=t.dtype, device=t.device)
+    wide[:, lead:lead + K] = t
+    return wide[:, lead:lead + K]
+
+
+@pytest.mark.parametrize("cfg", ["decode", "prefill_small"])
+@pytest.mark.parametrize("path", [aa.LORA_PATH_AUTO, DEC, PRE, FUS, GRP, RLY, TOK])
+def test_x_row_stride_wider_than_k(oracle_mod, cfg, path):
+    """x given as a window of wider rows (ldx = K + 72, starting 16 columns in)
+    gives the same bits as a contiguous x on every path that takes the shape."""
+    if cfg == "decode":
+        c = synth.config_decode()
+    else:
+        c = synth.config_prefill(seed=91, n_seq=5, total=700, K=1024, Nslice=512, R=64, L=6)
+    d = LinearOnDevice(c, guard=False)
+    try:
+        aa.lora_plan_packed(d.y, d.x, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+    except aa.LoraError:
+        pytest.skip("the path does not take this shape")
+    log(f"case x row stride cfg={cfg} path={path}")
+    d.apply(path)
+    want = d.y_host()
+    bounds.check_bf16_tolerance(want, oracle_y(oracle_mod, c))
+    xs = strided_rows(d.x, 16, 56)
+    assert xs.stride(0) == c.x.shape[1] + 72
+    d.reset_y()
+    aa.lora_apply_packed(d.y, xs, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
+    got = d.y_host()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
