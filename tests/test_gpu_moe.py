@@ -409,3 +409,41 @@ def test_side_stream_equals_default_stream(T, align):
         got = call(side)
         for w_, g_ in zip(want, got):
             assert np.array_equal(g_.view(np.uint32), w_.view(np.uint32)), rnd
+
+
+def window(t, lead, tail, fill):
+    """t's values as a column window of wider rows (the other columns = fill)."""
+    T, K = t.shape
+    wide = torch.full((T, lead + K + tail), fill, dtype=t.dtype, device=t.device)
+    wide[:, lead:lead + K] = t
+    return wide, wide[:, lead:lead + K]
+
+
+@pytest.mark.parametrize("T,align", [(64, False), (64, True), (512, True)])
+def test_row_strides_wider_than_rows(T, align):
+    """x / h and y given as windows of wider rows (row strides past K and N,
+    starting 16 columns in) give the bits of contiguous tensors, and the
+    columns outside the windows keep their values."""
+    c = synth.config_moe(T=T)
+    args13 = (c.gate_up0, c.x, c.A13, c.B13, None)
+    args2 = (c.out0, c.h, [c.A2], [c.B2], c.topk_w)
+    for kind, (y0, xin, A, B, tw) in ((W13, args13), (W2, args2)):
+        log(f"case moe row strides T={T} align={align} kind={kind}")
+        L, _, R, _ = A[0].shape
+        want = run_moe(kind, y0, xin, A, B, c.topk_ids, tw, c.idx, c.slot_rank, c.scale, c.E,
+                       align=align, guard=False)
+        ws = aa.alloc_moe_workspace(T, c.k, len(A), R, L, c.E)
+        flags = 0
+        if align:
+            aa.moe_lora_align(dev(c.topk_ids), dev(c.idx), dev(c.slot_rank), c.E, L, R, 16, ws)
+            flags = aa.LORA_FLAG_SEGMENTS_READY
+        _, xs = window(dev(xin, BF), 16, 48, 1024.0)
+        ywide, ys = window(dev(y0, BF), 16, 16, -7.0)
+        aa.moe_lora_apply(kind, ys, xs, [dev(a, BF) for a in A], [dev(b, BF) for b in B],
+                          dev(c.topk_ids), None if tw is None else dev(tw), dev(c.idx),
+                          dev(c.slot_rank), dev(c.scale), c.E, ws, flags=flags)
+        torch.cuda.synchronize()
+        got = host_f32(ys)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        outside = torch.cat([ywide[:, :16], ywide[:, 16 + ys.shape[1]:]], dim=1)
+        assert bool(torch.all(outside == -7.0))
