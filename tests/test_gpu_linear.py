@@ -974,3 +974,21 @@ def test_x_row_stride_wider_than_k(oracle_mod, cfg, path):
     aa.lora_apply_packed(d.y, xs, d.A, d.B, d.idx, d.rank, d.scale, d.ws, path=path)
     got = d.y_host()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("path", [DEC, PRE, GRP])
+def test_shrink_x_row_stride(path):
+    """lora_shrink with x as a window of wider rows (ldx = K + 72) writes the
+    buffer bits of a contiguous x."""
+    c = synth.make_linear("sh_stride", 300, 1024, [256, 128], 32, 5,
+                          idx=np.random.default_rng(4).integers(-1, 6, 300),
+                          slot_rank=[32, 8, 0, 16, 24], scale=[1, 1, 1, 1, 1], dtype="bf16",
+                          seed=32)
+    log(f"case shrink x stride path={path}")
+    d = LinearOnDevice(c, guard=False)
+    want = torch.zeros((c.S, c.T, c.R), dtype=torch.float32, device="cuda")
+    got = torch.full_like(want, 123.0)
+    aa.lora_shrink(want, d.x, d.A, d.idx, d.rank, d.ws, path=path)
+    aa.lora_shrink(got, strided_rows(d.x, 16, 56), d.A, d.idx, d.rank, d.ws, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
